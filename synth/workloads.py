@@ -1,0 +1,326 @@
+"""Seeded synthetic workloads shaped like the settings the pages describe.
+
+No dataset, checkpoint or benchmark item is used or reproduced: every tensor is
+drawn from a seeded generator and given planted structure of the kind the
+pages talk about (retrievable "needle" blocks, topic blocks, a local window),
+so that block selection and threshold skipping have something real to find.
+
+Recipe shared by every workload
+-------------------------------
+* Each (tensor, head) pair draws from its own PCG64 stream seeded with
+  ``SeedSequence([seed, tensor_code, head])``; any subset of heads can be
+  regenerated alone, and the draw order inside one stream is fixed.
+* Base values are N(0, 1) drawn in float32.  RoPE (when the workload uses it)
+  is applied in float64 with base 10000; planted structure is added after RoPE
+  so it stays visible at every distance.
+* Values are rounded once at the end: float64 -> float32 (round to nearest
+  even) -> bfloat16 (round to nearest even).  bf16 tensors are stored as their
+  raw uint16 bit patterns.  The oracle reads exactly these stored values.
+* Layout is [B, H, L, D] with the last dimension contiguous (B = 1).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+ROPE_HALF = 0          # FC i pairs dims (i, i + D/2)
+ROPE_INTERLEAVED = 1   # FC i pairs dims (2i, 2i + 1)
+ROPE_BASE = 10000.0
+
+# tensor codes for the per-(tensor, head) seed streams
+_Q, _K, _V = 1, 2, 3
+
+
+def _rng(seed: int, *keys: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *keys])))
+
+
+# ---------------------------------------------------------------- rounding ---
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest even); return uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 view of stored values (bf16 bit patterns or float32)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = np.asarray(x64, dtype=np.float32)
+    return f32_to_bf16_bits(x32) if dtype == "bf16" else x32
+
+
+# -------------------------------------------------------------------- RoPE ---
+def rope(x: np.ndarray, pos: np.ndarray, layout: int = ROPE_HALF, base: float = ROPE_BASE) -> np.ndarray:
+    """Rotate x[..., L, D] by RoPE at absolute positions pos[L] (float64).
+
+    Frequency chunk i in [0, D/2) turns at theta_i = base^(-2i/D); low FC index
+    means fast rotation.  This is data preparation: the library consumes
+    already-rotated vectors and never applies RoPE itself.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    half = D // 2
+    theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / D)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * theta[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty_like(x)
+    if layout == ROPE_HALF:
+        a, b = x[..., :half], x[..., half:]
+        out[..., :half] = a * c - b * s
+        out[..., half:] = b * c + a * s
+    elif layout == ROPE_INTERLEAVED:
+        a, b = x[..., 0::2], x[..., 1::2]
+        out[..., 0::2] = a * c - b * s
+        out[..., 1::2] = b * c + a * s
+    else:
+        raise ValueError(layout)
+    return out
+
+
+def hi_band_dims(D: int, layout: int) -> np.ndarray:
+    """Dims of the fast-rotating half of the frequency chunks (FC i < D/4)."""
+    fc = np.arange(D // 4)
+    if layout == ROPE_HALF:
+        return np.concatenate([fc, fc + D // 2])
+    return np.stack([2 * fc, 2 * fc + 1], axis=1).reshape(-1)
+
+
+def lo_band_dims(D: int, layout: int) -> np.ndarray:
+    return np.setdiff1d(np.arange(D), hi_band_dims(D, layout))
+
+
+def _normal(seed: int, code: int, head: int, shape) -> np.ndarray:
+    return _rng(seed, code, head).standard_normal(shape, dtype=np.float32).astype(np.float64)
+
+
+def _unit(rng: np.random.Generator, n: int, D: int, dims: np.ndarray | None = None) -> np.ndarray:
+    v = np.zeros((n, D))
+    d = np.arange(D) if dims is None else dims
+    w = rng.standard_normal((n, len(d)))
+    v[:, d] = w / np.linalg.norm(w, axis=1, keepdims=True)
+    return v
+
+
+# --------------------------------------------------------------- workload ---
+@dataclass
+class Workload:
+    name: str
+    dtype: str            # storage dtype of q, k, v: "bf16" (uint16 bits) or "f32"
+    q: np.ndarray         # [1, Hq, Lq, D]
+    k: np.ndarray         # [1, Hkv, L, D]
+    v: np.ndarray         # [1, Hkv, L, D]
+    params: dict          # method parameters (block sizes, budgets, flags)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def shape(self):
+        _, Hq, Lq, D = self.q.shape
+        return dict(Hq=Hq, Hkv=self.k.shape[1], Lq=Lq, L=self.k.shape[2], D=D)
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name) if hasattr(self, name) else self.extra[name]
+        return storage_to_f64(a, self.dtype)
+
+
+def tiny_decode(seed: int = 1, L: int = 1024, D: int = 64, block: int = 64) -> Workload:
+    """One query, one head, fp32, RoPE'd keys at 0..L-1 and the query at L-1.
+
+    Budget of 4 blocks: block 0 and the newest block are forced, two more are
+    scored picks (an NSA-style budget that counts its forced blocks).
+    """
+    pos_k = np.arange(L)
+    q = rope(_normal(seed, _Q, 0, (1, D)), np.array([L - 1]))
+    k = rope(_normal(seed, _K, 0, (L, D)), pos_k)
+    v = _normal(seed, _V, 0, (L, D))
+    params = dict(kv_block=block, q_block=1, q_pos0=L - 1, causal=0, topk=2, topk_num=0, topk_den=1,
+                  n_first=1, n_last=1, dual_band=0, layout=ROPE_HALF, scale=1.0 / math.sqrt(D))
+    return Workload("tiny_decode", "f32", _store(q[None, None], "f32"), _store(k[None, None], "f32"),
+                    _store(v[None, None], "f32"), params)
+
+
+def gqa_decode(seed: int = 2, L: int = 65536, Hq: int = 32, Hkv: int = 8, D: int = 128, block: int = 64,
+               n_needles: int = 8) -> Workload:
+    """GQA decode step over a long RoPE'd prefix, with planted needle blocks.
+
+    Per KV head, ``n_needles`` blocks drawn from {1 .. NB-3} get keys
+    0.5 * (mean of the group's RoPE'd queries) + N(0, 1).  Budget: 16 blocks =
+    block 0 + the 2 newest + 13 scored picks (NSA's selection setting).
+    """
+    G = Hq // Hkv
+    NB = -(-L // block)
+    qpos = np.array([L - 1])
+    q = np.stack([rope(_normal(seed, _Q, h, (1, D)), qpos) for h in range(Hq)])          # [Hq,1,D]
+    kb = np.empty((Hkv, L, D), dtype=np.uint16)
+    vb = np.empty((Hkv, L, D), dtype=np.uint16)
+    needles = np.zeros((Hkv, n_needles), dtype=np.int64)
+    pos_k = np.arange(L)
+    for g in range(Hkv):
+        kg = rope(_normal(seed, _K, g, (L, D)), pos_k)
+        qbar = q[g * G:(g + 1) * G, 0].mean(axis=0)
+        nd = np.sort(_rng(seed, 20, g).choice(np.arange(1, max(NB - 2, 2)), size=n_needles, replace=False))
+        needles[g] = nd
+        for j in nd:
+            kg[j * block:min((j + 1) * block, L)] += 0.5 * qbar
+        kb[g] = _store(kg, "bf16")
+        vb[g] = _store(_normal(seed, _V, g, (L, D)), "bf16")
+    params = dict(kv_block=block, q_block=1, q_pos0=L - 1, causal=0, topk=13, topk_num=0, topk_den=1,
+                  n_first=1, n_last=2, dual_band=0, layout=ROPE_HALF, scale=1.0 / math.sqrt(D))
+    return Workload("gqa_decode", "bf16", _store(q, "bf16")[None], kb[None], vb[None], params,
+                    dict(needles=needles))
+
+
+def dlm_denoise(seed: int = 3, L: int = 32768, R: int = 32, Hq: int = 32, Hkv: int = 8, D: int = 128,
+                block: int = 64, n_active: int = 8, n_needles: int = 8, theta: float = 0.1) -> Workload:
+    """One denoising step of a block-wise diffusion LM over a cached prefix.
+
+    The query block has R rows at positions L .. L+R-1.  Previous-step queries
+    (pre-RoPE) are u_g + N(0, 1) with a shared per-group direction u_g.  A
+    seeded set of ``n_active`` rows changes by N(0, 1) (all heads); the other
+    rows change by N(0, 0.01^2).  Per KV head, ``n_needles`` blocks get keys
+    0.5 * (mean RoPE'd previous query of the group) + N(0, 1).
+    Budget: 16 scored picks per row, no forced blocks, union over the block.
+    """
+    G = Hq // Hkv
+    NB = -(-L // block)
+    rpos = L + np.arange(R)
+    u = np.stack([_rng(seed, 30, g).standard_normal(D) for g in range(Hkv)])
+    q_prev = np.stack([rope(u[h // G][None, :] + _normal(seed, _Q, h, (R, D)), rpos) for h in range(Hq)])
+    active = np.sort(_rng(seed, 31).choice(R, size=n_active, replace=False))
+    is_act = np.zeros(R, dtype=bool)
+    is_act[active] = True
+    q_cur = np.empty_like(q_prev)
+    for h in range(Hq):
+        d = _rng(seed, 33, h).standard_normal((R, D))
+        q_cur[h] = q_prev[h] + np.where(is_act[:, None], d, 0.01 * d)
+    kb = np.empty((Hkv, L, D), dtype=np.uint16)
+    vb = np.empty((Hkv, L, D), dtype=np.uint16)
+    needles = np.zeros((Hkv, n_needles), dtype=np.int64)
+    pos_k = np.arange(L)
+    for g in range(Hkv):
+        kg = rope(_normal(seed, _K, g, (L, D)), pos_k)
+        qbar = q_prev[g * G:(g + 1) * G].reshape(-1, D).mean(axis=0)
+        nd = np.sort(_rng(seed, 32, g).choice(NB, size=min(n_needles, NB), replace=False))
+        needles[g, :len(nd)] = nd
+        for j in nd:
+            kg[j * block:min((j + 1) * block, L)] += 0.5 * qbar
+        kb[g] = _store(kg, "bf16")
+        vb[g] = _store(_normal(seed, _V, g, (L, D)), "bf16")
+    params = dict(kv_block=block, q_block=R, q_pos0=L, causal=0, topk=16, topk_num=0, topk_den=1,
+                  n_first=0, n_last=0, dual_band=0, layout=ROPE_HALF, scale=1.0 / math.sqrt(D),
+                  theta_act=theta)
+    return Workload("dlm_denoise", "bf16", _store(q_cur, "bf16")[None], kb[None], vb[None], params,
+                    dict(q_prev=_store(q_prev, "bf16")[None], active=active, needles=needles))
+
+
+def sparse_prefill(seed: int = 4, L: int = 32768, Hq: int = 32, Hkv: int = 8, D: int = 128, block: int = 128,
+                   n_topics: int = 16, topic_frac: float = 0.25, amp: float = 4.0, c_norm2: float = 64.0) -> Workload:
+    """Causal prefill with both a positional (fast band) and a topical (slow band) signal.
+
+    Interleaved RoPE layout, so the fast-rotating chunks are literally the
+    lower half of the head dims and the slow ones the upper half.
+    (i)  a fixed per-group vector c_g on fast-band dims, |c_g|^2 = c_norm2, is
+         added to every pre-RoPE query and key of the group: after RoPE it
+         yields a local ("slash") preference;
+    (ii) ``n_topics`` unit topic vectors per group on slow-band dims; every
+         query block and ``topic_frac`` of the key blocks get one topic,
+         amplitude ``amp``, added after RoPE.
+    Budget per query block i: blocks {0, i} plus ceil(0.10 * (i + 1)) scored picks.
+    """
+    G = Hq // Hkv
+    NB = -(-L // block)
+    layout = ROPE_INTERLEAVED
+    hi = hi_band_dims(D, layout)
+    lo = lo_band_dims(D, layout)
+    pos = np.arange(L)
+    qb = np.empty((Hq, L, D), dtype=np.uint16)
+    kb = np.empty((Hkv, L, D), dtype=np.uint16)
+    vb = np.empty((Hkv, L, D), dtype=np.uint16)
+    q_topic = np.zeros((Hkv, NB), dtype=np.int64)
+    k_topic = np.full((Hkv, NB), -1, dtype=np.int64)
+    for g in range(Hkv):
+        c = _unit(_rng(seed, 40, g), 1, D, hi)[0] * math.sqrt(c_norm2)
+        topics = _unit(_rng(seed, 41, g), n_topics, D, lo)
+        qt = _rng(seed, 42, g).integers(0, n_topics, size=NB)
+        rk = _rng(seed, 43, g)
+        kblocks = np.sort(rk.choice(NB, size=int(round(topic_frac * NB)), replace=False))
+        kt = rk.integers(0, n_topics, size=len(kblocks))
+        q_topic[g] = qt
+        k_topic[g, kblocks] = kt
+        qadd = np.repeat(amp * topics[qt], block, axis=0)[:L]
+        for h in range(g * G, (g + 1) * G):
+            qh = rope(_normal(seed, _Q, h, (L, D)) + c, pos, layout) + qadd
+            qb[h] = _store(qh, "bf16")
+        kg = rope(_normal(seed, _K, g, (L, D)) + c, pos, layout)
+        for j, t in zip(kblocks, kt):
+            kg[j * block:min((j + 1) * block, L)] += amp * topics[t]
+        kb[g] = _store(kg, "bf16")
+        vb[g] = _store(_normal(seed, _V, g, (L, D)), "bf16")
+    params = dict(kv_block=block, q_block=block, q_pos0=0, causal=1, topk=0, topk_num=1, topk_den=10,
+                  n_first=1, n_last=1, dual_band=1, layout=layout, scale=1.0 / math.sqrt(D))
+    return Workload("sparse_prefill", "bf16", qb[None], kb[None], vb[None], params,
+                    dict(q_topic=q_topic, k_topic=k_topic))
+
+
+def threshold_prefill(seed: int = 5, L: int = 131072, Hq: int = 32, Hkv: int = 8, D: int = 128, tile: int = 128,
+                      seg_tiles: int = 108, n_needles: int = 8, lam: float = 1e-3, logit_gap: float = 24.0,
+                      heads: list[int] | None = None) -> Workload:
+    """Causal prefill without RoPE, for the softmax-threshold skip.
+
+    Tokens fall into segments of ``seg_tiles`` tiles, each with a random unit
+    code e_m per group.  Queries add alpha*e_seg(r); keys add
+    alpha*(e_seg(s) + e_seg(s)+1), so a query sees its own and the previous
+    segment strongly (a local window).  Per KV head, ``n_needles`` tiles add
+    alpha*w_g to their keys while every query of the group adds alpha*w_g.
+    alpha^2 / sqrt(D) = ``logit_gap``.  Everything outside the window and the
+    needles sits far below the running max, so about 70% of causal tiles are
+    skippable at lambda = 1e-3 with the default sizes.
+
+    ``heads`` limits generation to some query heads (their KV heads are made
+    in full); other heads are left zero.  Used to bound host time when only a
+    sample of heads is checked.
+    """
+    G = Hq // Hkv
+    NT = -(-L // tile)
+    nseg = -(-NT // seg_tiles) + 1
+    alpha = math.sqrt(logit_gap * math.sqrt(D))
+    seg = (np.arange(L) // tile) // seg_tiles
+    qb = np.zeros((Hq, L, D), dtype=np.uint16)
+    kb = np.zeros((Hkv, L, D), dtype=np.uint16)
+    vb = np.zeros((Hkv, L, D), dtype=np.uint16)
+    needles = np.zeros((Hkv, n_needles), dtype=np.int64)
+    want = set(range(Hq)) if heads is None else set(heads)
+    for g in range(Hkv):
+        hs = [h for h in range(g * G, (g + 1) * G) if h in want]
+        if not hs:
+            continue
+        e = _unit(_rng(seed, 50, g), nseg + 1, D)
+        nd = np.sort(_rng(seed, 51, g).choice(NT, size=min(n_needles, NT), replace=False))
+        w = _unit(_rng(seed, 52, g), 1, D)[0]
+        needles[g, :len(nd)] = nd
+        qstruct = alpha * (e[seg] + w[None, :])
+        for h in hs:
+            qb[h] = _store(_normal(seed, _Q, h, (L, D)) + qstruct, "bf16")
+        kg = _normal(seed, _K, g, (L, D)) + alpha * (e[seg] + e[seg + 1])
+        for t in nd:
+            kg[t * tile:min((t + 1) * tile, L)] += alpha * w
+        kb[g] = _store(kg, "bf16")
+        vb[g] = _store(_normal(seed, _V, g, (L, D)), "bf16")
+    params = dict(tile=tile, causal=1, lam=lam, scale=1.0 / math.sqrt(D))
+    return Workload("threshold_prefill", "bf16", qb[None], kb[None], vb[None], params,
+                    dict(needles=needles, seg_tiles=seg_tiles, alpha=alpha))
