@@ -1,0 +1,170 @@
+"""Query-aware block-sparse attention on MI355X: thin torch binding of libbsa.
+
+Each function has the name of the C entry point it wraps and only marshals
+arguments: tensors become (device pointer, shape, strides) descriptors, the
+current torch stream becomes the HIP stream, and outputs/workspaces are
+allocated with torch.  Every step of the computation runs in the HIP kernels
+of libbsa.so; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import (  # noqa: F401
+    BSA_BF16, BSA_F32, BSA_ROPE_HALF, BSA_ROPE_INTERLEAVED, BsaAttnParams, BsaError, BsaSelectParams,
+    BsaTensor, BsaThreshParams, check, lib,
+)
+
+__all__ = ["bsa_build_block_summaries", "bsa_select_blocks", "bsa_active_rows", "bsa_sparse_attention_fwd",
+           "bsa_threshold_attention_fwd", "bsa_select_workspace_bytes", "bsa_attention_workspace_bytes",
+           "BsaError", "tensor_desc", "select_params", "attn_params", "lib"]
+
+_DT = {torch.bfloat16: BSA_BF16, torch.float32: BSA_F32}
+
+
+def tensor_desc(t: torch.Tensor) -> BsaTensor:
+    """Descriptor of a 4-D [B, H, L, D] device tensor with a contiguous last dim."""
+    if t.dim() != 4:
+        raise ValueError(f"expected a 4-D [B, H, L, D] tensor, got shape {tuple(t.shape)}")
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError("the last dim must be contiguous")
+    B, H, L, D = t.shape
+    return BsaTensor(t.data_ptr(), _DT[t.dtype], B, H, L, D, t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def select_params(kv_block, q_block=1, q_pos0=0, q_len=0, causal=0, pooled_q=0, topk=0, topk_num=0, topk_den=1,
+                  n_first=0, n_last=0, dual_band=0, layout=BSA_ROPE_HALF, scale=None, cap=None, D=128):
+    return BsaSelectParams(kv_block, q_block, q_pos0, q_len, causal, pooled_q, topk, topk_num, topk_den, n_first,
+                           n_last, dual_band, layout, 1.0 / math.sqrt(D) if scale is None else scale,
+                           0 if cap is None else cap)
+
+
+def attn_params(kv_block, q_block, cap, q_pos0=0, causal=0, scale=None, D=128):
+    return BsaAttnParams(1.0 / math.sqrt(D) if scale is None else scale, kv_block, q_block, q_pos0, causal, cap)
+
+
+def list_capacity(NB, rows_per_block, p: BsaSelectParams) -> int:
+    """Smallest capacity the selection accepts: min(NB, rows * (k' + forced))."""
+    kp = -(-(p.topk_num * NB) // p.topk_den) if p.topk_num > 0 else p.topk
+    return min(NB, rows_per_block * (kp + p.n_first + p.n_last))
+
+
+# --------------------------------------------------------------- summaries ---
+def bsa_build_block_summaries(x: torch.Tensor, block_size: int, layout: int = BSA_ROPE_HALF, first_block: int = 0,
+                              num_blocks: int = -1, mean: torch.Tensor | None = None,
+                              energy: torch.Tensor | None = None, with_energy: bool = True):
+    B, H, L, D = x.shape
+    NB = -(-L // block_size)
+    if mean is None:
+        mean = torch.empty((B, H, NB, D), dtype=torch.float32, device=x.device)
+    if energy is None and with_energy:
+        energy = torch.empty((B, H, NB, 2), dtype=torch.float32, device=x.device)
+    xd = tensor_desc(x)
+    check(lib().bsa_build_block_summaries(ctypes.byref(xd), block_size, layout, first_block, num_blocks,
+                                          mean.data_ptr(), _ptr(energy), _stream()), "bsa_build_block_summaries")
+    return mean, energy
+
+
+# --------------------------------------------------------------- selection ---
+def bsa_select_workspace_bytes(q: torch.Tensor, num_kv_heads: int, num_kv_blocks: int, p: BsaSelectParams) -> int:
+    qd = tensor_desc(q)
+    return lib().bsa_select_workspace_bytes(ctypes.byref(qd), num_kv_heads, num_kv_blocks, ctypes.byref(p))
+
+
+def bsa_select_blocks(q: torch.Tensor, k_mean: torch.Tensor, p: BsaSelectParams, k_energy=None, q_energy=None,
+                      row_mask=None, want_row_picks=False, want_tau=False, workspace=None):
+    """Returns (idx [B,Hkv,NQB,cap] int32, cnt [B,Hkv,NQB] int32, row_picks or None, tau or None)."""
+    B, Hkv, NB, D = k_mean.shape
+    Hq = q.shape[1]
+    if p.pooled_q:
+        NQB = q.shape[2]
+        R = NQB
+    else:
+        Lq = q.shape[2]
+        NQB = -(-Lq // p.q_block)
+        R = Lq
+    if p.cap <= 0:
+        p.cap = list_capacity(NB, 1 if p.pooled_q else min(p.q_block, q.shape[2]), p)
+    dev = q.device
+    idx = torch.empty((B, Hkv, NQB, p.cap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hkv, NQB), dtype=torch.int32, device=dev)
+    rp = torch.empty((B, Hkv, R, p.cap), dtype=torch.int32, device=dev) if want_row_picks else None
+    tau = torch.empty((B, Hq, 2), dtype=torch.float32, device=dev) if want_tau else None
+    qd = tensor_desc(q)
+    need = lib().bsa_select_workspace_bytes(ctypes.byref(qd), Hkv, NB, ctypes.byref(p))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    check(lib().bsa_select_blocks(ctypes.byref(qd), _ptr(q_energy), k_mean.data_ptr(), _ptr(k_energy), Hkv, NB,
+                                  ctypes.byref(p), _ptr(row_mask), idx.data_ptr(), cnt.data_ptr(), _ptr(rp),
+                                  _ptr(tau), workspace.data_ptr(), workspace.numel(), _stream()),
+          "bsa_select_blocks")
+    return idx, cnt, rp, tau
+
+
+# ------------------------------------------------------------- active rows ---
+def bsa_active_rows(q_cur: torch.Tensor, q_prev: torch.Tensor, theta: float, want_mse=True):
+    B, H, R, D = q_cur.shape
+    mask = torch.empty((B, R), dtype=torch.uint8, device=q_cur.device)
+    mse = torch.empty((B, R), dtype=torch.float32, device=q_cur.device) if want_mse else None
+    a, b = tensor_desc(q_cur), tensor_desc(q_prev)
+    check(lib().bsa_active_rows(ctypes.byref(a), ctypes.byref(b), theta, mask.data_ptr(), _ptr(mse), _stream()),
+          "bsa_active_rows")
+    return mask, mse
+
+
+# --------------------------------------------------------------- attention ---
+def bsa_attention_workspace_bytes(q: torch.Tensor, k: torch.Tensor, p: BsaAttnParams) -> int:
+    qd, kd = tensor_desc(q), tensor_desc(k)
+    return lib().bsa_attention_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(p))
+
+
+def bsa_sparse_attention_fwd(q, k, v, idx, cnt, p: BsaAttnParams, row_mask=None, o=None, lse=None, workspace=None):
+    """Returns (o, lse).  Rows with row_mask = 0 keep whatever o/lse held."""
+    B, Hq, Lq, D = q.shape
+    if o is None:
+        o = torch.zeros_like(q)
+    if lse is None:
+        lse = torch.zeros((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
+    need = lib().bsa_attention_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(p))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    check(lib().bsa_sparse_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),
+                                         cnt.data_ptr(), ctypes.byref(p), _ptr(row_mask), ctypes.byref(od),
+                                         lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
+          "bsa_sparse_attention_fwd")
+    return o, lse
+
+
+def bsa_threshold_attention_fwd(q, k, v, lam: float, scale: float | None = None, tile: int = 128, causal: int = 1,
+                                want_keep_map=False, o=None, lse=None, kept=None):
+    """Returns (o, lse, kept_tiles [B,Hq,NQT] int32, keep_map [B,Hq,NQT,NKT] uint8 or None)."""
+    B, Hq, Lq, D = q.shape
+    L = k.shape[2]
+    NQT, NKT = -(-Lq // tile), -(-L // tile)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if kept is None:
+        kept = torch.empty((B, Hq, NQT), dtype=torch.int32, device=q.device)
+    km = torch.zeros((B, Hq, NQT, NKT), dtype=torch.uint8, device=q.device) if want_keep_map else None
+    p = BsaThreshParams(1.0 / math.sqrt(D) if scale is None else scale, lam, tile, causal)
+    qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
+    check(lib().bsa_threshold_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(p),
+                                            ctypes.byref(od), lse.data_ptr(), kept.data_ptr(), _ptr(km), _stream()),
+          "bsa_threshold_attention_fwd")
+    return o, lse, kept, km

@@ -1,0 +1,247 @@
+// C ABI of libbsa: host-side validation, workspace sizing and dispatch.
+// Every argument is checked before anything is enqueued; a non-OK status
+// leaves all outputs untouched and records a message for bsa_last_error().
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace bsa {
+
+static thread_local char g_err[512] = "";
+
+bsa_status fail(bsa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bsa_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = 0;
+  return BSA_OK;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape, dtype and alignment checks common to every tensor argument.
+static bsa_status check_tensor(const bsa_tensor* t, const char* name, bool allow_empty_l) {
+  if (!t) return fail(BSA_ERR_INVALID, "%s: null tensor descriptor", name);
+  if (t->dtype != BSA_BF16 && t->dtype != BSA_F32) return fail(BSA_ERR_INVALID, "%s: unknown dtype %d", name, t->dtype);
+  if (t->B <= 0 || t->H <= 0 || t->D <= 0 || t->L < 0 || (!allow_empty_l && t->L == 0))
+    return fail(BSA_ERR_INVALID, "%s: bad shape [%d,%d,%d,%d]", name, t->B, t->H, t->L, t->D);
+  if (t->D != 64 && t->D != 128) return fail(BSA_ERR_UNSUPPORTED, "%s: head dim %d (supported: 64, 128)", name, t->D);
+  if (!t->data) return fail(BSA_ERR_INVALID, "%s: null data pointer", name);
+  const int64_t es = (int64_t)dtype_size(t->dtype);
+  if (!aligned16(t->data)) return fail(BSA_ERR_INVALID, "%s: data not 16-byte aligned", name);
+  if (t->stride_b < 0 || t->stride_h < 0 || t->stride_l < 0) return fail(BSA_ERR_INVALID, "%s: negative stride", name);
+  if ((t->stride_b * es) % 16 || (t->stride_h * es) % 16 || (t->stride_l * es) % 16)
+    return fail(BSA_ERR_INVALID, "%s: strides must be multiples of 16 bytes", name);
+  if (t->L > 1 && t->stride_l < t->D) return fail(BSA_ERR_INVALID, "%s: rows overlap (stride_l < D)", name);
+  return BSA_OK;
+}
+
+static bool same_shape(const bsa_tensor* a, const bsa_tensor* b) {
+  return a->B == b->B && a->H == b->H && a->L == b->L && a->D == b->D && a->dtype == b->dtype;
+}
+
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" {
+
+int32_t bsa_version(void) { return 1; }
+
+const char* bsa_status_string(int32_t s) {
+  switch (s) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_INVALID: return "invalid argument";
+    case BSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BSA_ERR_CAPACITY: return "index-list capacity too small";
+    case BSA_ERR_WORKSPACE: return "workspace too small";
+    case BSA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* bsa_last_error(void) { return g_err; }
+
+// --------------------------------------------------------------- summaries ---
+bsa_status bsa_build_block_summaries(const bsa_tensor* x, int32_t block_size, int32_t layout, int32_t first_block,
+                                     int32_t num_blocks, float* mean, float* energy, void* stream) {
+  bsa_status st = check_tensor(x, "x", true);
+  if (st != BSA_OK) return st;
+  if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128 && block_size != 256)
+    return fail(BSA_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32, 64, 128, 256)", block_size);
+  if (layout != BSA_ROPE_HALF && layout != BSA_ROPE_INTERLEAVED) return fail(BSA_ERR_INVALID, "layout %d", layout);
+  if (!mean) return fail(BSA_ERR_INVALID, "mean: null pointer");
+  const int NB = (int)ceil_div(x->L, block_size);
+  if (first_block < 0 || first_block > NB) return fail(BSA_ERR_INVALID, "first_block %d outside [0, %d]", first_block, NB);
+  const int n = num_blocks < 0 ? NB - first_block : num_blocks;
+  if (first_block + n > NB) return fail(BSA_ERR_INVALID, "blocks %d..%d beyond NB = %d", first_block, first_block + n - 1, NB);
+  if (n == 0) { g_err[0] = 0; return BSA_OK; }
+  launch_summaries(*x, block_size, layout, first_block, n, mean, energy, static_cast<hipStream_t>(stream));
+  return check_launch("block summaries");
+}
+
+// --------------------------------------------------------------- selection ---
+static bsa_status validate_select(const bsa_tensor* q, int32_t Hkv, int32_t NB, const bsa_select_params* p,
+                                  SelectPlan& pl) {
+  if (!p) return fail(BSA_ERR_INVALID, "params: null");
+  bsa_status st = check_tensor(q, "q", false);
+  if (st != BSA_OK) return st;
+  if (p->pooled_q && q->dtype != BSA_F32) return fail(BSA_ERR_INVALID, "pooled queries must be f32");
+  if (Hkv <= 0 || q->H % Hkv) return fail(BSA_ERR_INVALID, "num_kv_heads %d must divide Hq = %d", Hkv, q->H);
+  if (NB <= 0) return fail(BSA_ERR_INVALID, "num_kv_blocks %d", NB);
+  if (NB > 4096) return fail(BSA_ERR_UNSUPPORTED, "num_kv_blocks %d > 4096", NB);
+  if (p->kv_block <= 0 || p->q_block <= 0) return fail(BSA_ERR_INVALID, "kv_block/q_block must be positive");
+  if (p->topk < 0 || p->topk_num < 0 || p->topk_den <= 0 || p->n_first < 0 || p->n_last < 0)
+    return fail(BSA_ERR_INVALID, "negative budget or topk_den <= 0");
+  if (p->layout != BSA_ROPE_HALF && p->layout != BSA_ROPE_INTERLEAVED) return fail(BSA_ERR_INVALID, "layout %d", p->layout);
+  if (p->dual_band != 0 && p->dual_band != 1) return fail(BSA_ERR_INVALID, "dual_band %d", p->dual_band);
+  if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(BSA_ERR_INVALID, "scale must be finite and > 0");
+  if (p->q_pos0 < 0 || p->q_len < 0) return fail(BSA_ERR_INVALID, "negative q_pos0/q_len");
+  if (p->pooled_q && p->q_len > 0 && ceil_div(p->q_len, p->q_block) != q->L)
+    return fail(BSA_ERR_INVALID, "q_len %d does not give %d query blocks of %d", p->q_len, q->L, p->q_block);
+  plan_select(*q, NB, *p, pl);
+  pl.Hkv = Hkv;
+  pl.G = q->H / Hkv;
+  const int R = p->pooled_q ? 1 : std::min(p->q_block, pl.Lq);
+  const int64_t bound = std::min<int64_t>(NB, (int64_t)R * ((int64_t)pl.kp_max + p->n_first + p->n_last));
+  if (p->cap < bound) return fail(BSA_ERR_CAPACITY, "cap %d < %lld (rows per block %d x (k' %d + forced %d))", p->cap,
+                                  (long long)bound, R, pl.kp_max, p->n_first + p->n_last);
+  const int Rtot = p->pooled_q ? pl.NQB : pl.Lq;
+  const size_t nz = (size_t)pl.B * q->H * Rtot * (p->dual_band ? 2 : 1) * NB;
+  pl.z_bytes = align256(nz * 4);
+  pl.tau_bytes = p->dual_band ? align256((size_t)pl.B * q->H * 2 * 4) : 0;
+  return BSA_OK;
+}
+
+size_t bsa_select_workspace_bytes(const bsa_tensor* q, int32_t num_kv_heads, int32_t num_kv_blocks,
+                                  const bsa_select_params* p) {
+  SelectPlan pl;
+  if (validate_select(q, num_kv_heads, num_kv_blocks, p, pl) != BSA_OK) return 0;
+  return pl.z_bytes + pl.tau_bytes;
+}
+
+bsa_status bsa_select_blocks(const bsa_tensor* q, const float* q_energy, const float* k_mean, const float* k_energy,
+                             int32_t num_kv_heads, int32_t num_kv_blocks, const bsa_select_params* p,
+                             const uint8_t* row_mask, int32_t* idx, int32_t* cnt, int32_t* row_picks, float* tau_out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  SelectPlan pl;
+  bsa_status st = validate_select(q, num_kv_heads, num_kv_blocks, p, pl);
+  if (st != BSA_OK) return st;
+  if (!k_mean || !idx || !cnt) return fail(BSA_ERR_INVALID, "k_mean, idx and cnt are required");
+  if (!aligned16(k_mean)) return fail(BSA_ERR_INVALID, "k_mean not 16-byte aligned");
+  if (p->dual_band) {
+    if (!k_energy) return fail(BSA_ERR_INVALID, "dual band needs k_energy");
+    if (p->pooled_q && !q_energy) return fail(BSA_ERR_INVALID, "dual band with pooled queries needs q_energy");
+  }
+  if (row_mask && p->pooled_q) return fail(BSA_ERR_INVALID, "row_mask applies to raw query rows only");
+  const size_t need = pl.z_bytes + pl.tau_bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  launch_select(*q, p->pooled_q ? q_energy : nullptr, k_mean, k_energy, *p, pl, row_mask, idx, cnt, row_picks,
+                tau_out, workspace, static_cast<hipStream_t>(stream));
+  return check_launch("block selection");
+}
+
+// ------------------------------------------------------------- active rows ---
+bsa_status bsa_active_rows(const bsa_tensor* q_cur, const bsa_tensor* q_prev, float theta, uint8_t* row_mask,
+                           float* mse, void* stream) {
+  bsa_status st = check_tensor(q_cur, "q_cur", false);
+  if (st != BSA_OK) return st;
+  st = check_tensor(q_prev, "q_prev", false);
+  if (st != BSA_OK) return st;
+  if (!same_shape(q_cur, q_prev)) return fail(BSA_ERR_INVALID, "q_cur and q_prev differ in shape or dtype");
+  if (!row_mask) return fail(BSA_ERR_INVALID, "row_mask: null pointer");
+  if (!std::isfinite(theta)) return fail(BSA_ERR_INVALID, "theta must be finite");
+  launch_active_rows(*q_cur, *q_prev, theta, row_mask, mse, static_cast<hipStream_t>(stream));
+  return check_launch("active rows");
+}
+
+// --------------------------------------------------------------- attention ---
+static bsa_status validate_attention(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                     const bsa_attn_params* p, AttnPlan& pl) {
+  if (!p) return fail(BSA_ERR_INVALID, "params: null");
+  bsa_status st = check_tensor(q, "q", true);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(k, "k", false)) != BSA_OK) return st;
+  if ((st = check_tensor(v, "v", false)) != BSA_OK) return st;
+  if (!same_shape(k, v)) return fail(BSA_ERR_INVALID, "k and v differ in shape or dtype");
+  if (q->dtype != k->dtype) return fail(BSA_ERR_INVALID, "q and k differ in dtype");
+  if (q->B != k->B || q->D != k->D || q->H % k->H) return fail(BSA_ERR_INVALID, "q/k shapes are incompatible");
+  if (p->kv_block <= 0 || p->q_block <= 0 || p->cap <= 0) return fail(BSA_ERR_INVALID, "kv_block, q_block, cap > 0");
+  if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(BSA_ERR_INVALID, "scale must be finite and > 0");
+  if (p->q_pos0 < 0) return fail(BSA_ERR_INVALID, "negative q_pos0");
+  plan_attention(*q, *k, *p, pl);
+  if (pl.kind == 0) {
+    if (pl.G != 1 && pl.G != 2 && pl.G != 4 && pl.G != 8)
+      return fail(BSA_ERR_UNSUPPORTED, "decode path needs Hq/Hkv in {1, 2, 4, 8}, got %d", pl.G);
+  } else {
+    if (q->dtype != BSA_BF16 || q->D != 128)
+      return fail(BSA_ERR_UNSUPPORTED, "multi-row query blocks need bf16 and D = 128");
+    if (p->kv_block != 64 && p->kv_block != 128)
+      return fail(BSA_ERR_UNSUPPORTED, "multi-row query blocks need kv_block 64 or 128");
+    if (pl.kind == 1 && p->q_block > 128) return fail(BSA_ERR_UNSUPPORTED, "q_block %d > 128", p->q_block);
+  }
+  return BSA_OK;
+}
+
+size_t bsa_attention_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, const bsa_attn_params* p) {
+  AttnPlan pl;
+  if (!k || validate_attention(q, k, k, p, pl) != BSA_OK) return 0;
+  return pl.part_bytes;
+}
+
+bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const int32_t* idx,
+                                    const int32_t* cnt, const bsa_attn_params* p, const uint8_t* row_mask,
+                                    const bsa_tensor* o, float* lse, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  AttnPlan pl;
+  bsa_status st = validate_attention(q, k, v, p, pl);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(o, "o", true)) != BSA_OK) return st;
+  if (!same_shape(q, o)) return fail(BSA_ERR_INVALID, "o must match q in shape and dtype");
+  if (!idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "idx, cnt and lse are required");
+  if (pl.part_bytes && (!workspace || workspace_bytes < pl.part_bytes))
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, pl.part_bytes);
+  if (pl.part_bytes && !aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  if (q->L == 0) { g_err[0] = 0; return BSA_OK; }
+  launch_attention(*q, *k, *v, idx, cnt, *p, pl, row_mask, *o, lse, workspace, static_cast<hipStream_t>(stream));
+  return check_launch("sparse attention");
+}
+
+// ----------------------------------------------------- threshold attention ---
+bsa_status bsa_threshold_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                       const bsa_thresh_params* p, const bsa_tensor* o, float* lse,
+                                       int32_t* kept_tiles, uint8_t* keep_map, void* stream) {
+  if (!p) return fail(BSA_ERR_INVALID, "params: null");
+  bsa_status st = check_tensor(q, "q", true);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(k, "k", false)) != BSA_OK) return st;
+  if ((st = check_tensor(v, "v", false)) != BSA_OK) return st;
+  if ((st = check_tensor(o, "o", true)) != BSA_OK) return st;
+  if (!same_shape(k, v) || !same_shape(q, o)) return fail(BSA_ERR_INVALID, "k/v or q/o shapes differ");
+  if (q->dtype != k->dtype || q->B != k->B || q->D != k->D || q->H % k->H)
+    return fail(BSA_ERR_INVALID, "q/k shapes are incompatible");
+  if (q->dtype != BSA_BF16 || q->D != 128) return fail(BSA_ERR_UNSUPPORTED, "threshold attention needs bf16, D = 128");
+  if (p->tile != 128) return fail(BSA_ERR_UNSUPPORTED, "tile %d (supported: 128)", p->tile);
+  if (!(p->lambda >= 0.f && p->lambda <= 1.f)) return fail(BSA_ERR_INVALID, "lambda %g outside [0, 1]", p->lambda);
+  if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(BSA_ERR_INVALID, "scale must be finite and > 0");
+  if (p->causal && q->L != k->L) return fail(BSA_ERR_UNSUPPORTED, "causal threshold attention needs Lq == L");
+  if (!lse) return fail(BSA_ERR_INVALID, "lse is required");
+  if (q->L == 0) { g_err[0] = 0; return BSA_OK; }
+  launch_threshold(*q, *k, *v, *p, *o, lse, kept_tiles, keep_map, static_cast<hipStream_t>(stream));
+  return check_launch("threshold attention");
+}
+
+}  // extern "C"

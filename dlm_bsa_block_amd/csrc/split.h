@@ -1,0 +1,45 @@
+// Argument blocks of the split-KV attention kernels and their combine.
+//
+// Partial results live in the caller's workspace:
+//   part_o [B][Hkv][NQB][items][QV][D]  unnormalised sum of p * v
+//   part_ml[B][Hkv][NQB][items][QV][2]  (running max in log2 units, sum of p)
+// with QV = q_block * G query vectors per query block (qv = row * G + head).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+constexpr int kDecTok = 32;       // list tokens per decode workgroup
+constexpr int kSplitBlocks = 8;   // list entries per MFMA split workgroup
+
+struct DecArgs {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  int64_t qsb, qsh, qsl, ksb, ksh, ksl, vsb, vsh, vsl;
+  const int32_t* idx;
+  const int32_t* cnt;
+  int cap, NQB, Hkv, L, kv_block, causal, q_pos0, Lq, items;
+  float c2;                       // scale * log2(e)
+  const uint8_t* row_mask;
+  float* part_o;
+  float* part_ml;
+};
+
+struct CombArgs {
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* cnt;
+  int items, unit_num, unit_den;  // valid slices = ceil(cnt * unit_num / unit_den)
+  int Hkv, G, NQB, q_block, Lq, D, QV;
+  const uint8_t* row_mask;
+  void* o;
+  int64_t osb, osh, osl;
+  float* lse;
+};
+
+void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s);
+void launch_combine(const CombArgs& a, int odt, int B, hipStream_t s);
+
+}  // namespace bsa

@@ -1,0 +1,176 @@
+// Softmax-threshold attention (BLASST page, technical summary sec. 2): inside
+// the blockwise online softmax, a KV tile whose max logit trails the running
+// row max by more than ln(1/lambda) is skipped -- no exponentials, no V load
+// from HBM and no PV product.  The test reuses statistics the online softmax
+// computes anyway.
+//
+// One workgroup per (query tile of 128 rows, query head); 4 waves of 32 rows.
+// KV tiles are visited from the diagonal (the newest visible tile) down to
+// tile 0.  For each tile S = K Q^T is always computed (the max needs it); each
+// wave votes through a ballot, the votes meet in LDS, and the whole workgroup
+// takes the same keep/skip branch.  Only a kept tile loads V, and its V loads
+// are issued before the exponentials so their latency overlaps that work.
+// Workgroups of one KV group run on one XCD (heads of a query tile adjacent),
+// so K/V tiles are shared through that XCD's L2.
+#include <cmath>
+
+#include "internal.h"
+#include "mfma_tile.cuh"
+
+namespace bsa {
+
+struct ThrArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t qsb, qsh, qsl, ksb, ksh, ksl, vsb, vsh, vsl;
+  int B, Hkv, G, L, Lq, NQT, NKT, causal;
+  float c2;        // scale * log2(e)
+  float lnlam2;    // ln(lambda) * log2(e); -inf when lambda = 0
+  uint16_t* o;
+  int64_t osb, osh, osl;
+  float* lse;
+  int32_t* kept;
+  uint8_t* keep_map;
+};
+
+constexpr int kTile = 128;
+
+__global__ __launch_bounds__(256, 2) void threshold_kernel(ThrArgs a) {
+  constexpr int VST = VtStride<kTile>::value;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * kKStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * VST];
+  __shared__ int flags[4];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r32 = lane & 31;
+  const int total = gridDim.x, n = blockIdx.x;
+  const int wi = (total % 8 == 0) ? (n % 8) * (total / 8) + n / 8 : n;
+  const int hl = wi % a.G;
+  const int rest = wi / a.G;
+  const int qt = a.NQT - 1 - rest % a.NQT;
+  const int bgi = rest / a.NQT;
+  const int b = bgi / a.Hkv, g = bgi - b * a.Hkv;
+  const int h = g * a.G + hl;
+  const int Hq = a.Hkv * a.G;
+
+  const int row = qt * kTile + 32 * w + r32;
+  const bool valid = row < a.Lq;
+  const bool wave_busy = qt * kTile + 32 * w < a.Lq;
+  int wave_min_pos = valid ? row : 0x7FFFFFFF;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) wave_min_pos = min(wave_min_pos, wave_xor(wave_min_pos, m));
+  const int last_row = min(a.Lq, (qt + 1) * kTile) - 1;
+  const int jmax = a.causal ? min(a.NKT - 1, last_row / kTile) : a.NKT - 1;
+
+  bf16x8 qf[8];
+  load_q_frag(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)row * a.qsl, valid, qf);
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  int nkept = 0;
+  const uint16_t* kbg = a.k + (int64_t)b * a.ksb + (int64_t)g * a.ksh;
+  const uint16_t* vbg = a.v + (int64_t)b * a.vsb + (int64_t)g * a.vsh;
+  uint8_t* kmap = a.keep_map ? a.keep_map + (((int64_t)b * Hq + h) * a.NQT + qt) * a.NKT : nullptr;
+
+  for (int j = jmax; j >= 0; --j) {
+    const int key0 = j * kTile;
+    const int nk = min(kTile, a.L - key0);
+    stage_kv_tile<kTile>(kbg + (int64_t)key0 * a.ksl, a.ksl, nullptr, 0, nk, Ks, Vt, true, false);
+    __syncthreads();
+    f32x16 s[kTile / 32];
+    float tm2 = -INFINITY;
+    if (wave_busy) {
+      qk_tile<kTile>(Ks, qf, s);
+      const bool need_mask = nk < kTile || (a.causal && key0 + kTile - 1 > wave_min_pos) || !valid ||
+                             qt * kTile + 32 * w + 31 >= a.Lq;
+      if (need_mask) {
+        int lim = valid ? nk - 1 : -1;
+        if (a.causal) lim = min(lim, row - key0);
+        mask_tile<kTile / 32>(s, lim);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < kTile / 32; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+      mx = fmaxf(mx, wave_xor(mx, 32));
+      tm2 = mx * a.c2;
+      const bool vote = tm2 != -INFINITY && (m_run == -INFINITY || tm2 - m_run >= a.lnlam2);
+      const unsigned long long bal = __ballot(vote);
+      if (lane == 0) flags[w] = bal != 0ull;
+    } else if (lane == 0) {
+      flags[w] = 0;
+    }
+    __syncthreads();
+    const bool keep = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+    if (tid == 0 && kmap) kmap[j] = keep ? 1 : 0;
+    if (keep) {
+      ++nkept;
+      stage_kv_tile<kTile>(nullptr, 0, vbg + (int64_t)key0 * a.vsl, a.vsl, nk, Ks, Vt, false, true);
+      if (wave_busy) {
+        const float m_new = fmaxf(m_run, tm2);
+        const float msafe = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - msafe);
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < kTile / 32; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float pr = fast_exp2(fmaf(s[kt][i], a.c2, -msafe));
+            s[kt][i] = pr;
+            ls += pr;
+          }
+        l_run = fmaf(l_run, alpha, ls);
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      }
+      __syncthreads();
+      if (wave_busy) pv_tile<kTile>(Vt, s, o);
+    }
+    __syncthreads();
+  }
+
+  if (tid == 0 && a.kept) a.kept[((int64_t)b * Hq + h) * a.NQT + qt] = nkept;
+  if (!valid) return;
+  const float l_tot = l_run + wave_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  uint16_t* orow = a.o + (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = o_dim(dt, 4 * i4);
+      u32x2 pk = {pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
+                  pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + d) = pk;
+    }
+  if (lane < 32)
+    a.lse[((int64_t)b * Hq + h) * a.Lq + row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+void launch_threshold(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, const bsa_thresh_params& p,
+                      const bsa_tensor& o, float* lse, int32_t* kept, uint8_t* keep_map, hipStream_t s) {
+  ThrArgs a;
+  a.q = static_cast<const uint16_t*>(q.data);
+  a.k = static_cast<const uint16_t*>(k.data);
+  a.v = static_cast<const uint16_t*>(v.data);
+  a.qsb = q.stride_b; a.qsh = q.stride_h; a.qsl = q.stride_l;
+  a.ksb = k.stride_b; a.ksh = k.stride_h; a.ksl = k.stride_l;
+  a.vsb = v.stride_b; a.vsh = v.stride_h; a.vsl = v.stride_l;
+  a.B = q.B; a.Hkv = k.H; a.G = q.H / k.H; a.L = k.L; a.Lq = q.L;
+  a.NQT = (int)ceil_div(q.L, kTile);
+  a.NKT = (int)ceil_div(k.L, kTile);
+  a.causal = p.causal;
+  a.c2 = p.scale * kLog2e;
+  a.lnlam2 = p.lambda > 0.f ? (float)(std::log((double)p.lambda) * 1.4426950408889634) : -INFINITY;
+  a.o = static_cast<uint16_t*>(o.data); a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
+  a.lse = lse; a.kept = kept; a.keep_map = keep_map;
+  dim3 grid(a.B * a.Hkv * a.NQT * a.G);
+  hipLaunchKernelGGL(threshold_kernel, grid, dim3(256), 0, s, a);
+}
+
+}  // namespace bsa

@@ -1,0 +1,238 @@
+/*
+ * bsa.h -- query-aware block-sparse attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbsa.so.  Every entry point takes plain pointers and sizes:
+ *
+ *   - Tensor data pointers are HIP DEVICE pointers.  The caller owns every
+ *     buffer (inputs, outputs, workspace); the library never allocates or
+ *     frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream).  All work is enqueued asynchronously on it; no call
+ *     synchronises with the host.
+ *   - Arguments are validated on the host before anything is launched.  On a
+ *     non-OK status nothing has been enqueued and no output was written;
+ *     bsa_last_error() returns a thread-local message with the detail.
+ *   - Results are deterministic: two calls with the same inputs produce the
+ *     same bytes (fixed reduction orders, no floating-point atomics).
+ *
+ * Sources (pages cited by title and section):
+ *   LoSA   -- "LoSA: Locality Aware Sparse Attention for Block-Wise Diffusion
+ *             Language Models", technical summary sec. 1-2.
+ *   Prism  -- "Prism: Spectral-Aware Block-Sparse Attention", technical
+ *             summary sec. 1-3.
+ *   NSA    -- "Native Sparse Attention: Hardware-Aligned and Natively
+ *             Trainable Sparse Attention" (news article), NSA structure
+ *             section and implementation-challenges section.
+ *   FASA   -- "FASA: Frequency-aware Sparse Attention", technical summary
+ *             sec. 2.
+ *   BLASST -- "BLASST: Dynamic BLocked Attention Sparsity via Softmax
+ *             Thresholding", technical summary sec. 2.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID = 1,      /* null pointer, bad shape, misaligned or inconsistent argument */
+  BSA_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels implement (dtype, D, block) */
+  BSA_ERR_CAPACITY = 3,     /* index-list capacity below the bound the selection can reach */
+  BSA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the *_workspace_bytes query */
+  BSA_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
+} bsa_status;
+
+typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype;
+
+/* Which head dims a RoPE frequency chunk (FC) owns.  FC i (0 <= i < D/2)
+ * rotates at base^(-2i/D); a low FC index is a fast rotation.
+ *   BSA_ROPE_HALF:        FC i owns dims i and i + D/2 (rotate-half layout)
+ *   BSA_ROPE_INTERLEAVED: FC i owns dims 2i and 2i + 1
+ * The fast (high-frequency) band is FC i < D/4; the slow band the rest. */
+typedef enum { BSA_ROPE_HALF = 0, BSA_ROPE_INTERLEAVED = 1 } bsa_rope_layout;
+
+/* A 4-D tensor [B, H, L, D] in device memory, strides in elements.  The D
+ * axis must be contiguous (stride 1).  `data` must be 16-byte aligned and
+ * stride_l * element size a multiple of 16 bytes.  Input tensors are never
+ * written through. */
+typedef struct {
+  void* data;
+  int32_t dtype;                 /* bsa_dtype */
+  int32_t B, H, L, D;
+  int64_t stride_b, stride_h, stride_l;
+} bsa_tensor;
+
+/* ------------------------------------------------------------------------ *
+ * Block summaries (Prism sec. 1-2: a KV block is scored through the mean of
+ * its vectors; pooling acts as a low-pass filter on RoPE'd vectors).
+ *
+ * For x [B, H, L, D] (bf16 or f32) and block size b, NB = ceil(L / b).  For
+ * block j with tokens [j*b, min((j+1)*b, L)) writes
+ *   mean[b][h][j][:]      = average of the block's vectors           (f32)
+ *   energy[b][h][j][0..1] = average over tokens of ||x_t[band]||^2 for the
+ *                           fast and the slow band (per `layout`)    (f32)
+ * A ragged last block averages its valid tokens only.  Only blocks
+ * first_block .. first_block + num_blocks - 1 are computed and written
+ * (num_blocks < 0: through the last block), so a decode step can refresh just
+ * the newest block.  `mean` is [B, H, NB, D] and `energy` [B, H, NB, 2], both
+ * contiguous; `energy` may be NULL.
+ * Supported: D in {64, 128}; b in {16, 32, 64, 128, 256}; bf16 or f32.
+ * ------------------------------------------------------------------------ */
+bsa_status bsa_build_block_summaries(const bsa_tensor* x, int32_t block_size, int32_t layout,
+                                     int32_t first_block, int32_t num_blocks,
+                                     float* mean, float* energy, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Block selection: scoring, top-k per GQA group, union over a query block.
+ *
+ * Selection rows.  Raw mode (pooled_q = 0): every query row is a selection
+ * row; q is [B, Hq, Lq, D] bf16/f32 and query block i holds rows
+ * i*q_block .. min((i+1)*q_block, Lq) - 1.  Pooled mode (pooled_q = 1): q is
+ * an f32 tensor [B, Hq, NQB, D] of mean-pooled queries (from
+ * bsa_build_block_summaries) and each query block has exactly one selection
+ * row; q_len gives Lq.  (Prism sec. 3: purely block-level estimation.)
+ *
+ * Candidates C of query block i: all NB KV blocks, or with causal = 1 the
+ * blocks j whose first key j*kv_block is <= q_pos0 + (last row of block i).
+ * Forced F: the first n_first and the last n_last candidates (NSA structure
+ * section: block 0 and the 2 newest blocks are always among the 16; for causal
+ * prefill the newest candidate is the diagonal block).  Scored picks
+ * k' = topk, or ceil(topk_num * |C| / topk_den) when topk_num > 0, capped at
+ * |C \ F|.
+ *
+ * Scores, per selection row r and KV group g (the selection is shared by the
+ * query heads of a GQA group -- NSA implementation-challenges section):
+ *   single band: z_h[j] = scale * q_h . kmean_g[j];  p_h = softmax over C
+ *   dual band  : z_h^band[j] = scale * q_h[band] . kmean_g[j][band] / tau_h^band
+ *                p_h = (softmax(z_h^fast) + softmax(z_h^slow)) / 2
+ *   group score s[j] = sum over heads h of g of p_h[j]     (fp32)
+ * Temperatures (dual band; Prism sec. 3, energy-based calibration):
+ *   rho_X^band = sum_j ||mean_X[j][band]||^2 / sum_j energy_X[j][band]
+ *   tau_h^band = max(1e-6, sqrt(rho_Q^band(h) * rho_K^band(g)))
+ * with rho_Q = 1 in raw mode.  Row picks = F + the k' best of C \ F by s
+ * (ties: lower block index).  The list of a query block is the union of its
+ * rows' picks over rows with row_mask = 1 (LoSA sec. 1: traffic is set by the
+ * union over the block; sec. 2: selecting for active rows only shrinks it).
+ *
+ * Outputs: idx [B, Hkv, NQB, cap] int32 -- the list, ascending and unique,
+ * in the first cnt entries (the rest is left unwritten); cnt [B, Hkv, NQB].
+ * Optional: row_picks [B, Hkv, R, cap] int32 (R = Lq raw or NQB pooled): each
+ * selection row's own sorted picks padded with -1 (-1 everywhere for masked
+ * rows); tau_out [B, Hq, 2] (dual band).
+ * k_mean/k_energy: [B, Hkv, NB, D] / [B, Hkv, NB, 2] f32 contiguous with
+ * Hkv = num_kv_heads dividing Hq and NB = num_kv_blocks; q_energy
+ * [B, Hq, NQB, 2] (pooled + dual band), else NULL.  row_mask [B, Lq] uint8 or
+ * NULL (raw mode only).  workspace: bsa_select_workspace_bytes() bytes.
+ * Errors: BSA_ERR_CAPACITY when cap < min(NB, R_per_block * (k'_max + n_first
+ * + n_last)); BSA_ERR_UNSUPPORTED for NB > 4096, D not in {64, 128}, or more
+ * than 64 query rows per block in raw mode.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t kv_block;          /* tokens per KV block (summary granularity) */
+  int32_t q_block;           /* query rows per query block */
+  int32_t q_pos0;            /* absolute position of query row 0 */
+  int32_t q_len;             /* Lq in pooled mode (0: NQB * q_block) */
+  int32_t causal;
+  int32_t pooled_q;
+  int32_t topk, topk_num, topk_den;
+  int32_t n_first, n_last;
+  int32_t dual_band;
+  int32_t layout;            /* bsa_rope_layout */
+  float scale;               /* logit scale, usually 1/sqrt(D) */
+  int32_t cap;               /* entries per index list */
+} bsa_select_params;
+
+size_t bsa_select_workspace_bytes(const bsa_tensor* q, int32_t num_kv_heads, int32_t num_kv_blocks,
+                                  const bsa_select_params* p);
+
+bsa_status bsa_select_blocks(const bsa_tensor* q, const float* q_energy,
+                             const float* k_mean, const float* k_energy,
+                             int32_t num_kv_heads, int32_t num_kv_blocks,
+                             const bsa_select_params* p, const uint8_t* row_mask,
+                             int32_t* idx, int32_t* cnt, int32_t* row_picks, float* tau_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Locality pruning (LoSA sec. 2): row r of a denoising block is active when
+ * the mean over heads and dims of (q_cur - q_prev)^2 exceeds theta (taken in
+ * fp32).  q_cur/q_prev [B, H, R, D] bf16/f32 of the same shape; writes
+ * row_mask [B, R] (1 active / 0 stable) and, if non-NULL, mse [B, R] f32.
+ * ------------------------------------------------------------------------ */
+bsa_status bsa_active_rows(const bsa_tensor* q_cur, const bsa_tensor* q_prev, float theta,
+                           uint8_t* row_mask, float* mse, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Attention over the selected blocks (FASA sec. 2, focused attention: full
+ * head-dim attention on the chosen tokens at their original positions).
+ *
+ * Each query row of block i (rows with row_mask = 1, or all rows when
+ * row_mask is NULL) of head h attends to the tokens of the blocks listed in
+ * idx[b][h / G][i][0 .. cnt-1]; with causal = 1 keys after the row's absolute
+ * position q_pos0 + r are masked.  Exact online softmax in fp32 from bf16/f32
+ * inputs:  O = sum_t softmax_t(scale * q . k_t) v_t,
+ *          LSE = ln sum_t exp(scale * q . k_t)   (natural log, scale included).
+ * A row that sees no key gets O = 0 and LSE = -inf.  Rows with row_mask = 0
+ * are NOT written: the caller's cached O/LSE stay in place (LoSA sec. 2, stable
+ * tokens reuse the previous step's output and statistics).
+ * q, k, v share dtype; o has q's shape and dtype; lse is [B, Hq, Lq] f32
+ * contiguous.  Supported: bf16 with D = 128 and kv_block in {64, 128}; f32
+ * or D = 64 only for single-row query blocks (decode).  workspace:
+ * bsa_attention_workspace_bytes() bytes (split-KV partial results).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  float scale;
+  int32_t kv_block;
+  int32_t q_block;
+  int32_t q_pos0;
+  int32_t causal;
+  int32_t cap;               /* entries per index list (as given to bsa_select_blocks) */
+} bsa_attn_params;
+
+size_t bsa_attention_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, const bsa_attn_params* p);
+
+bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                    const int32_t* idx, const int32_t* cnt, const bsa_attn_params* p,
+                                    const uint8_t* row_mask, const bsa_tensor* o, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Softmax-threshold attention (BLASST sec. 2).  Per head and query tile of
+ * `tile` rows, KV tiles are visited from the last one the tile can see down
+ * to tile 0.  For a visited tile, S = scale * q k^T (causal-masked) and
+ * tm_r = max of row r over the tile; row r votes keep when tm_r is finite and
+ * either its running max m_r is still -inf or tm_r - m_r >= ln(lambda).  The
+ * tile is processed (exp, V load, PV product, m_r = max(m_r, tm_r)) when any
+ * row of the query tile votes keep, and skipped entirely otherwise.
+ * lambda = 0 never skips (plain causal attention); lambda must lie in [0, 1].
+ * O (q's shape/dtype), lse [B, Hq, Lq] f32.  Optional diagnostics:
+ * kept_tiles [B, Hq, NQT] int32 (tiles processed per query tile) and keep_map
+ * [B, Hq, NQT, NKT] uint8 (1 = processed; entries of tiles never visited are
+ * left unwritten).  Supported: bf16, D = 128, tile = 128, Lq == L (self
+ * attention from position q_pos0 = 0) or non-causal.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  float scale;
+  float lambda;
+  int32_t tile;
+  int32_t causal;
+} bsa_thresh_params;
+
+bsa_status bsa_threshold_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                       const bsa_thresh_params* p, const bsa_tensor* o, float* lse,
+                                       int32_t* kept_tiles, uint8_t* keep_map, void* stream);
+
+/* Status text and the calling thread's last error detail. */
+const char* bsa_status_string(int32_t status);
+const char* bsa_last_error(void);
+int32_t bsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

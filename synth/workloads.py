@@ -285,8 +285,9 @@ def threshold_prefill(seed: int = 5, L: int = 131072, Hq: int = 32, Hkv: int = 8
     Tokens fall into segments of ``seg_tiles`` tiles, each with a random unit
     code e_m per group.  Queries add alpha*e_seg(r); keys add
     alpha*(e_seg(s) + e_seg(s)+1), so a query sees its own and the previous
-    segment strongly (a local window).  Per KV head, ``n_needles`` tiles add
-    alpha*w_g to their keys while every query of the group adds alpha*w_g.
+    segment strongly (a local window).  Per KV head, ``n_needles`` tiles carry
+    alpha*w_g in their keys instead of the segment codes, while every query of
+    the group adds alpha*w_g: a needle is seen by every later query.
     alpha^2 / sqrt(D) = ``logit_gap``.  Everything outside the window and the
     needles sits far below the running max, so about 70% of causal tiles are
     skippable at lambda = 1e-3 with the default sizes.
@@ -316,9 +317,12 @@ def threshold_prefill(seed: int = 5, L: int = 131072, Hq: int = 32, Hkv: int = 8
         qstruct = alpha * (e[seg] + w[None, :])
         for h in hs:
             qb[h] = _store(_normal(seed, _Q, h, (L, D)) + qstruct, "bf16")
-        kg = _normal(seed, _K, g, (L, D)) + alpha * (e[seg] + e[seg + 1])
+        kstruct = alpha * (e[seg] + e[seg + 1])
         for t in nd:
-            kg[t * tile:min((t + 1) * tile, L)] += alpha * w
+            # a needle tile carries the needle code instead of its segment codes, so
+            # inside a query's window it scores like the window, not twice as high
+            kstruct[t * tile:min((t + 1) * tile, L)] = alpha * w
+        kg = _normal(seed, _K, g, (L, D)) + kstruct
         kb[g] = _store(kg, "bf16")
         vb[g] = _store(_normal(seed, _V, g, (L, D)), "bf16")
     params = dict(tile=tile, causal=1, lam=lam, scale=1.0 / math.sqrt(D))

@@ -1,0 +1,168 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments on the host before any launch.
+
+Pointers passed here are fake (never dereferenced): every call below returns
+from host-side validation, which runs before anything touches the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+bsa = pytest.importorskip("dlm_bsa_block_amd")
+from dlm_bsa_block_amd import _lib as L  # noqa: E402
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libbsa.so not built")
+    return L.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L._SIGS, f"binding has no signature for {n}"
+
+
+def test_status_strings(lib):
+    assert lib.bsa_status_string(0) == b"ok"
+    assert lib.bsa_status_string(3) == b"index-list capacity too small"
+    assert lib.bsa_version() >= 1
+
+
+def _t(B=1, H=8, Lq=64, D=128, dtype=L.BSA_BF16, data=FAKE):
+    return L.BsaTensor(data, dtype, B, H, Lq, D, H * Lq * D, Lq * D, D)
+
+
+def _err(lib):
+    return lib.bsa_last_error().decode()
+
+
+def test_summaries_rejects_bad_arguments(lib):
+    x = _t()
+    st = lib.bsa_build_block_summaries(ctypes.byref(x), 48, 0, 0, -1, FAKE, None, None)
+    assert st == L.BSA_ERR_UNSUPPORTED and "block_size" in _err(lib)
+    st = lib.bsa_build_block_summaries(ctypes.byref(_t(D=96)), 64, 0, 0, -1, FAKE, None, None)
+    assert st == L.BSA_ERR_UNSUPPORTED
+    st = lib.bsa_build_block_summaries(ctypes.byref(_t(data=FAKE + 8)), 64, 0, 0, -1, FAKE, None, None)
+    assert st == L.BSA_ERR_INVALID and "aligned" in _err(lib)
+    st = lib.bsa_build_block_summaries(ctypes.byref(x), 64, 0, 0, 5, FAKE, None, None)
+    assert st == L.BSA_ERR_INVALID            # 64 tokens -> 1 block, 5 requested
+    st = lib.bsa_build_block_summaries(ctypes.byref(x), 64, 7, 0, -1, FAKE, None, None)
+    assert st == L.BSA_ERR_INVALID
+    st = lib.bsa_build_block_summaries(None, 64, 0, 0, -1, FAKE, None, None)
+    assert st == L.BSA_ERR_INVALID
+    st = lib.bsa_build_block_summaries(ctypes.byref(x), 64, 0, 0, -1, None, None, None)
+    assert st == L.BSA_ERR_INVALID
+    # empty sequence: nothing to do, nothing launched
+    st = lib.bsa_build_block_summaries(ctypes.byref(_t(Lq=0)), 64, 0, 0, -1, FAKE, None, None)
+    assert st == L.BSA_OK
+
+
+def test_select_capacity_and_workspace(lib):
+    q = _t(H=32, Lq=1)
+    p = bsa.select_params(kv_block=64, q_block=1, topk=13, n_first=1, n_last=2, cap=15)
+    st = lib.bsa_select_blocks(ctypes.byref(q), None, FAKE, None, 8, 1024, ctypes.byref(p), None, FAKE, FAKE, None,
+                               None, FAKE, 1 << 30, None)
+    assert st == L.BSA_ERR_CAPACITY and "cap 15 < 16" in _err(lib)
+    p.cap = 16
+    need = lib.bsa_select_workspace_bytes(ctypes.byref(q), 8, 1024, ctypes.byref(p))
+    assert need >= 32 * 1024 * 4
+    st = lib.bsa_select_blocks(ctypes.byref(q), None, FAKE, None, 8, 1024, ctypes.byref(p), None, FAKE, FAKE, None,
+                               None, FAKE, need - 1, None)
+    assert st == L.BSA_ERR_WORKSPACE
+    st = lib.bsa_select_blocks(ctypes.byref(q), None, FAKE, None, 7, 1024, ctypes.byref(p), None, FAKE, FAKE, None,
+                               None, FAKE, need, None)
+    assert st == L.BSA_ERR_INVALID            # 7 does not divide 32
+    st = lib.bsa_select_blocks(ctypes.byref(q), None, FAKE, None, 8, 5000, ctypes.byref(p), None, FAKE, FAKE, None,
+                               None, FAKE, 1 << 30, None)
+    assert st == L.BSA_ERR_UNSUPPORTED
+    # dual band needs energies; pooled queries must be f32
+    p2 = bsa.select_params(kv_block=128, q_block=128, pooled_q=1, causal=1, topk_num=1, topk_den=10, n_first=1,
+                           n_last=1, dual_band=1, cap=256)
+    qm = _t(H=32, Lq=256, dtype=L.BSA_F32)
+    st = lib.bsa_select_blocks(ctypes.byref(qm), None, FAKE, None, 8, 256, ctypes.byref(p2), None, FAKE, FAKE, None,
+                               None, FAKE, 1 << 30, None)
+    assert st == L.BSA_ERR_INVALID and "energy" in _err(lib)
+    st = lib.bsa_select_blocks(ctypes.byref(_t(H=32, Lq=256)), FAKE, FAKE, FAKE, 8, 256, ctypes.byref(p2), None,
+                               FAKE, FAKE, None, None, FAKE, 1 << 30, None)
+    assert st == L.BSA_ERR_INVALID and "f32" in _err(lib)
+    # union over a 32-row block: capacity bound is min(NB, 32 * 16)
+    p3 = bsa.select_params(kv_block=64, q_block=32, topk=16, cap=511)
+    st = lib.bsa_select_blocks(ctypes.byref(_t(H=32, Lq=32)), None, FAKE, None, 8, 512, ctypes.byref(p3), None,
+                               FAKE, FAKE, None, None, FAKE, 1 << 30, None)
+    assert st == L.BSA_ERR_CAPACITY
+
+
+def test_attention_rejects_bad_arguments(lib):
+    q, k = _t(H=32, Lq=32), _t(H=8, Lq=4096)
+    p = bsa.attn_params(kv_block=64, q_block=32, cap=512)
+    need = lib.bsa_attention_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(p))
+    assert need > 0
+    st = lib.bsa_sparse_attention_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), FAKE, FAKE,
+                                      ctypes.byref(p), None, ctypes.byref(q), FAKE, FAKE, need - 1, None)
+    assert st == L.BSA_ERR_WORKSPACE
+    qf = _t(H=32, Lq=32, dtype=L.BSA_F32)
+    st = lib.bsa_sparse_attention_fwd(ctypes.byref(qf), ctypes.byref(k), ctypes.byref(k), FAKE, FAKE,
+                                      ctypes.byref(p), None, ctypes.byref(qf), FAKE, FAKE, 1 << 30, None)
+    assert st == L.BSA_ERR_INVALID            # dtype mismatch q/k
+    p96 = bsa.attn_params(kv_block=96, q_block=32, cap=512)
+    st = lib.bsa_sparse_attention_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), FAKE, FAKE,
+                                      ctypes.byref(p96), None, ctypes.byref(q), FAKE, FAKE, 1 << 30, None)
+    assert st == L.BSA_ERR_UNSUPPORTED
+    # decode path supports G in {1, 2, 4, 8}
+    q3, k3 = _t(H=48, Lq=1), _t(H=3, Lq=4096)
+    pd = bsa.attn_params(kv_block=64, q_block=1, cap=16)
+    st = lib.bsa_sparse_attention_fwd(ctypes.byref(q3), ctypes.byref(k3), ctypes.byref(k3), FAKE, FAKE,
+                                      ctypes.byref(pd), None, ctypes.byref(q3), FAKE, FAKE, 1 << 30, None)
+    assert st == L.BSA_ERR_UNSUPPORTED
+
+
+def test_threshold_rejects_bad_arguments(lib):
+    q, k = _t(H=32, Lq=1024), _t(H=8, Lq=1024)
+    for lam, tile, want in ((1.5, 128, L.BSA_ERR_INVALID), (-0.1, 128, L.BSA_ERR_INVALID),
+                            (1e-3, 64, L.BSA_ERR_UNSUPPORTED)):
+        p = L.BsaThreshParams(0.088, lam, tile, 1)
+        st = lib.bsa_threshold_attention_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(p),
+                                             ctypes.byref(q), FAKE, None, None, None)
+        assert st == want, (lam, tile, _err(lib))
+    p = L.BsaThreshParams(0.088, 1e-3, 128, 1)
+    kk = _t(H=8, Lq=2048)
+    st = lib.bsa_threshold_attention_fwd(ctypes.byref(q), ctypes.byref(kk), ctypes.byref(kk), ctypes.byref(p),
+                                         ctypes.byref(q), FAKE, None, None, None)
+    assert st == L.BSA_ERR_UNSUPPORTED        # causal needs Lq == L
+
+
+def test_active_rows_rejects_mismatch(lib):
+    a, b = _t(H=32, Lq=32), _t(H=32, Lq=31)
+    st = lib.bsa_active_rows(ctypes.byref(a), ctypes.byref(b), 0.1, FAKE, None, None)
+    assert st == L.BSA_ERR_INVALID
+    st = lib.bsa_active_rows(ctypes.byref(a), ctypes.byref(a), float("nan"), FAKE, None, None)
+    assert st == L.BSA_ERR_INVALID
+
+
+def test_product_path_does_not_import_oracle():
+    """The library binding never reaches the CPU oracle."""
+    import sys
+    pkg = os.path.join(ROOT, "dlm_bsa_block_amd")
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            src = open(os.path.join(pkg, f)).read()
+            assert "oracle" not in src.replace("oracle/", ""), f
+    assert "oracle" not in sys.modules.get("dlm_bsa_block_amd").__dict__

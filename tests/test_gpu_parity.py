@@ -1,0 +1,368 @@
+"""GPU vs fp64 oracle parity for every step of the hot path (needs an MI355X).
+
+Each case generates seeded synthetic inputs, runs the HIP library through its
+C ABI (via the thin binding) and checks the results against the oracle on the
+same stored values: block summaries and energies, band temperatures, per-row
+picks and per-block lists (tie band 1e-6), attention outputs and LSE, active
+rows, and threshold keep/skip decisions.  Small cases span several tiles and
+a ragged tail; the full-size cases use the shapes and launch configuration
+the benchmark times, checked on sampled rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import synth
+from parity import (THRESH_EPS, ambiguous, check_list, check_outputs, check_row_picks, from_dev, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import dlm_bsa_block_amd as m
+    m.lib()          # raises when libbsa.so is missing: never silently skipped on a GPU
+    return m
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------- summaries ---
+@pytest.mark.parametrize("dtype,D,L,block,layout", [
+    ("bf16", 128, 1000, 64, 0), ("bf16", 128, 4000, 128, 1), ("f32", 64, 1024, 64, 0),
+    ("bf16", 64, 777, 16, 1), ("f32", 128, 300, 256, 0), ("bf16", 128, 96, 32, 0)])
+def test_summaries(bsa, dtype, D, L, block, layout):
+    rng = np.random.default_rng(L + D)
+    x64 = rng.standard_normal((2, 3, L, D)) * 1.5
+    xs = synth.f32_to_bf16_bits(x64.astype(np.float32)) if dtype == "bf16" else x64.astype(np.float32)
+    xr = synth.storage_to_f64(xs, dtype)
+    xd = to_dev(xs, dtype)
+    mean, energy = bsa.bsa_build_block_summaries(xd, block, layout)
+    _sync()
+    m_ref, e_ref = orc.block_summaries(xr, block, layout)
+    assert np.allclose(from_dev(mean), m_ref, rtol=1e-5, atol=2e-6)
+    assert np.allclose(from_dev(energy), e_ref, rtol=1e-5, atol=1e-5)
+    # partial rebuild: only the newest block is written
+    NB = m_ref.shape[2]
+    mean2 = torch.full_like(mean, float("nan"))
+    bsa.bsa_build_block_summaries(xd, block, layout, first_block=NB - 1, num_blocks=1, mean=mean2, energy=energy)
+    _sync()
+    m2 = from_dev(mean2)
+    assert np.isnan(m2[:, :, :NB - 1]).all()
+    assert np.allclose(m2[:, :, NB - 1], m_ref[:, :, NB - 1], rtol=1e-5, atol=2e-6)
+
+
+def test_summaries_strided_view(bsa):
+    """A [B, H, L, D] view with a padded row stride (e.g. a slice of a larger cache)."""
+    rng = np.random.default_rng(5)
+    big = synth.f32_to_bf16_bits(rng.standard_normal((1, 2, 512, 192)).astype(np.float32))
+    xd = to_dev(big, "bf16")[:, :, :, 32:160]
+    mean, _ = bsa.bsa_build_block_summaries(xd, 64, 0)
+    _sync()
+    m_ref, _ = orc.block_summaries(synth.storage_to_f64(big, "bf16")[:, :, :, 32:160], 64, 0)
+    assert np.allclose(from_dev(mean), m_ref, rtol=1e-5, atol=2e-6)
+
+
+# -------------------------------------------------------------- pipelines ---
+def _dev_workload(w):
+    return to_dev(w.q, w.dtype), to_dev(w.k, w.dtype), to_dev(w.v, w.dtype)
+
+
+def _select_raw(bsa, w, qd, kmean, row_mask=None):
+    p = w.params
+    D = w.q.shape[3]
+    sp = bsa.select_params(kv_block=p["kv_block"], q_block=p["q_block"], q_pos0=p["q_pos0"], causal=p["causal"],
+                           topk=p["topk"], topk_num=p["topk_num"], topk_den=p["topk_den"], n_first=p["n_first"],
+                           n_last=p["n_last"], layout=p["layout"], scale=p["scale"], D=D)
+    idx, cnt, rp, _ = bsa.bsa_select_blocks(qd, kmean, sp, row_mask=row_mask, want_row_picks=True)
+    return idx, cnt, rp, sp.cap
+
+
+def _check_selection(sel, idx, cnt, rp, rows_of_block, where):
+    """Per-row picks with the tie band, then every list; returns the tie-band sizes."""
+    idx, cnt, rp = idx.cpu().numpy(), cnt.cpu().numpy(), rp.cpu().numpy()
+    bands = {}
+    for (b, g, r), row in sel["rows"].items():
+        check_row_picks(rp[b, g, r], row, f"{where} row b{b} g{g} r{r}")
+    B, Hkv, NQB = cnt.shape
+    n_tie = 0
+    for b in range(B):
+        for g in range(Hkv):
+            for qb in range(NQB):
+                band = set()
+                for r in rows_of_block(qb):
+                    if (b, g, r) in sel["rows"]:
+                        band |= ambiguous(sel["rows"][(b, g, r)])
+                n_tie += len(band)
+                check_list(idx[b, g, qb], int(cnt[b, g, qb]), sel["lists"][b][g][qb], band, f"{where} list g{g} qb{qb}")
+                bands[(b, g, qb)] = band
+    return idx, cnt, n_tie
+
+
+def _reference_lists(sel, idx, cnt):
+    """The oracle's lists, except where the GPU's list differs inside the tie band
+    (already checked): there either answer is correct and the GPU's is used."""
+    B, Hkv, NQB = cnt.shape
+    out = [[[None] * NQB for _ in range(Hkv)] for _ in range(B)]
+    for b in range(B):
+        for g in range(Hkv):
+            for qb in range(NQB):
+                gl = idx[b, g, qb, :cnt[b, g, qb]].astype(np.int64)
+                ol = sel["lists"][b][g][qb]
+                out[b][g][qb] = ol if np.array_equal(gl, ol) else gl
+    return out
+
+
+def _decode_case(bsa, w):
+    p = w.params
+    qd, kd, vd = _dev_workload(w)
+    kmean, kenergy = bsa.bsa_build_block_summaries(kd, p["kv_block"], p["layout"])
+    idx, cnt, rp, cap = _select_raw(bsa, w, qd, kmean)
+    ap = bsa.attn_params(kv_block=p["kv_block"], q_block=1, cap=cap, q_pos0=p["q_pos0"], causal=p["causal"],
+                         scale=p["scale"])
+    o, lse = bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap)
+    _sync()
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    km_ref, _ = orc.block_summaries(k, p["kv_block"], p["layout"])
+    assert np.allclose(from_dev(kmean), km_ref, rtol=1e-5, atol=2e-6)
+    sel = orc.select_blocks(p, km_ref, q=q)
+    idx_np, cnt_np, n_tie = _check_selection(sel, idx, cnt, rp, lambda qb: [qb], w.name)
+    O_ref, L_ref = orc.sparse_attention(p, q, k, v, _reference_lists(sel, idx_np, cnt_np))
+    stats = check_outputs(from_dev(o), O_ref, from_dev(lse), L_ref, w.name)
+    return stats, idx_np, cnt_np, n_tie
+
+
+def test_tiny_decode_exact_config(bsa):
+    w = synth.tiny_decode()
+    stats, idx, cnt, n_tie = _decode_case(bsa, w)
+    assert cnt[0, 0, 0] == 4 and {0, 15} <= set(idx[0, 0, 0, :4].tolist())
+
+
+@pytest.mark.parametrize("L", [8192, 8000, 1000])
+def test_gqa_decode_small(bsa, L):
+    w = synth.gqa_decode(L=L, n_needles=4)
+    stats, idx, cnt, _ = _decode_case(bsa, w)
+    NB = -(-L // 64)
+    for g in range(8):
+        lst = set(idx[0, g, 0, :cnt[0, g, 0]].tolist())
+        assert len(lst) == 16 and {0, NB - 2, NB - 1} <= lst
+        assert set(w.extra["needles"][g].tolist()) <= lst
+
+
+def test_gqa_decode_full_size(bsa):
+    """64K decode, 32 query / 8 KV heads: the benchmark's workload and launch."""
+    w = synth.gqa_decode()
+    stats, idx, cnt, _ = _decode_case(bsa, w)
+    assert (cnt == 16).all()
+
+
+def test_decode_select_everything_is_dense(bsa):
+    """k' >= |C \\ F|: the list is every block, output equals dense attention."""
+    w = synth.gqa_decode(L=2000, Hq=8, Hkv=2, n_needles=2)
+    w.params.update(topk=1000)
+    stats, idx, cnt, _ = _decode_case(bsa, w)
+    assert (cnt == 32).all()
+
+
+def _dlm_case(bsa, w, union_active: bool, full_check_rows=None):
+    p = w.params
+    qd, kd, vd = _dev_workload(w)
+    qprev = to_dev(w.extra["q_prev"], "bf16")
+    mask, mse = bsa.bsa_active_rows(qd, qprev, p["theta_act"])
+    kmean, _ = bsa.bsa_build_block_summaries(kd, p["kv_block"], p["layout"])
+    idx, cnt, rp, cap = _select_raw(bsa, w, qd, kmean, row_mask=mask if union_active else None)
+    ap = bsa.attn_params(kv_block=p["kv_block"], q_block=p["q_block"], cap=cap, q_pos0=p["q_pos0"],
+                         causal=p["causal"], scale=p["scale"])
+    # cached outputs of the previous step: any values; stable rows must keep them bit for bit
+    cache_o = torch.randn(qd.shape, device="cuda").to(torch.bfloat16)
+    cache_l = torch.randn(qd.shape[:3], device="cuda")
+    o, lse = bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap, row_mask=mask, o=cache_o.clone(),
+                                          lse=cache_l.clone())
+    _sync()
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    m_ref, mse_ref = orc.active_rows(q, w.f64("q_prev"), p["theta_act"])
+    assert np.array_equal(mask.cpu().numpy().astype(bool), m_ref)
+    assert np.allclose(mse.cpu().numpy(), mse_ref, rtol=1e-5)
+    km_ref, _ = orc.block_summaries(k, p["kv_block"], p["layout"])
+    sel = orc.select_blocks(p, km_ref, q=q, row_mask=m_ref if union_active else None)
+    R = p["q_block"]
+    idx_np, cnt_np, _ = _check_selection(sel, idx, cnt, rp, lambda qb: range(qb * R, (qb + 1) * R), w.name)
+    O_ref, L_ref = orc.sparse_attention(p, q, k, v, _reference_lists(sel, idx_np, cnt_np), row_mask=m_ref)
+    act = np.nonzero(m_ref[0])[0]
+    o_np, l_np = from_dev(o), lse.cpu().numpy()
+    stats = check_outputs(o_np[:, :, act], O_ref[:, :, act], l_np[:, :, act], L_ref[:, :, act], w.name)
+    stable = np.nonzero(~m_ref[0])[0]
+    assert torch.equal(o[:, :, stable], cache_o[:, :, stable])
+    assert torch.equal(lse[:, :, stable], cache_l[:, :, stable])
+    return stats, cnt_np
+
+
+@pytest.mark.parametrize("union_active", [False, True])
+def test_dlm_denoise_small(bsa, union_active):
+    w = synth.dlm_denoise(L=4096 + 100, n_needles=4)
+    _dlm_case(bsa, w, union_active)
+
+
+def test_dlm_denoise_full_size(bsa):
+    w = synth.dlm_denoise()
+    _, cnt_all = _dlm_case(bsa, w, False)
+    _, cnt_act = _dlm_case(bsa, w, True)
+    assert (cnt_act <= cnt_all).all() and (cnt_act < cnt_all).any()
+
+
+def test_dlm_no_active_rows_writes_nothing(bsa):
+    w = synth.dlm_denoise(L=2048, n_needles=2)
+    p = w.params
+    qd, kd, vd = _dev_workload(w)
+    kmean, _ = bsa.bsa_build_block_summaries(kd, 64, 0)
+    mask = torch.zeros((1, 32), dtype=torch.uint8, device="cuda")
+    idx, cnt, rp, cap = _select_raw(bsa, w, qd, kmean, row_mask=mask)
+    ap = bsa.attn_params(kv_block=64, q_block=32, cap=cap, q_pos0=p["q_pos0"])
+    o0 = torch.randn(qd.shape, device="cuda").to(torch.bfloat16)
+    o, lse = bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap, row_mask=mask, o=o0.clone())
+    _sync()
+    assert (cnt == 0).all() and torch.equal(o, o0)
+    assert (rp == -1).all()
+
+
+def _prefill_case(bsa, w, sample_qb=None):
+    p = w.params
+    qd, kd, vd = _dev_workload(w)
+    b = p["kv_block"]
+    qmean, qen = bsa.bsa_build_block_summaries(qd, b, p["layout"])
+    kmean, ken = bsa.bsa_build_block_summaries(kd, b, p["layout"])
+    Lq = w.q.shape[2]
+    sp = bsa.select_params(kv_block=b, q_block=p["q_block"], q_pos0=0, q_len=Lq, causal=1, pooled_q=1,
+                           topk_num=p["topk_num"], topk_den=p["topk_den"], n_first=p["n_first"], n_last=p["n_last"],
+                           dual_band=1, layout=p["layout"], scale=p["scale"])
+    idx, cnt, rp, tau = bsa.bsa_select_blocks(qmean, kmean, sp, k_energy=ken, q_energy=qen, want_row_picks=True,
+                                              want_tau=True)
+    ap = bsa.attn_params(kv_block=b, q_block=p["q_block"], cap=sp.cap, q_pos0=0, causal=1, scale=p["scale"])
+    o, lse = bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap)
+    _sync()
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    qm_ref, qe_ref = orc.block_summaries(q, b, p["layout"])
+    km_ref, ke_ref = orc.block_summaries(k, b, p["layout"])
+    assert np.allclose(from_dev(qmean), qm_ref, rtol=1e-5, atol=2e-6)
+    assert np.allclose(from_dev(ken), ke_ref, rtol=1e-5, atol=1e-5)
+    G = w.q.shape[1] // w.k.shape[1]
+    tau_ref = orc.band_temperatures(km_ref, ke_ref, p["layout"], G, qm_ref, qe_ref)
+    assert np.allclose(tau.cpu().numpy(), tau_ref, rtol=2e-5)
+    sel = orc.select_blocks(p, km_ref, q_mean=qm_ref, tau=tau_ref, Lq=Lq)
+    idx_np, cnt_np, n_tie = _check_selection(sel, idx, cnt, rp, lambda qb: [qb], w.name)
+    NQB = cnt_np.shape[2]
+    qbs = list(range(NQB)) if sample_qb is None else sample_qb
+    O_ref, L_ref = orc.sparse_attention(p, q, k, v, _reference_lists(sel, idx_np, cnt_np), qblocks=qbs)
+    rows = np.concatenate([np.arange(i * b, min((i + 1) * b, Lq)) for i in qbs])
+    stats = check_outputs(from_dev(o)[:, :, rows], O_ref[:, :, rows], lse.cpu().numpy()[:, :, rows],
+                          L_ref[:, :, rows], w.name)
+    return stats, cnt_np
+
+
+@pytest.mark.parametrize("L", [4096, 4000])
+def test_sparse_prefill_small(bsa, L):
+    w = synth.sparse_prefill(L=L, Hq=8, Hkv=2)
+    stats, cnt = _prefill_case(bsa, w)
+    NQB = cnt.shape[2]
+    for i in range(NQB):
+        assert cnt[0, 0, i] == min(i + 1, (2 if i else 1) + -(-(i + 1) // 10))
+
+
+def test_sparse_prefill_full_size(bsa):
+    """32K causal prefill, 32/8 heads: selection on every query block, outputs on 16 sampled blocks."""
+    w = synth.sparse_prefill()
+    rng = np.random.default_rng(4)
+    sample = sorted(set([0, 255] + rng.choice(256, 14, replace=False).tolist()))
+    stats, cnt = _prefill_case(bsa, w, sample_qb=sample)
+    assert int(cnt[0].sum(axis=1)[0]) == 3915
+
+
+# --------------------------------------------------------------- threshold ---
+def _threshold_case(bsa, w, lam, pairs):
+    """The oracle walks each sampled (head, query tile) with its own decisions.  If
+    the GPU's keep map matches, outputs are compared with that walk.  Otherwise
+    every differing decision must sit within THRESH_EPS of the fp64 threshold;
+    the walk is then replayed on the GPU's choices (each of which must agree with
+    the fp64 state along that path outside the band) and outputs are compared
+    with the replay."""
+    p = w.params
+    qd, kd, vd = _dev_workload(w)
+    o, lse, kept, km = bsa.bsa_threshold_attention_fwd(qd, kd, vd, lam, scale=p["scale"], tile=p["tile"],
+                                                       causal=p["causal"], want_keep_map=True)
+    _sync()
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    km_np, kept_np = km.cpu().numpy(), kept.cpu().numpy()
+    o_np, l_np = from_dev(o), lse.cpu().numpy()
+    G = w.q.shape[1] // w.k.shape[1]
+    T = p["tile"]
+    Lq = w.q.shape[2]
+    n_replayed = 0
+    for (b, h, qt) in pairs:
+        jmax = min(Lq - 1, (qt + 1) * T - 1) // T
+        dec = {j: bool(km_np[b, h, qt, j]) for j in range(jmax + 1)}
+        rows = np.arange(qt * T, min((qt + 1) * T, Lq))
+        args = (q[b, h, rows], k[b, h // G], v[b, h // G], rows, T, lam, p["scale"], bool(p["causal"]))
+        r = orc.threshold_walk(*args)
+        if r["decision"] != dec:
+            # tiles are visited from the highest index down: the first differing
+            # choice must sit in the rounding band of the fp64 walk
+            first = max(j for j in dec if dec[j] != r["decision"][j])
+            assert abs(r["margin"][first]) <= THRESH_EPS, \
+                f"h{h} qt{qt} tile {first}: gpu keep={dec[first]}, fp64 margin {r['margin'][first]:.4g}"
+            r = orc.threshold_walk(*args, decisions=dec)
+            n_replayed += 1
+            for j, mg in r["margin"].items():
+                if abs(mg) > THRESH_EPS:
+                    assert dec[j] == (mg >= 0), f"h{h} qt{qt} tile {j}: gpu keep={dec[j]}, fp64 margin {mg:.4g}"
+        assert kept_np[b, h, qt] == len(r["kept"])
+        check_outputs(o_np[b, h, rows], r["O"], l_np[b, h, rows], r["lse"], f"thr h{h} qt{qt}")
+    return kept_np, n_replayed
+
+
+@pytest.mark.parametrize("L,lam", [(4096, 1e-3), (4000, 1e-3), (2048, 0.0), (4096, 0.3)])
+def test_threshold_small(bsa, L, lam):
+    w = synth.threshold_prefill(L=L, Hq=8, Hkv=2, seg_tiles=5, n_needles=2)
+    NQT = -(-L // 128)
+    pairs = [(0, h, qt) for h in (0, 3, 5) for qt in range(NQT)]
+    kept, _ = _threshold_case(bsa, w, lam, pairs)
+    if lam == 0.0:
+        assert np.array_equal(kept[0, 0], np.arange(1, NQT + 1))
+
+
+def test_threshold_full_size_sampled(bsa):
+    """128K causal prefill with lambda = 1e-3: sampled query tiles of two heads."""
+    heads = [0, 13]
+    w = synth.threshold_prefill(heads=heads)
+    rng = np.random.default_rng(5)
+    qts = sorted(set([0, 1023] + rng.choice(1024, 4, replace=False).tolist()))
+    kept, _ = _threshold_case(bsa, w, 1e-3, [(0, h, qt) for h in heads for qt in qts])
+    frac_skip = 1.0 - kept[0, heads].sum() / (len(heads) * 1024 * 1025 / 2)
+    assert 0.66 < frac_skip < 0.74
+
+
+# ------------------------------------------------------------- determinism ---
+def test_bitwise_repeatable(bsa):
+    w = synth.sparse_prefill(L=2048, Hq=8, Hkv=2)
+    outs = []
+    for _ in range(2):
+        qd, kd, vd = _dev_workload(w)
+        p = w.params
+        qmean, qen = bsa.bsa_build_block_summaries(qd, 128, p["layout"])
+        kmean, ken = bsa.bsa_build_block_summaries(kd, 128, p["layout"])
+        sp = bsa.select_params(kv_block=128, q_block=128, q_len=2048, causal=1, pooled_q=1, topk_num=1, topk_den=10,
+                               n_first=1, n_last=1, dual_band=1, layout=p["layout"])
+        idx, cnt, _, _ = bsa.bsa_select_blocks(qmean, kmean, sp, k_energy=ken, q_energy=qen)
+        ap = bsa.attn_params(kv_block=128, q_block=128, cap=sp.cap, causal=1)
+        o, lse = bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap)
+        o2, lse2, kept, _ = bsa.bsa_threshold_attention_fwd(qd, kd, vd, 1e-3)
+        _sync()
+        outs.append([t.clone() for t in (qmean, kmean, idx, cnt, o, lse, o2, lse2, kept)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -389,7 +389,7 @@ def test_threshold_workload_skip_fraction_on_sample():
     q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
     seg = w.extra["seg_tiles"]
     needle = int(w.extra["needles"][0, 0])
-    for qt in (5, 20, 37, 50):      # the needle (tile 63 for this seed) is not yet visible
+    for qt in (5, 20, 37, 50, 63):
         r = orc.threshold_attention(p, q, k, v, [(0, 0, qt)])[(0, 0, qt)]
         m = qt // seg
         window = set(range(max(0, (m - 1) * seg), qt + 1))
