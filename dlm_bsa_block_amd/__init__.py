@@ -85,8 +85,11 @@ def bsa_select_workspace_bytes(q: torch.Tensor, num_kv_heads: int, num_kv_blocks
 
 
 def bsa_select_blocks(q: torch.Tensor, k_mean: torch.Tensor, p: BsaSelectParams, k_energy=None, q_energy=None,
-                      row_mask=None, want_row_picks=False, want_tau=False, workspace=None):
-    """Returns (idx [B,Hkv,NQB,cap] int32, cnt [B,Hkv,NQB] int32, row_picks or None, tau or None)."""
+                      row_mask=None, want_row_picks=False, want_tau=False, workspace=None, idx=None, cnt=None):
+    """Returns (idx [B,Hkv,NQB,cap] int32, cnt [B,Hkv,NQB] int32, row_picks or None, tau or None).
+
+    idx, cnt and workspace may be passed in (e.g. for graph capture, where
+    nothing may be allocated)."""
     B, Hkv, NB, D = k_mean.shape
     Hq = q.shape[1]
     if p.pooled_q:
@@ -99,14 +102,16 @@ def bsa_select_blocks(q: torch.Tensor, k_mean: torch.Tensor, p: BsaSelectParams,
     if p.cap <= 0:
         p.cap = list_capacity(NB, 1 if p.pooled_q else min(p.q_block, q.shape[2]), p)
     dev = q.device
-    idx = torch.empty((B, Hkv, NQB, p.cap), dtype=torch.int32, device=dev)
-    cnt = torch.empty((B, Hkv, NQB), dtype=torch.int32, device=dev)
+    if idx is None:
+        idx = torch.empty((B, Hkv, NQB, p.cap), dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv, NQB), dtype=torch.int32, device=dev)
     rp = torch.empty((B, Hkv, R, p.cap), dtype=torch.int32, device=dev) if want_row_picks else None
     tau = torch.empty((B, Hq, 2), dtype=torch.float32, device=dev) if want_tau else None
     qd = tensor_desc(q)
     need = lib().bsa_select_workspace_bytes(ctypes.byref(qd), Hkv, NB, ctypes.byref(p))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)   # counters start at zero
     check(lib().bsa_select_blocks(ctypes.byref(qd), _ptr(q_energy), k_mean.data_ptr(), _ptr(k_energy), Hkv, NB,
                                   ctypes.byref(p), _ptr(row_mask), idx.data_ptr(), cnt.data_ptr(), _ptr(rp),
                                   _ptr(tau), workspace.data_ptr(), workspace.numel(), _stream()),
@@ -115,10 +120,12 @@ def bsa_select_blocks(q: torch.Tensor, k_mean: torch.Tensor, p: BsaSelectParams,
 
 
 # ------------------------------------------------------------- active rows ---
-def bsa_active_rows(q_cur: torch.Tensor, q_prev: torch.Tensor, theta: float, want_mse=True):
+def bsa_active_rows(q_cur: torch.Tensor, q_prev: torch.Tensor, theta: float, want_mse=True, mask=None, mse=None):
     B, H, R, D = q_cur.shape
-    mask = torch.empty((B, R), dtype=torch.uint8, device=q_cur.device)
-    mse = torch.empty((B, R), dtype=torch.float32, device=q_cur.device) if want_mse else None
+    if mask is None:
+        mask = torch.empty((B, R), dtype=torch.uint8, device=q_cur.device)
+    if mse is None and want_mse:
+        mse = torch.empty((B, R), dtype=torch.float32, device=q_cur.device)
     a, b = tensor_desc(q_cur), tensor_desc(q_prev)
     check(lib().bsa_active_rows(ctypes.byref(a), ctypes.byref(b), theta, mask.data_ptr(), _ptr(mse), _stream()),
           "bsa_active_rows")
@@ -141,7 +148,7 @@ def bsa_sparse_attention_fwd(q, k, v, idx, cnt, p: BsaAttnParams, row_mask=None,
     qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
     need = lib().bsa_attention_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(p))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)   # counters start at zero
     check(lib().bsa_sparse_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),
                                          cnt.data_ptr(), ctypes.byref(p), _ptr(row_mask), ctypes.byref(od),
                                          lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),

@@ -118,9 +118,12 @@ static bsa_status validate_select(const bsa_tensor* q, int32_t Hkv, int32_t NB, 
   if (p->cap < bound) return fail(BSA_ERR_CAPACITY, "cap %d < %lld (rows per block %d x (k' %d + forced %d))", p->cap,
                                   (long long)bound, R, pl.kp_max, p->n_first + p->n_last);
   const int Rtot = p->pooled_q ? pl.NQB : pl.Lq;
-  const size_t nz = (size_t)pl.B * q->H * Rtot * (p->dual_band ? 2 : 1) * NB;
+  const size_t nz = (size_t)pl.B * q->H * Rtot * (p->dual_band ? 2 : 1) * (size_t)((NB + 3) & ~3);
   pl.z_bytes = align256(nz * 4);
   pl.tau_bytes = p->dual_band ? align256((size_t)pl.B * q->H * 2 * 4) : 0;
+  const bool multi_row = !p->pooled_q && std::min(p->q_block, pl.Lq) > 1;
+  pl.bits_bytes = multi_row ? align256((size_t)pl.B * Hkv * Rtot * 128 * 4) : 0;
+  pl.cnt_bytes = 0;
   return BSA_OK;
 }
 
@@ -128,7 +131,7 @@ size_t bsa_select_workspace_bytes(const bsa_tensor* q, int32_t num_kv_heads, int
                                   const bsa_select_params* p) {
   SelectPlan pl;
   if (validate_select(q, num_kv_heads, num_kv_blocks, p, pl) != BSA_OK) return 0;
-  return pl.z_bytes + pl.tau_bytes;
+  return pl.z_bytes + pl.tau_bytes + pl.bits_bytes + pl.cnt_bytes;
 }
 
 bsa_status bsa_select_blocks(const bsa_tensor* q, const float* q_energy, const float* k_mean, const float* k_energy,
@@ -145,7 +148,7 @@ bsa_status bsa_select_blocks(const bsa_tensor* q, const float* q_energy, const f
     if (p->pooled_q && !q_energy) return fail(BSA_ERR_INVALID, "dual band with pooled queries needs q_energy");
   }
   if (row_mask && p->pooled_q) return fail(BSA_ERR_INVALID, "row_mask applies to raw query rows only");
-  const size_t need = pl.z_bytes + pl.tau_bytes;
+  const size_t need = pl.z_bytes + pl.tau_bytes + pl.bits_bytes + pl.cnt_bytes;
   if (!workspace || workspace_bytes < need)
     return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");

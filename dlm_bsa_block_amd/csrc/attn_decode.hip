@@ -1,14 +1,16 @@
-// Decode attention over the selected blocks, split over the KV list, plus the
-// fixed-order combine of split partials (also used by the MFMA split path).
+// Decode attention over the selected blocks, split over the KV list, and the
+// fixed-order combine of split partials.
 //
 // Decode is memory bound (NSA page, decode-speed section: the speed-up tracks
 // the tokens read).  Work is spread so that every CU streams a slice of the
-// selected KV: one workgroup per (32-token slice of the list, query row,
-// KV group).  The G query heads of the group share each K/V load (NSA
-// implementation-challenges section: GQA-aware access).  All of a thread's
-// loads are issued before any arithmetic.  Each workgroup writes an
-// unnormalised partial (m, l, acc) per query head; the combine merges them in
-// ascending slice order, so the result does not depend on scheduling.
+// selected KV: one workgroup per (slice of the list, query row, KV group).  The
+// G query heads of the group share each K/V load (NSA implementation-challenges
+// section: GQA-aware access).  A thread's K and V loads are issued before any
+// arithmetic.  Each workgroup writes an unnormalised partial (m, l, acc) per
+// query head; a combine kernel merges the partials in ascending slice order,
+// so the result does not depend on scheduling.  (Merging inside the last
+// workgroup to finish would need a device-scope fence per workgroup, which
+// costs far more than the extra kernel boundary on this chip.)
 #include "common.cuh"
 #include "internal.h"
 #include "split.h"
@@ -16,11 +18,11 @@
 namespace bsa {
 
 template <int DT, int D, int G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs a) {
+__global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   constexpr int ES = DT == BSA_BF16 ? 2 : 4;
   constexpr int LPT = D / 8;            // lanes per token
   constexpr int TPP = 64 / LPT;         // tokens per wave pass
-  constexpr int TPW = kDecTok / 4;      // tokens per wave
+  constexpr int TPW = kDecTok / 4;      // tokens per wave and chunk
   constexpr int PASSES = TPW / TPP;
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sm_acc[4][G][D];
@@ -31,40 +33,15 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs a) {
   const int tg = lane / LPT, d0 = (lane % LPT) * 8;
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
   const int row = qb;                                   // one query row per block
+  const int Hq = a.Hkv * G;
   if (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) return;
   const int64_t ntok = (int64_t)a.cnt[li] * a.kv_block;
-  const int64_t t_begin = (int64_t)item * kDecTok;
-  if (t_begin >= ntok) return;                          // the combine never reads this slice
+  const int64_t t_begin = (int64_t)item * a.tok_per_item;
+  if (ntok == 0) return;                                // the combine writes O = 0, LSE = -inf
+  if (t_begin >= ntok) return;                          // no slice of the list for this workgroup
   const int qpos = a.q_pos0 + row;
+  const int64_t t_end = min(ntok, t_begin + a.tok_per_item);
 
-  int pos[PASSES];
-  bool ok[PASSES];
-#pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int64_t t = t_begin + w * TPW + p * TPP + tg;
-    ok[p] = t < ntok;
-    pos[p] = 0;
-    if (ok[p]) {
-      const int e = (int)(t / a.kv_block), off = (int)(t - (int64_t)e * a.kv_block);
-      const int blk = a.idx[li * a.cap + e];
-      const int key = blk * a.kv_block + off;
-      ok[p] = blk >= 0 && key < a.L && (!a.causal || key <= qpos);
-      pos[p] = key;
-    }
-  }
-  float kx[PASSES][8], vx[PASSES][8];
-  const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + d0) * ES;
-  const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + d0) * ES;
-#pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    if (ok[p]) {
-      load8<DT>(kb + (int64_t)pos[p] * a.ksl * ES, kx[p]);
-      load8<DT>(vb + (int64_t)pos[p] * a.vsl * ES, vx[p]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { kx[p][e] = 0.f; vx[p][e] = 0.f; }
-    }
-  }
   float qx[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -72,49 +49,96 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) qx[h][e] *= a.c2;
   }
-
+  float wm[G], wl[G], wacc[G][8];                       // this wave's running state
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float s[PASSES];
+    wm[h] = -INFINITY;
+    wl[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wacc[h][e] = 0.f;
+  }
+  const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + d0) * ES;
+  const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + d0) * ES;
+
+  for (int64_t c0 = t_begin; c0 < t_end; c0 += kDecTok) {
+    int pos[PASSES];
+    bool ok[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      float dot = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot = fmaf(qx[h][e], kx[p][e], dot);
-#pragma unroll
-      for (int m = 1; m < LPT; m <<= 1) dot += wave_xor(dot, m);
-      s[p] = ok[p] ? dot : -INFINITY;
+      const int64_t t = c0 + w * TPW + p * TPP + tg;
+      ok[p] = t < t_end;
+      pos[p] = 0;
+      if (ok[p]) {
+        const int e = (int)(t / a.kv_block), off = (int)(t - (int64_t)e * a.kv_block);
+        const int blk = a.idx[li * a.cap + e];
+        const int key = blk * a.kv_block + off;
+        ok[p] = blk >= 0 && key < a.L && (!a.causal || key <= qpos);
+        pos[p] = key;
+      }
     }
-    float mx = s[0];
+    float kx[PASSES][8], vx[PASSES][8];
 #pragma unroll
-    for (int p = 1; p < PASSES; ++p) mx = fmaxf(mx, s[p]);
+    for (int p = 0; p < PASSES; ++p) {
+      if (ok[p]) {
+        load8<DT>(kb + (int64_t)pos[p] * a.ksl * ES, kx[p]);
+        load8<DT>(vb + (int64_t)pos[p] * a.vsl * ES, vx[p]);
+      } else {
 #pragma unroll
-    for (int m = LPT; m < 64; m <<= 1) mx = fmaxf(mx, wave_xor(mx, m));
-    float l = 0.f, acc[8];
+        for (int e = 0; e < 8; ++e) { kx[p][e] = 0.f; vx[p][e] = 0.f; }
+      }
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    if (mx != -INFINITY) {
+    for (int h = 0; h < G; ++h) {
+      float s[PASSES];
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
-        const float pr = ok[p] ? fast_exp2(s[p] - mx) : 0.f;
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = fmaf(qx[h][e], kx[p][e], dot);
+#pragma unroll
+        for (int m = 1; m < LPT; m <<= 1) dot += wave_xor(dot, m);
+        s[p] = ok[p] ? dot : -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int p = 1; p < PASSES; ++p) mx = fmaxf(mx, s[p]);
+#pragma unroll
+      for (int m = LPT; m < 64; m <<= 1) mx = fmaxf(mx, wave_xor(mx, m));
+      const float m_new = fmaxf(wm[h], mx);
+      if (m_new == -INFINITY) continue;                  // nothing visible yet (wave-uniform)
+      const float alpha = fast_exp2(wm[h] - m_new);
+      float l = 0.f, acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const float pr = ok[p] ? fast_exp2(s[p] - m_new) : 0.f;
         l += pr;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = fmaf(pr, vx[p][e], acc[e]);
       }
-    }
 #pragma unroll
-    for (int m = LPT; m < 64; m <<= 1) {
-      l += wave_xor(l, m);
+      for (int m = LPT; m < 64; m <<= 1) {
+        l += wave_xor(l, m);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wave_xor(acc[e], m);
+        for (int e = 0; e < 8; ++e) acc[e] += wave_xor(acc[e], m);
+      }
+      wm[h] = m_new;
+      wl[h] = fmaf(wl[h], alpha, l);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wacc[h][e] = fmaf(wacc[h][e], alpha, acc[e]);
     }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
     if (lane < LPT) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[w][h][d0 + e] = acc[e];
+      for (int e = 0; e < 8; ++e) sm_acc[w][h][d0 + e] = wacc[h][e];
     }
-    if (lane == 0) { sm_m[w][h] = mx; sm_l[w][h] = l; }
+    if (lane == 0) { sm_m[w][h] = wm[h]; sm_l[w][h] = wl[h]; }
   }
   __syncthreads();
+  // merge the 4 waves into this workgroup's partial
   const int64_t pbase = (li * a.items + item) * G;
   for (int i = tid; i < G * D; i += 256) {
     const int h = i / D, d = i - h * D;
@@ -139,52 +163,88 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs a) {
   }
 }
 
-// Merge the split partials of every active (row, head) of a query block in
-// ascending slice order; write O (q's dtype) and the natural-log LSE.
+// Merge the split partials of active (row, head) pairs of a query block in
+// ascending slice order; write O (q's dtype) and the natural-log LSE.  One
+// workgroup per (chunk of a.qvc <= kCombQV query vectors, query block, KV
+// group).  A thread's partial loads for a batch of slices are issued together.
 template <int ODT>
 __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
-  const int qb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  __shared__ float sm_w[kCombQV][kCombMaxItems];
+  __shared__ float sm_M[kCombQV], sm_L[kCombQV];
+  __shared__ int sm_ok[kCombQV];
+  const int QVC = a.qvc;
+  const int nchunk = (a.QV + QVC - 1) / QVC;
+  const int qb = blockIdx.x / nchunk, qv0 = (blockIdx.x % nchunk) * QVC;
+  const int g = blockIdx.y, b = blockIdx.z;
   const int G = a.G, QV = a.QV, D = a.D, Hq = a.Hkv * G;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
   const int64_t nunits = (int64_t)a.cnt[li] * a.unit_num;
   const int nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
-  for (int i = threadIdx.x; i < QV * D; i += blockDim.x) {
-    const int qv = i / D, d = i - qv * D;
-    const int rl = qv / G, hl = qv - rl * G;
+  const int64_t p0 = li * a.items;
+  for (int c = w; c < QVC; c += 4) {
+    const int qv = qv0 + c;
+    const int rl = qv / G;
     const int row = qb * a.q_block + rl;
-    if (rl >= a.q_block || row >= a.Lq) continue;
-    if (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) continue;
-    float M = -INFINITY;
-    for (int it = 0; it < nvalid; ++it) M = fmaxf(M, a.part_ml[((li * a.items + it) * QV + qv) * 2]);
-    float acc = 0.f, lsum = 0.f;
-    if (M != -INFINITY) {
-      for (int it = 0; it < nvalid; ++it) {
-        const int64_t pi = (li * a.items + it) * QV + qv;
-        const float m = a.part_ml[pi * 2];
-        if (m == -INFINITY) continue;
-        const float wgt = fast_exp2(m - M);
-        lsum = fmaf(a.part_ml[pi * 2 + 1], wgt, lsum);
-        acc = fmaf(a.part_o[pi * D + d], wgt, acc);
+    const bool ok = qv < QV && row < a.Lq && (!a.row_mask || a.row_mask[(int64_t)b * a.Lq + row] != 0);
+    float M = -INFINITY, L = 0.f;
+    if (ok) {
+      float mv[kCombMaxItems / 64], lv[kCombMaxItems / 64];
+#pragma unroll
+      for (int u = 0; u < kCombMaxItems / 64; ++u) {
+        const int it = lane + 64 * u;
+        mv[u] = it < nvalid ? a.part_ml[((p0 + it) * QV + qv) * 2] : -INFINITY;
+        lv[u] = it < nvalid ? a.part_ml[((p0 + it) * QV + qv) * 2 + 1] : 0.f;
       }
+#pragma unroll
+      for (int u = 0; u < kCombMaxItems / 64; ++u) M = fmaxf(M, mv[u]);
+      M = wave_max(M);
+#pragma unroll
+      for (int u = 0; u < kCombMaxItems / 64; ++u) {
+        const int it = lane + 64 * u;
+        const float wgt = mv[u] == -INFINITY ? 0.f : fast_exp2(mv[u] - M);
+        if (it < nvalid) sm_w[c][it] = wgt;
+        L = fmaf(lv[u], wgt, L);
+      }
+      L = wave_sum(L);
     }
-    const float out = lsum > 0.f ? acc / lsum : 0.f;
+    if (lane == 0) { sm_M[c] = M; sm_L[c] = L; sm_ok[c] = ok; }
+  }
+  __syncthreads();
+  for (int i = tid; i < QVC * D; i += 256) {
+    const int c = i / D, d = i - c * D;
+    if (!sm_ok[c]) continue;
+    const int qv = qv0 + c, rl = qv / G, hl = qv - rl * G;
+    const int row = qb * a.q_block + rl;
+    float acc = 0.f;
+    for (int it0 = 0; it0 < nvalid; it0 += 32) {
+      float pv[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        pv[u] = (it0 + u < nvalid) ? a.part_o[((p0 + it0 + u) * QV + qv) * D + d] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (it0 + u < nvalid) acc = fmaf(pv[u], sm_w[c][it0 + u], acc);
+    }
+    const float L = sm_L[c];
+    const float out = L > 0.f ? acc / L : 0.f;
     const int h = g * G + hl;
     const int64_t oi = (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl + d;
     if (ODT == BSA_BF16) reinterpret_cast<uint16_t*>(a.o)[oi] = (uint16_t)f32_to_bf16(out);
     else reinterpret_cast<float*>(a.o)[oi] = out;
-    if (d == 0) a.lse[((int64_t)b * Hq + h) * a.Lq + row] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+    if (d == 0) a.lse[((int64_t)b * Hq + h) * a.Lq + row] = L > 0.f ? (sm_M[c] + log2f(L)) * kLn2 : -INFINITY;
   }
 }
 
 void launch_combine(const CombArgs& a, int odt, int B, hipStream_t s) {
-  dim3 grid(a.NQB, a.Hkv, B);
+  dim3 grid(a.NQB * ((a.QV + a.qvc - 1) / a.qvc), a.Hkv, B);
   if (odt == BSA_BF16) hipLaunchKernelGGL(combine_kernel<BSA_BF16>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(combine_kernel<BSA_F32>, grid, dim3(256), 0, s, a);
 }
 
 void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s) {
   dim3 grid(a.items, a.NQB, B * a.Hkv);
-#define BSA_DEC(DT, DD, GG) hipLaunchKernelGGL((decode_partial_kernel<DT, DD, GG>), grid, dim3(256), 0, s, a)
+#define BSA_DEC(DT, DD, GG) hipLaunchKernelGGL((decode_kernel<DT, DD, GG>), grid, dim3(256), 0, s, a)
 #define BSA_DEC_G(DT, DD)                              \
   do {                                                 \
     switch (G) {                                       \

@@ -12,6 +12,8 @@
 // K/V tiles are staged in LDS (V transposed) and shared by the 4 waves; each
 // wave owns 32 query vectors.  Online softmax in fp32 with exp2; the running
 // max and sum are lane-local (see mfma_tile.cuh).
+#include <algorithm>
+
 #include "internal.h"
 #include "mfma_tile.cuh"
 #include "split.h"
@@ -229,7 +231,11 @@ bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_par
   pl.NQB = (int)ceil_div(q.L, p.q_block);
   if (p.q_block == 1) {
     pl.kind = 0;
-    pl.items = (int)ceil_div((int64_t)p.cap * p.kv_block, kDecTok);
+    const int64_t toks = (int64_t)p.cap * p.kv_block;
+    // slices of at least kDecMinSlice tokens (whole chunks), at most kDecMaxItems of them
+    const int64_t per = std::max<int64_t>(kDecMinSlice / kDecTok, ceil_div(ceil_div(toks, kDecTok), kDecMaxItems));
+    pl.tok_per_item = (int)(per * kDecTok);
+    pl.items = (int)ceil_div(toks, pl.tok_per_item);
     pl.qv = pl.G;
   } else if (p.q_block * pl.G <= 128 && p.q_block <= 64) {
     pl.kind = 2;
@@ -268,6 +274,7 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
     a.vsb = v.stride_b; a.vsh = v.stride_h; a.vsl = v.stride_l;
     a.idx = idx; a.cnt = cnt; a.cap = p.cap; a.NQB = pl.NQB; a.Hkv = pl.Hkv; a.L = pl.L;
     a.kv_block = p.kv_block; a.causal = p.causal; a.q_pos0 = p.q_pos0; a.Lq = pl.Lq; a.items = pl.items;
+    a.tok_per_item = pl.tok_per_item;
     a.c2 = c2; a.row_mask = row_mask; a.part_o = part_o; a.part_ml = part_ml;
     launch_decode(a, q.dtype, pl.D, pl.G, pl.B, s);
   } else {
@@ -288,8 +295,8 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
   if (pl.kind != 1) {
     CombArgs c;
     c.part_o = part_o; c.part_ml = part_ml; c.cnt = cnt; c.items = pl.items;
-    if (pl.kind == 0) { c.unit_num = p.kv_block; c.unit_den = kDecTok; }
-    else { c.unit_num = 1; c.unit_den = kSplitBlocks; }
+    if (pl.kind == 0) { c.unit_num = p.kv_block; c.unit_den = pl.tok_per_item; c.qvc = 1; }
+    else { c.unit_num = 1; c.unit_den = kSplitBlocks; c.qvc = kCombQV; }
     c.Hkv = pl.Hkv; c.G = pl.G; c.NQB = pl.NQB; c.q_block = p.q_block; c.Lq = pl.Lq; c.D = pl.D; c.QV = pl.qv;
     c.row_mask = row_mask; c.o = o.data; c.osb = o.stride_b; c.osh = o.stride_h; c.osl = o.stride_l; c.lse = lse;
     launch_combine(c, o.dtype, pl.B, s);

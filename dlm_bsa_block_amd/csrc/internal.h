@@ -22,7 +22,7 @@ void launch_summaries(const bsa_tensor& x, int block, int layout, int first, int
 struct SelectPlan {
   int B, Hq, Hkv, G, D, NB, NQB, Lq, R;   // R = selection rows per query block (1 when pooled)
   int kp_max, cap;
-  size_t z_bytes, tau_bytes;
+  size_t z_bytes, tau_bytes, bits_bytes, cnt_bytes;   // workspace regions, in this order
 };
 bool plan_select(const bsa_tensor& q, int NB, const bsa_select_params& p, SelectPlan& pl);
 void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_mean, const float* k_energy,
@@ -36,6 +36,7 @@ struct AttnPlan {
   int kind;                 // 0 = VALU decode split, 1 = MFMA gather (direct), 2 = MFMA gather split
   int B, Hq, Hkv, G, D, Lq, L, NQB;
   int items;                // split-KV items per (b, g, q-block)
+  int tok_per_item;         // decode: list tokens per item
   int qv;                   // query vectors per (b, g, q-block) in split mode
   size_t part_bytes;
 };

@@ -11,11 +11,17 @@
 //                  keys (and pooled queries) -> tau[b][h][band]
 //   logits_kernel  LDS-tiled fp32 products z = scale * q.kmean (/ tau), written
 //                  to workspace Z[b][g][row][head-in-group][band][block]
-//   pick_kernel    per (query block, KV group, batch): per selection row, the
-//                  per-head softmax over the candidates, the group score, a
-//                  wavefront radix select of the k' best non-forced blocks
-//                  (ties -> lower index), then an LDS bitmap union over rows
-//                  and an ordered compaction to the sorted index list.
+//   pick_kernel    one wavefront per (selection row, KV group, batch): stages the
+//                  row's logits in LDS, takes the per-head (per-band) softmax over
+//                  the candidates, sums the group score, and runs a wavefront
+//                  radix select of the k' best non-forced blocks (ties -> lower
+//                  index) into an LDS bitmap.  A query block with one selection
+//                  row compacts its bitmap straight into the sorted index list;
+//                  otherwise every row publishes its bitmap and the last row of
+//                  the block to finish (a self-resetting counter) ORs them and
+//                  compacts the union.
+#include <algorithm>
+
 #include "common.cuh"
 #include "internal.h"
 
@@ -78,9 +84,267 @@ __global__ __launch_bounds__(256) void tau_kernel(const float* __restrict__ k_me
   }
 }
 
+// -------------------------------------------------------------------- pick ---
+struct PickArgs {
+  const float* Z;
+  int NB, NBp, Rtot, G, Hkv, nbands, NQB;
+  int q_block, kv_block, q_pos0, Lq, causal, pooled;
+  int topk, topk_num, topk_den, n_first, n_last, cap;
+  const uint8_t* row_mask;
+  int32_t* idx;
+  int32_t* cnt;
+  int32_t* row_picks;
+  uint32_t* row_bits;      // [B][Hkv][Rtot][128] row bitmaps (blocks with several rows)
+};
+
+constexpr int kPickMaxWords = 128;     // NB <= 4096
+constexpr int kPickThreads = 256;
+constexpr int kPickRegs = 32;          // logits held per thread at once
+
+struct RowPlan {
+  int qb, rows, nC, nf_first, last_lo, kp, n_free;
+};
+
+__device__ __forceinline__ RowPlan row_plan(const PickArgs& a, int row) {
+  RowPlan r;
+  r.qb = a.pooled ? row : row / a.q_block;
+  r.rows = a.pooled ? 1 : min(a.q_block, a.Lq - r.qb * a.q_block);
+  int jmax = a.NB - 1;
+  if (a.causal) {
+    const int last_row = min((r.qb + 1) * a.q_block, a.Lq) - 1;
+    jmax = min(a.NB - 1, (a.q_pos0 + last_row) / a.kv_block);
+  }
+  r.nC = jmax + 1;
+  r.nf_first = min(a.n_first, r.nC);
+  r.last_lo = max(r.nf_first, r.nC - a.n_last);       // forced: j < nf_first or j >= last_lo
+  const int n_forced = r.nf_first + (r.nC - r.last_lo);
+  int kp = a.topk_num > 0 ? (int)(((int64_t)a.topk_num * r.nC + a.topk_den - 1) / a.topk_den) : a.topk;
+  r.kp = max(0, min(kp, r.nC - n_forced));
+  r.n_free = r.nC - n_forced;
+  return r;
+}
+
+// Sum of a value over the 256 threads, identical bits in every thread
+// (fixed butterfly inside each wave, then the 4 wave totals in order).
+__device__ __forceinline__ float block_sum(float v, float* red, int slot) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[slot * 4 + (threadIdx.x >> 6)] = v;
+  __syncthreads();
+  return red[slot * 4] + red[slot * 4 + 1] + red[slot * 4 + 2] + red[slot * 4 + 3];
+}
+__device__ __forceinline__ float block_max(float v, float* red, int slot) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[slot * 4 + (threadIdx.x >> 6)] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[slot * 4], red[slot * 4 + 1]), fmaxf(red[slot * 4 + 2], red[slot * 4 + 3]));
+}
+
+// Ordered compaction of a bitmap (nw <= 128 words) into ascending indices,
+// padding out[total .. pad_to) with -1; returns the count.  One wavefront.
+__device__ int wave_compact(const uint32_t* bits, int nw, int32_t* out, int pad_to) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t w0 = (2 * lane < nw) ? bits[2 * lane] : 0u;
+  const uint32_t w1 = (2 * lane + 1 < nw) ? bits[2 * lane + 1] : 0u;
+  const int c = __popc(w0) + __popc(w1);
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  int pos = incl - c;
+  const int total = __shfl(incl, 63, 64);
+  uint32_t wd = w0;
+  for (int k = 0; k < 2; ++k) {
+    const int base = (2 * lane + k) * 32;
+    while (wd) {
+      const int bit = __ffs(wd) - 1;
+      out[pos++] = base + bit;
+      wd &= wd - 1;
+    }
+    wd = w1;
+  }
+  for (int i = total + lane; i < pad_to; i += 64) out[i] = -1;
+  return total;
+}
+
+// One workgroup per (selection row, KV group, batch).  Thread t owns the
+// candidates j = t + 256*u.  Per (head, band) channel: block-wide max, sum of
+// exp2 (logits are in log2 units), then the group score s[j] = sum over
+// channels of w * exp2(z - M) / S in a fixed channel order, kept in registers.
+// The k' best free candidates (ties -> lower index) come from a workgroup
+// radix select (four 8-bit passes over the score bits, LDS histogram); forced
+// blocks are always taken.  Blocks with one selection row write their sorted
+// list directly; otherwise the row's bitmap goes to the workspace for the
+// union kernel.
+template <int U>
+__global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t bits[kPickMaxWords];
+  __shared__ float red[16 * 4];
+  __shared__ int misc[2];
+  __shared__ int eqcnt[U][4];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const RowPlan rp = row_plan(a, row);
+  const int NBW = (a.NB + 31) / 32, nC = rp.nC, NBp = a.NBp;
+  const int nchan = a.G * a.nbands;
+  const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + rp.qb;
+  if (tid < kPickMaxWords) bits[tid] = 0u;
+  const bool active = a.pooled || !a.row_mask || a.row_mask[(int64_t)b * a.Lq + row] != 0;
+  if (active) {
+    const float* zrow = a.Z + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * (int64_t)nchan * NBp;
+    const float wband = a.nbands == 2 ? 0.5f : 1.0f;
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) s[u] = 0.f;
+    constexpr int CC = kPickRegs / U > 0 ? kPickRegs / U : 1;   // channels per register batch
+    for (int c0 = 0; c0 < nchan; c0 += CC) {
+      float z[CC][U];
+#pragma unroll
+      for (int cc = 0; cc < CC; ++cc)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = tid + kPickThreads * u;
+          z[cc][u] = (c0 + cc < nchan && j < nC) ? zrow[(int64_t)(c0 + cc) * NBp + j] : -INFINITY;
+        }
+#pragma unroll
+      for (int cc = 0; cc < CC; ++cc) {
+        if (c0 + cc >= nchan) continue;                 // uniform over the workgroup
+        float mx = z[cc][0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mx = fmaxf(mx, z[cc][u]);
+        mx = block_max(mx, red, 2 * cc);
+        float sm = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          z[cc][u] = fast_exp2(z[cc][u] - mx);          // -inf (not a candidate) -> 0
+          sm += z[cc][u];
+        }
+        sm = block_sum(sm, red, 2 * cc + 1);
+        const float inv = wband / sm;
+#pragma unroll
+        for (int u = 0; u < U; ++u) s[u] = fmaf(z[cc][u], inv, s[u]);
+      }
+      __syncthreads();                                  // red[] is reused by the next batch
+    }
+    // ---- keys: free candidates only; scores are >= 0, so float bits order like values
+    uint32_t key[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = tid + kPickThreads * u;
+      key[u] = (j < nC && j >= rp.nf_first && j < rp.last_lo) ? __float_as_uint(s[u]) + 1u : 0u;
+    }
+    uint32_t T = 0xFFFFFFFFu;
+    int need_eq = 0;
+    if (rp.kp > 0 && rp.kp < rp.n_free) {
+      uint32_t prefix = 0, pmask = 0;
+      int remaining = rp.kp;
+      for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        hist[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (key[u] != 0u && (key[u] & pmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255u], 1u);
+        __syncthreads();
+        if (w == 0) {
+          // lane owns digits 255-4*lane .. 252-4*lane; prefix sum in descending digit order
+          uint32_t c[4], tot = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; tot += c[i]; }
+          uint32_t incl = tot;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t t = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += t;
+          }
+          uint32_t run = incl - tot;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (run < (uint32_t)remaining && run + c[i] >= (uint32_t)remaining) {
+              misc[0] = 255 - 4 * lane - i;
+              misc[1] = (int)run;
+            }
+            run += c[i];
+          }
+        }
+        __syncthreads();
+        remaining -= misc[1];
+        prefix |= (uint32_t)misc[0] << shift;
+        pmask |= 0xFFu << shift;
+      }
+      T = prefix;
+      need_eq = remaining;
+    } else if (rp.kp > 0) {
+      T = 1u;                       // every free candidate
+      need_eq = 1 << 30;
+    }
+    // ---- ties at T go to the lowest indices: rank equal keys in j order
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const unsigned long long m = __ballot(key[u] != 0u && key[u] == T);
+      if (lane == 0) eqcnt[u][w] = __popcll(m);
+    }
+    __syncthreads();
+    int before = 0;                                     // equal keys at smaller j
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool eq = key[u] != 0u && key[u] == T;
+      const unsigned long long m = __ballot(eq);
+      int rank = before + __popcll(m & ((1ull << lane) - 1ull));
+      for (int ww = 0; ww < w; ++ww) rank += eqcnt[u][ww];
+      const int j = tid + kPickThreads * u;
+      const bool forced = j < nC && (j < rp.nf_first || j >= rp.last_lo);
+      const bool take = forced || (key[u] != 0u && key[u] > T) || (eq && rank < need_eq);
+      if (take) atomicOr(&bits[j >> 5], 1u << (j & 31));
+      before += eqcnt[u][0] + eqcnt[u][1] + eqcnt[u][2] + eqcnt[u][3];
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    if (a.row_picks)
+      wave_compact(bits, NBW, a.row_picks + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * a.cap, a.cap);
+    if (rp.rows == 1) {
+      const int n = wave_compact(bits, NBW, a.idx + li * a.cap, 0);
+      if (lane == 0) a.cnt[li] = n;
+    } else {
+      uint32_t* mine = a.row_bits + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * kPickMaxWords;
+      for (int i = lane; i < NBW; i += 64) mine[i] = bits[i];
+    }
+  }
+}
+
+// Union of the rows' picks of each query block (blocks with several rows):
+// OR of the row bitmaps, then an ordered compaction.  One wavefront per block.
+__global__ __launch_bounds__(64) void union_kernel(PickArgs a) {
+  __shared__ uint32_t bits[kPickMaxWords];
+  const int qb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int NBW = (a.NB + 31) / 32;
+  const int rows = min(a.q_block, a.Lq - qb * a.q_block);
+  const uint32_t* first = a.row_bits + (((int64_t)b * a.Hkv + g) * a.Rtot + (int64_t)qb * a.q_block) * kPickMaxWords;
+  for (int i = lane; i < NBW; i += 64) {
+    uint32_t u = 0u;
+    for (int r0 = 0; r0 < rows; r0 += 16) {
+      uint32_t v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = r0 + k < rows ? first[(int64_t)(r0 + k) * kPickMaxWords + i] : 0u;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) u |= v[k];
+    }
+    bits[i] = u;
+  }
+  wave_sync_lds();
+  const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
+  const int n = wave_compact(bits, NBW, a.idx + li * a.cap, 0);
+  if (lane == 0) a.cnt[li] = n;
+}
+
 // ------------------------------------------------------------------ logits ---
 // Workgroup tile: TM query vectors (m = row * G + head-in-group) x TJ blocks.
 // Thread (tx, ty) owns rows ty*RPT + r and blocks tx + TX*c.
+// Logits are written in log2 units (scale includes log2(e)), so the pick stage
+// can use exp2.
 template <int DT, int D, int TX, int TY, int RPT, int CPT, bool DUAL>
 __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__ qdata, int64_t qsb, int64_t qsh,
                                                      int64_t qsl, const float* __restrict__ k_mean, int NB, int Rtot,
@@ -88,6 +352,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
                                                      int layout, int causal, int q_block, int kv_block, int q_pos0,
                                                      int pooled, int Lq, float* __restrict__ Z) {
   constexpr int TM = TY * RPT, TJ = TX * CPT;
+  const int NBp = (NB + 3) & ~3;          // row stride of Z, a multiple of 4 floats
   constexpr int ES = DT == BSA_BF16 ? 2 : 4;
   constexpr int NBANDS = DUAL ? 2 : 1;
   __shared__ float Qs[TM][D + 1];
@@ -175,206 +440,14 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
 #pragma unroll
     for (int n = 0; n < NBANDS; ++n)
       inv_t[n] = DUAL ? scale / tau[((int64_t)b * Hq + g * G + hl) * 2 + n] : scale;
-    float* zr = Z + ((((int64_t)b * Hkv + g) * Rtot + row) * G + hl) * NBANDS * NB;
+    float* zr = Z + ((((int64_t)b * Hkv + g) * Rtot + row) * G + hl) * NBANDS * NBp;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int j = j0 + tx + TX * c;
       if (j >= NB) continue;
 #pragma unroll
-      for (int n = 0; n < NBANDS; ++n) zr[(int64_t)n * NB + j] = acc[r][c][n] * inv_t[n];
+      for (int n = 0; n < NBANDS; ++n) zr[(int64_t)n * NBp + j] = acc[r][c][n] * inv_t[n];
     }
-  }
-}
-
-// -------------------------------------------------------------------- pick ---
-struct PickArgs {
-  const float* Z;
-  int NB, Rtot, G, Hkv, nbands;
-  int q_block, kv_block, q_pos0, Lq, causal, pooled;
-  int topk, topk_num, topk_den, n_first, n_last, cap;
-  const uint8_t* row_mask;
-  int32_t* idx;
-  int32_t* cnt;
-  int32_t* row_picks;
-};
-
-// Wavefront radix select on 32-bit keys (0 = not a candidate): finds the
-// k-th largest key T and how many keys equal to T belong to the top k.
-// Four 8-bit digit passes, most significant first, with a per-wave LDS
-// histogram and a wave prefix scan over the digits in descending order.
-template <typename KeyFn>
-__device__ void wave_radix_select(KeyFn keyof, int n, int k, uint32_t* hist, uint32_t& T, int& need_eq) {
-  const int lane = threadIdx.x & 63;
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = lane; i < 256; i += 64) hist[i] = 0u;
-    wave_sync_lds();
-    for (int j = lane; j < n; j += 64) {
-      const uint32_t key = keyof(j);
-      if (key != 0u && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    wave_sync_lds();
-    uint32_t c[4], tot = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; tot += c[i]; }
-    uint32_t incl = tot;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t t = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += t;
-    }
-    uint32_t run = incl - tot;
-    int found = -1;
-    uint32_t above = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (found < 0 && run < (uint32_t)remaining && run + c[i] >= (uint32_t)remaining) {
-        found = 255 - 4 * lane - i;
-        above = run;
-      }
-      run += c[i];
-    }
-    const unsigned long long bal = __ballot(found >= 0);
-    const int src = __ffsll((long long)bal) - 1;
-    found = __shfl(found, src, 64);
-    above = __shfl(above, src, 64);
-    remaining -= (int)above;
-    prefix |= (uint32_t)found << shift;
-    pmask |= 0xFFu << shift;
-    wave_sync_lds();
-  }
-  T = prefix;
-  need_eq = remaining;
-}
-
-// Ordered compaction of a bitmap (nw <= 128 words) into ascending indices,
-// padding out[total .. pad_to) with -1; returns the count.
-__device__ int wave_compact(const uint32_t* bits, int nw, int32_t* out, int pad_to) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t w0 = (2 * lane < nw) ? bits[2 * lane] : 0u;
-  const uint32_t w1 = (2 * lane + 1 < nw) ? bits[2 * lane + 1] : 0u;
-  const int c = __popc(w0) + __popc(w1);
-  int incl = c;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += t;
-  }
-  int pos = incl - c;
-  const int total = __shfl(incl, 63, 64);
-  uint32_t wd = w0;
-  for (int k = 0; k < 2; ++k) {
-    const int base = (2 * lane + k) * 32;
-    while (wd) {
-      const int bit = __ffs(wd) - 1;
-      out[pos++] = base + bit;
-      wd &= wd - 1;
-    }
-    wd = w1;
-  }
-  for (int i = total + lane; i < pad_to; i += 64) out[i] = -1;
-  return total;
-}
-
-constexpr int kPickMaxWords = 128;   // NB <= 4096
-
-__device__ __forceinline__ size_t pick_wave_bytes(int NB) { return (size_t)NB * 4 + 256 * 4 + kPickMaxWords * 4; }
-
-__global__ __launch_bounds__(256) void pick_kernel(PickArgs a) {
-  extern __shared__ uint32_t smem[];
-  const int NB = a.NB, NBW = (NB + 31) / 32;
-  const int W = blockDim.x / 64, w = threadIdx.x / 64, lane = threadIdx.x & 63;
-  uint32_t* ubits = smem;                                              // [128] union bitmap
-  uint8_t* wbase = reinterpret_cast<uint8_t*>(smem + kPickMaxWords) + (size_t)w * pick_wave_bytes(NB);
-  float* s = reinterpret_cast<float*>(wbase);                          // [NB] group scores
-  uint32_t* hist = reinterpret_cast<uint32_t*>(s + NB);                // [256]
-  uint32_t* rbits = hist + 256;                                        // [128] this row's picks
-
-  const int qb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int Hkv = a.Hkv, G = a.G, NQB = gridDim.x;
-  const int rows = a.pooled ? 1 : min(a.q_block, a.Lq - qb * a.q_block);
-  // candidates [0, jmax], forced blocks, and the number of scored picks
-  int jmax = NB - 1;
-  if (a.causal) {
-    const int last_row = min((qb + 1) * a.q_block, a.Lq) - 1;
-    jmax = min(NB - 1, (a.q_pos0 + last_row) / a.kv_block);
-  }
-  const int nC = jmax + 1;
-  const int nf_first = min(a.n_first, nC);
-  const int last_lo = max(nf_first, nC - a.n_last);          // forced: j < nf_first or j >= last_lo
-  const int n_forced = nf_first + (nC - last_lo);
-  int kp = a.topk_num > 0 ? (int)(((int64_t)a.topk_num * nC + a.topk_den - 1) / a.topk_den) : a.topk;
-  kp = max(0, min(kp, nC - n_forced));
-  const int n_free = nC - n_forced;
-
-  for (int i = threadIdx.x; i < kPickMaxWords; i += blockDim.x) ubits[i] = 0u;
-  __syncthreads();
-
-  for (int rl = w; rl < rows; rl += W) {
-    const int row = a.pooled ? qb : qb * a.q_block + rl;
-    int32_t* rp = a.row_picks ? a.row_picks + (((int64_t)b * Hkv + g) * a.Rtot + row) * a.cap : nullptr;
-    if (!a.pooled && a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) {
-      if (rp) for (int i = lane; i < a.cap; i += 64) rp[i] = -1;
-      continue;
-    }
-    for (int i = lane; i < kPickMaxWords; i += 64) rbits[i] = 0u;
-    for (int j = lane; j < nC; j += 64) s[j] = 0.f;
-    // group score: sum over heads (and bands) of softmax probabilities, fixed order
-    const float wband = a.nbands == 2 ? 0.5f : 1.0f;
-    for (int hl = 0; hl < G; ++hl) {
-      for (int bd = 0; bd < a.nbands; ++bd) {
-        const float* z = a.Z + (((((int64_t)b * Hkv + g) * a.Rtot + row) * G + hl) * a.nbands + bd) * NB;
-        float mx = -INFINITY;
-        for (int j = lane; j < nC; j += 64) mx = fmaxf(mx, z[j]);
-        mx = wave_max(mx);
-        float sm = 0.f;
-        for (int j = lane; j < nC; j += 64) sm += expf(z[j] - mx);
-        sm = wave_sum(sm);
-        const float inv = wband / sm;
-        for (int j = lane; j < nC; j += 64) s[j] = fmaf(expf(z[j] - mx), inv, s[j]);
-      }
-    }
-    wave_sync_lds();
-    auto keyof = [&](int j) -> uint32_t {
-      const bool free_ = (j >= nf_first) && (j < last_lo);
-      return free_ ? __float_as_uint(s[j]) + 1u : 0u;
-    };
-    uint32_t T = 0xFFFFFFFFu;
-    int need_eq = 0;
-    if (kp > 0 && kp < n_free) {
-      wave_radix_select(keyof, nC, kp, hist, T, need_eq);
-    } else if (kp > 0) {
-      T = 1u;                       // take every non-forced candidate
-      need_eq = 0x7FFFFFFF;
-    }
-    int taken = 0;
-    for (int j0 = 0; j0 < nC; j0 += 64) {
-      const int j = j0 + lane;
-      const uint32_t key = j < nC ? keyof(j) : 0u;
-      const bool forced = j < nC && (j < nf_first || j >= last_lo);
-      const bool gt = key != 0u && key > T;
-      const bool eq = key != 0u && key == T;
-      const unsigned long long m = __ballot(eq);
-      const int rank = __popcll(m & ((1ull << lane) - 1ull));
-      const bool take = forced || gt || (eq && taken + rank < need_eq);
-      taken += __popcll(m);
-      if (take) atomicOr(&rbits[j >> 5], 1u << (j & 31));
-    }
-    wave_sync_lds();
-    for (int i = lane; i < NBW; i += 64) {
-      const uint32_t v = rbits[i];
-      if (v) atomicOr(&ubits[i], v);
-    }
-    if (rp) wave_compact(rbits, NBW, rp, a.cap);
-    wave_sync_lds();
-  }
-  __syncthreads();
-  if (w == 0) {
-    const int64_t li = ((int64_t)b * Hkv + g) * NQB + qb;
-    const int n = wave_compact(ubits, NBW, a.idx + li * a.cap, 0);
-    if (lane == 0) a.cnt[li] = n;
   }
 }
 
@@ -400,9 +473,6 @@ bool plan_select(const bsa_tensor& q, int NB, const bsa_select_params& p, Select
   return true;
 }
 
-static size_t pick_smem_bytes(int NB, int W) {
-  return kPickMaxWords * 4 + (size_t)W * ((size_t)NB * 4 + 256 * 4 + kPickMaxWords * 4);
-}
 
 void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_mean, const float* k_energy,
                    const bsa_select_params& p, const SelectPlan& pl, const uint8_t* row_mask, int32_t* idx,
@@ -419,39 +489,15 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
   }
   const int M = Rtot * G;
   const uint8_t* qd = static_cast<const uint8_t*>(q.data);
-#define BSA_LOGITS(DT, DD, TX, TY, RPT, CPT, DUAL)                                                        \
-  do {                                                                                                    \
-    dim3 grid((unsigned)ceil_div(NB, TX * CPT), (unsigned)ceil_div(M, TY * RPT), (unsigned)(pl.B * Hkv)); \
-    hipLaunchKernelGGL((logits_kernel<DT, DD, TX, TY, RPT, CPT, DUAL>), grid, dim3(256), 0, s, qd,        \
-                       q.stride_b, q.stride_h, q.stride_l, k_mean, NB, Rtot, G, Hkv, p.scale, tau, p.layout, \
-                       p.causal, p.q_block, p.kv_block, p.q_pos0, p.pooled_q, pl.Lq, Z);                 \
-  } while (0)
-#define BSA_LOGITS_SHAPE(DT, DD, DUAL)                   \
-  do {                                                   \
-    if (M <= 8) BSA_LOGITS(DT, DD, 64, 4, 2, 1, DUAL);   \
-    else BSA_LOGITS(DT, DD, 16, 16, 2, 4, DUAL);         \
-  } while (0)
-#define BSA_LOGITS_D(DT, DUAL)                                              \
-  do {                                                                      \
-    if (pl.D == 128) BSA_LOGITS_SHAPE(DT, 128, DUAL);                       \
-    else BSA_LOGITS_SHAPE(DT, 64, DUAL);                                    \
-  } while (0)
-  if (q.dtype == BSA_BF16) {
-    if (p.dual_band) BSA_LOGITS_D(BSA_BF16, true); else BSA_LOGITS_D(BSA_BF16, false);
-  } else {
-    if (p.dual_band) BSA_LOGITS_D(BSA_F32, true); else BSA_LOGITS_D(BSA_F32, false);
-  }
-#undef BSA_LOGITS_D
-#undef BSA_LOGITS_SHAPE
-#undef BSA_LOGITS
-
   PickArgs a;
   a.Z = Z;
   a.NB = NB;
+  a.NBp = (NB + 3) & ~3;
   a.Rtot = Rtot;
   a.G = G;
   a.Hkv = Hkv;
   a.nbands = nb;
+  a.NQB = pl.NQB;
   a.q_block = p.q_block;
   a.kv_block = p.kv_block;
   a.q_pos0 = p.q_pos0;
@@ -468,15 +514,42 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
   a.idx = idx;
   a.cnt = cnt;
   a.row_picks = row_picks;
-  const int W = p.pooled_q ? 1 : (pl.R >= 4 ? 4 : pl.R);
-  const size_t smem = pick_smem_bytes(NB, W);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&pick_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
+  a.row_bits = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + pl.z_bytes + pl.tau_bytes);
+  const float scale2 = p.scale * kLog2e;
+#define BSA_LOGITS(DT, DD, TX, TY, RPT, CPT, DUAL)                                                        \
+  do {                                                                                                    \
+    dim3 grid((unsigned)ceil_div(NB, TX * CPT), (unsigned)ceil_div(M, TY * RPT), (unsigned)(pl.B * Hkv)); \
+    hipLaunchKernelGGL((logits_kernel<DT, DD, TX, TY, RPT, CPT, DUAL>), grid, dim3(256), 0, s, qd,        \
+                       q.stride_b, q.stride_h, q.stride_l, k_mean, NB, Rtot, G, Hkv, scale2, tau, p.layout, \
+                       p.causal, p.q_block, p.kv_block, p.q_pos0, p.pooled_q, pl.Lq, Z);                 \
+  } while (0)
+#define BSA_LOGITS_SHAPE(DT, DD, DUAL)                                   \
+  do {                                                                   \
+    if (M <= 8) BSA_LOGITS(DT, DD, 32, 8, 1, 1, DUAL);                   \
+    else BSA_LOGITS(DT, DD, 16, 16, 2, 4, DUAL);                         \
+  } while (0)
+#define BSA_LOGITS_D(DT, DUAL)                                              \
+  do {                                                                      \
+    if (pl.D == 128) BSA_LOGITS_SHAPE(DT, 128, DUAL);                       \
+    else BSA_LOGITS_SHAPE(DT, 64, DUAL);                                    \
+  } while (0)
+  if (q.dtype == BSA_BF16) {
+    if (p.dual_band) BSA_LOGITS_D(BSA_BF16, true); else BSA_LOGITS_D(BSA_BF16, false);
+  } else {
+    if (p.dual_band) BSA_LOGITS_D(BSA_F32, true); else BSA_LOGITS_D(BSA_F32, false);
   }
-  hipLaunchKernelGGL(pick_kernel, dim3(pl.NQB, Hkv, pl.B), dim3(64 * W), smem, s, a);
+#undef BSA_LOGITS_D
+#undef BSA_LOGITS_SHAPE
+#undef BSA_LOGITS
+  const int U = (int)ceil_div(a.NBp, kPickThreads);
+  dim3 pgrid(Rtot, Hkv, pl.B);
+  if (U <= 1) hipLaunchKernelGGL(pick_kernel<1>, pgrid, dim3(kPickThreads), 0, s, a);
+  else if (U <= 2) hipLaunchKernelGGL(pick_kernel<2>, pgrid, dim3(kPickThreads), 0, s, a);
+  else if (U <= 4) hipLaunchKernelGGL(pick_kernel<4>, pgrid, dim3(kPickThreads), 0, s, a);
+  else if (U <= 8) hipLaunchKernelGGL(pick_kernel<8>, pgrid, dim3(kPickThreads), 0, s, a);
+  else hipLaunchKernelGGL(pick_kernel<16>, pgrid, dim3(kPickThreads), 0, s, a);
+  if (!p.pooled_q && std::min(p.q_block, pl.Lq) > 1)
+    hipLaunchKernelGGL(union_kernel, dim3(pl.NQB, Hkv, pl.B), dim3(64), 0, s, a);
 }
 
 }  // namespace bsa

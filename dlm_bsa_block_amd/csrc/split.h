@@ -10,8 +10,12 @@
 
 namespace bsa {
 
-constexpr int kDecTok = 32;       // list tokens per decode workgroup
-constexpr int kSplitBlocks = 8;   // list entries per MFMA split workgroup
+constexpr int kDecTok = 32;         // list tokens per decode chunk (4 waves x 8 tokens)
+constexpr int kDecMaxItems = 512;   // decode slices per (row, group)
+constexpr int kDecMinSlice = 32;    // list tokens per decode slice, at least
+constexpr int kSplitBlocks = 8;     // list entries per MFMA split workgroup
+constexpr int kCombQV = 4;          // query vectors per combine workgroup
+constexpr int kCombMaxItems = 512;  // split slices the combine can merge
 
 struct DecArgs {
   const uint8_t* q;
@@ -20,7 +24,7 @@ struct DecArgs {
   int64_t qsb, qsh, qsl, ksb, ksh, ksl, vsb, vsh, vsl;
   const int32_t* idx;
   const int32_t* cnt;
-  int cap, NQB, Hkv, L, kv_block, causal, q_pos0, Lq, items;
+  int cap, NQB, Hkv, L, kv_block, causal, q_pos0, Lq, items, tok_per_item;
   float c2;                       // scale * log2(e)
   const uint8_t* row_mask;
   float* part_o;
@@ -33,6 +37,7 @@ struct CombArgs {
   const int32_t* cnt;
   int items, unit_num, unit_den;  // valid slices = ceil(cnt * unit_num / unit_den)
   int Hkv, G, NQB, q_block, Lq, D, QV;
+  int qvc;                        // query vectors per combine workgroup (<= kCombQV)
   const uint8_t* row_mask;
   void* o;
   int64_t osb, osh, osl;

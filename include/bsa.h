@@ -127,7 +127,9 @@ bsa_status bsa_build_block_summaries(const bsa_tensor* x, int32_t block_size, in
  * k_mean/k_energy: [B, Hkv, NB, D] / [B, Hkv, NB, 2] f32 contiguous with
  * Hkv = num_kv_heads dividing Hq and NB = num_kv_blocks; q_energy
  * [B, Hq, NQB, 2] (pooled + dual band), else NULL.  row_mask [B, Lq] uint8 or
- * NULL (raw mode only).  workspace: bsa_select_workspace_bytes() bytes.
+ * NULL (raw mode only).  workspace: bsa_select_workspace_bytes() bytes of
+ * scratch (no initial contents needed; calls that overlap on one workspace
+ * race).
  * Errors: BSA_ERR_CAPACITY when cap < min(NB, R_per_block * (k'_max + n_first
  * + n_last)); BSA_ERR_UNSUPPORTED for NB > 4096, D not in {64, 128}, or more
  * than 64 query rows per block in raw mode.
@@ -182,7 +184,8 @@ bsa_status bsa_active_rows(const bsa_tensor* q_cur, const bsa_tensor* q_prev, fl
  * q, k, v share dtype; o has q's shape and dtype; lse is [B, Hq, Lq] f32
  * contiguous.  Supported: bf16 with D = 128 and kv_block in {64, 128}; f32
  * or D = 64 only for single-row query blocks (decode).  workspace:
- * bsa_attention_workspace_bytes() bytes (split-KV partial results).
+ * bsa_attention_workspace_bytes() bytes (split-KV partial results; no
+ * initial contents needed; calls that overlap on one workspace race).
  * ------------------------------------------------------------------------ */
 typedef struct {
   float scale;
