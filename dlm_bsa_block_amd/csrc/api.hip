@@ -195,6 +195,11 @@ static bsa_status validate_attention(const bsa_tensor* q, const bsa_tensor* k, c
     if (p->kv_block != 64 && p->kv_block != 128)
       return fail(BSA_ERR_UNSUPPORTED, "multi-row query blocks need kv_block 64 or 128");
     if (pl.kind == 1 && p->q_block > 128) return fail(BSA_ERR_UNSUPPORTED, "q_block %d > 128", p->q_block);
+    if (pl.kind == 1 && p->cap > kMaxListMfma)
+      return fail(BSA_ERR_UNSUPPORTED, "cap %d > %d for query blocks over 64 rows", p->cap, kMaxListMfma);
+    // the tile copies address a row of a K/V tile with a 32-bit byte offset
+    if ((int64_t)p->kv_block * 2 * std::max(k->stride_l, v->stride_l) >= (int64_t(1) << 31))
+      return fail(BSA_ERR_UNSUPPORTED, "K/V row stride too large for kv_block %d", p->kv_block);
   }
   return BSA_OK;
 }

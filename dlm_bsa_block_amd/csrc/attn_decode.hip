@@ -33,7 +33,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   const int tg = lane / LPT, d0 = (lane % LPT) * 8;
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
   const int row = qb;                                   // one query row per block
-  const int Hq = a.Hkv * G;
   if (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) return;
   const int64_t ntok = (int64_t)a.cnt[li] * a.kv_block;
   const int64_t t_begin = (int64_t)item * a.tok_per_item;

@@ -11,6 +11,8 @@ namespace bsa {
 bsa_status fail(bsa_status s, const char* fmt, ...);
 bsa_status check_launch(const char* what);
 
+constexpr int kMaxListMfma = 4096;   // list entries a multi-row MFMA workgroup stages in LDS
+
 inline size_t dtype_size(int dt) { return dt == BSA_BF16 ? 2 : 4; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }

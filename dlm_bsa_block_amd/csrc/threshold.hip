@@ -4,14 +4,17 @@
 // from HBM and no PV product.  The test reuses statistics the online softmax
 // computes anyway.
 //
-// One workgroup per (query tile of 128 rows, query head); 4 waves of 32 rows.
+// One workgroup per (query tile of 128 rows, pair of query heads of one KV
+// group -- one head when the group size is odd); 4 waves of 32 rows per head.
 // KV tiles are visited from the diagonal (the newest visible tile) down to
 // tile 0.  For each tile S = K Q^T is always computed (the max needs it); each
-// wave votes through a ballot, the votes meet in LDS, and the whole workgroup
-// takes the same keep/skip branch.  Only a kept tile loads V, and its V loads
-// are issued before the exponentials so their latency overlaps that work.
-// Workgroups of one KV group run on one XCD (heads of a query tile adjacent),
-// so K/V tiles are shared through that XCD's L2.
+// wave votes through a ballot, the votes of a head meet in LDS, and all waves
+// of that head take the same keep/skip branch.  V is loaded only when a head
+// of the workgroup keeps the tile, and its copy is issued before the
+// exponentials so their latency overlaps it.  The K tile of the next step is
+// copied into a second LDS buffer while the current one is used.  Workgroups
+// of one KV group run on one XCD (heads of a query tile adjacent), so K/V
+// tiles are shared through that XCD's L2.
 #include <cmath>
 
 #include "internal.h"
@@ -36,26 +39,30 @@ struct ThrArgs {
 
 constexpr int kTile = 128;
 
-__global__ __launch_bounds__(256, 2) void threshold_kernel(ThrArgs a) {
-  constexpr int VST = VtStride<kTile>::value;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * VST];
-  __shared__ int flags[4];
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void threshold_kernel(ThrArgs a) {
+  constexpr int TILE = kTile * kRow;
+  constexpr int HPW = NW / 4;                      // heads per workgroup (4 waves of 32 rows each)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * TILE];   // K0 K1 V
+  __shared__ int flags[NW];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keep/skip branches stay scalar
+  const int wr = w & 3, hh = w >> 2;
   const int total = gridDim.x, n = blockIdx.x;
   const int wi = (total % 8 == 0) ? (n % 8) * (total / 8) + n / 8 : n;
-  const int hl = wi % a.G;
-  const int rest = wi / a.G;
+  const int sets = a.G / HPW;
+  const int h0 = (wi % sets) * HPW;
+  const int rest = wi / sets;
   const int qt = a.NQT - 1 - rest % a.NQT;
   const int bgi = rest / a.NQT;
   const int b = bgi / a.Hkv, g = bgi - b * a.Hkv;
-  const int h = g * a.G + hl;
+  const int h = g * a.G + h0 + hh;
   const int Hq = a.Hkv * a.G;
 
-  const int row = qt * kTile + 32 * w + r32;
+  const int row = qt * kTile + 32 * wr + r32;
   const bool valid = row < a.Lq;
-  const bool wave_busy = qt * kTile + 32 * w < a.Lq;
+  const bool wave_busy = qt * kTile + 32 * wr < a.Lq;
   int wave_min_pos = valid ? row : 0x7FFFFFFF;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) wave_min_pos = min(wave_min_pos, wave_xor(wave_min_pos, m));
@@ -64,38 +71,41 @@ __global__ __launch_bounds__(256, 2) void threshold_kernel(ThrArgs a) {
 
   bf16x8 qf[8];
   load_q_frag(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)row * a.qsl, valid, qf);
+  int kofs[8], vofs[8];
+  k_offsets(kofs);
+  v_offsets(vofs);
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;            // running max of the kept tiles (log2 units) and sum
   int nkept = 0;
   const uint16_t* kbg = a.k + (int64_t)b * a.ksb + (int64_t)g * a.ksh;
   const uint16_t* vbg = a.v + (int64_t)b * a.vsb + (int64_t)g * a.vsh;
   uint8_t* kmap = a.keep_map ? a.keep_map + (((int64_t)b * Hq + h) * a.NQT + qt) * a.NKT : nullptr;
+  uint16_t* Vs = lds + 2 * TILE;
 
-  for (int j = jmax; j >= 0; --j) {
+  const uint32_t lds0 = lds_addr(lds);
+  issue_tile<kTile, NW>(kbg + (int64_t)jmax * kTile * a.ksl, a.ksl, min(kTile, a.L - jmax * kTile), lds0);
+  for (int j = jmax, t = 0; j >= 0; --j, ++t) {
     const int key0 = j * kTile;
     const int nk = min(kTile, a.L - key0);
-    stage_kv_tile<kTile>(kbg + (int64_t)key0 * a.ksl, a.ksl, nullptr, 0, nk, Ks, Vt, true, false);
-    __syncthreads();
+    const uint16_t* Ks = lds + (t & 1) * TILE;
+    wait_tile_loads();                             // K of tile j (this wave's part)
+    __syncthreads();                               // K visible; tile j + 1 finished (its K buffer and V free)
+    if (j > 0)
+      issue_tile<kTile, NW>(kbg + (int64_t)(key0 - kTile) * a.ksl, a.ksl, kTile, lds0 + (uint32_t)(((t + 1) & 1) * TILE * 2));
     f32x16 s[kTile / 32];
     float tm2 = -INFINITY;
     if (wave_busy) {
-      qk_tile<kTile>(Ks, qf, s);
+      qk_tile<kTile, false>(Ks, kofs, qf, s);
       const bool need_mask = nk < kTile || (a.causal && key0 + kTile - 1 > wave_min_pos) || !valid ||
-                             qt * kTile + 32 * w + 31 >= a.Lq;
+                             qt * kTile + 32 * wr + 31 >= a.Lq;
       if (need_mask) {
         int lim = valid ? nk - 1 : -1;
         if (a.causal) lim = min(lim, row - key0);
         mask_tile<kTile / 32>(s, lim);
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < kTile / 32; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-      mx = fmaxf(mx, wave_xor(mx, 32));
-      tm2 = mx * a.c2;
+      tm2 = tile_max<kTile / 32>(s) * a.c2;
       const bool vote = tm2 != -INFINITY && (m_run == -INFINITY || tm2 - m_run >= a.lnlam2);
       const unsigned long long bal = __ballot(vote);
       if (lane == 0) flags[w] = bal != 0ull;
@@ -103,38 +113,29 @@ __global__ __launch_bounds__(256, 2) void threshold_kernel(ThrArgs a) {
       flags[w] = 0;
     }
     __syncthreads();
-    const bool keep = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
-    if (tid == 0 && kmap) kmap[j] = keep ? 1 : 0;
+    bool keep_any = false, keep = false;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) {
+      keep_any |= flags[x] != 0;
+      if ((x >> 2) == hh) keep |= flags[x] != 0;
+    }
+    if (wr == 0 && lane == 0 && kmap) kmap[j] = keep ? 1 : 0;
+    if (keep_any) issue_tile<kTile, NW>(vbg + (int64_t)key0 * a.vsl, a.vsl, nk, lds0 + (uint32_t)(2 * TILE * 2));
     if (keep) {
       ++nkept;
-      stage_kv_tile<kTile>(nullptr, 0, vbg + (int64_t)key0 * a.vsl, a.vsl, nk, Ks, Vt, false, true);
       if (wave_busy) {
-        const float m_new = fmaxf(m_run, tm2);
-        const float msafe = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - msafe);
-        float ls = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < kTile / 32; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float pr = fast_exp2(fmaf(s[kt][i], a.c2, -msafe));
-            s[kt][i] = pr;
-            ls += pr;
-          }
-        l_run = fmaf(l_run, alpha, ls);
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        const float msub = softmax_rescale(tm2, m_run, l_run, o);
+        softmax_probs<kTile / 32>(s, a.c2, msub, l_run);
       }
-      __syncthreads();
-      if (wave_busy) pv_tile<kTile>(Vt, s, o);
     }
-    __syncthreads();
+    if (keep_any) {
+      wait_tile_loads();                           // V of tile j (and K of tile j - 1)
+      __syncthreads();
+      if (keep && wave_busy) pv_tile<kTile>(Vs, vofs, s, o);
+    }
   }
 
-  if (tid == 0 && a.kept) a.kept[((int64_t)b * Hq + h) * a.NQT + qt] = nkept;
+  if (wr == 0 && lane == 0 && a.kept) a.kept[((int64_t)b * Hq + h) * a.NQT + qt] = nkept;
   if (!valid) return;
   const float l_tot = l_run + wave_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -169,8 +170,13 @@ void launch_threshold(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
   a.lnlam2 = p.lambda > 0.f ? (float)(std::log((double)p.lambda) * 1.4426950408889634) : -INFINITY;
   a.o = static_cast<uint16_t*>(o.data); a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
   a.lse = lse; a.kept = kept; a.keep_map = keep_map;
-  dim3 grid(a.B * a.Hkv * a.NQT * a.G);
-  hipLaunchKernelGGL(threshold_kernel, grid, dim3(256), 0, s, a);
+  if (a.G % 2 == 0) {
+    dim3 grid(a.B * a.Hkv * a.NQT * (a.G / 2));
+    hipLaunchKernelGGL(threshold_kernel<8>, grid, dim3(512), 0, s, a);
+  } else {
+    dim3 grid(a.B * a.Hkv * a.NQT * a.G);
+    hipLaunchKernelGGL(threshold_kernel<4>, grid, dim3(256), 0, s, a);
+  }
 }
 
 }  // namespace bsa
