@@ -42,9 +42,11 @@ struct GatherArgs {
 // One workgroup = NW waves of 32 query vectors.  Direct mode: NW / 4 heads of
 // one KV group (4 waves of 32 rows each per head) share every K/V tile.  Split
 // mode (NW = 4): the active (row, head) pairs of a query block, compacted.
-// K/V tiles are double-buffered in LDS: the copy of list entry e + 1 runs
-// while entry e is computed, so one barrier per entry suffices.
-template <int KVB, int NW, bool SPLIT>
+// K/V tiles are double-buffered in LDS: the copy of tile u + 1 runs while
+// tile u is computed, so one barrier per tile suffices.  A list entry (a KV
+// block of SUB * KVB keys) is walked as SUB tiles of KVB keys: with 64-key
+// tiles two workgroups fit on a CU and their waves overlap freely.
+template <int KVB, int NW, bool SPLIT, int SUB = 1>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gather_mfma_kernel(GatherArgs a) {
   constexpr int TILE = KVB * kRow;                 // elements of one K or V tile
   constexpr int HPW = SPLIT ? 1 : NW / 4;          // heads per workgroup
@@ -136,11 +138,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   const uint16_t* kbg = a.k + (int64_t)b * a.ksb + (int64_t)g * a.ksh;
   const uint16_t* vbg = a.v + (int64_t)b * a.vsb + (int64_t)g * a.vsh;
   const int32_t* list = a.idx + li * a.cap;
-  // rows of list entry e inside the KV sequence (0 for an index outside it: nothing is read)
-  auto entry_rows = [&](int e, int& key0) {
-    const int j = list[e];
-    key0 = j * KVB;
-    return (j < 0 || key0 >= a.L) ? 0 : min(KVB, a.L - key0);
+  // rows of tile u (of list entry e0 + u / SUB) inside the KV sequence (0 for
+  // an index outside it, or a part beyond the end: nothing is read)
+  auto entry_rows = [&](int u, int& key0) {
+    const int j = list[e0 + u / SUB];
+    const int blk0 = j * (KVB * SUB);
+    key0 = blk0 + (u % SUB) * KVB;
+    return (j < 0 || blk0 >= a.L || key0 >= a.L) ? 0 : min(KVB, a.L - key0);
   };
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int e, int buf) {
@@ -151,15 +155,21 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     issue_tile<KVB, NW>(vbg + (int64_t)key0 * a.vsl, a.vsl, nk, lds0 + (uint32_t)((buf * 2 + 1) * TILE * 2));
   };
 
-  if (e0 < e1) issue(e0, 0);
-  for (int e = e0; e < e1; ++e) {
-    const int buf = (e - e0) & 1;
+  const int nt = (e1 - e0) * SUB;
+  // largest query position of the wave: a tile wholly after it is skipped
+  int wave_max_pos = valid ? qpos : -1;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) wave_max_pos = max(wave_max_pos, wave_xor(wave_max_pos, m));
+  wave_max_pos = __builtin_amdgcn_readfirstlane(wave_max_pos);
+  if (nt > 0) issue(0, 0);
+  for (int u = 0; u < nt; ++u) {
+    const int buf = u & 1;
     int key0;
-    const int nk = entry_rows(e, key0);
-    wait_tile_loads();                             // this wave's part of entry e is in LDS
-    __syncthreads();                               // ... and everyone's; entry e - 1 is finished
-    if (e + 1 < e1) issue(e + 1, buf ^ 1);
-    if (nk == 0 || !wave_busy) continue;
+    const int nk = entry_rows(u, key0);
+    wait_tile_loads();                             // this wave's part of tile u is in LDS
+    __syncthreads();                               // ... and everyone's; tile u - 1 is finished
+    if (u + 1 < nt) issue(u + 1, buf ^ 1);
+    if (nk == 0 || !wave_busy || (a.causal && key0 > wave_max_pos)) continue;
     const uint16_t* Ks = lds + buf * 2 * TILE;
     const uint16_t* Vs = Ks + TILE;
     f32x16 s[KVB / 32];
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   }
 
   if (!wave_busy) return;
-  const float l_tot = l_run + wave_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (!SPLIT) {
     if (!valid) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -354,7 +364,7 @@ __global__ __launch_bounds__(512, 1) void gather_pp_kernel(GatherArgs a) {
   }
 
   if (!wave_busy || !valid) return;
-  const float l_tot = l_run + wave_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   uint16_t* orow = a.o + (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl;
 #pragma unroll
@@ -380,8 +390,9 @@ void launch_gather(const GatherArgs& a, int kv_block, bool split, hipStream_t s)
     if (kv_block == 128) hipLaunchKernelGGL((gather_pp_kernel<128>), grid, dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gather_pp_kernel<64>), grid, dim3(512), 0, s, a);
   } else {
+    // odd group size: one head per workgroup, 64-key tiles (two workgroups per CU)
     dim3 grid(a.B * a.Hkv * a.NQB * a.G);
-    if (kv_block == 128) hipLaunchKernelGGL((gather_mfma_kernel<128, 4, false>), grid, dim3(256), 0, s, a);
+    if (kv_block == 128) hipLaunchKernelGGL((gather_mfma_kernel<64, 4, false, 2>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((gather_mfma_kernel<64, 4, false>), grid, dim3(256), 0, s, a);
   }
 }

@@ -61,6 +61,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// The values of lanes l % 32 and l % 32 + 32 (gfx950 v_permlane32_swap: one
+// instruction, no LDS round trip): {v[l & 31], v[(l & 31) + 32]} on every lane.
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+// Sum over the lane pair (l, l ^ 32), the same bits on both lanes.
+__device__ __forceinline__ float pair_sum(float v) {
+  float lo, hi;
+  lane_pair(v, lo, hi);
+  return lo + hi;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Which half of the frequency chunks a head dim belongs to: 0 = fast band

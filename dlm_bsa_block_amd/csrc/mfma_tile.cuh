@@ -267,7 +267,9 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[NT]) {
       n = m + (r ? 1 : 0);
     }
   }
-  return max3f(x[0], wave_xor(x[0], 32), x[0]);
+  float lo, hi;
+  lane_pair(x[0], lo, hi);
+  return max3f(lo, hi, hi);
 }
 
 // Online-softmax bookkeeping for one tile, in log2 units.  m_ref is the

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(NW * 64, 1) void threshold_kernel(ThrArgs a) {
 
   if (wr == 0 && lane == 0 && a.kept) a.kept[((int64_t)b * Hq + h) * a.NQT + qt] = nkept;
   if (!valid) return;
-  const float l_tot = l_run + wave_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   uint16_t* orow = a.o + (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl;
 #pragma unroll

@@ -275,6 +275,13 @@ def test_sparse_prefill_small(bsa, L):
         assert cnt[0, 0, i] == min(i + 1, (2 if i else 1) + -(-(i + 1) // 10))
 
 
+def test_sparse_prefill_odd_group(bsa):
+    """Odd group size (3 query heads per KV head) takes the one-head-per-workgroup
+    path with 64-key tiles; ragged tail (2944 = 23 blocks of 128)."""
+    w = synth.sparse_prefill(L=2944, Hq=3, Hkv=1)
+    _prefill_case(bsa, w)
+
+
 def test_sparse_prefill_full_size(bsa):
     """32K causal prefill, 32/8 heads: selection on every query block, outputs on 16 sampled blocks."""
     w = synth.sparse_prefill()
@@ -334,6 +341,14 @@ def test_threshold_small(bsa, L, lam):
     kept, _ = _threshold_case(bsa, w, lam, pairs)
     if lam == 0.0:
         assert np.array_equal(kept[0, 0], np.arange(1, NQT + 1))
+
+
+def test_threshold_odd_group(bsa):
+    """Odd group size: one head per workgroup; ragged tail."""
+    L = 1900
+    w = synth.threshold_prefill(L=L, Hq=3, Hkv=1, seg_tiles=5, n_needles=2)
+    NQT = -(-L // 128)
+    _threshold_case(bsa, w, 1e-3, [(0, h, qt) for h in range(3) for qt in range(NQT)])
 
 
 def test_threshold_full_size_sampled(bsa):
