@@ -61,6 +61,68 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wavefront reductions through DPP (no LDS round trips): quad swaps, row
+// mirrors, then the row broadcasts fold the four 16-lane rows into lane 63,
+// whose value is read back as a scalar.  Fixed order: identical bits in every
+// lane.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xf, false);
+}
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+  return __uint_as_float(dpp_u32<CTRL, ROWMASK>(__float_as_uint(old), __float_as_uint(v)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0xB1>(0.f, v);          // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(0.f, v);          // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(0.f, v);         // row_half_mirror
+  v += dpp_f32<0x140>(0.f, v);         // row_mirror
+  v += dpp_f32<0x142, 0xa>(0.f, v);    // row_bcast:15 into rows 1, 3
+  v += dpp_f32<0x143, 0xc>(0.f, v);    // row_bcast:31 into rows 2, 3
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x4E>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x141>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x140>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x142, 0xa>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x143, 0xc>(-INFINITY, v));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+// Inclusive prefix sum over the lanes (Hillis-Steele inside each 16-lane row
+// with row shifts, then the row broadcasts carry the row totals).
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += dpp_u32<0x111>(0u, v);          // row_shr:1
+  v += dpp_u32<0x112>(0u, v);          // row_shr:2
+  v += dpp_u32<0x114>(0u, v);          // row_shr:4
+  v += dpp_u32<0x118>(0u, v);          // row_shr:8
+  v += dpp_u32<0x142, 0xa>(0u, v);     // row_bcast:15 into rows 1, 3
+  v += dpp_u32<0x143, 0xc>(0u, v);     // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Wavefront-wide (key, idx) with the largest key, the smallest idx among
+// equal keys; the result is uniform.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ void argmax_step(uint32_t& k, uint32_t& i) {
+  const uint32_t ok = dpp_u32<CTRL, ROWMASK>(0u, k), oi = dpp_u32<CTRL, ROWMASK>(0xFFFFFFFFu, i);
+  const bool better = ok > k || (ok == k && oi < i);
+  k = better ? ok : k;
+  i = better ? oi : i;
+}
+__device__ __forceinline__ void wave_argmax_dpp(uint32_t& k, uint32_t& i) {
+  argmax_step<0xB1>(k, i);
+  argmax_step<0x4E>(k, i);
+  argmax_step<0x141>(k, i);
+  argmax_step<0x140>(k, i);
+  argmax_step<0x142, 0xa>(k, i);
+  argmax_step<0x143, 0xc>(k, i);
+  k = __builtin_amdgcn_readlane(k, 63);
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
 // The values of lanes l % 32 and l % 32 + 32 (gfx950 v_permlane32_swap: one
 // instruction, no LDS round trip): {v[l & 31], v[(l & 31) + 32]} on every lane.
 __device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {

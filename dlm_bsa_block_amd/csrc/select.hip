@@ -125,15 +125,15 @@ __device__ __forceinline__ RowPlan row_plan(const PickArgs& a, int row) {
 }
 
 // Sum of a value over the 256 threads, identical bits in every thread
-// (fixed butterfly inside each wave, then the 4 wave totals in order).
+// (fixed DPP order inside each wave, then the 4 wave totals in order).
 __device__ __forceinline__ float block_sum(float v, float* red, int slot) {
-  v = wave_sum(v);
+  v = wave_sum_dpp(v);
   if ((threadIdx.x & 63) == 0) red[slot * 4 + (threadIdx.x >> 6)] = v;
   __syncthreads();
   return red[slot * 4] + red[slot * 4 + 1] + red[slot * 4 + 2] + red[slot * 4 + 3];
 }
 __device__ __forceinline__ float block_max(float v, float* red, int slot) {
-  v = wave_max(v);
+  v = wave_max_dpp(v);
   if ((threadIdx.x & 63) == 0) red[slot * 4 + (threadIdx.x >> 6)] = v;
   __syncthreads();
   return fmaxf(fmaxf(red[slot * 4], red[slot * 4 + 1]), fmaxf(red[slot * 4 + 2], red[slot * 4 + 3]));
@@ -253,12 +253,7 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
           uint32_t c[4], tot = 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; tot += c[i]; }
-          uint32_t incl = tot;
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t t = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += t;
-          }
+          const uint32_t incl = wave_incl_scan_dpp(tot);
           uint32_t run = incl - tot;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
