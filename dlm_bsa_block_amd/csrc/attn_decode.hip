@@ -94,15 +94,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot = fmaf(qx[h][e], kx[p][e], dot);
-#pragma unroll
-        for (int m = 1; m < LPT; m <<= 1) dot += wave_xor(dot, m);
+        dot = group_sum<LPT>(dot);
         s[p] = ok[p] ? dot : -INFINITY;
       }
       float mx = s[0];
 #pragma unroll
       for (int p = 1; p < PASSES; ++p) mx = fmaxf(mx, s[p]);
-#pragma unroll
-      for (int m = LPT; m < 64; m <<= 1) mx = fmaxf(mx, wave_xor(mx, m));
+      mx = groups_max<LPT>(mx);
       const float m_new = fmaxf(wm[h], mx);
       if (m_new == -INFINITY) continue;                  // nothing visible yet (wave-uniform)
       const float alpha = fast_exp2(wm[h] - m_new);
@@ -116,12 +114,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = fmaf(pr, vx[p][e], acc[e]);
       }
+      l = groups_sum<LPT>(l);
 #pragma unroll
-      for (int m = LPT; m < 64; m <<= 1) {
-        l += wave_xor(l, m);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += wave_xor(acc[e], m);
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = groups_sum<LPT>(acc[e]);
       wm[h] = m_new;
       wl[h] = fmaf(wl[h], alpha, l);
 #pragma unroll
@@ -164,75 +159,62 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 
 // Merge the split partials of active (row, head) pairs of a query block in
 // ascending slice order; write O (q's dtype) and the natural-log LSE.  One
-// workgroup per (chunk of a.qvc <= kCombQV query vectors, query block, KV
-// group).  A thread's partial loads for a batch of slices are issued together.
+// thread per (query vector, dim): it loads the (m, l) of every slice and its
+// dim of every partial O together -- one round trip to memory, no exchange
+// between threads -- and merges them with a running maximum, 32 slices at a
+// time.
 template <int ODT>
 __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
-  __shared__ float sm_w[kCombQV][kCombMaxItems];
-  __shared__ float sm_M[kCombQV], sm_L[kCombQV];
-  __shared__ int sm_ok[kCombQV];
+  constexpr int BATCH = 32;
   const int QVC = a.qvc;
   const int nchunk = (a.QV + QVC - 1) / QVC;
   const int qb = blockIdx.x / nchunk, qv0 = (blockIdx.x % nchunk) * QVC;
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = a.G, QV = a.QV, D = a.D, Hq = a.Hkv * G;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
+  const int c = tid / D, d = tid - c * D;          // 256 threads cover QVC * D <= 256 (D >= 64)
+  if (c >= QVC) return;
+  const int qv = qv0 + c;
+  const int rl = qv / G, hl = qv - rl * G;
+  const int row = qb * a.q_block + rl;
+  if (qv >= QV || row >= a.Lq || (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0)) return;
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
   const int64_t nunits = (int64_t)a.cnt[li] * a.unit_num;
   const int nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
   const int64_t p0 = li * a.items;
-  for (int c = w; c < QVC; c += 4) {
-    const int qv = qv0 + c;
-    const int rl = qv / G;
-    const int row = qb * a.q_block + rl;
-    const bool ok = qv < QV && row < a.Lq && (!a.row_mask || a.row_mask[(int64_t)b * a.Lq + row] != 0);
-    float M = -INFINITY, L = 0.f;
-    if (ok) {
-      float mv[kCombMaxItems / 64], lv[kCombMaxItems / 64];
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int it0 = 0; it0 < nvalid; it0 += BATCH) {
+    float mv[BATCH], lv[BATCH], ov[BATCH];
 #pragma unroll
-      for (int u = 0; u < kCombMaxItems / 64; ++u) {
-        const int it = lane + 64 * u;
-        mv[u] = it < nvalid ? a.part_ml[((p0 + it) * QV + qv) * 2] : -INFINITY;
-        lv[u] = it < nvalid ? a.part_ml[((p0 + it) * QV + qv) * 2 + 1] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < kCombMaxItems / 64; ++u) M = fmaxf(M, mv[u]);
-      M = wave_max(M);
-#pragma unroll
-      for (int u = 0; u < kCombMaxItems / 64; ++u) {
-        const int it = lane + 64 * u;
-        const float wgt = mv[u] == -INFINITY ? 0.f : fast_exp2(mv[u] - M);
-        if (it < nvalid) sm_w[c][it] = wgt;
-        L = fmaf(lv[u], wgt, L);
-      }
-      L = wave_sum(L);
+    for (int u = 0; u < BATCH; ++u) {
+      const int it = min(it0 + u, nvalid - 1);        // clamped: loads need no branch
+      const int64_t pi = (p0 + it) * QV + qv;
+      mv[u] = a.part_ml[pi * 2];
+      lv[u] = a.part_ml[pi * 2 + 1];
+      ov[u] = a.part_o[pi * D + d];
     }
-    if (lane == 0) { sm_M[c] = M; sm_L[c] = L; sm_ok[c] = ok; }
-  }
-  __syncthreads();
-  for (int i = tid; i < QVC * D; i += 256) {
-    const int c = i / D, d = i - c * D;
-    if (!sm_ok[c]) continue;
-    const int qv = qv0 + c, rl = qv / G, hl = qv - rl * G;
-    const int row = qb * a.q_block + rl;
-    float acc = 0.f;
-    for (int it0 = 0; it0 < nvalid; it0 += 32) {
-      float pv[32];
+    float bm = M;
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        pv[u] = (it0 + u < nvalid) ? a.part_o[((p0 + it0 + u) * QV + qv) * D + d] : 0.f;
+    for (int u = 0; u < BATCH; ++u)
+      if (it0 + u < nvalid) bm = fmaxf(bm, mv[u]);
+    if (bm == -INFINITY) continue;                    // nothing visible so far
+    const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+    L *= alpha;
+    acc *= alpha;
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        if (it0 + u < nvalid) acc = fmaf(pv[u], sm_w[c][it0 + u], acc);
+    for (int u = 0; u < BATCH; ++u) {
+      const float wgt = (it0 + u < nvalid && mv[u] != -INFINITY) ? fast_exp2(mv[u] - bm) : 0.f;
+      L = fmaf(lv[u], wgt, L);
+      acc = fmaf(ov[u], wgt, acc);
     }
-    const float L = sm_L[c];
-    const float out = L > 0.f ? acc / L : 0.f;
-    const int h = g * G + hl;
-    const int64_t oi = (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl + d;
-    if (ODT == BSA_BF16) reinterpret_cast<uint16_t*>(a.o)[oi] = (uint16_t)f32_to_bf16(out);
-    else reinterpret_cast<float*>(a.o)[oi] = out;
-    if (d == 0) a.lse[((int64_t)b * Hq + h) * a.Lq + row] = L > 0.f ? (sm_M[c] + log2f(L)) * kLn2 : -INFINITY;
+    M = bm;
   }
+  const float out = L > 0.f ? acc / L : 0.f;
+  const int h = g * G + hl;
+  const int64_t oi = (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl + d;
+  if (ODT == BSA_BF16) reinterpret_cast<uint16_t*>(a.o)[oi] = (uint16_t)f32_to_bf16(out);
+  else reinterpret_cast<float*>(a.o)[oi] = out;
+  if (d == 0) a.lse[((int64_t)b * Hq + h) * a.Lq + row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 void launch_combine(const CombArgs& a, int odt, int B, hipStream_t s) {

@@ -473,8 +473,9 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
   if (pl.kind != 1) {
     CombArgs c;
     c.part_o = part_o; c.part_ml = part_ml; c.cnt = cnt; c.items = pl.items;
-    if (pl.kind == 0) { c.unit_num = p.kv_block; c.unit_den = pl.tok_per_item; c.qvc = 1; }
-    else { c.unit_num = 1; c.unit_den = kSplitBlocks; c.qvc = kCombQV; }
+    if (pl.kind == 0) { c.unit_num = p.kv_block; c.unit_den = pl.tok_per_item; }
+    else { c.unit_num = 1; c.unit_den = kSplitBlocks; }
+    c.qvc = 256 / pl.D;                          // one thread per (query vector, dim)
     c.Hkv = pl.Hkv; c.G = pl.G; c.NQB = pl.NQB; c.q_block = p.q_block; c.Lq = pl.Lq; c.D = pl.D; c.QV = pl.qv;
     c.row_mask = row_mask; c.o = o.data; c.osb = o.stride_b; c.osh = o.stride_h; c.osl = o.stride_l; c.lse = lse;
     launch_combine(c, o.dtype, pl.B, s);

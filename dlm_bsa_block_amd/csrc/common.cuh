@@ -130,6 +130,48 @@ __device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
   lo = __uint_as_float(r[0]);
   hi = __uint_as_float(r[1]);
 }
+// The values of lanes l with bit 4 clear and set (v_permlane16_swap):
+// {v[l & ~16], v[l | 16]} on every lane.
+__device__ __forceinline__ void lane_pair16(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+// Sum / max over the lanes l ^ (N * k): across the N-lane groups, lane by
+// lane (N = 16: the four 16-lane rows; N = 8: the eight 8-lane groups); the
+// same bits on every lane of such a set.
+template <int N>
+__device__ __forceinline__ float groups_sum(float v) {
+  static_assert(N == 8 || N == 16, "group width");
+  float lo, hi;
+  if (N == 8) v += dpp_f32<0x128>(0.f, v);         // row_ror:8: lane i reads lane i ^ 8
+  lane_pair16(v, lo, hi);
+  v = lo + hi;
+  lane_pair(v, lo, hi);
+  return lo + hi;
+}
+template <int N>
+__device__ __forceinline__ float groups_max(float v) {
+  static_assert(N == 8 || N == 16, "group width");
+  float lo, hi;
+  if (N == 8) v = fmaxf(v, dpp_f32<0x128>(-INFINITY, v));
+  lane_pair16(v, lo, hi);
+  v = fmaxf(lo, hi);
+  lane_pair(v, lo, hi);
+  return fmaxf(lo, hi);
+}
+// Sum inside each N-lane group (N = 8 or 16) by DPP butterflies; the same
+// bits on every lane of the group.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "group width");
+  v += dpp_f32<0xB1>(0.f, v);          // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(0.f, v);          // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(0.f, v);         // row_half_mirror
+  if (N == 16) v += dpp_f32<0x140>(0.f, v);   // row_mirror
+  return v;
+}
+
 // Sum over the lane pair (l, l ^ 32), the same bits on both lanes.
 __device__ __forceinline__ float pair_sum(float v) {
   float lo, hi;

@@ -14,7 +14,6 @@ constexpr int kDecTok = 32;         // list tokens per decode chunk (4 waves x 8
 constexpr int kDecMaxItems = 512;   // decode slices per (row, group)
 constexpr int kDecMinSlice = 32;    // list tokens per decode slice, at least
 constexpr int kSplitBlocks = 8;     // list entries per MFMA split workgroup
-constexpr int kCombQV = 4;          // query vectors per combine workgroup
 constexpr int kCombMaxItems = 512;  // split slices the combine can merge
 
 struct DecArgs {
@@ -37,7 +36,7 @@ struct CombArgs {
   const int32_t* cnt;
   int items, unit_num, unit_den;  // valid slices = ceil(cnt * unit_num / unit_den)
   int Hkv, G, NQB, q_block, Lq, D, QV;
-  int qvc;                        // query vectors per combine workgroup (<= kCombQV)
+  int qvc;                        // query vectors per combine workgroup (256 / D)
   const uint8_t* row_mask;
   void* o;
   int64_t osb, osh, osl;
