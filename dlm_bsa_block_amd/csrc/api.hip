@@ -120,7 +120,10 @@ static bsa_status validate_select(const bsa_tensor* q, int32_t Hkv, int32_t NB, 
   const int Rtot = p->pooled_q ? pl.NQB : pl.Lq;
   const size_t nz = (size_t)pl.B * q->H * Rtot * (p->dual_band ? 2 : 1) * (size_t)((NB + 3) & ~3);
   pl.z_bytes = align256(nz * 4);
-  pl.tau_bytes = p->dual_band ? align256((size_t)pl.B * q->H * 2 * 4) : 0;
+  // tau [B][Hq][2], then the chunk sums [B][Hkv + Hq][chunks][4]
+  pl.tau_bytes = p->dual_band ? align256((size_t)pl.B * q->H * 2 * 4) +
+                                    align256((size_t)pl.B * (Hkv + q->H) * tau_chunks(NB, p->pooled_q ? q->L : 0) * 16)
+                              : 0;
   const bool multi_row = !p->pooled_q && std::min(p->q_block, pl.Lq) > 1;
   pl.bits_bytes = multi_row ? align256((size_t)pl.B * Hkv * Rtot * 128 * 4) : 0;
   pl.cnt_bytes = 0;

@@ -21,6 +21,10 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 void launch_summaries(const bsa_tensor& x, int block, int layout, int first, int nblk,
                       float* mean, float* energy, hipStream_t s);
 
+// Band-temperature sums are taken over chunks of this many pooled vectors.
+constexpr int kTauChunk = 16;
+inline int tau_chunks(int nb_k, int nb_q) { return (int)ceil_div(nb_k > nb_q ? nb_k : nb_q, kTauChunk); }
+
 struct SelectPlan {
   int B, Hq, Hkv, G, D, NB, NQB, Lq, R;   // R = selection rows per query block (1 when pooled)
   int kp_max, cap;

@@ -44,7 +44,7 @@ __device__ __forceinline__ void band_energy_ratio_terms(const float* __restrict_
 }
 
 __device__ __forceinline__ float block_sum256(float v, float* sh) {
-  v = wave_sum(v);
+  v = wave_sum_dpp(v);
   const int tid = threadIdx.x;
   __syncthreads();
   if ((tid & 63) == 0) sh[tid >> 6] = v;
@@ -52,36 +52,68 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
   return sh[0] + sh[1] + sh[2] + sh[3];
 }
 
-__global__ __launch_bounds__(256) void tau_kernel(const float* __restrict__ k_mean, const float* __restrict__ k_energy,
-                                                  int NB, const float* __restrict__ q_mean, int64_t qsb, int64_t qsh,
-                                                  int64_t qsl, const float* __restrict__ q_energy, int NQB, int D,
-                                                  int G, int layout, float* __restrict__ tau_ws,
-                                                  float* __restrict__ tau_out) {
+// Partial band sums of one chunk of kTauChunk pooled vectors: for K (one
+// workgroup per (chunk, KV head)) and, when queries are pooled, for Q (per
+// (chunk, query head)).  part[b][id][chunk] = {sum |mean|^2 fast band, slow
+// band, sum energy fast, slow}, id = KV head, or Hkv + query head.
+__global__ __launch_bounds__(256) void tau_partial_kernel(const float* __restrict__ k_mean,
+                                                          const float* __restrict__ k_energy, int NB,
+                                                          const float* __restrict__ q_mean, int64_t qsb, int64_t qsh,
+                                                          int64_t qsl, const float* __restrict__ q_energy, int NQB,
+                                                          int D, int Hkv, int Hq, int layout, int nchunk,
+                                                          float* __restrict__ part) {
   __shared__ float sh[4];
-  const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x, Hkv = Hq / G, g = h / G;
-  float nf, ns, df, ds;
-  const int64_t kbase = ((int64_t)b * Hkv + g) * NB;
-  band_energy_ratio_terms(k_mean + kbase * D, D, k_energy + kbase * 2, NB, D, layout, nf, ns, df, ds);
-  float r[2];
-  {
-    const float a = block_sum256(nf, sh), c = block_sum256(ns, sh);
-    const float e0 = block_sum256(df, sh), e1 = block_sum256(ds, sh);
-    r[0] = e0 > 0.f ? a / e0 : 1.f;
-    r[1] = e1 > 0.f ? c / e1 : 1.f;
+  const int c = blockIdx.x, id = blockIdx.y, b = blockIdx.z;
+  const bool is_q = id >= Hkv;
+  const int nblk = is_q ? NQB : NB;
+  const int j0 = c * kTauChunk, j1 = min(nblk, j0 + kTauChunk);
+  float nf = 0.f, ns = 0.f, df = 0.f, ds = 0.f;
+  if (j0 < nblk) {
+    const float* mean;
+    const float* energy;
+    int64_t rs;
+    if (is_q) {
+      const int h = id - Hkv;
+      mean = q_mean + b * qsb + h * qsh + (int64_t)j0 * qsl;
+      rs = qsl;
+      energy = q_energy + (((int64_t)b * Hq + h) * NQB + j0) * 2;
+    } else {
+      mean = k_mean + (((int64_t)b * Hkv + id) * NB + j0) * D;
+      rs = D;
+      energy = k_energy + (((int64_t)b * Hkv + id) * NB + j0) * 2;
+    }
+    band_energy_ratio_terms(mean, rs, energy, j1 - j0, D, layout, nf, ns, df, ds);
   }
-  if (q_mean != nullptr) {
-    const int64_t qe = ((int64_t)b * Hq + h) * NQB;
-    band_energy_ratio_terms(q_mean + b * qsb + h * qsh, qsl, q_energy + qe * 2, NQB, D, layout, nf, ns, df, ds);
-    const float a = block_sum256(nf, sh), c = block_sum256(ns, sh);
-    const float e0 = block_sum256(df, sh), e1 = block_sum256(ds, sh);
-    r[0] *= e0 > 0.f ? a / e0 : 1.f;
-    r[1] *= e1 > 0.f ? c / e1 : 1.f;
+  const float a0 = block_sum256(nf, sh), a1 = block_sum256(ns, sh);
+  const float e0 = block_sum256(df, sh), e1 = block_sum256(ds, sh);
+  if (threadIdx.x == 0) {
+    float* o = part + (((int64_t)b * (Hkv + Hq) + id) * nchunk + c) * 4;
+    o[0] = a0; o[1] = a1; o[2] = e0; o[3] = e1;
   }
-  if (threadIdx.x < 2) {
-    const float t = fmaxf(1e-6f, sqrtf(r[threadIdx.x]));
-    tau_ws[((int64_t)b * Hq + h) * 2 + threadIdx.x] = t;
-    if (tau_out) tau_out[((int64_t)b * Hq + h) * 2 + threadIdx.x] = t;
-  }
+}
+
+// Temperature per (query head, band) from the chunk sums, added in chunk
+// order: tau = max(1e-6, sqrt(rho_K (* rho_Q))), rho = pooled / mean energy.
+__global__ __launch_bounds__(64) void tau_final_kernel(const float* __restrict__ part, int Hkv, int G, int nchunk,
+                                                       int with_q, float* __restrict__ tau_ws,
+                                                       float* __restrict__ tau_out) {
+  const int h = blockIdx.x, b = blockIdx.y, Hq = Hkv * G;
+  if (threadIdx.x >= 2) return;
+  const int band = threadIdx.x;
+  auto ratio = [&](int id) {
+    const float* p = part + ((int64_t)b * (Hkv + Hq) + id) * nchunk * 4;
+    float num = 0.f, den = 0.f;
+    for (int c = 0; c < nchunk; ++c) {
+      num += p[c * 4 + band];
+      den += p[c * 4 + 2 + band];
+    }
+    return den > 0.f ? num / den : 1.f;
+  };
+  float r = ratio(h / G);
+  if (with_q) r *= ratio(Hkv + h);
+  const float t = fmaxf(1e-6f, sqrtf(r));
+  tau_ws[((int64_t)b * Hq + h) * 2 + band] = t;
+  if (tau_out) tau_out[((int64_t)b * Hq + h) * 2 + band] = t;
 }
 
 // -------------------------------------------------------------------- pick ---
@@ -479,8 +511,14 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
   float* tau = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.z_bytes);
   if (p.dual_band) {
     const float* qm = p.pooled_q ? static_cast<const float*>(q.data) : nullptr;
-    hipLaunchKernelGGL(tau_kernel, dim3(pl.Hq, pl.B), dim3(256), 0, s, k_mean, k_energy, NB, qm, q.stride_b,
-                       q.stride_h, q.stride_l, q_energy, pl.NQB, pl.D, G, p.layout, tau, tau_out);
+    const int nchunk = tau_chunks(NB, p.pooled_q ? pl.NQB : 0);
+    float* part = tau + align256((size_t)pl.B * pl.Hq * 2 * 4) / 4;
+    const int ids = Hkv + (qm ? pl.Hq : 0);
+    hipLaunchKernelGGL(tau_partial_kernel, dim3(nchunk, ids, pl.B), dim3(256), 0, s, k_mean, k_energy, NB, qm,
+                       q.stride_b, q.stride_h, q.stride_l, q_energy, pl.NQB, pl.D, Hkv, pl.Hq, p.layout, nchunk,
+                       part);
+    hipLaunchKernelGGL(tau_final_kernel, dim3(pl.Hq, pl.B), dim3(64), 0, s, part, Hkv, G, nchunk, qm ? 1 : 0, tau,
+                       tau_out);
   }
   const int M = Rtot * G;
   const uint8_t* qd = static_cast<const uint8_t*>(q.data);
