@@ -37,6 +37,7 @@ struct GatherArgs {
   float* part_o;
   float* part_ml;
   int items;
+  int wpg;                        // streaming kernel: workgroups per (batch, KV group)
 };
 
 // One workgroup = NW waves of 32 query vectors.  Direct mode: NW / 4 heads of
@@ -234,52 +235,149 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
 // each; the K copy of entry e + 1 is issued once B has finished reading the
 // K buffer it replaces (one phase after A did), the V copy likewise, so each
 // copy has a whole entry of compute to land.
+//
+// The work items of one (batch, KV group) -- (query block, head pair) -- are
+// dealt out to wpg workgroups (about one per CU), largest query block first
+// and in alternating direction per round, so every workgroup gets a
+// near-equal share of tiles.  A workgroup stages the lists of all its items in
+// LDS once and walks them as one stream of list entries: the copies, barriers
+// and the half-entry offset of the two groups run on across item boundaries,
+// so starting an item costs neither a list round trip nor a pipeline fill.
+// Workgroup n runs on XCD n % 8 and serves KV group n % (B * Hkv), so a
+// group's K/V tiles stay in the L2 of its XCD.
+constexpr int kMaxItemsWG = 64;    // work items one streaming workgroup takes
+
 template <int KVB>
-__global__ __launch_bounds__(512, 1) void gather_pp_kernel(GatherArgs a) {
+__global__ __launch_bounds__(512, 1) void gather_stream_kernel(GatherArgs a) {
   constexpr int NW = 8;
   constexpr int TILE = KVB * kRow;
   constexpr int IT = KVB / 4 / NW;                 // copy instructions per wave for one K or V tile
-  // K buffers 0, 1 then V buffers 0, 1, always addressed with a compile-time
-  // parity so that the LDS reads use immediate offsets.
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE];   // K0 K1 V0 V1
   __shared__ int list_sh[kMaxListMfma];
+  __shared__ uint8_t ent_sh[kMaxListMfma];         // item | 64 (first entry of it) | 128 (last entry)
+  __shared__ int it_r[kMaxItemsWG], it_start[kMaxItemsWG + 1];
+  __shared__ uint32_t empty_sh[2];
 
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: role branches stay scalar
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = w >> 2, wr = w & 3;
-  // XCD-aware order: workgroup n runs on XCD n % 8; give each XCD a contiguous
-  // run of (batch, group, query block descending, head pair) work items.
-  const int total = gridDim.x, nb = blockIdx.x;
-  const int wi = (total % 8 == 0) ? (nb % 8) * (total / 8) + nb / 8 : nb;
-  const int sets = a.G / 2;
-  const int h0 = (wi % sets) * 2;
-  const int rest = wi / sets;
-  const int qb = a.NQB - 1 - rest % a.NQB;
-  const int bgi = rest / a.NQB;
-  const int b = bgi / a.Hkv, g = bgi - b * a.Hkv;
-  const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
-  const int n = min(a.cnt[li], a.cap);
-  const int32_t* list = a.idx + li * a.cap;
-  for (int i = tid; i < n; i += NW * 64) list_sh[i] = list[i];
+  const int BG = a.B * a.Hkv, bg = blockIdx.x % BG, slot = blockIdx.x / BG;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int sets = a.G / 2, NI = a.NQB * sets, S = a.wpg;
+  // item i of this workgroup: rank r of the group's items (largest query block first)
+  auto item_rank = [&](int i) __attribute__((always_inline)) {
+    return i * S + ((i & 1) ? S - 1 - slot : slot);
+  };
+  const int rounds = (NI + S - 1) / S;
+  const int nit = rounds == 0 ? 0 : rounds - 1 + (item_rank(rounds - 1) < NI ? 1 : 0);
+  if (nit == 0) return;                            // uniform over the workgroup
+
+  // Per-item state of a wave, all wave-uniform: the lane's query is row
+  // wmin - q_pos0 + r32 of head h.
+  struct Ctx {
+    int h, wmin;
+    bool busy;
+  };
+  auto ctx = [&](int r) __attribute__((always_inline)) {
+    Ctx c;
+    const int qb = a.NQB - 1 - r / sets;
+    c.h = g * a.G + (r % sets) * 2 + grp;
+    c.busy = 32 * wr < a.q_block && qb * a.q_block + 32 * wr < a.Lq;
+    c.wmin = a.q_pos0 + qb * a.q_block + 32 * wr;  // smallest query position of the wave
+    return c;
+  };
+  const int64_t li0 = (int64_t)bg * a.NQB;
+  bf16x8 qf[8];
+  // Per-lane address terms below come from a copy of threadIdx.x passed
+  // through an empty asm, so they are rebuilt where used instead of being held
+  // (and spilled) across the loop: a spill reload would wait for every tile
+  // copy in flight.
+  auto lane_id = []() __attribute__((always_inline)) {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t & 63;
+  };
+  auto load_q = [&](const Ctx& c) __attribute__((always_inline)) {
+    const int ln = lane_id();
+    const int row = c.wmin - a.q_pos0 + (ln & 31);
+    const bool ok = 32 * wr + (ln & 31) < a.q_block && row < a.Lq;
+    const uint16_t* qrow = a.q + (int64_t)b * a.qsb + (int64_t)c.h * a.qsh + (int64_t)row * a.qsl;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      u32x4 v = ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * (ln >> 5)) : u32x4{0, 0, 0, 0};
+      qf[st] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
+
+  Ctx cur = ctx(item_rank(0));
+  load_q(cur);
+  // item table and the flattened list
+  if (w == 0) {
+    int n_i = 0;
+    if (lane < nit) {
+      const int r = item_rank(lane);
+      n_i = min(a.cnt[li0 + (a.NQB - 1 - r / sets)], a.cap);
+      it_r[lane] = r;
+    }
+    const int incl = (int)wave_incl_scan_dpp((uint32_t)n_i);
+    if (lane < nit) it_start[lane + 1] = incl;
+    if (lane == 0) it_start[0] = 0;
+    const unsigned long long em = __ballot(lane < nit && n_i == 0);
+    if (lane == 0) { empty_sh[0] = (uint32_t)em; empty_sh[1] = (uint32_t)(em >> 32); }
+  }
+  __syncthreads();
+  const int N = __builtin_amdgcn_readfirstlane(it_start[nit]);
+  for (int e = tid; e < N; e += NW * 64) {
+    int lo = 0, hi = nit - 1;                      // the item whose entries hold e
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (it_start[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    const int st = it_start[lo];
+    const int qb = a.NQB - 1 - it_r[lo] / sets;
+    list_sh[e] = a.idx[(li0 + qb) * a.cap + (e - st)];
+    ent_sh[e] = (uint8_t)(lo | (e == st ? 64 : 0) | (e + 1 == it_start[lo + 1] ? 128 : 0));
+  }
   __syncthreads();
 
-  const int h = g * a.G + h0 + grp;
-  const int qv = 32 * wr + r32;
-  const int row = qb * a.q_block + qv;
-  const bool valid = qv < a.q_block && row < a.Lq;
-  const bool wave_busy = 32 * wr < a.q_block && qb * a.q_block + 32 * wr < a.Lq;
-  const int qpos = a.q_pos0 + row;
-  int wave_min_pos = valid ? qpos : 0x7FFFFFFF;
+  f32x16 o[4];
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) wave_min_pos = min(wave_min_pos, wave_xor(wave_min_pos, m));
-  wave_min_pos = __builtin_amdgcn_readfirstlane(wave_min_pos);
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  auto epilogue = [&](const Ctx& c) __attribute__((always_inline)) {
+    if (!c.busy) return;
+    const float l_tot = pair_sum(l_run);
+    const int ln = lane_id();
+    const int row = c.wmin - a.q_pos0 + (ln & 31);
+    if (32 * wr + (ln & 31) >= a.q_block || row >= a.Lq) return;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow = a.o + (int64_t)b * a.osb + (int64_t)c.h * a.osh + (int64_t)row * a.osl;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * dt + 8 * i4 + 4 * (ln >> 5);   // dims of O elements 4 i4 .. 4 i4 + 3
+        u32x2 pk = {pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
+                    pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d) = pk;
+      }
+    if (ln < 32)
+      a.lse[((int64_t)b * a.Hkv * a.G + c.h) * a.Lq + row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  };
+  // items with an empty list: O = 0, LSE = -inf (o, m, l hold exactly that now)
+  {
+    unsigned long long em = ((unsigned long long)__builtin_amdgcn_readfirstlane(empty_sh[1]) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane(empty_sh[0]);
+    while (em) {
+      const int i = __builtin_ctzll(em);
+      em &= em - 1;
+      epilogue(ctx(item_rank(i)));
+    }
+  }
 
   const uint16_t* kbg = a.k + (int64_t)b * a.ksb + (int64_t)g * a.ksh;
   const uint16_t* vbg = a.v + (int64_t)b * a.vsb + (int64_t)g * a.vsh;
   const uint32_t kvoff = tile_lane_offset<NW>(a.ksl), vvoff = tile_lane_offset<NW>(a.vsl);
-  // Copy K or V of list entry e into dst.  Always IT instructions per wave, so
-  // the vmcnt bookkeeping below holds; an index outside the sequence copies
-  // the first rows (the entry is then masked out entirely).
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int e, bool is_v, int buf) __attribute__((always_inline)) {
     const uint32_t dst = lds0 + (uint32_t)((is_v ? 2 + buf : buf) * TILE * 2);
@@ -293,91 +391,150 @@ __global__ __launch_bounds__(512, 1) void gather_pp_kernel(GatherArgs a) {
     else
       issue_tile<KVB, NW>(base + (ok ? (int64_t)key0 * sl : 0), sl, ok ? a.L - key0 : min(KVB, a.L), dst);
   };
-  bf16x8 qf[8];
-  load_q_frag(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)row * a.qsl, valid, qf);
+  auto ent = [&](int e) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane((int)ent_sh[e]);
+  };
   // Let the Q loads land before any tile copy is issued: a use of Q inside the
   // loop would otherwise wait on every copy in flight.
+  if (N == 0) return;                              // uniform over the workgroup
+  if (ent(0) & 63) {                               // the first item has an empty list
+    cur = ctx(__builtin_amdgcn_readfirstlane(it_r[ent(0) & 63]));
+    load_q(cur);
+  }
   settle(qf);
-  if (n > 0) { issue(0, false, 0); issue(0, true, 0); }
-  if (n > 1) { issue(1, false, 1); issue(1, true, 1); }
+  issue(0, false, 0);
+  issue(0, true, 0);
+  if (N > 1) { issue(1, false, 1); issue(1, true, 1); }
+  f32x16 s[KVB / 32];
   int kofs[8], vofs[8];
   k_offsets(kofs);
   v_offsets(vofs);
-  f32x16 o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 s[KVB / 32];
+  auto qk = [&](int t) __attribute__((always_inline)) { qk_tile<KVB>(lds + (t & 1) * TILE, kofs, qf, s); };
 
-  auto smpv = [&](int e, const uint16_t* Vs) __attribute__((always_inline)) {
+  auto smpv = [&](int e, const Ctx& c, const uint16_t* Vs) __attribute__((always_inline)) {
     const int j = __builtin_amdgcn_readfirstlane(list_sh[e]);
     const int key0 = j * KVB;
     const int nk = (j < 0 || key0 >= a.L) ? 0 : min(KVB, a.L - key0);
-    if (nk < KVB || (a.causal && key0 + KVB - 1 > wave_min_pos)) {
+    if (nk < KVB || (a.causal && key0 + KVB - 1 > c.wmin)) {
       int lim = nk - 1;                            // largest visible key offset of this lane's query
-      if (a.causal) lim = min(lim, qpos - key0);
+      if (a.causal) lim = min(lim, c.wmin + r32 - key0);
       mask_tile<KVB / 32>(s, lim);
     }
     const float msub = softmax_rescale(tile_max<KVB / 32>(s) * a.c2, m_run, l_run, o);
     softmax_pv_tile<KVB>(Vs, vofs, s, a.c2, msub, l_run, o);
   };
-
-  // Entry t lives in the buffers of parity t & 1; the copies of entry t + 1
-  // go to the other ones.  Both roles pass the same two barriers per entry.
+  // Two barriers per list entry for both groups.  Loads issued after a
+  // copy (queries, output stores) only make the waits below stricter.
   auto sync_k = [&](int t) __attribute__((always_inline)) {
-    // K of entry t must be in LDS: the copies issued after it (V of t, and at
-    // the start K and V of entry 1) may still be in flight
-    if (t == 0 && n > 1) wait_loads_but<3 * IT>();
+    if (t == 0 && N > 1) wait_loads_but<3 * IT>();
     else wait_loads_but<IT>();
-    lds_barrier();                                 // ... for every wave; B is done with the K buffer of t - 1
-    if (t >= 1 && t + 1 < n) issue(t + 1, false, (t + 1) & 1);
+    lds_barrier();
+    if (t >= 1 && t + 1 < N) issue(t + 1, false, (t + 1) & 1);
   };
   auto sync_v = [&](int t) __attribute__((always_inline)) {
-    // V of entry t must be in LDS: only the K copy of entry t + 1 (or at the
-    // start K and V of entry 1) may still be in flight
     if (t == 0) {
-      if (n > 1) wait_loads_but<2 * IT>();
+      if (N > 1) wait_loads_but<2 * IT>();
       else wait_loads_but<0>();
-    } else if (t + 1 < n) {
+    } else if (t + 1 < N) {
       wait_loads_but<IT>();
     } else {
       wait_loads_but<0>();
     }
-    lds_barrier();                                 // ... for every wave; B is done with the V buffer of t - 1
-    if (t >= 1 && t + 1 < n) issue(t + 1, true, (t + 1) & 1);
+    lds_barrier();
+    if (t >= 1 && t + 1 < N) issue(t + 1, true, (t + 1) & 1);
   };
-  if (grp == 0) {                                  // A: K Q^T of t, then softmax + P V of t
-    for (int t = 0; t < n; ++t) {
+  // A new item needs no zeroing of o: with the running max at -inf its first
+  // visible tile rescales o by exp2(-inf) = 0 (o is always finite), and a row
+  // that never sees a key is written as 0 through l = 0.
+  auto restart = [&]() __attribute__((always_inline)) {
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+  // Each role walks the entries of one item in an inner loop that loads
+  // nothing the compiler can see, and handles the entry that crosses into the
+  // next item in straight-line code after it: there the next queries load,
+  // unconditionally (the current item's again after the last item), and are
+  // awaited before the next tile copy is issued.  A load whose wait the
+  // compiler cannot place on every path would make it wait for all copies in
+  // flight before each K Q^T.
+  int cur_it = ent(0) & 63;
+  auto item_end = [&](int it) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(it_start[it + 1]);
+  };
+  if (grp == 0) {
+    // A: K Q^T of t, then softmax + P V of t; the next item's queries load
+    // during the softmax of an item's last entry
+    int t = 0;
+    while (true) {
+      const int last = item_end(cur_it) - 1;
+      for (; t < last; ++t) {
+        sync_k(t);
+        if (cur.busy) qk(t);
+        sync_v(t);
+        if (cur.busy) smpv(t, cur, lds + (2 + (t & 1)) * TILE);
+      }
       sync_k(t);
-      if (wave_busy) qk_tile<KVB>(lds + (t & 1) * TILE, kofs, qf, s);
+      if (cur.busy) qk(t);
       sync_v(t);
-      if (wave_busy) smpv(t, lds + (2 + (t & 1)) * TILE);
+      const bool more = t + 1 < N;
+      const int nit_idx = more ? (ent(t + 1) & 63) : cur_it;
+      const Ctx nc = ctx(__builtin_amdgcn_readfirstlane(it_r[nit_idx]));
+      load_q(nc);
+      if (cur.busy) smpv(t, cur, lds + (2 + (t & 1)) * TILE);
+      epilogue(cur);
+      restart();
+      settle(qf);
+      cur = nc;
+      cur_it = nit_idx;
+      ++t;
+      if (!more) break;
     }
-  } else {                                         // B: softmax + P V of t - 1, then K Q^T of t
-    for (int t = 0; t < n; ++t) {
-      sync_k(t);
-      if (wave_busy && t >= 1) smpv(t - 1, lds + (2 + ((t - 1) & 1)) * TILE);
+  } else {
+    // B: softmax + P V of t - 1, then K Q^T of t; the queries of a new item
+    // load once the last K Q^T of the previous one is done
+    sync_k(0);
+    sync_v(0);
+    if (cur.busy) qk(0);
+    int t = 1;
+    while (true) {
+      const int end = item_end(cur_it);
+      for (; t < end; ++t) {                       // t - 1 and t in the same item
+        sync_k(t);
+        if (cur.busy) smpv(t - 1, cur, lds + (2 + ((t - 1) & 1)) * TILE);
+        sync_v(t);
+        if (cur.busy) qk(t);
+      }
+      if (t >= N) break;
+      sync_k(t);                                   // t opens the next item
+      const int nit_idx = ent(t) & 63;
+      const Ctx nc = ctx(__builtin_amdgcn_readfirstlane(it_r[nit_idx]));
+      load_q(nc);
+      if (cur.busy) smpv(t - 1, cur, lds + (2 + ((t - 1) & 1)) * TILE);
+      epilogue(cur);
+      restart();
+      settle(qf);
+      cur = nc;
+      cur_it = nit_idx;
       sync_v(t);
-      if (wave_busy) qk_tile<KVB>(lds + (t & 1) * TILE, kofs, qf, s);
+      if (cur.busy) qk(t);
+      ++t;
     }
-    if (wave_busy && n > 0) smpv(n - 1, lds + (2 + ((n - 1) & 1)) * TILE);
+    if (cur.busy) smpv(N - 1, cur, lds + (2 + ((N - 1) & 1)) * TILE);
+    epilogue(cur);
   }
+}
 
-  if (!wave_busy || !valid) return;
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* orow = a.o + (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = o_dim(dt, 4 * i4);
-      u32x2 pk = {pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
-                  pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + d) = pk;
-    }
-  if (lane < 32)
-    a.lse[((int64_t)b * a.Hkv * a.G + h) * a.Lq + row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 void launch_gather(const GatherArgs& a, int kv_block, bool split, hipStream_t s) {
@@ -386,9 +543,17 @@ void launch_gather(const GatherArgs& a, int kv_block, bool split, hipStream_t s)
     if (kv_block == 128) hipLaunchKernelGGL((gather_mfma_kernel<128, 4, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((gather_mfma_kernel<64, 4, true>), grid, dim3(256), 0, s, a);
   } else if (a.G % 2 == 0) {
-    dim3 grid(a.B * a.Hkv * a.NQB * (a.G / 2));
-    if (kv_block == 128) hipLaunchKernelGGL((gather_pp_kernel<128>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gather_pp_kernel<64>), grid, dim3(512), 0, s, a);
+    // streaming kernel: about one workgroup per CU, each (batch, KV group) served by wpg of them
+    const int BG = a.B * a.Hkv, NI = a.NQB * (a.G / 2);
+    const int per_wg_max = std::min(kMaxItemsWG, kMaxListMfma / std::max(1, a.cap));
+    int wpg = std::max(1, cu_count() / BG);
+    wpg = std::max(wpg, (int)ceil_div(NI, per_wg_max));
+    wpg = std::min(wpg, NI);
+    GatherArgs b = a;
+    b.wpg = wpg;
+    dim3 grid(BG * wpg);
+    if (kv_block == 128) hipLaunchKernelGGL((gather_stream_kernel<128>), grid, dim3(512), 0, s, b);
+    else hipLaunchKernelGGL((gather_stream_kernel<64>), grid, dim3(512), 0, s, b);
   } else {
     // odd group size: one head per workgroup, 64-key tiles (two workgroups per CU)
     dim3 grid(a.B * a.Hkv * a.NQB * a.G);
