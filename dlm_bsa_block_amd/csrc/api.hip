@@ -47,9 +47,10 @@ static bsa_status check_tensor(const bsa_tensor* t, const char* name, bool allow
   return BSA_OK;
 }
 
-static bool same_shape(const bsa_tensor* a, const bsa_tensor* b) {
-  return a->B == b->B && a->H == b->H && a->L == b->L && a->D == b->D && a->dtype == b->dtype;
+static bool same_dims(const bsa_tensor* a, const bsa_tensor* b) {
+  return a->B == b->B && a->H == b->H && a->L == b->L && a->D == b->D;
 }
+static bool same_shape(const bsa_tensor* a, const bsa_tensor* b) { return same_dims(a, b) && a->dtype == b->dtype; }
 
 }  // namespace bsa
 
@@ -221,7 +222,8 @@ bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, co
   bsa_status st = validate_attention(q, k, v, p, pl);
   if (st != BSA_OK) return st;
   if ((st = check_tensor(o, "o", true)) != BSA_OK) return st;
-  if (!same_shape(q, o)) return fail(BSA_ERR_INVALID, "o must match q in shape and dtype");
+  if (!same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
+    return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
   if (!idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "idx, cnt and lse are required");
   if (pl.part_bytes && (!workspace || workspace_bytes < pl.part_bytes))
     return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, pl.part_bytes);
@@ -241,7 +243,8 @@ bsa_status bsa_threshold_attention_fwd(const bsa_tensor* q, const bsa_tensor* k,
   if ((st = check_tensor(k, "k", false)) != BSA_OK) return st;
   if ((st = check_tensor(v, "v", false)) != BSA_OK) return st;
   if ((st = check_tensor(o, "o", true)) != BSA_OK) return st;
-  if (!same_shape(k, v) || !same_shape(q, o)) return fail(BSA_ERR_INVALID, "k/v or q/o shapes differ");
+  if (!same_shape(k, v) || !same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
+    return fail(BSA_ERR_INVALID, "k/v shapes differ, or o does not match q in shape (dtype: q's or f32)");
   if (q->dtype != k->dtype || q->B != k->B || q->D != k->D || q->H % k->H)
     return fail(BSA_ERR_INVALID, "q/k shapes are incompatible");
   if (q->dtype != BSA_BF16 || q->D != 128) return fail(BSA_ERR_UNSUPPORTED, "threshold attention needs bf16, D = 128");

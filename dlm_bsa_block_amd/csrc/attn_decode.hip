@@ -34,12 +34,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
   const int row = qb;                                   // one query row per block
   if (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) return;
-  const int64_t ntok = (int64_t)a.cnt[li] * a.kv_block;
   const int64_t t_begin = (int64_t)item * a.tok_per_item;
-  if (ntok == 0) return;                                // the combine writes O = 0, LSE = -inf
-  if (t_begin >= ntok) return;                          // no slice of the list for this workgroup
   const int qpos = a.q_pos0 + row;
-  const int64_t t_end = min(ntok, t_begin + a.tok_per_item);
+  // The list count, the queries and the block indices of the first chunk are
+  // loaded together: an index slot past the count holds a stale value that is
+  // only used once the count has ruled it in.
+  const int64_t cap_tok = (int64_t)a.cap * a.kv_block;
+  int blk[PASSES], off[PASSES];
+  auto load_blocks = [&](int64_t c0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int64_t t = c0 + w * TPW + p * TPP + tg;
+      const int e = (int)(t / a.kv_block);
+      off[p] = (int)(t - (int64_t)e * a.kv_block);
+      blk[p] = t < cap_tok ? a.idx[li * a.cap + e] : -1;
+    }
+  };
+  const int n_list = a.cnt[li];
+  load_blocks(t_begin);
 
   float qx[G][8];
 #pragma unroll
@@ -48,6 +60,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) qx[h][e] *= a.c2;
   }
+  const int64_t ntok = (int64_t)n_list * a.kv_block;
+  if (ntok == 0) return;                                // the combine writes O = 0, LSE = -inf
+  if (t_begin >= ntok) return;                          // no slice of the list for this workgroup
+  const int64_t t_end = min(ntok, t_begin + a.tok_per_item);
   float wm[G], wl[G], wacc[G][8];                       // this wave's running state
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -60,20 +76,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + d0) * ES;
 
   for (int64_t c0 = t_begin; c0 < t_end; c0 += kDecTok) {
+    if (c0 != t_begin) load_blocks(c0);
     int pos[PASSES];
     bool ok[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int64_t t = c0 + w * TPW + p * TPP + tg;
-      ok[p] = t < t_end;
-      pos[p] = 0;
-      if (ok[p]) {
-        const int e = (int)(t / a.kv_block), off = (int)(t - (int64_t)e * a.kv_block);
-        const int blk = a.idx[li * a.cap + e];
-        const int key = blk * a.kv_block + off;
-        ok[p] = blk >= 0 && key < a.L && (!a.causal || key <= qpos);
-        pos[p] = key;
-      }
+      const int64_t key = (int64_t)blk[p] * a.kv_block + off[p];
+      ok[p] = t < t_end && blk[p] >= 0 && key < a.L && (!a.causal || key <= qpos);
+      pos[p] = ok[p] ? (int)key : 0;
     }
     float kx[PASSES][8], vx[PASSES][8];
 #pragma unroll
@@ -179,20 +190,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
   const int row = qb * a.q_block + rl;
   if (qv >= QV || row >= a.Lq || (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0)) return;
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
-  const int64_t nunits = (int64_t)a.cnt[li] * a.unit_num;
-  const int nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
   const int64_t p0 = li * a.items;
-  float M = -INFINITY, L = 0.f, acc = 0.f;
-  for (int it0 = 0; it0 < nvalid; it0 += BATCH) {
-    float mv[BATCH], lv[BATCH], ov[BATCH];
+  float mv[BATCH], lv[BATCH], ov[BATCH];
+  // Slots are clamped to the workspace, not to the valid count, so the first
+  // batch loads together with the count; slots past the count may hold stale
+  // values and are excluded by selects (never multiplied by a zero weight).
+  auto load_batch = [&](int it0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const int it = min(it0 + u, nvalid - 1);        // clamped: loads need no branch
+      const int it = min(it0 + u, a.items - 1);
       const int64_t pi = (p0 + it) * QV + qv;
       mv[u] = a.part_ml[pi * 2];
       lv[u] = a.part_ml[pi * 2 + 1];
       ov[u] = a.part_o[pi * D + d];
     }
+  };
+  const int64_t nunits = (int64_t)a.cnt[li] * a.unit_num;
+  load_batch(0);
+  const int nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int it0 = 0; it0 < nvalid; it0 += BATCH) {
+    if (it0 > 0) load_batch(it0);
     float bm = M;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u)
@@ -203,9 +221,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
     acc *= alpha;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const float wgt = (it0 + u < nvalid && mv[u] != -INFINITY) ? fast_exp2(mv[u] - bm) : 0.f;
-      L = fmaf(lv[u], wgt, L);
-      acc = fmaf(ov[u], wgt, acc);
+      if (it0 + u < nvalid && mv[u] != -INFINITY) {
+        const float wgt = fast_exp2(mv[u] - bm);
+        L = fmaf(lv[u], wgt, L);
+        acc = fmaf(ov[u], wgt, acc);
+      }
     }
     M = bm;
   }

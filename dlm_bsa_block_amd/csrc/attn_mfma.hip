@@ -31,7 +31,8 @@ struct GatherArgs {
   int B, cap, NQB, Hkv, G, L, Lq, q_block, q_pos0, causal;
   float c2;                       // scale * log2(e)
   const uint8_t* row_mask;
-  uint16_t* o;
+  void* o;                        // bf16, or f32 when o_f32
+  int o_f32;
   int64_t osb, osh, osl;
   float* lse;
   float* part_o;
@@ -191,16 +192,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   if (!SPLIT) {
     if (!valid) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = a.o + (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = o_dim(dt, 4 * i4);
-        u32x2 pk = {pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
-                    pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d) = pk;
-      }
+    const int64_t oi = (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl;
+    store_o_row(a.o_f32 ? (void*)(static_cast<float*>(a.o) + oi) : (void*)(static_cast<uint16_t*>(a.o) + oi),
+                a.o_f32, o, inv, lane >> 5);
     if (lane < 32)
       a.lse[((int64_t)b * a.Hkv * a.G + h) * a.Lq + row] =
           l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
@@ -351,16 +345,9 @@ __global__ __launch_bounds__(512, 1) void gather_stream_kernel(GatherArgs a) {
     const int row = c.wmin - a.q_pos0 + (ln & 31);
     if (32 * wr + (ln & 31) >= a.q_block || row >= a.Lq) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = a.o + (int64_t)b * a.osb + (int64_t)c.h * a.osh + (int64_t)row * a.osl;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = 32 * dt + 8 * i4 + 4 * (ln >> 5);   // dims of O elements 4 i4 .. 4 i4 + 3
-        u32x2 pk = {pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
-                    pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d) = pk;
-      }
+    const int64_t oi = (int64_t)b * a.osb + (int64_t)c.h * a.osh + (int64_t)row * a.osl;
+    store_o_row(a.o_f32 ? (void*)(static_cast<float*>(a.o) + oi) : (void*)(static_cast<uint16_t*>(a.o) + oi),
+                a.o_f32, o, inv, ln >> 5);
     if (ln < 32)
       a.lse[((int64_t)b * a.Hkv * a.G + c.h) * a.Lq + row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   };
@@ -631,7 +618,7 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
     a.idx = idx; a.cnt = cnt; a.B = pl.B; a.cap = p.cap; a.NQB = pl.NQB; a.Hkv = pl.Hkv; a.G = pl.G;
     a.L = pl.L; a.Lq = pl.Lq; a.q_block = p.q_block; a.q_pos0 = p.q_pos0; a.causal = p.causal; a.c2 = c2;
     a.row_mask = row_mask;
-    a.o = static_cast<uint16_t*>(o.data); a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
+    a.o = o.data; a.o_f32 = o.dtype == BSA_F32; a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
     a.lse = lse; a.part_o = part_o; a.part_ml = part_ml; a.items = pl.items;
     launch_gather(a, p.kv_block, pl.kind == 2, s);
   }

@@ -380,6 +380,25 @@ __device__ __forceinline__ int o_dim(int dt, int i) {
   return 32 * dt + 8 * (i >> 2) + 4 * hi + (i & 3);
 }
 
+// Store the lane's part of one normalised output row, O^T tiles o scaled by
+// inv: element 4 i4 + e of tile dt is dim 32 dt + 8 i4 + 4 hi + e.  The row
+// is bf16 (rounded to nearest even) or f32.
+__device__ __forceinline__ void store_o_row(void* orow, bool f32, const f32x16 (&o)[4], float inv, int hi) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = 32 * dt + 8 * i4 + 4 * hi;
+      const float a = o[dt][4 * i4] * inv, b = o[dt][4 * i4 + 1] * inv;
+      const float c = o[dt][4 * i4 + 2] * inv, e = o[dt][4 * i4 + 3] * inv;
+      if (f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(orow) + d) = f32x4{a, b, c, e};
+      } else {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(orow) + d) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, e)};
+      }
+    }
+}
+
 // Make the compiler wait here for the loads that filled qf (an empty asm
 // that reads them), so that it need not wait for them later, when tile
 // copies it cannot see are in flight behind them.

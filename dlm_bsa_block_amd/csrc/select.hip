@@ -132,6 +132,7 @@ struct PickArgs {
 constexpr int kPickMaxWords = 128;     // NB <= 4096
 constexpr int kPickThreads = 256;
 constexpr int kPickRegs = 32;          // logits held per thread at once
+constexpr int kPickChanBatch = 16;     // (head, band) channels reduced together, at most
 
 struct RowPlan {
   int qb, rows, nC, nf_first, last_lo, kp, n_free;
@@ -169,6 +170,39 @@ __device__ __forceinline__ float block_max(float v, float* red, int slot) {
   if ((threadIdx.x & 63) == 0) red[slot * 4 + (threadIdx.x >> 6)] = v;
   __syncthreads();
   return fmaxf(fmaxf(red[slot * 4], red[slot * 4 + 1]), fmaxf(red[slot * 4 + 2], red[slot * 4 + 3]));
+}
+// The first n of N maxima (or sums) over the 256 threads behind a single
+// barrier, in slots slot0 .. slot0 + N - 1; same fixed order as the one-value
+// forms.
+template <int N>
+__device__ __forceinline__ void block_max_n(float (&v)[N], int n, float* red, int slot0) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i < n) v[i] = wave_max_dpp(v[i]);                   // n is uniform: unused values skip the reduction
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int i = 0; i < N; ++i) red[(slot0 + i) * 4 + (threadIdx.x >> 6)] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float* r = red + (slot0 + i) * 4;
+    v[i] = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
+  }
+}
+template <int N>
+__device__ __forceinline__ void block_sum_n(float (&v)[N], int n, float* red, int slot0) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i < n) v[i] = wave_sum_dpp(v[i]);                   // n is uniform: unused values skip the reduction
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int i = 0; i < N; ++i) red[(slot0 + i) * 4 + (threadIdx.x >> 6)] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float* r = red + (slot0 + i) * 4;
+    v[i] = r[0] + r[1] + r[2] + r[3];
+  }
 }
 
 // Ordered compaction of a bitmap (nw <= 128 words) into ascending indices,
@@ -213,7 +247,7 @@ template <int U>
 __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bits[kPickMaxWords];
-  __shared__ float red[16 * 4];
+  __shared__ float red[2 * kPickChanBatch * 4];
   __shared__ int misc[2];
   __shared__ int eqcnt[U][4];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -230,7 +264,7 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
     float s[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) s[u] = 0.f;
-    constexpr int CC = kPickRegs / U > 0 ? kPickRegs / U : 1;   // channels per register batch
+    constexpr int CC = kPickRegs / U > kPickChanBatch ? kPickChanBatch : (kPickRegs / U > 0 ? kPickRegs / U : 1);
     for (int c0 = 0; c0 < nchan; c0 += CC) {
       float z[CC][U];
 #pragma unroll
@@ -240,21 +274,31 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
           const int j = tid + kPickThreads * u;
           z[cc][u] = (c0 + cc < nchan && j < nC) ? zrow[(int64_t)(c0 + cc) * NBp + j] : -INFINITY;
         }
+      // all channels of the batch share the two barriers of their max and sum
+      float mx[CC], sm[CC];
 #pragma unroll
       for (int cc = 0; cc < CC; ++cc) {
-        if (c0 + cc >= nchan) continue;                 // uniform over the workgroup
-        float mx = z[cc][0];
+        mx[cc] = z[cc][0];
 #pragma unroll
-        for (int u = 1; u < U; ++u) mx = fmaxf(mx, z[cc][u]);
-        mx = block_max(mx, red, 2 * cc);
-        float sm = 0.f;
+        for (int u = 1; u < U; ++u) mx[cc] = fmaxf(mx[cc], z[cc][u]);
+      }
+      const int nb = min(CC, nchan - c0);             // channels in this batch
+      block_max_n<CC>(mx, nb, red, 0);
+#pragma unroll
+      for (int cc = 0; cc < CC; ++cc) {
+        sm[cc] = 0.f;
+        if (c0 + cc >= nchan) continue;                 // uniform over the workgroup
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          z[cc][u] = fast_exp2(z[cc][u] - mx);          // -inf (not a candidate) -> 0
-          sm += z[cc][u];
+          z[cc][u] = fast_exp2(z[cc][u] - mx[cc]);      // -inf (not a candidate) -> 0
+          sm[cc] += z[cc][u];
         }
-        sm = block_sum(sm, red, 2 * cc + 1);
-        const float inv = wband / sm;
+      }
+      block_sum_n<CC>(sm, nb, red, CC);
+#pragma unroll
+      for (int cc = 0; cc < CC; ++cc) {
+        if (c0 + cc >= nchan) continue;
+        const float inv = wband / sm[cc];
 #pragma unroll
         for (int u = 0; u < U; ++u) s[u] = fmaf(z[cc][u], inv, s[u]);
       }

@@ -30,7 +30,8 @@ struct ThrArgs {
   int B, Hkv, G, L, Lq, NQT, NKT, causal;
   float c2;        // scale * log2(e)
   float lnlam2;    // ln(lambda) * log2(e); -inf when lambda = 0
-  uint16_t* o;
+  void* o;                        // bf16, or f32 when o_f32
+  int o_f32;
   int64_t osb, osh, osl;
   float* lse;
   int32_t* kept;
@@ -139,16 +140,9 @@ __global__ __launch_bounds__(NW * 64, 1) void threshold_kernel(ThrArgs a) {
   if (!valid) return;
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* orow = a.o + (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = o_dim(dt, 4 * i4);
-      u32x2 pk = {pack_bf16x2(o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv),
-                  pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + d) = pk;
-    }
+  const int64_t oi = (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl;
+  store_o_row(a.o_f32 ? (void*)(static_cast<float*>(a.o) + oi) : (void*)(static_cast<uint16_t*>(a.o) + oi),
+              a.o_f32, o, inv, lane >> 5);
   if (lane < 32)
     a.lse[((int64_t)b * Hq + h) * a.Lq + row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
@@ -168,7 +162,7 @@ void launch_threshold(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
   a.causal = p.causal;
   a.c2 = p.scale * kLog2e;
   a.lnlam2 = p.lambda > 0.f ? (float)(std::log((double)p.lambda) * 1.4426950408889634) : -INFINITY;
-  a.o = static_cast<uint16_t*>(o.data); a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
+  a.o = o.data; a.o_f32 = o.dtype == BSA_F32; a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
   a.lse = lse; a.kept = kept; a.keep_map = keep_map;
   if (a.G % 2 == 0) {
     dim3 grid(a.B * a.Hkv * a.NQT * (a.G / 2));

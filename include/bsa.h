@@ -181,7 +181,8 @@ bsa_status bsa_active_rows(const bsa_tensor* q_cur, const bsa_tensor* q_prev, fl
  * A row that sees no key gets O = 0 and LSE = -inf.  Rows with row_mask = 0
  * are NOT written: the caller's cached O/LSE stay in place (LoSA sec. 2, stable
  * tokens reuse the previous step's output and statistics).
- * q, k, v share dtype; o has q's shape and dtype; lse is [B, Hq, Lq] f32
+ * q, k, v share dtype; o has q's shape and either q's dtype or f32 (the fp32
+ * result before rounding); lse is [B, Hq, Lq] f32
  * contiguous.  Supported: bf16 with D = 128 and kv_block in {64, 128}; f32
  * or D = 64 only for single-row query blocks (decode).  workspace:
  * bsa_attention_workspace_bytes() bytes (split-KV partial results; no
@@ -212,7 +213,7 @@ bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, co
  * tile is processed (exp, V load, PV product, m_r = max(m_r, tm_r)) when any
  * row of the query tile votes keep, and skipped entirely otherwise.
  * lambda = 0 never skips (plain causal attention); lambda must lie in [0, 1].
- * O (q's shape/dtype), lse [B, Hq, Lq] f32.  Optional diagnostics:
+ * O (q's shape; bf16 or f32), lse [B, Hq, Lq] f32.  Optional diagnostics:
  * kept_tiles [B, Hq, NQT] int32 (tiles processed per query tile) and keep_map
  * [B, Hq, NQT, NKT] uint8 (1 = processed; entries of tiles never visited are
  * left unwritten).  Supported: bf16, D = 128, tile = 128, Lq == L (self

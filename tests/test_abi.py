@@ -132,6 +132,11 @@ def test_attention_rejects_bad_arguments(lib):
     st = lib.bsa_sparse_attention_fwd(ctypes.byref(q3), ctypes.byref(k3), ctypes.byref(k3), FAKE, FAKE,
                                       ctypes.byref(pd), None, ctypes.byref(q3), FAKE, FAKE, 1 << 30, None)
     assert st == L.BSA_ERR_UNSUPPORTED
+    # o takes q's dtype or f32: an f32 decode query with a bf16 output is refused
+    qd, kd, od = _t(H=32, Lq=1, dtype=L.BSA_F32), _t(H=8, Lq=4096, dtype=L.BSA_F32), _t(H=32, Lq=1)
+    st = lib.bsa_sparse_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(kd), FAKE, FAKE,
+                                      ctypes.byref(pd), None, ctypes.byref(od), FAKE, FAKE, 1 << 30, None)
+    assert st == L.BSA_ERR_INVALID and "o must match q" in _err(lib)
 
 
 def test_threshold_rejects_bad_arguments(lib):
