@@ -237,6 +237,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
 // LDS once and walks them as one stream of list entries: the copies, barriers
 // and the half-entry offset of the two groups run on across item boundaries,
 // so starting an item costs neither a list round trip nor a pipeline fill.
+// An item's list is walked from its highest block down: the diagonal tile,
+// whose nearby keys tend to score highest, comes first and sets a running
+// max that later tiles seldom raise, which skips most O rescales (the sum is
+// order-independent up to rounding).
 // Workgroup n runs on XCD n % 8 and serves KV group n % (B * Hkv), so a
 // group's K/V tiles stay in the L2 of its XCD.
 constexpr int kMaxItemsWG = 64;    // work items one streaming workgroup takes
@@ -327,9 +331,9 @@ __global__ __launch_bounds__(512, 1) void gather_stream_kernel(GatherArgs a) {
       const int mid = (lo + hi + 1) >> 1;
       if (it_start[mid] <= e) lo = mid; else hi = mid - 1;
     }
-    const int st = it_start[lo];
+    const int st = it_start[lo], n = it_start[lo + 1] - st;
     const int qb = a.NQB - 1 - it_r[lo] / sets;
-    list_sh[e] = a.idx[(li0 + qb) * a.cap + (e - st)];
+    list_sh[e] = a.idx[(li0 + qb) * a.cap + (n - 1 - (e - st))];   // highest block first
     ent_sh[e] = (uint8_t)(lo | (e == st ? 64 : 0) | (e + 1 == it_start[lo + 1] ? 128 : 0));
   }
   __syncthreads();
