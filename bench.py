@@ -10,7 +10,8 @@ with inputs resident in HBM.
 
 Also measured (reported under "secondary"): the block-wise diffusion denoising
 step (32 query rows, 32K prefix), causal block-sparse prefill at 32K with
-dual-band selection, and softmax-threshold prefill at 128K.
+dual-band selection, softmax-threshold prefill at 128K, and softmax-threshold
+decode over the whole 64K cache.
 
 Prints ONE JSON line.  Inputs are seeded synthetic tensors (see synth/).
 """
@@ -28,6 +29,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+# Softmax-threshold decode: lambda = a / L (BLASST: one constant per model and
+# phase); a chosen so that about 70% of the V tiles are skipped at 64K on the
+# synthetic GQA decode workload.
+THRESH_DECODE_A = 0.4 * 65536
+THRESH_DECODE_SPLIT = 1024     # keys per split-KV slice
 
 
 def log(msg):
@@ -57,7 +63,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", default="all", choices=["all", "decode", "dlm", "prefill", "threshold"],
+    ap.add_argument("--only", default="all", choices=["all", "decode", "dlm", "prefill", "threshold", "tdecode"],
                     help="which workloads to run (the headline line needs decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
@@ -81,12 +87,15 @@ def time_calls(torch, fn, reps, warmup=3):
 
 
 def time_cold(torch, fn, reps, flush):
-    """Like time_calls, but each call follows an untimed write of a 2 GiB buffer
-    that evicts the inputs from L2 and the 256 MB Infinity Cache."""
+    """Like time_calls, but each call follows an untimed read of a 2 GiB buffer
+    that evicts the inputs from L2 and the 256 MB Infinity Cache.  The pass is
+    read-only, so the caches then hold clean lines, as after the other layers'
+    KV reads between two decode steps of one layer (after a write pass, the
+    dirty lines' write-back halves the HBM read rate of the next kernel)."""
     s = torch.cuda.current_stream()
     tot = 0.0
     for _ in range(reps):
-        flush.add_(1)
+        flush.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(s)
         fn()
@@ -290,6 +299,60 @@ def bench_threshold(torch, bsa, synth, reps):
                 speedup_vs_lambda0=round(t0 / t, 3))
 
 
+# ------------------------------------------------------- threshold decode ---
+def bench_threshold_decode(torch, bsa, synth, reps, flush, w=None):
+    """Dense decode over the whole 64K cache with the softmax-threshold skip at
+    lambda = a / L: every K tile is read, V only for tiles some head keeps."""
+    if w is None:
+        log("tdecode: generating the 64K GQA workload")
+        w = synth.gqa_decode()
+    p = w.params
+    q, k, v = (to_dev(torch, x, "bf16") for x in (w.q, w.k, w.v))
+    B, Hkv, L, D = k.shape
+    Hq = q.shape[1]
+    G = Hq // Hkv
+    lam = min(1.0, THRESH_DECODE_A / L)
+    ws = torch.zeros(bsa.bsa_threshold_decode_workspace_bytes(q, k, THRESH_DECODE_SPLIT), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+    kept = torch.empty((B, Hq), dtype=torch.int32, device="cuda")
+
+    def run(lm):
+        return lambda: bsa.bsa_threshold_decode_fwd(q, k, v, lm, scale=p["scale"], kv_split=THRESH_DECODE_SPLIT,
+                                                    o=o, lse=lse, kept=kept, workspace=ws)
+
+    _, _, _, km = bsa.bsa_threshold_decode_fwd(q, k, v, lam, scale=p["scale"], kv_split=THRESH_DECODE_SPLIT,
+                                               want_keep_map=True, workspace=ws)
+    nt = km.shape[2]
+    v_tiles = int(km.view(B, Hkv, G, nt).amax(dim=2).sum().item())        # tiles whose V is loaded
+    head_kept = int(km.sum().item())
+    t_warm = time_calls(torch, run(lam), reps)
+    t_cold = time_cold(torch, run(lam), reps, flush)
+    t0_cold = time_cold(torch, run(0.0), reps, flush)
+    k_bytes = B * Hkv * L * D * 2
+    alg = k_bytes + v_tiles * 64 * D * 2 + 2 * B * Hq * D * 2            # all K, loaded V, q and o
+    dense = 2 * k_bytes + 2 * B * Hq * D * 2
+    other = {}
+    for Ls in (16384, 32768):                                             # the same a at other lengths
+        ws_ = synth.gqa_decode(L=Ls)
+        qs, ks, vs = (to_dev(torch, x, "bf16") for x in (ws_.q, ws_.k, ws_.v))
+        lm = min(1.0, THRESH_DECODE_A / Ls)
+        _, _, _, kms = bsa.bsa_threshold_decode_fwd(qs, ks, vs, lm, scale=p["scale"], kv_split=THRESH_DECODE_SPLIT,
+                                                    want_keep_map=True)
+        vt = kms.view(B, Hkv, G, -1).amax(dim=2)
+        other[str(Ls)] = dict(lam=round(lm, 4), skip_head_tiles=round(1 - kms.float().mean().item(), 4),
+                              skip_v_tiles=round(1 - vt.float().mean().item(), 4))
+        del qs, ks, vs
+    gbs = alg / (t_cold * 1e3)
+    return dict(us_cold=round(t_cold, 2), us_warm=round(t_warm, 2), lam=round(lam, 4), a=THRESH_DECODE_A,
+                kv_split=THRESH_DECODE_SPLIT, skip_head_tiles=round(1 - head_kept / (B * Hq * nt), 4),
+                skip_v_tiles=round(1 - v_tiles / (B * Hkv * nt), 4), algorithmic_bytes=alg,
+                gbs_cold=round(gbs, 1), hbm_frac_cold=round(gbs / HBM_PEAK_GBS, 4),
+                lambda0_us_cold=round(t0_cold, 2), lambda0_gbs_cold=round(dense / (t0_cold * 1e3), 1),
+                speedup_vs_lambda0=round(t0_cold / t_cold, 3), other_lengths=other)
+
+
 # ------------------------------------------------------------ cpu baseline ---
 def cpu_baseline(w, seconds):
     """The fp64 oracle's decode step on the host, repeated for about `seconds`."""
@@ -332,6 +395,8 @@ def main():
         sys.exit(1)
     bsa.lib()
     flush = torch.empty(512 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    flush.zero_()
+    flush.add_(1)          # one elementwise pass of known size (reads and writes 2 GiB): HBM counter calibration
     result = {}
     secondary = {}
     reps = max(20, args.steps // 4)
@@ -340,6 +405,10 @@ def main():
         log(f"decode: {1000 * d['ms_per_step']:.2f} us/step; attention {d['t_att']:.2f} us warm, "
             f"{d['t_att_cold']:.2f} us cold")
         result["decode"] = d
+    if args.only in ("all", "tdecode"):
+        secondary["threshold_decode_64k"] = bench_threshold_decode(
+            torch, bsa, synth, reps, flush, result["decode"]["workload"] if "decode" in result else None)
+        log(f"tdecode: {secondary['threshold_decode_64k']}")
     if args.only in ("all", "dlm"):
         secondary["dlm_denoise_32k"] = bench_dlm(torch, bsa, synth, reps)
         log(f"dlm: {secondary['dlm_denoise_32k']}")

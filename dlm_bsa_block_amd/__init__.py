@@ -19,7 +19,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["bsa_build_block_summaries", "bsa_select_blocks", "bsa_active_rows", "bsa_sparse_attention_fwd",
-           "bsa_threshold_attention_fwd", "bsa_select_workspace_bytes", "bsa_attention_workspace_bytes",
+           "bsa_threshold_attention_fwd", "bsa_threshold_decode_fwd", "bsa_select_workspace_bytes",
+           "bsa_attention_workspace_bytes", "bsa_threshold_decode_workspace_bytes",
            "BsaError", "tensor_desc", "select_params", "attn_params", "lib"]
 
 _DT = {torch.bfloat16: BSA_BF16, torch.float32: BSA_F32}
@@ -174,4 +175,35 @@ def bsa_threshold_attention_fwd(q, k, v, lam: float, scale: float | None = None,
     check(lib().bsa_threshold_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(p),
                                             ctypes.byref(od), lse.data_ptr(), kept.data_ptr(), _ptr(km), _stream()),
           "bsa_threshold_attention_fwd")
+    return o, lse, kept, km
+
+
+# -------------------------------------------------------- threshold decode ---
+def bsa_threshold_decode_workspace_bytes(q: torch.Tensor, k: torch.Tensor, kv_split: int) -> int:
+    return int(lib().bsa_threshold_decode_workspace_bytes(ctypes.byref(tensor_desc(q)), ctypes.byref(tensor_desc(k)),
+                                                          kv_split))
+
+
+def bsa_threshold_decode_fwd(q, k, v, lam: float, scale: float | None = None, kv_split: int = 1024,
+                             want_keep_map=False, o=None, lse=None, kept=None, workspace=None):
+    """One query row per head over all keys.  Returns (o, lse [B,Hq,1], kept_tiles [B,Hq] int32,
+    keep_map [B,Hq,ceil(L/64)] uint8 or None)."""
+    B, Hq, Lq, D = q.shape
+    L = k.shape[2]
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if kept is None:
+        kept = torch.empty((B, Hq), dtype=torch.int32, device=q.device)
+    km = torch.zeros((B, Hq, -(-L // 64)), dtype=torch.uint8, device=q.device) if want_keep_map else None
+    need = bsa_threshold_decode_workspace_bytes(q, k, kv_split)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    check(lib().bsa_threshold_decode_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), sc, lam, kv_split,
+                                         ctypes.byref(od), lse.data_ptr(), kept.data_ptr(), _ptr(km),
+                                         workspace.data_ptr(), workspace.numel(), _stream()),
+          "bsa_threshold_decode_fwd")
     return o, lse, kept, km

@@ -53,6 +53,9 @@ _SIGS = {
                                            c_void_p, c_void_p, c_size_t, c_void_p]),
     "bsa_threshold_attention_fwd": (c_int32, [_T, _T, _T, POINTER(BsaThreshParams), _T, c_void_p, c_void_p,
                                               c_void_p, c_void_p]),
+    "bsa_threshold_decode_workspace_bytes": (c_size_t, [_T, _T, c_int32]),
+    "bsa_threshold_decode_fwd": (c_int32, [_T, _T, _T, c_float, c_float, c_int32, _T, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_size_t, c_void_p]),
     "bsa_status_string": (c_char_p, [c_int32]),
     "bsa_last_error": (c_char_p, []),
     "bsa_version": (c_int32, []),

@@ -258,4 +258,54 @@ bsa_status bsa_threshold_attention_fwd(const bsa_tensor* q, const bsa_tensor* k,
   return check_launch("threshold attention");
 }
 
+// ------------------------------------------------------ threshold decode ---
+static bsa_status validate_threshold_decode(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, float scale,
+                                            float lambda, int32_t kv_split) {
+  bsa_status st = check_tensor(q, "q", false);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(k, "k", false)) != BSA_OK) return st;
+  if ((st = check_tensor(v, "v", false)) != BSA_OK) return st;
+  if (!same_shape(k, v)) return fail(BSA_ERR_INVALID, "k and v differ in shape or dtype");
+  if (q->dtype != k->dtype || q->B != k->B || q->D != k->D || q->H % k->H)
+    return fail(BSA_ERR_INVALID, "q/k shapes are incompatible");
+  if (q->L != 1) return fail(BSA_ERR_INVALID, "threshold decode takes one query row (q.L = %d)", q->L);
+  if (q->dtype != BSA_BF16 || q->D != 128) return fail(BSA_ERR_UNSUPPORTED, "threshold decode needs bf16, D = 128");
+  const int64_t G = q->H / k->H;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(BSA_ERR_UNSUPPORTED, "group size %d (supported: 1, 2, 4, 8)", (int)G);
+  if (kv_split < 64 || kv_split > 2048 || kv_split % 64)
+    return fail(BSA_ERR_UNSUPPORTED, "kv_split %d (a multiple of 64 in [64, 2048])", kv_split);
+  if (v->stride_l * 2 * (int64_t)kv_split >= (int64_t)1 << 31)
+    return fail(BSA_ERR_UNSUPPORTED, "v row stride %lld too large for a slice of %d keys", (long long)v->stride_l, kv_split);
+  if (!(lambda >= 0.f && lambda <= 1.f)) return fail(BSA_ERR_INVALID, "lambda %g outside [0, 1]", lambda);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(BSA_ERR_INVALID, "scale must be finite and > 0");
+  return BSA_OK;
+}
+
+size_t bsa_threshold_decode_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, int32_t kv_split) {
+  if (!q || !k || q->H <= 0 || k->H <= 0 || k->L <= 0 || kv_split < 64 || kv_split % 64) return 0;
+  size_t bytes = 0;
+  plan_threshold_decode(*q, *k, kv_split, bytes);
+  return bytes;
+}
+
+bsa_status bsa_threshold_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, float scale,
+                                    float lambda, int32_t kv_split, const bsa_tensor* o, float* lse,
+                                    int32_t* kept_tiles, uint8_t* keep_map, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  bsa_status st = validate_threshold_decode(q, k, v, scale, lambda, kv_split);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(o, "o", false)) != BSA_OK) return st;
+  if (!same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
+    return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
+  if (!lse) return fail(BSA_ERR_INVALID, "lse is required");
+  size_t need = 0;
+  plan_threshold_decode(*q, *k, kv_split, need);
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  launch_threshold_decode(*q, *k, *v, scale, lambda, kv_split, *o, lse, kept_tiles, keep_map, workspace,
+                          static_cast<hipStream_t>(stream));
+  return check_launch("threshold decode");
+}
+
 }  // extern "C"

@@ -172,11 +172,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 // ascending slice order; write O (q's dtype) and the natural-log LSE.  One
 // thread per (query vector, dim): it loads the (m, l) of every slice and its
 // dim of every partial O together -- one round trip to memory, no exchange
-// between threads -- and merges them with a running maximum, 32 slices at a
-// time.
-template <int ODT>
+// between threads -- and merges them with a running maximum, BATCH slices at
+// a time (32, or 64 when there are more than 32).
+template <int ODT, int BATCH>
 __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
-  constexpr int BATCH = 32;
   const int QVC = a.qvc;
   const int nchunk = (a.QV + QVC - 1) / QVC;
   const int qb = blockIdx.x / nchunk, qv0 = (blockIdx.x % nchunk) * QVC;
@@ -195,17 +194,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
   // Slots are clamped to the workspace, not to the valid count, so the first
   // batch loads together with the count; slots past the count may hold stale
   // values and are excluded by selects (never multiplied by a zero weight).
+  // uniform slice bases, 32-bit lane offsets (one VGPR per load, not an address pair)
+  const uint32_t lo_ml = (uint32_t)qv * 2u, lo_o = (uint32_t)(qv * D + d);
   auto load_batch = [&](int it0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const int it = min(it0 + u, a.items - 1);
-      const int64_t pi = (p0 + it) * QV + qv;
-      mv[u] = a.part_ml[pi * 2];
-      lv[u] = a.part_ml[pi * 2 + 1];
-      ov[u] = a.part_o[pi * D + d];
+      const int64_t it = min(it0 + u, a.items - 1);
+      const float* bml = a.part_ml + (p0 + it) * QV * 2;
+      const float* bo = a.part_o + (p0 + it) * QV * D;
+      mv[u] = bml[lo_ml];
+      lv[u] = bml[lo_ml + 1u];
+      ov[u] = bo[lo_o];
     }
   };
-  const int64_t nunits = (int64_t)a.cnt[li] * a.unit_num;
+  const int64_t nunits = a.cnt ? (int64_t)a.cnt[li] * a.unit_num : (int64_t)a.items * a.unit_den;
   load_batch(0);
   const int nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
   float M = -INFINITY, L = 0.f, acc = 0.f;
@@ -239,8 +241,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
 
 void launch_combine(const CombArgs& a, int odt, int B, hipStream_t s) {
   dim3 grid(a.NQB * ((a.QV + a.qvc - 1) / a.qvc), a.Hkv, B);
-  if (odt == BSA_BF16) hipLaunchKernelGGL(combine_kernel<BSA_BF16>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(combine_kernel<BSA_F32>, grid, dim3(256), 0, s, a);
+  const bool wide = a.items > 32;
+  if (odt == BSA_BF16) {
+    if (wide) hipLaunchKernelGGL((combine_kernel<BSA_BF16, 64>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<BSA_BF16, 32>), grid, dim3(256), 0, s, a);
+  } else {
+    if (wide) hipLaunchKernelGGL((combine_kernel<BSA_F32, 64>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<BSA_F32, 32>), grid, dim3(256), 0, s, a);
+  }
 }
 
 void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s) {

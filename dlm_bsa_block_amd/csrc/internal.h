@@ -51,6 +51,11 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
                       const int32_t* cnt, const bsa_attn_params& p, const AttnPlan& pl, const uint8_t* row_mask,
                       const bsa_tensor& o, float* lse, void* ws, hipStream_t s);
 
+bool plan_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, int kv_split, size_t& bytes);
+void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, float scale,
+                             float lambda, int kv_split, const bsa_tensor& o, float* lse, int32_t* kept,
+                             uint8_t* keep_map, void* ws, hipStream_t s);
+
 void launch_threshold(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, const bsa_thresh_params& p,
                       const bsa_tensor& o, float* lse, int32_t* kept, uint8_t* keep_map, hipStream_t s);
 

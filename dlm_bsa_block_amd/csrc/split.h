@@ -33,7 +33,7 @@ struct DecArgs {
 struct CombArgs {
   const float* part_o;
   const float* part_ml;
-  const int32_t* cnt;
+  const int32_t* cnt;             // null: every one of the items slices is valid
   int items, unit_num, unit_den;  // valid slices = ceil(cnt * unit_num / unit_den)
   int Hkv, G, NQB, q_block, Lq, D, QV;
   int qvc;                        // query vectors per combine workgroup (256 / D)

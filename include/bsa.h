@@ -230,6 +230,39 @@ bsa_status bsa_threshold_attention_fwd(const bsa_tensor* q, const bsa_tensor* k,
                                        const bsa_thresh_params* p, const bsa_tensor* o, float* lse,
                                        int32_t* kept_tiles, uint8_t* keep_map, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * Softmax-threshold decode (BLASST sec. 2, decode kernel: the same skip rule,
+ * where the saving is the V load of a skipped block).  One query row per
+ * head, q [B, Hq, 1, D], attending to all L keys of k, v [B, Hkv, L, D].  The
+ * keys are cut into tiles of 64; per head, the tiles are visited from the
+ * newest down with a running max m (log of the largest logit kept so far):
+ * with tm the tile's largest logit scale * q . k, the newest tile is kept,
+ * and an older one when tm - m >= ln(lambda); a kept tile raises m.  A
+ * skipped tile never exceeds m, so m before a tile is the max over all newer
+ * tiles, and the decisions do not depend on kv_split.  O (bf16 or f32, q's
+ * shape) and lse [B, Hq, 1] (natural log) are the exact softmax over every
+ * head's kept tiles.  kv_split (keys per slice) sets how the work is cut:
+ * each slice's kept keys are summed by one workgroup and the slices are
+ * merged in order.  V of a tile is loaded only when some head of its KV
+ * group keeps it.  lambda in [0, 1] (0 keeps all).
+ * Optional: kept_tiles [B, Hq] int32 (tiles kept per head) and keep_map
+ * [B, Hq, ceil(L / 64)] uint8 (1 = kept).  Supported: bf16, D = 128, group
+ * size 1, 2, 4 or 8, kv_split a multiple of 64 in [64, 2048], v row stride
+ * times 2 * kv_split below 2^31 bytes.  workspace:
+ * bsa_threshold_decode_workspace_bytes() bytes (scores, tile maxima and
+ * per-slice partial results; no initial contents needed; calls that overlap
+ * on one workspace, or on one kept_tiles array, race).  Errors:
+ * BSA_ERR_INVALID for bad shapes, strides, lambda or scale, a missing lse
+ * or a misaligned workspace; BSA_ERR_UNSUPPORTED outside the supported set;
+ * BSA_ERR_WORKSPACE when the workspace is smaller than required.
+ * ------------------------------------------------------------------------ */
+size_t bsa_threshold_decode_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, int32_t kv_split);
+
+bsa_status bsa_threshold_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, float scale,
+                                    float lambda, int32_t kv_split, const bsa_tensor* o, float* lse,
+                                    int32_t* kept_tiles, uint8_t* keep_map, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Status text and the calling thread's last error detail. */
 const char* bsa_status_string(int32_t status);
 const char* bsa_last_error(void);

@@ -422,19 +422,19 @@ def threshold_attention(p: dict, q: np.ndarray, k: np.ndarray, v: np.ndarray, pa
 
 
 def threshold_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float, scale: float, tile: int,
-                     kv_split: int):
+                     decisions: np.ndarray | None = None):
     """Softmax-threshold decode ([BLASST] sec. 2, decode kernel: the same skip
     rule, where the saving is the V load of a skipped block).
 
-    q [B, Hq, 1, D]; k, v [B, Hkv, L, D]; the query sees every key.
-    READING (the pages state the rule for decode, not its walk): the KV
-    sequence is cut into slices of kv_split keys, the split-KV decomposition a
-    decode kernel runs in parallel; each query head walks each slice with
-    ``threshold_walk`` on its single row (tiles newest first, own running max,
-    so a slice's first visited tile is always kept); the slices' outputs are
-    merged exactly through their LSE.  A tile's V is needed when any head of
-    its KV group keeps it.
-    Returns O [B, Hq, 1, D], LSE [B, Hq, 1], keep [B, Hq, ntiles] bool.
+    q [B, Hq, 1, D]; k, v [B, Hkv, L, D]; the query sees every key.  Each query
+    head walks the whole sequence with ``threshold_walk`` on its single row:
+    tiles of ``tile`` keys from the newest down (READING, as for prefill), its
+    own running max, the rule of the pages.  A tile's V is needed when any head
+    of its KV group keeps it.
+    ``decisions`` (optional, [B, Hq, ntiles] bool) replays another
+    implementation's choices, as in ``threshold_walk``.
+    Returns O [B, Hq, 1, D], LSE [B, Hq, 1], keep [B, Hq, ntiles] bool and
+    margin [B, Hq, ntiles] (this walk's tm - m - ln(lambda) per tile).
     """
     B, Hq, _, D = q.shape
     Hkv, L = k.shape[1], k.shape[2]
@@ -443,23 +443,18 @@ def threshold_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float, sc
     O = np.zeros((B, Hq, 1, v.shape[3]))
     LSE = np.zeros((B, Hq, 1))
     keep = np.zeros((B, Hq, nt), dtype=bool)
+    margin = np.zeros((B, Hq, nt))
     for b in range(B):
         for h in range(Hq):
-            g = h // G
-            parts = []
-            for s0 in range(0, L, kv_split):
-                s1 = min(L, s0 + kv_split)
-                r = threshold_walk(q[b, h], k[b, g, s0:s1], v[b, g, s0:s1], np.array([L - 1]), tile, lam, scale,
-                                   causal=False)
-                for j in r["kept"]:
-                    keep[b, h, s0 // tile + j] = True
-                parts.append((r["O"][0], float(r["lse"][0])))
-            lses = np.array([l for _, l in parts])
-            top = lses.max()
-            w = np.exp(lses - top)
-            O[b, h, 0] = sum(wi * o for wi, (o, _) in zip(w, parts)) / w.sum()
-            LSE[b, h, 0] = top + math.log(w.sum())
-    return O, LSE, keep
+            dec = None if decisions is None else {j: bool(decisions[b, h, j]) for j in range(nt)}
+            r = threshold_walk(q[b, h], k[b, h // G], v[b, h // G], np.array([L - 1]), tile, lam, scale,
+                               causal=False, decisions=dec)
+            keep[b, h, r["kept"]] = True
+            for j, mg in r["margin"].items():
+                margin[b, h, j] = mg
+            O[b, h, 0] = r["O"][0]
+            LSE[b, h, 0] = r["lse"][0]
+    return O, LSE, keep, margin
 
 
 # ------------------------------------------------------------ decode step ---

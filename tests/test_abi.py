@@ -154,6 +154,22 @@ def test_threshold_rejects_bad_arguments(lib):
     assert st == L.BSA_ERR_UNSUPPORTED        # causal needs Lq == L
 
 
+def test_threshold_decode_rejects_bad_arguments(lib):
+    q, k = _t(H=32, Lq=1), _t(H=8, Lq=4096)
+    need = lib.bsa_threshold_decode_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 1024)
+    assert need > 0
+
+    def call(qq, split, lam, ws=need):
+        return lib.bsa_threshold_decode_fwd(ctypes.byref(qq), ctypes.byref(k), ctypes.byref(k), 0.088, lam, split,
+                                            ctypes.byref(qq), FAKE, None, None, FAKE, ws, None)
+    assert call(q, 1024, 0.3, need - 1) == L.BSA_ERR_WORKSPACE
+    assert call(q, 1000, 0.3) == L.BSA_ERR_UNSUPPORTED and "kv_split" in _err(lib)
+    assert call(q, 4096, 0.3) == L.BSA_ERR_UNSUPPORTED
+    assert call(q, 1024, 1.5) == L.BSA_ERR_INVALID and "lambda" in _err(lib)
+    assert call(_t(H=32, Lq=2), 1024, 0.3) == L.BSA_ERR_INVALID and "one query row" in _err(lib)
+    assert call(_t(H=24, Lq=1), 1024, 0.3) == L.BSA_ERR_UNSUPPORTED      # group size 3
+
+
 def test_active_rows_rejects_mismatch(lib):
     a, b = _t(H=32, Lq=32), _t(H=32, Lq=31)
     st = lib.bsa_active_rows(ctypes.byref(a), ctypes.byref(b), 0.1, FAKE, None, None)

@@ -368,6 +368,58 @@ def test_prefill_handmade_lists(bsa, B, Hkv, G):
     check_outputs(from_dev(o), O_ref, lse.cpu().numpy(), L_ref, f"handmade B={B} Hkv={Hkv} G={G}")
 
 
+# --------------------------------------------------------- threshold decode ---
+def _threshold_decode_case(bsa, w, lam, kv_split, where):
+    """GPU keep map replayed in the fp64 walk: each choice must agree with the
+    fp64 margin outside THRESH_EPS; outputs are then compared with the replay."""
+    qd, kd, vd = _dev_workload(w)
+    scale = w.params["scale"]
+    o, lse, kept, km = bsa.bsa_threshold_decode_fwd(qd, kd, vd, lam, scale=scale, kv_split=kv_split,
+                                                    want_keep_map=True)
+    o32, lse32, kept32, _ = bsa.bsa_threshold_decode_fwd(qd, kd, vd, lam, scale=scale, kv_split=kv_split,
+                                                         o=_f32_out(qd))
+    _sync()
+    _check_rounding(o, o32)
+    assert torch.equal(lse, lse32) and torch.equal(kept, kept32)
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    gkeep = km.cpu().numpy().astype(bool)
+    assert np.array_equal(gkeep.sum(axis=2), kept.cpu().numpy()), f"{where}: kept counts disagree with the map"
+    O_ref, L_ref, _, margin = orc.threshold_decode(q, k, v, lam, scale, 64, decisions=gkeep)
+    bad = (gkeep != (margin >= 0)) & (np.abs(margin) > THRESH_EPS)
+    assert not bad.any(), f"{where}: {int(bad.sum())} keep/skip choices disagree with the fp64 walk"
+    check_outputs(from_dev(o32), O_ref, lse.cpu().numpy(), L_ref, where)
+    return float(1.0 - gkeep.mean())
+
+
+@pytest.mark.parametrize("L,lam,kv_split", [(4096, 0.0, 1024), (4096, 0.3, 1024), (4096, 0.6, 256),
+                                            (3000, 0.3, 512), (3000, 1.0, 2048), (3001, 0.3, 64)])
+def test_threshold_decode_small(bsa, L, lam, kv_split):
+    """Ragged slices and tiles (3000 = 46 tiles of 64 + 56; 3001), lambda from 0 (keep
+    all) to 1 (keep only tiles that raise the running max); the decisions do
+    not depend on the slicing, which only spreads the work."""
+    w = synth.gqa_decode(L=L, n_needles=2)
+    skipped = _threshold_decode_case(bsa, w, lam, kv_split, f"threshold decode L={L} lam={lam}")
+    if lam == 0.0:
+        assert skipped == 0.0
+    else:
+        assert skipped > 0.0
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (2, 2)])
+def test_threshold_decode_group_sizes(bsa, Hq, Hkv):
+    w = synth.gqa_decode(L=2048, Hq=Hq, Hkv=Hkv, n_needles=2)
+    _threshold_decode_case(bsa, w, 0.4, 512, f"threshold decode G={Hq // Hkv}")
+
+
+def test_threshold_decode_full_size(bsa):
+    """64K GQA decode, every head, at the benchmark's lambda = a / L and slices."""
+    import bench
+    w = synth.gqa_decode()
+    lam = bench.THRESH_DECODE_A / w.k.shape[2]
+    skipped = _threshold_decode_case(bsa, w, lam, bench.THRESH_DECODE_SPLIT, "threshold decode 64K")
+    assert skipped > 0.3
+
+
 # --------------------------------------------------------------- threshold ---
 def _threshold_case(bsa, w, lam, pairs):
     """The oracle walks each sampled (head, query tile) with its own decisions.  If

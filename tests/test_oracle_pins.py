@@ -381,51 +381,52 @@ def test_threshold_skipped_mass_bound():
     assert n_skipped > 0 and worst > 0
 
 
-@pytest.mark.parametrize("lam,kept", [
-    # slice {t2, t3}: t3 (max 5) first and kept; t2 (-8 - 5 = -13)
-    # slice {t0, t1}: t1 (max 2) first and kept; t0 (0 - 2 = -2)
-    (0.1, [0, 1, 3]),     # ln = -2.30: keep t0, skip t2
-    (0.2, [1, 3]),        # ln = -1.61: skip t0 and t2
-    (1e-6, [0, 1, 2, 3]), # ln = -13.8: keep everything
-])
-def test_threshold_decode_hand_example(lam, kept):
-    """Two slices of two tiles each: every slice starts its own walk, so t1 is
-    kept although it trails the global max by 3 (one walk at lambda = 0.1
-    keeps only t3)."""
+def test_threshold_decode_is_the_walk_per_head():
+    """Decode runs the prefill walk on each head's single row; the hand example
+    gives the same kept tiles through either entry."""
     q, k, v, a = _hand_example()
-    O, lse, keep = orc.threshold_decode(q[None, :, None, :][:, 0:1], k[None, None], v[None, None], lam, 1.0, 2, 4)
-    assert np.flatnonzero(keep[0, 0]).tolist() == kept
-    toks = np.concatenate([[2 * j, 2 * j + 1] for j in kept])
-    w = softmax(a[toks])
-    assert np.allclose(O[0, 0, 0], w @ v[toks])
-    assert lse[0, 0, 0] == pytest.approx(logsumexp(a[toks]))
+    for lam, kept in ((1e-3, [0, 1, 3]), (0.1, [3]), (0.04, [1, 3])):
+        O, lse, keep, _ = orc.threshold_decode(q[None, :, None, :][:, 0:1], k[None, None], v[None, None], lam,
+                                               1.0, 2)
+        assert np.flatnonzero(keep[0, 0]).tolist() == kept
+        toks = np.concatenate([[2 * j, 2 * j + 1] for j in kept])
+        assert np.allclose(O[0, 0, 0], softmax(a[toks]) @ v[toks])
+        assert lse[0, 0, 0] == pytest.approx(logsumexp(a[toks]))
 
 
-def test_threshold_decode_lambda_zero_is_dense_for_any_slicing():
+def test_threshold_decisions_follow_the_prefix_max():
+    """A skipped tile never raises the running max (it trails it by at least
+    ln(1/lambda) >= 0), so the walk's max before tile j is the max over all
+    newer tiles, kept or not: tile j is kept iff tm_j - max(tm_i, i > j) >=
+    ln(lambda).  Checked by brute force against the sequential walk."""
+    rng = np.random.default_rng(23)
+    L, D, T = 64 * 40, 16, 64
+    for trial in range(6):
+        q = rng.standard_normal((1, 3, 1, D)) * (1 + trial)
+        k = rng.standard_normal((1, 1, L, D))
+        v = rng.standard_normal((1, 1, L, D))
+        lam = (0.02, 0.2, 0.5, 0.8, 1.0, 1e-4)[trial]
+        _, _, keep, _ = orc.threshold_decode(q, k, v, lam, 0.4, T)
+        for h in range(3):
+            s = 0.4 * (k[0, 0] @ q[0, h, 0])
+            tm = s.reshape(-1, T).max(axis=1)
+            newer = np.array([tm[j + 1:].max() if j + 1 < len(tm) else -np.inf for j in range(len(tm))])
+            want = (newer == -np.inf) | (tm - newer >= math.log(lam))
+            assert np.array_equal(keep[0, h], want), (trial, h)
+
+
+def test_threshold_decode_lambda_zero_is_dense():
     rng = np.random.default_rng(21)
     L, D = 300, 16
     q = rng.standard_normal((2, 4, 1, D))
     k = rng.standard_normal((2, 2, L, D))
     v = rng.standard_normal((2, 2, L, D))
-    for split in (64, 128, 300):
-        O, lse, keep = orc.threshold_decode(q, k, v, 0.0, 0.3, 32, split)
-        assert keep.all()
-        for b in range(2):
-            for h in range(4):
-                o2, l2 = _dense(q[b, h], k[b, h // 2], v[b, h // 2], 0.3)
-                assert np.allclose(O[b, h], o2, atol=1e-12) and np.allclose(lse[b, h], l2)
-
-
-def test_threshold_decode_one_slice_is_one_walk():
-    rng = np.random.default_rng(22)
-    L, D = 256, 8
-    q = rng.standard_normal((1, 1, 1, D)) * 3
-    k = rng.standard_normal((1, 1, L, D)) * 3
-    v = rng.standard_normal((1, 1, L, D))
-    O, lse, keep = orc.threshold_decode(q, k, v, 0.05, 0.5, 16, L)
-    r = orc.threshold_walk(q[0, 0], k[0, 0], v[0, 0], np.array([L - 1]), 16, 0.05, 0.5, causal=False)
-    assert np.flatnonzero(keep[0, 0]).tolist() == r["kept"] and 0 < len(r["kept"]) < 16
-    assert np.allclose(O[0, 0], r["O"]) and np.allclose(lse[0, 0], r["lse"])
+    O, lse, keep, _ = orc.threshold_decode(q, k, v, 0.0, 0.3, 32)
+    assert keep.all()
+    for b in range(2):
+        for h in range(4):
+            o2, l2 = _dense(q[b, h], k[b, h // 2], v[b, h // 2], 0.3)
+            assert np.allclose(O[b, h], o2, atol=1e-12) and np.allclose(lse[b, h], l2)
 
 
 def test_threshold_workload_skip_fraction_on_sample():
