@@ -299,7 +299,8 @@ bsa_status bsa_threshold_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, co
     return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
   if (!lse) return fail(BSA_ERR_INVALID, "lse is required");
   size_t need = 0;
-  plan_threshold_decode(*q, *k, kv_split, need);
+  if (!plan_threshold_decode(*q, *k, kv_split, need))
+    return fail(BSA_ERR_UNSUPPORTED, "L = %lld: more than 4096 decision chunks per head", (long long)k->L);
   if (!workspace || workspace_bytes < need)
     return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");

@@ -8,16 +8,18 @@
 // m: the running max before tile j is the max of all newer tiles' maxima,
 // kept or not.  The sequential walk therefore splits into independent work:
 //   1. scores_kernel: one workgroup per (slice of kv_split keys, KV group);
-//      K of the slice streams through (eight 16-key passes of loads in flight
-//      per thread), q.k for the G heads of the group (log2 units) and each
-//      tile's max go to the workspace;
-//   2. pv_kernel: same grid; the max over all newer slices' tiles seeds the
-//      walk of the slice's own tiles, which decides every (head, tile); V is
+//      K of the slice streams through the matrix cores, and q.k for the G
+//      heads of the group (log2 units), each tile's max and the slice's max
+//      go to the workspace;
+//   2. pv_kernel: one workgroup per (chunk of up to 4 tiles, KV group); the
+//      max over all newer tiles decides every (head, tile) of the chunk; V is
 //      loaded only for tiles some head keeps (the G heads share each load,
-//      NSA implementation-challenges section), and each head accumulates
-//      2^(s - m_s) v over its kept tiles, m_s being its largest kept tile max
-//      in the slice;
-//   3. the combine kernel merges the slices' (m, l, o) in order.
+//      NSA implementation-challenges section), and each head sums
+//      2^(s - m_c) v over its kept keys, m_c being its largest kept tile max
+//      in the chunk.  The walk keeps most tiles near the newest end, so small
+//      chunks spread that work over many compute units;
+//   3. combine_kernel: per head, the chunks' maxima in one round trip, then
+//      the partial sums of the chunks that kept anything, merged in order.
 #include "common.cuh"
 #include "internal.h"
 #include "split.h"
@@ -26,24 +28,28 @@ namespace bsa {
 
 constexpr int kTDecTile = 64;           // keys per tile
 constexpr int kTDecMaxSplit = 2048;     // keys per slice, at most
-constexpr int kTDecPass = 16;           // keys per workgroup pass (4 waves x 4 keys)
-constexpr int kTDecBatch = 8;           // passes whose loads are in flight together
+constexpr int kTDecChunkTiles = 4;     // tiles per decision / P V chunk, at most
+constexpr int kTDecMaxChunks = 4096;    // chunks per head the combine takes
 
 struct TDecArgs {
   const uint8_t* q;
   const uint8_t* k;
   const uint8_t* v;
   int64_t qsb, qsh, ksb, ksh, ksl, vsb, vsh, vsl;
-  int Hkv, L, Lpad, split, nsplit, ntiles;
+  int Hkv, G, L, Lpad, split, nsplit, ntiles, ctiles, nchunk;   // ctiles: tiles per chunk
   float c2;                             // scale * log2(e)
   float ln_lam2;                        // ln(lambda) * log2(e); -inf for lambda = 0
   float* scores;                        // [B][Hkv][G][Lpad], log2 units; Lpad = L rounded up to 4
   float* tmax;                          // [B][Hkv][G][ntiles]
   float* smax;                          // [B][Hkv][G][nsplit] max over a slice's tiles
-  float* part_o;                        // [B][Hkv][nsplit][G][D]
-  float* part_ml;                       // [B][Hkv][nsplit][G][2]
+  float* part_o;                        // [B][Hkv][nchunk][G][D] (written only where the chunk kept a tile)
+  float* part_ml;                       // [B][Hkv][nchunk][G][2] (m: largest kept tile max or -inf; l)
+  int32_t* part_cnt;                    // [B][Hkv][nchunk][G] kept tiles
   int32_t* kept;                        // [B][Hq] kept tiles per head, or null
   uint8_t* keep_map;                    // [B][Hq][ntiles] or null
+  void* o;                              // [B][Hq][1][D], bf16 or f32
+  int64_t osb, osh;
+  float* lse;                           // [B][Hq][1]
 };
 
 // Scores of one slice: q.k (log2 units) for the G heads of the group, and the
@@ -152,51 +158,50 @@ __global__ __launch_bounds__(512) void tdec_scores_kernel(TDecArgs a) {
     float mx = -INFINITY;
     for (int t = 0; t < nt; ++t) mx = fmaxf(mx, tmx[tid][t]);
     a.smax[(hb + tid) * a.nsplit + split] = mx;
-    if (split == 0 && a.kept) a.kept[hb + tid] = 0;   // the decision kernel adds every slice's count
   }
 }
 
-// Decisions, V and P V of one slice, eight waves.  Round trip one brings the
-// slice's scores (into LDS, key-major), its tile maxima and the maxima of all
-// newer slices; every wave then takes the decisions of all (head, tile) pairs
-// itself -- tile j of head h is kept iff its max tm passes the test against
-// the max of every newer tile -- and issues its V loads at once.  The waves
-// split the head dims (16 each, 4 lanes x 4 dims per key row, 16 keys per
-// pass), so every wave walks all kept tiles of the slice (the G heads share
-// each V load) and the work stays even however few tiles are kept.  While the
-// loads are in flight the workgroup turns the kept scores into
-// p = 2^(s - m_s) in place (m_s: the head's largest kept tile max in the
-// slice; 0 for a tile or key the head does not keep).
+// Decisions, V and P V of one chunk (up to 4 tiles), four waves.  Round trip
+// one brings the chunk's scores (into LDS, key-major), the maxima of its
+// slice's tiles from the chunk on, and the maxima of all newer slices; the
+// decisions follow -- tile j of head h is kept iff its max tm passes the test
+// against the max of every newer tile -- and then the V loads of all kept
+// tiles at once.  The waves split the head dims (32 each: 8 lanes x 4 dims
+// per key row, 8 keys per pass), so each wave walks every kept tile.  While
+// the loads are in flight the workgroup turns the kept scores into
+// p = 2^(s - m_c) in place (0 for a tile or key the head does not keep).
 template <int G>
-__global__ __launch_bounds__(512, G == 8 ? 2 : 4) void tdec_pv_kernel(TDecArgs a) {
-  constexpr int D = 128, T = kTDecTile, NW = 8, NT = 512;
-  constexpr int MAXT = kTDecMaxSplit / T;           // 32 tiles per slice at most
+__global__ __launch_bounds__(256) void tdec_pv_kernel(TDecArgs a) {
+  constexpr int D = 128, T = kTDecTile, NW = 4, NT = 256;
+  constexpr int MAXT = kTDecMaxSplit / T;           // tiles per slice, at most 32
+  constexpr int MAXC = kTDecChunkTiles;
   constexpr int NPAIR = (2 * G + 3) / 4;            // ballots of (head, tile) pairs: 2 heads x 32 tiles each
   constexpr int DW = D / NW, LPK = DW / 4;          // dims per wave, lanes per key row
   constexpr int KPP = 64 / LPK, PPT = T / KPP;      // keys per pass, passes per tile
-  constexpr int CH = 8;                             // kept tiles whose loads are in flight together
-  constexpr int TPI = NT / (T * G);                 // tiles per step of the p pass
-  static_assert(TPI >= 1, "one tile of (key, head) pairs per step at most");
-  __shared__ __align__(16) float sc[kTDecMaxSplit * G];   // [key][head]: scores, then p
+  __shared__ __align__(16) float sc[MAXC * T * G];  // [key][head]: scores, then p
   __shared__ float tmx[G][MAXT];
   __shared__ float newer_sh[G];
 
-  const int split = a.nsplit - 1 - (int)blockIdx.x;         // newest slices (most kept tiles) first
+  const int chunk = a.nchunk - 1 - (int)blockIdx.x;         // newest chunks (most kept tiles) first
   const int bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int s0 = split * a.split;
-  const int n = min(a.split, a.L - s0);
+  const int t0 = chunk * a.ctiles;                          // first tile of the chunk
+  const int s0 = t0 * T;
+  const int n = min(a.ctiles * T, a.L - s0);                // keys of the chunk
   const int nt = (n + T - 1) / T;
+  const int sp = s0 / a.split;                              // the slice holding the chunk
+  const int ntail = min((sp + 1) * (a.split / T), a.ntiles) - t0;   // tiles from t0 to the slice's end
   const int nq = (n + 3) / 4;                               // 16-byte score chunks per head row
   const int64_t hb = ((int64_t)b * a.Hkv + g) * G;
 
   // ---- round trip 1
   {
-    f32x4 sv[G];
+    constexpr int NR = (MAXC * T / 4 * G + NT - 1) / NT;
+    f32x4 sv[NR];
 #pragma unroll
-    for (int r = 0; r < G; ++r) {
+    for (int r = 0; r < NR; ++r) {
       const int i = min(tid + NT * r, G * nq - 1);
       const int h = i / nq, c = i - h * nq;
       sv[r] = *reinterpret_cast<const f32x4*>(a.scores + (hb + h) * a.Lpad + s0 + 4 * c);
@@ -204,17 +209,17 @@ __global__ __launch_bounds__(512, G == 8 ? 2 : 4) void tdec_pv_kernel(TDecArgs a
     float tv = -INFINITY;
     if (tid < G * MAXT) {
       const int h = tid / MAXT, j = tid - h * MAXT;
-      if (j < nt) tv = a.tmax[(hb + h) * a.ntiles + s0 / T + j];
+      if (j < ntail) tv = a.tmax[(hb + h) * a.ntiles + t0 + j];
     }
     float nv[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       nv[h] = -INFINITY;
       if (w == NW - 1)
-        for (int sp = split + 1 + lane; sp < a.nsplit; sp += 64) nv[h] = fmaxf(nv[h], a.smax[(hb + h) * a.nsplit + sp]);
+        for (int q = sp + 1 + lane; q < a.nsplit; q += 64) nv[h] = fmaxf(nv[h], a.smax[(hb + h) * a.nsplit + q]);
     }
 #pragma unroll
-    for (int r = 0; r < G; ++r) {
+    for (int r = 0; r < NR; ++r) {
       const int i = tid + NT * r;
       if (i < G * nq) {
         const int h = i / nq, c = i - h * nq;
@@ -233,23 +238,24 @@ __global__ __launch_bounds__(512, G == 8 ? 2 : 4) void tdec_pv_kernel(TDecArgs a
   }
   __syncthreads();
 
-  // ---- decisions: ballot r covers heads 2r (lanes 0-31) and 2r + 1 (lanes 32-63), lane % 32 = tile
+  // ---- decisions: ballot r covers heads 2r (lanes 0-31) and 2r + 1 (lanes 32-63), lane % 32 = tile - t0
   uint32_t kb[G];
   float mk[G];
   uint32_t any = 0u;
 #pragma unroll
   for (int r = 0; r < NPAIR; ++r) {
     const int h = 2 * r + lane / 32, j = lane % 32;
-    const bool valid = h < G && j < nt;
+    const bool valid = h < G && j < ntail;
     const float tm = valid ? tmx[h < G ? h : 0][j] : -INFINITY;
-    // max over tiles j' > j of the slice (shuffles stay inside each 32-lane half)
+    // max over the slice's tiles after j (shuffles stay inside each 32-lane half)
     float incl = tm;
 #pragma unroll
     for (int sft = 1; sft < 32; sft <<= 1) incl = fmaxf(incl, __shfl_down(incl, sft, 32));
     float excl = __shfl_down(incl, 1, 32);
     if (j == 31) excl = -INFINITY;
     const float M = fmaxf(valid ? newer_sh[h] : -INFINITY, excl);
-    const bool keep = valid && tm > -INFINITY && (M == -INFINITY || tm - M >= a.ln_lam2);
+    const bool mine = valid && j < nt;                      // a tile of this chunk
+    const bool keep = mine && tm > -INFINITY && (M == -INFINITY || tm - M >= a.ln_lam2);
     const uint64_t bal = __ballot(keep);
     float x = keep ? tm : -INFINITY;
 #pragma unroll
@@ -258,21 +264,15 @@ __global__ __launch_bounds__(512, G == 8 ? 2 : 4) void tdec_pv_kernel(TDecArgs a
     const float x1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 32));
     if (2 * r < G) { kb[2 * r] = (uint32_t)bal; mk[2 * r] = x0; any |= (uint32_t)bal; }
     if (2 * r + 1 < G) { kb[2 * r + 1] = (uint32_t)(bal >> 32); mk[2 * r + 1] = x1; any |= (uint32_t)(bal >> 32); }
-    if (w == 0 && valid && a.keep_map) a.keep_map[(hb + h) * a.ntiles + s0 / T + j] = keep ? 1 : 0;
+    if (w == 0 && mine && a.keep_map) a.keep_map[(hb + h) * a.ntiles + t0 + j] = keep ? 1 : 0;
   }
   float msub[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) msub[h] = mk[h] == -INFINITY ? 0.f : mk[h];
-  if (w == 0 && lane < G && a.kept) {
-    uint32_t c = 0u;
-#pragma unroll
-    for (int h = 0; h < G; ++h) if (lane == h) c = __popc(kb[h]);
-    atomicAdd(a.kept + hb + lane, (int)c);
-  }
 
-  // ---- V of the kept tiles (CH at a time), p in place, P V
+  // ---- V of the kept tiles, p in place, P V
   const int kw = lane / LPK, dl = w * DW + (lane % LPK) * 4;   // key row of the pass, first dim
-  // uniform base of the slice's V rows, 32-bit lane offsets (the host bounds kv_split rows of stride vsl)
+  // uniform base of the chunk's V rows, 32-bit lane offsets (the host bounds the row stride)
   const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + (int64_t)s0 * a.vsl) * 2;
   const uint32_t rowb = (uint32_t)a.vsl * 2u;
   float acc[G][4], lsum[G];
@@ -282,52 +282,41 @@ __global__ __launch_bounds__(512, G == 8 ? 2 : 4) void tdec_pv_kernel(TDecArgs a
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
   }
-  uint32_t todo = any;
-  bool pdone = false;
-  while (todo) {                                     // the same on every wave
-    int tl[CH];
+  if (any) {                                         // the same on every wave
+    u32x2 vv[MAXC][PPT];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      tl[c] = todo ? __builtin_ctz(todo) : -1;
-      todo &= todo - 1u;
-    }
-    u32x2 vv[CH][PPT];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (tl[c] < 0) continue;
+    for (int c = 0; c < MAXC; ++c) {
+      if (!((any >> c) & 1u)) continue;
 #pragma unroll
       for (int p = 0; p < PPT; ++p) {
-        const uint32_t kr = (uint32_t)min(tl[c] * T + KPP * p + kw, n - 1);
+        const uint32_t kr = (uint32_t)min(c * T + KPP * p + kw, n - 1);
         vv[c][p] = *reinterpret_cast<const u32x2*>(vb + (kr * rowb + (uint32_t)dl * 2u));
       }
     }
-    if (!pdone) {
-      // p for every (key, head) of every kept tile, keys past the slice included (p = 0)
-      const int ts = tid / (T * G), ke = tid % (T * G);
-      const int h = ke % G;
-      uint32_t kbh = 0u;
-      float ms = 0.f;
+    // p for every (key, head) of every kept tile, keys past the chunk included (p = 0)
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-        if (hh == h) { kbh = kb[hh]; ms = msub[hh]; }
-      for (int t0 = 0; t0 < nt; t0 += TPI) {
-        const int t = t0 + ts;
-        if (t < nt && ((any >> t) & 1u)) {
-          const int key = t * T + ke / G;
-          float* ps = &sc[key * G + h];
-          const bool use = ((kbh >> t) & 1u) && key < n;
-          *ps = use ? fast_exp2(*ps - ms) : 0.f;
-        }
+    for (int r = 0; r < MAXC * T * G / NT; ++r) {
+      const int e = tid + NT * r;
+      const int c = e / (T * G), ke = e - c * (T * G);
+      const int h = ke % G, key = c * T + ke / G;
+      if ((any >> c) & 1u) {
+        uint32_t kbh = 0u;
+        float ms = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+          if (hh == h) { kbh = kb[hh]; ms = msub[hh]; }
+        float* ps = &sc[key * G + h];
+        const bool use = ((kbh >> c) & 1u) && key < n;
+        *ps = use ? fast_exp2(*ps - ms) : 0.f;
       }
-      __syncthreads();
-      pdone = true;
     }
+    __syncthreads();
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (tl[c] < 0) continue;
+    for (int c = 0; c < MAXC; ++c) {
+      if (!((any >> c) & 1u)) continue;
 #pragma unroll
       for (int p = 0; p < PPT; ++p) {
-        const int key = tl[c] * T + KPP * p + kw;
+        const int key = c * T + KPP * p + kw;
         float pr[G];
         if constexpr (G >= 4) {
 #pragma unroll
@@ -352,15 +341,15 @@ __global__ __launch_bounds__(512, G == 8 ? 2 : 4) void tdec_pv_kernel(TDecArgs a
     }
   }
 
-  // ---- sums over the 16 key rows of the wave; each wave owns its dims
-  const int64_t pbase = (((int64_t)b * a.Hkv + g) * a.nsplit + split) * G;
+  // ---- sums over the 8 key rows of the wave; each wave owns its dims
+  const int64_t pbase = (((int64_t)b * a.Hkv + g) * a.nchunk + chunk) * G;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    if (mk[h] == -INFINITY) continue;                // uniform: the combine reads no o for this chunk
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float x = acc[h][e];
-      x += dpp_f32<0x124>(0.f, x);                  // row_ror:4
-      x += dpp_f32<0x128>(0.f, x);                  // row_ror:8
+      x += dpp_f32<0x128>(0.f, x);                  // row_ror:8: lanes i and i ^ 8
       acc[h][e] = groups_sum<16>(x);
     }
     if (lane < LPK)
@@ -373,27 +362,152 @@ __global__ __launch_bounds__(512, G == 8 ? 2 : 4) void tdec_pv_kernel(TDecArgs a
       if (lane == 0) {
         a.part_ml[(pbase + h) * 2] = mk[h];
         a.part_ml[(pbase + h) * 2 + 1] = l;
+        a.part_cnt[pbase + h] = __popc(kb[h]);
       }
     }
   }
 }
 
-static size_t tdec_sizes(const bsa_tensor& q, const bsa_tensor& k, int kv_split, size_t (&sz)[5]) {
+// Merge of one head's chunks in ascending order.  Round trip one brings every
+// chunk's (m, l) and kept count; the chunks that kept a tile are compacted
+// (ballots, one scan of the per-wave counts); round trip two brings their
+// partial O (four threads per dim share the list); the global max M is known
+// first, so every term is scaled once by 2^(m - M).
+template <int ODT>
+__global__ __launch_bounds__(512) void tdec_combine_kernel(TDecArgs a) {
+  constexpr int D = 128, NT = 512, NW = 8, MAXC = kTDecMaxChunks, NI = MAXC / NT;
+  constexpr int PARTS = NT / D, BJ = 32;             // threads per dim, chunks per batch per thread
+  __shared__ float ms[MAXC], ls[MAXC];
+  __shared__ int list[MAXC];
+  __shared__ int goff[MAXC / 64];
+  __shared__ float redm[NW];
+  __shared__ int redk[NW], nlist;
+  __shared__ float part_acc[PARTS - 1][D], part_l[PARTS - 1];
+
+  const int G = a.G, Hq = a.Hkv * G;
+  const int bh = blockIdx.x;
+  const int b = bh / Hq, h = bh - b * Hq, g = h / G, hl = h - g * G;
+  const int64_t base = ((int64_t)b * a.Hkv + g) * a.nchunk;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int nc = a.nchunk, ni = (nc + NT - 1) / NT;
+
+  // ---- round trip 1: (m, l) and counts of every chunk
+  f32x2 mlv[NI];
+  int cv[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i < ni) {
+      const int64_t pi = (base + min(tid + NT * i, nc - 1)) * G + hl;
+      mlv[i] = *reinterpret_cast<const f32x2*>(a.part_ml + pi * 2);
+      cv[i] = a.part_cnt[pi];
+    }
+  }
+  float mx = -INFINITY;
+  int kt = 0;
+  uint64_t bal[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    bal[i] = 0;
+    if (i < ni) {
+      const int c = tid + NT * i;
+      const bool valid = c < nc;
+      const float m = valid ? mlv[i][0] : -INFINITY;
+      if (valid) { ms[c] = m; ls[c] = mlv[i][1]; kt += cv[i]; }
+      mx = fmaxf(mx, m);
+      bal[i] = __ballot(m > -INFINITY);
+      if (lane == 0) goff[i * NW + w] = __popcll(bal[i]);      // chunks 64 (NW i + w) ...
+    }
+  }
+  mx = wave_max_dpp(mx);
+  const int ktw = (int)wave_sum_dpp((float)kt);              // counts stay far below 2^24
+  if (lane == 0) { redm[w] = mx; redk[w] = ktw; }
+  __syncthreads();
+  if (w == 0) {                                              // exclusive scan of the group counts
+    const int ng = ni * NW;
+    const uint32_t x = lane < ng ? (uint32_t)goff[lane] : 0u;
+    const uint32_t incl = wave_incl_scan_dpp(x);
+    if (lane < ng) goff[lane] = (int)(incl - x);
+    if (lane == 63) nlist = (int)incl;
+  }
+  float M = redm[0];
+  int ktot = redk[0];
+#pragma unroll
+  for (int ww = 1; ww < NW; ++ww) { M = fmaxf(M, redm[ww]); ktot += redk[ww]; }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i < ni && ((bal[i] >> lane) & 1ull)) {
+      const int below = __popcll(bal[i] & ((1ull << lane) - 1ull));
+      list[goff[i * NW + w] + below] = tid + NT * i;
+    }
+  }
+  __syncthreads();
+
+  // ---- round trip 2: partial O of the listed chunks
+  const int K = nlist;
+  const int d = tid % D, part = tid / D;
+  float acc = 0.f, lsum = 0.f;
+  for (int j0 = 0; j0 * PARTS < K; j0 += BJ) {
+    float ov[BJ];
+    int cl[BJ];
+#pragma unroll
+    for (int u = 0; u < BJ; ++u) {
+      const int e = min((j0 + u) * PARTS + part, K - 1);
+      cl[u] = list[e];
+      ov[u] = a.part_o[((base + cl[u]) * G + hl) * D + d];
+    }
+#pragma unroll
+    for (int u = 0; u < BJ; ++u) {
+      if ((j0 + u) * PARTS + part < K) {
+        const float wgt = fast_exp2(ms[cl[u]] - M);
+        acc = fmaf(ov[u], wgt, acc);
+        lsum = fmaf(ls[cl[u]], wgt, lsum);
+      }
+    }
+  }
+  if (part > 0) {
+    part_acc[part - 1][d] = acc;
+    if (d == 0) part_l[part - 1] = lsum;
+  }
+  __syncthreads();
+  if (part == 0) {
+#pragma unroll
+    for (int q = 0; q < PARTS - 1; ++q) { acc += part_acc[q][d]; lsum += part_l[q]; }
+    const float out = lsum > 0.f ? acc / lsum : 0.f;
+    const int64_t oi = (int64_t)b * a.osb + (int64_t)h * a.osh + d;
+    if (ODT == BSA_BF16) reinterpret_cast<uint16_t*>(a.o)[oi] = (uint16_t)f32_to_bf16(out);
+    else reinterpret_cast<float*>(a.o)[oi] = out;
+    if (d == 0) {
+      a.lse[(int64_t)b * Hq + h] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+      if (a.kept) a.kept[(int64_t)b * Hq + h] = ktot;
+    }
+  }
+}
+
+// tiles per decision chunk: 4 when a slice holds whole chunks of 4, else 2 or 1
+static int tdec_chunk_tiles(int kv_split) {
+  const int t = kv_split / kTDecTile;
+  return t % 4 == 0 ? 4 : (t % 2 == 0 ? 2 : 1);
+}
+
+static size_t tdec_sizes(const bsa_tensor& q, const bsa_tensor& k, int kv_split, size_t (&sz)[6]) {
   const int64_t nsplit = ceil_div(k.L, kv_split), ntiles = ceil_div(k.L, kTDecTile);
+  const int64_t nchunk = ceil_div(ntiles, tdec_chunk_tiles(kv_split));
   const size_t heads = (size_t)q.B * q.H;            // B * Hkv * G
-  const size_t n = heads * nsplit;
+  const size_t n = heads * nchunk;
   sz[0] = align256(heads * ((k.L + 3) & ~3LL) * 4);    // scores, rows padded to 16 bytes
   sz[1] = align256(heads * ntiles * 4);                // tile maxima
   sz[2] = align256(n * q.D * 4);                       // partial O
   sz[3] = align256(n * 2 * 4);                         // partial (m, l)
-  sz[4] = align256(n * 4);                             // slice maxima
-  return sz[0] + sz[1] + sz[2] + sz[3] + sz[4];
+  sz[4] = align256(n * 4);                             // kept tiles per chunk
+  sz[5] = align256(heads * nsplit * 4);                // slice maxima
+  return sz[0] + sz[1] + sz[2] + sz[3] + sz[4] + sz[5];
 }
 
 bool plan_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, int kv_split, size_t& bytes) {
-  size_t sz[5];
+  size_t sz[6];
   bytes = tdec_sizes(q, k, kv_split, sz);
-  return true;
+  return ceil_div(ceil_div(k.L, kTDecTile), tdec_chunk_tiles(kv_split)) <= kTDecMaxChunks;
 }
 
 void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, float scale,
@@ -407,25 +521,35 @@ void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa
   a.qsb = q.stride_b; a.qsh = q.stride_h;
   a.ksb = k.stride_b; a.ksh = k.stride_h; a.ksl = k.stride_l;
   a.vsb = v.stride_b; a.vsh = v.stride_h; a.vsl = v.stride_l;
-  a.Hkv = (int)k.H; a.L = (int)k.L; a.Lpad = (int)((k.L + 3) & ~3LL); a.split = kv_split;
+  a.Hkv = (int)k.H; a.G = G; a.L = (int)k.L; a.Lpad = (int)((k.L + 3) & ~3LL); a.split = kv_split;
   a.nsplit = (int)ceil_div(k.L, kv_split);
   a.ntiles = (int)ceil_div(k.L, kTDecTile);
+  a.ctiles = tdec_chunk_tiles(kv_split);
+  a.nchunk = (int)ceil_div(a.ntiles, a.ctiles);
   a.c2 = scale * kLog2e;
   a.ln_lam2 = lambda > 0.f ? logf(lambda) * kLog2e : -INFINITY;
-  size_t sz[5];
+  size_t sz[6];
   tdec_sizes(q, k, kv_split, sz);
   uint8_t* p = static_cast<uint8_t*>(ws);
   a.scores = reinterpret_cast<float*>(p);
-  a.tmax = reinterpret_cast<float*>(p + sz[0]);
-  a.part_o = reinterpret_cast<float*>(p + sz[0] + sz[1]);
-  a.part_ml = reinterpret_cast<float*>(p + sz[0] + sz[1] + sz[2]);
-  a.smax = reinterpret_cast<float*>(p + sz[0] + sz[1] + sz[2] + sz[3]);
+  p += sz[0];
+  a.tmax = reinterpret_cast<float*>(p);
+  p += sz[1];
+  a.part_o = reinterpret_cast<float*>(p);
+  p += sz[2];
+  a.part_ml = reinterpret_cast<float*>(p);
+  p += sz[3];
+  a.part_cnt = reinterpret_cast<int32_t*>(p);
+  p += sz[4];
+  a.smax = reinterpret_cast<float*>(p);
   a.kept = kept;
   a.keep_map = keep_map;
-  dim3 grid(a.nsplit, q.B * k.H);
+  a.o = o.data; a.osb = o.stride_b; a.osh = o.stride_h;
+  a.lse = lse;
+  const dim3 gs(a.nsplit, q.B * k.H), gp(a.nchunk, q.B * k.H);
 #define BSA_TDEC(GG)                                                                  \
-  hipLaunchKernelGGL(tdec_scores_kernel<GG>, grid, dim3(512), 0, s, a);               \
-  hipLaunchKernelGGL(tdec_pv_kernel<GG>, grid, dim3(512), 0, s, a)
+  hipLaunchKernelGGL(tdec_scores_kernel<GG>, gs, dim3(512), 0, s, a);                 \
+  hipLaunchKernelGGL(tdec_pv_kernel<GG>, gp, dim3(256), 0, s, a)
   switch (G) {
     case 1: BSA_TDEC(1); break;
     case 2: BSA_TDEC(2); break;
@@ -433,13 +557,8 @@ void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa
     default: BSA_TDEC(8); break;
   }
 #undef BSA_TDEC
-  CombArgs c;
-  c.part_o = a.part_o; c.part_ml = a.part_ml; c.cnt = nullptr; c.items = a.nsplit;
-  c.unit_num = 1; c.unit_den = 1;
-  c.qvc = 256 / (int)q.D;
-  c.Hkv = (int)k.H; c.G = G; c.NQB = 1; c.q_block = 1; c.Lq = 1; c.D = (int)q.D; c.QV = G;
-  c.row_mask = nullptr; c.o = o.data; c.osb = o.stride_b; c.osh = o.stride_h; c.osl = o.stride_l; c.lse = lse;
-  launch_combine(c, o.dtype, (int)q.B, s);
+  if (o.dtype == BSA_BF16) hipLaunchKernelGGL(tdec_combine_kernel<BSA_BF16>, dim3(q.B * q.H), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL(tdec_combine_kernel<BSA_F32>, dim3(q.B * q.H), dim3(512), 0, s, a);
 }
 
 }  // namespace bsa

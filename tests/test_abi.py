@@ -168,6 +168,12 @@ def test_threshold_decode_rejects_bad_arguments(lib):
     assert call(q, 1024, 1.5) == L.BSA_ERR_INVALID and "lambda" in _err(lib)
     assert call(_t(H=32, Lq=2), 1024, 0.3) == L.BSA_ERR_INVALID and "one query row" in _err(lib)
     assert call(_t(H=24, Lq=1), 1024, 0.3) == L.BSA_ERR_UNSUPPORTED      # group size 3
+    # more decision chunks per head than the merge takes (4096 of 4 tiles = 1M keys)
+    long_k = _t(H=8, Lq=4096 * 256 + 64)
+    big = lib.bsa_threshold_decode_workspace_bytes(ctypes.byref(q), ctypes.byref(long_k), 1024)
+    st = lib.bsa_threshold_decode_fwd(ctypes.byref(q), ctypes.byref(long_k), ctypes.byref(long_k), 0.088, 0.3,
+                                      1024, ctypes.byref(q), FAKE, None, None, FAKE, big, None)
+    assert st == L.BSA_ERR_UNSUPPORTED and "chunks" in _err(lib)
 
 
 def test_active_rows_rejects_mismatch(lib):
