@@ -9,7 +9,8 @@ select blocks, attend over the selection.  Steps are replayed from a HIP graph
 with inputs resident in HBM.
 
 Also measured (reported under "secondary"): the block-wise diffusion denoising
-step (32 query rows, 32K prefix), causal block-sparse prefill at 32K with
+step (32 query rows, 32K prefix) alone and as an 8-step loop (dense first step,
+then locality pruning, the block's own keys merged in), causal block-sparse prefill at 32K with
 dual-band selection, softmax-threshold prefill at 128K, and softmax-threshold
 decode over the whole 64K cache.
 
@@ -30,8 +31,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # Softmax-threshold decode: lambda = a / L (BLASST: one constant per model and
-# phase); a chosen so that about 70% of the V tiles are skipped at 64K on the
-# synthetic GQA decode workload.
+# phase); with this a, 93% of the (head, tile) pairs and 81% of the V tiles are
+# skipped at 64K on the synthetic GQA decode workload.
 THRESH_DECODE_A = 0.4 * 65536
 THRESH_DECODE_SPLIT = 1024     # keys per split-KV slice
 
@@ -84,6 +85,33 @@ def time_calls(torch, fn, reps, warmup=3):
         b.record(s)
     torch.cuda.synchronize()
     return 1000.0 * sum(a.elapsed_time(b) for a, b in ev) / reps
+
+
+def time_graph(torch, fn, reps, warmup=3, inner=8):
+    """Average duration (us) of fn(), captured ``inner`` times in a row in one
+    HIP graph and replayed: the GPU time of a sequence of short kernels without
+    the host's launch gaps (fn must give the same result when repeated)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(inner):
+            fn()
+    for _ in range(warmup):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1000.0 * e0.elapsed_time(e1) / (reps * inner)
 
 
 def time_cold(torch, fn, reps, flush):
@@ -221,6 +249,98 @@ def bench_dlm(torch, bsa, synth, reps):
                          union_blocks_per_group=[int(x) for x in u], union_kv_bytes=ubytes,
                          attention_gbs=round(ubytes / (t_att * 1e3), 1), active_rows=int(mask.sum().item()))
     return out
+
+
+def bench_dlm_steps(torch, bsa, synth, reps):
+    """Denoising steps of one 32-token block over the 32K prefix: step 0 dense
+    over the prefix for every row (builds the prefix cache), later steps with
+    locality pruning (4 rows change per step): active rows, selection for the
+    active rows, sparse prefix attention for them, attention over the block's
+    own keys for every row, and the merge.  Each step is also run with every
+    row recomputed (selection union over all rows), the form without pruning.
+    Steps are timed as HIP graph replays (GPU time, no host launch gaps)."""
+    log("dlm steps: generating the multi-step denoising workload")
+    w = synth.dlm_denoise_steps()
+    p = w.params
+    B, Hq, R, D = w.q.shape
+    Hkv, L = w.k.shape[1], w.k.shape[2]
+    NB = L // p["kv_block"]
+    kd, vd = to_dev(torch, w.k, "bf16"), to_dev(torch, w.v, "bf16")
+    steps = [tuple(to_dev(torch, x, "bf16") for x in t)
+             for t in zip(w.extra["q_steps"], w.extra["kb_steps"], w.extra["vb_steps"])]
+    kmean, _ = bsa.bsa_build_block_summaries(kd, p["kv_block"], p["layout"], with_energy=False)
+    sp = bsa.select_params(kv_block=64, q_block=R, q_pos0=p["q_pos0"], topk=p["topk"], scale=p["scale"])
+    sp.cap = bsa.list_capacity(NB, R, sp)
+    ws_sel = torch.zeros(bsa.bsa_select_workspace_bytes(steps[0][0], Hkv, NB, sp), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Hkv, 1, sp.cap), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Hkv, 1), dtype=torch.int32, device="cuda")
+    idx_dense = torch.arange(NB, dtype=torch.int32, device="cuda").view(1, 1, 1, NB).repeat(B, Hkv, 1, 1)
+    cnt_dense = torch.full((B, Hkv, 1), NB, dtype=torch.int32, device="cuda")
+    ap_dense = bsa.attn_params(kv_block=64, q_block=R, cap=NB, q_pos0=p["q_pos0"], scale=p["scale"])
+    ap = bsa.attn_params(kv_block=64, q_block=R, cap=sp.cap, q_pos0=p["q_pos0"], scale=p["scale"])
+    ws_att = torch.zeros(max(bsa.bsa_attention_workspace_bytes(steps[0][0], kd, ap),
+                             bsa.bsa_attention_workspace_bytes(steps[0][0], kd, ap_dense)), dtype=torch.uint8,
+                         device="cuda")
+    idx_in = torch.zeros((B, Hkv, 1, 1), dtype=torch.int32, device="cuda")
+    cnt_in = torch.ones((B, Hkv, 1), dtype=torch.int32, device="cuda")
+    ap_in = bsa.attn_params(kv_block=64, q_block=R, cap=1, q_pos0=0, causal=0, scale=p["scale"])
+    ws_in = torch.zeros(bsa.bsa_attention_workspace_bytes(steps[0][0], steps[0][1], ap_in), dtype=torch.uint8,
+                        device="cuda")
+    cache_o = torch.zeros((B, Hq, R, D), device="cuda")
+    cache_l = torch.zeros((B, Hq, R), device="cuda")
+    o_in = torch.zeros((B, Hq, R, D), device="cuda")
+    l_in = torch.zeros((B, Hq, R), device="cuda")
+    out = torch.empty((B, Hq, R, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, R), device="cuda")
+    mask = torch.empty((B, R), dtype=torch.uint8, device="cuda")
+
+    def block_and_merge(qd, kbd, vbd):
+        bsa.bsa_block_attention_merge(qd, kbd, vbd, cache_o, cache_l, scale=p["scale"], o=out, lse=lse)
+
+    def block_and_merge_pieces(qd, kbd, vbd):
+        bsa.bsa_sparse_attention_fwd(qd, kbd, vbd, idx_in, cnt_in, ap_in, o=o_in, lse=l_in, workspace=ws_in)
+        bsa.bsa_merge_attention_states(cache_o, cache_l, o_in, l_in, o=out, lse=lse)
+
+    def dense_step(s):
+        qd, kbd, vbd = steps[s]
+        bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx_dense, cnt_dense, ap_dense, o=cache_o, lse=cache_l,
+                                     workspace=ws_att)
+        block_and_merge(qd, kbd, vbd)
+
+    def sparse_step(s, pruned=True):
+        qd, kbd, vbd = steps[s]
+        bsa.bsa_active_rows(qd, steps[s - 1][0], p["theta_act"], want_mse=False, mask=mask)
+        rm = mask if pruned else None
+        bsa.bsa_select_blocks(qd, kmean, sp, row_mask=rm, workspace=ws_sel, idx=idx, cnt=cnt)
+        bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap, row_mask=rm, o=cache_o,
+                                     lse=cache_l, workspace=ws_att)
+        block_and_merge(qd, kbd, vbd)
+
+    per_step = []
+    t_dense = time_graph(torch, lambda: dense_step(0), reps)
+    per_step.append(dict(step=0, active_rows=R, list_blocks_mean=float(NB), us=round(t_dense, 2)))
+    for s in range(1, len(steps)):
+        saved = (cache_o.clone(), cache_l.clone())
+        t_all = time_graph(torch, lambda: sparse_step(s, pruned=False), reps)
+        u_all = cnt.float().mean().item()
+        cache_o.copy_(saved[0])
+        cache_l.copy_(saved[1])
+        t = time_graph(torch, lambda: sparse_step(s), reps)
+        per_step.append(dict(step=s, active_rows=int(mask.sum().item()), list_blocks_mean=round(cnt.float().mean().item(), 1),
+                             us=round(t, 2), all_rows_list_blocks_mean=round(u_all, 1), all_rows_us=round(t_all, 2)))
+    qd, kbd, vbd = steps[-1]
+    t_fused = time_graph(torch, lambda: block_and_merge(qd, kbd, vbd), reps)
+    t_pieces = time_graph(torch, lambda: block_and_merge_pieces(qd, kbd, vbd), reps)
+    sp_steps = per_step[1:]
+    mean_us = sum(x["us"] for x in sp_steps) / len(sp_steps)
+    mean_all = sum(x["all_rows_us"] for x in sp_steps) / len(sp_steps)
+    dens = sum(x["list_blocks_mean"] for x in sp_steps) / len(sp_steps) / NB
+    dens_all = sum(x["all_rows_list_blocks_mean"] for x in sp_steps) / len(sp_steps) / NB
+    return dict(steps=len(steps), dense_first_step_us=round(t_dense, 2), pruned_step_us_mean=round(mean_us, 2),
+                all_rows_step_us_mean=round(mean_all, 2), kv_density_pruned=round(dens, 4),
+                kv_density_all_rows=round(dens_all, 4), active_fraction_per_step=[x["active_rows"] / R for x in per_step],
+                block_attention_merge_us=round(t_fused, 2), block_attention_then_merge_us=round(t_pieces, 2),
+                per_step=per_step)
 
 
 # ---------------------------------------------------------------- prefill ---
@@ -412,6 +532,8 @@ def main():
     if args.only in ("all", "dlm"):
         secondary["dlm_denoise_32k"] = bench_dlm(torch, bsa, synth, reps)
         log(f"dlm: {secondary['dlm_denoise_32k']}")
+        secondary["dlm_denoise_steps_32k"] = bench_dlm_steps(torch, bsa, synth, reps)
+        log(f"dlm steps: {secondary['dlm_denoise_steps_32k']}")
     if args.only in ("all", "prefill"):
         secondary["sparse_prefill_32k"] = bench_prefill(torch, bsa, synth, reps)
         log(f"prefill: {secondary['sparse_prefill_32k']}")

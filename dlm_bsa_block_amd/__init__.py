@@ -18,7 +18,9 @@ from ._lib import (  # noqa: F401
     BsaTensor, BsaThreshParams, check, lib,
 )
 
-__all__ = ["bsa_build_block_summaries", "bsa_select_blocks", "bsa_active_rows", "bsa_sparse_attention_fwd",
+__all__ = ["bsa_build_block_summaries", "bsa_select_blocks", "bsa_active_rows", "bsa_merge_attention_states",
+           "bsa_block_attention_merge",
+           "bsa_sparse_attention_fwd",
            "bsa_threshold_attention_fwd", "bsa_threshold_decode_fwd", "bsa_select_workspace_bytes",
            "bsa_attention_workspace_bytes", "bsa_threshold_decode_workspace_bytes",
            "BsaError", "tensor_desc", "select_params", "attn_params", "lib"]
@@ -131,6 +133,35 @@ def bsa_active_rows(q_cur: torch.Tensor, q_prev: torch.Tensor, theta: float, wan
     check(lib().bsa_active_rows(ctypes.byref(a), ctypes.byref(b), theta, mask.data_ptr(), _ptr(mse), _stream()),
           "bsa_active_rows")
     return mask, mse
+
+
+def bsa_merge_attention_states(o_a, lse_a, o_b, lse_b, o=None, lse=None):
+    """Returns (o, lse): the state over the union of two disjoint key sets.
+    o may be o_a or o_b and lse may be lse_a or lse_b (in place)."""
+    if o is None:
+        o = torch.empty_like(o_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    a, b, c = tensor_desc(o_a), tensor_desc(o_b), tensor_desc(o)
+    check(lib().bsa_merge_attention_states(ctypes.byref(a), lse_a.data_ptr(), ctypes.byref(b), lse_b.data_ptr(),
+                                           ctypes.byref(c), lse.data_ptr(), _stream()), "bsa_merge_attention_states")
+    return o, lse
+
+
+def bsa_block_attention_merge(q, kb, vb, o_pre, lse_pre, scale=None, o=None, lse=None):
+    """Returns (o, lse): attention of the block's rows over the block's own keys
+    merged with the cached prefix state (o may be o_pre, lse may be lse_pre)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[3])
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty_like(lse_pre)
+    qd, kd, vd, pd, od = tensor_desc(q), tensor_desc(kb), tensor_desc(vb), tensor_desc(o_pre), tensor_desc(o)
+    check(lib().bsa_block_attention_merge(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), scale,
+                                          ctypes.byref(pd), lse_pre.data_ptr(), ctypes.byref(od), lse.data_ptr(),
+                                          _stream()), "bsa_block_attention_merge")
+    return o, lse
 
 
 # --------------------------------------------------------------- attention ---

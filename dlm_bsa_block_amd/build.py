@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build", "libbsa")
 LIB = os.path.join(HERE, "libbsa.so")
 SOURCES = ["api.hip", "summaries.hip", "select.hip", "locality.hip", "attn_decode.hip", "attn_mfma.hip",
-           "threshold.hip", "threshold_decode.hip"]
+           "threshold.hip", "threshold_decode.hip", "merge.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          # never let the compiler form packed fp32 math (v_pk_*_f32)

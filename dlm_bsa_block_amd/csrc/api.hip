@@ -281,6 +281,60 @@ static bsa_status validate_threshold_decode(const bsa_tensor* q, const bsa_tenso
   return BSA_OK;
 }
 
+bsa_status bsa_merge_attention_states(const bsa_tensor* o_a, const float* lse_a, const bsa_tensor* o_b,
+                                      const float* lse_b, const bsa_tensor* o, float* lse, void* stream) {
+  bsa_status st = check_tensor(o_a, "o_a", true);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(o_b, "o_b", true)) != BSA_OK) return st;
+  if ((st = check_tensor(o, "o", true)) != BSA_OK) return st;
+  if (!same_dims(o_a, o_b) || !same_dims(o_a, o)) return fail(BSA_ERR_INVALID, "o_a, o_b and o differ in shape");
+  if (!lse_a || !lse_b || !lse) return fail(BSA_ERR_INVALID, "lse_a, lse_b and lse are required");
+  const int64_t rows = o_a->B * o_a->H * o_a->L;
+  if (rows == 0 || o_a->D == 0) return BSA_OK;
+  MergeArgs a;
+  a.o_a = o_a->data; a.o_b = o_b->data; a.lse_a = lse_a; a.lse_b = lse_b; a.o = o->data; a.lse = lse;
+  a.asb = o_a->stride_b; a.ash = o_a->stride_h; a.asl = o_a->stride_l;
+  a.bsb = o_b->stride_b; a.bsh = o_b->stride_h; a.bsl = o_b->stride_l;
+  a.osb = o->stride_b; a.osh = o->stride_h; a.osl = o->stride_l;
+  a.rows = rows; a.H = (int)o_a->H; a.L = (int)o_a->L; a.D = (int)o_a->D;
+  launch_merge_states(a, o_a->dtype, o_b->dtype, o->dtype, static_cast<hipStream_t>(stream));
+  return check_launch("merge attention states");
+}
+
+bsa_status bsa_block_attention_merge(const bsa_tensor* q, const bsa_tensor* kb, const bsa_tensor* vb, float scale,
+                                     const bsa_tensor* o_pre, const float* lse_pre, const bsa_tensor* o, float* lse,
+                                     void* stream) {
+  bsa_status st = check_tensor(q, "q", false);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(kb, "kb", false)) != BSA_OK) return st;
+  if ((st = check_tensor(vb, "vb", false)) != BSA_OK) return st;
+  if ((st = check_tensor(o_pre, "o_pre", false)) != BSA_OK) return st;
+  if ((st = check_tensor(o, "o", false)) != BSA_OK) return st;
+  if (!same_shape(kb, vb)) return fail(BSA_ERR_INVALID, "kb and vb differ in shape or dtype");
+  if (q->B != kb->B || q->L != kb->L || q->D != kb->D || q->H % kb->H || q->dtype != kb->dtype)
+    return fail(BSA_ERR_INVALID, "q and kb/vb are incompatible");
+  if (!same_dims(q, o_pre) || !same_dims(q, o)) return fail(BSA_ERR_INVALID, "o_pre and o must have q's shape");
+  if (q->dtype != BSA_BF16 || q->D != 128 || q->L > 32)
+    return fail(BSA_ERR_UNSUPPORTED, "block attention needs bf16, D = 128 and at most 32 rows (got %d)", (int)q->L);
+  if (!lse_pre || !lse) return fail(BSA_ERR_INVALID, "lse_pre and lse are required");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(BSA_ERR_INVALID, "scale must be finite and > 0");
+  BlockMergeArgs a;
+  a.q = static_cast<const uint8_t*>(q->data);
+  a.kb = static_cast<const uint8_t*>(kb->data);
+  a.vb = static_cast<const uint8_t*>(vb->data);
+  a.o_pre = o_pre->data; a.lse_pre = lse_pre; a.o = o->data; a.lse = lse;
+  a.qsb = q->stride_b; a.qsh = q->stride_h; a.qsl = q->stride_l;
+  a.ksb = kb->stride_b; a.ksh = kb->stride_h; a.ksl = kb->stride_l;
+  a.vsb = vb->stride_b; a.vsh = vb->stride_h; a.vsl = vb->stride_l;
+  a.psb = o_pre->stride_b; a.psh = o_pre->stride_h; a.psl = o_pre->stride_l;
+  a.osb = o->stride_b; a.osh = o->stride_h; a.osl = o->stride_l;
+  a.B = (int)q->B; a.Hq = (int)q->H; a.G = (int)(q->H / kb->H); a.R = (int)q->L;
+  a.pre_f32 = o_pre->dtype == BSA_F32;
+  a.scale = scale;
+  launch_block_attn_merge(a, o->dtype, static_cast<hipStream_t>(stream));
+  return check_launch("block attention merge");
+}
+
 size_t bsa_threshold_decode_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, int32_t kv_split) {
   if (!q || !k || q->H <= 0 || k->H <= 0 || k->L <= 0 || kv_split < 64 || kv_split % 64) return 0;
   size_t bytes = 0;

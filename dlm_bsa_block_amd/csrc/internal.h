@@ -38,6 +38,35 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
 void launch_active_rows(const bsa_tensor& a, const bsa_tensor& b, float theta, uint8_t* mask, float* mse,
                         hipStream_t s);
 
+// Merge of two attention states (o_x [B, H, L, D] any of bf16/f32, lse_x [B, H, L] natural log).
+struct MergeArgs {
+  const void* o_a;
+  const void* o_b;
+  const float* lse_a;
+  const float* lse_b;
+  void* o;
+  float* lse;
+  int64_t asb, ash, asl, bsb, bsh, bsl, osb, osh, osl;
+  int64_t rows;                      // B * H * L
+  int H, L, D;
+};
+void launch_merge_states(const MergeArgs& a, int da, int db, int dout, hipStream_t s);
+
+// A denoising block's attention over its own keys merged with the cached prefix state.
+struct BlockMergeArgs {
+  const uint8_t* q;                  // [B, Hq, R, D] bf16
+  const uint8_t* kb;                 // [B, Hkv, R, D] bf16
+  const uint8_t* vb;
+  const void* o_pre;                 // [B, Hq, R, D] bf16 or f32
+  const float* lse_pre;              // [B, Hq, R]
+  void* o;                           // [B, Hq, R, D] bf16 or f32
+  float* lse;                        // [B, Hq, R]
+  int64_t qsb, qsh, qsl, ksb, ksh, ksl, vsb, vsh, vsl, psb, psh, psl, osb, osh, osl;
+  int B, Hq, G, R, pre_f32;
+  float scale;
+};
+void launch_block_attn_merge(const BlockMergeArgs& a, int dout, hipStream_t s);
+
 struct AttnPlan {
   int kind;                 // 0 = VALU decode split, 1 = MFMA gather (direct), 2 = MFMA gather split
   int B, Hq, Hkv, G, D, Lq, L, NQB;

@@ -263,6 +263,42 @@ bsa_status bsa_threshold_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, co
                                     int32_t* kept_tiles, uint8_t* keep_map, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * Merge of two attention states over disjoint key sets (LoSA sec. 2: a stable
+ * token of a denoising block reuses its cached prefix-attention output and
+ * statistics; the full attention combines that state with the one over the
+ * block's own keys).  For each (batch, head, row):
+ *   lse = ln(e^lse_a + e^lse_b),  O = e^(lse_a - lse) O_a + e^(lse_b - lse) O_b.
+ * o_a, o_b: [B, H, L, D], bf16 or f32 each (any strides as for every tensor);
+ * lse_a, lse_b: [B, H, L] f32, natural log, -inf for an empty state (its O is
+ * then ignored).  Outputs o [B, H, L, D] bf16 or f32 and lse [B, H, L] f32;
+ * rows where both states are empty get O = 0 and lse = -inf.  o may be o_a or
+ * o_b (the same tensor, elementwise in place) and lse may be lse_a or lse_b.
+ * Errors: BSA_ERR_INVALID for null pointers, differing shapes or a misaligned
+ * tensor; BSA_ERR_UNSUPPORTED for a head dim other than 64 or 128.  Nothing
+ * is allocated; the call is enqueued on stream.
+ * ------------------------------------------------------------------------ */
+bsa_status bsa_merge_attention_states(const bsa_tensor* o_a, const float* lse_a, const bsa_tensor* o_b,
+                                      const float* lse_b, const bsa_tensor* o, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * One denoising step's attention over the block's own keys, merged with the
+ * cached prefix state (LoSA sec. 2: each row's prefix attention output and
+ * statistics are kept between steps; the block's own tokens are attended in
+ * both directions).  q [B, Hq, R, D], kb/vb [B, Hkv, R, D] (the block's keys
+ * and values; Hkv divides Hq), bf16, D = 128, 1 <= R <= 32.  o_pre [B, Hq,
+ * R, D] bf16 or f32 and lse_pre [B, Hq, R] f32 (natural log; -inf for an
+ * empty prefix) hold the prefix state.  Writes o [B, Hq, R, D] bf16 or f32
+ * and lse [B, Hq, R]: the exact softmax of scale * q . k over the prefix
+ * keys behind the cached state and the block's R keys.  o may be o_pre and
+ * lse may be lse_pre (in place).  Errors: BSA_ERR_INVALID for null pointers,
+ * mismatched shapes or dtypes, misaligned tensors or a bad scale;
+ * BSA_ERR_UNSUPPORTED outside bf16, D = 128, R <= 32.
+ * ------------------------------------------------------------------------ */
+bsa_status bsa_block_attention_merge(const bsa_tensor* q, const bsa_tensor* kb, const bsa_tensor* vb, float scale,
+                                     const bsa_tensor* o_pre, const float* lse_pre, const bsa_tensor* o, float* lse,
+                                     void* stream);
+
 /* Status text and the calling thread's last error detail. */
 const char* bsa_status_string(int32_t status);
 const char* bsa_last_error(void);

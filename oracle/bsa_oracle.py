@@ -342,6 +342,66 @@ def active_rows(q_cur: np.ndarray, q_prev: np.ndarray, theta: float):
     return mask, mse
 
 
+# ------------------------------------------------- full denoising step ---
+def merge_states(O_a: np.ndarray, L_a: np.ndarray, O_b: np.ndarray, L_b: np.ndarray):
+    """Attention state over the union of two disjoint key sets from the states
+    over each: [LoSA] sec. 2 keeps a stable token's prefix-attention output and
+    statistics, which combine with the attention over the block's own keys.
+
+    Softmax over a disjoint union: with weights w_x = e^(L_x - L) and
+    L = ln(e^L_a + e^L_b), O = w_a O_a + w_b O_b.  An LSE of -inf is an empty
+    set, whose O is ignored; both empty gives O = 0, L = -inf.
+    O_x [..., D], L_x [...] (natural log).
+    """
+    m = np.maximum(L_a, L_b)
+    L = np.full(m.shape, -np.inf)
+    ok = np.isfinite(m)
+    with np.errstate(invalid="ignore"):                # -inf - -inf where both sides are empty (masked)
+        wa = np.where(np.isfinite(L_a), np.exp(np.where(ok, L_a - m, 0.0)), 0.0)
+        wb = np.where(np.isfinite(L_b), np.exp(np.where(ok, L_b - m, 0.0)), 0.0)
+    tot = wa + wb
+    L[ok] = m[ok] + np.log(tot[ok])
+    fa = np.where(ok, wa / np.where(ok, tot, 1.0), 0.0)[..., None]
+    fb = np.where(ok, wb / np.where(ok, tot, 1.0), 0.0)[..., None]
+    O = np.where(fa > 0, fa * np.nan_to_num(O_a), 0.0) + np.where(fb > 0, fb * np.nan_to_num(O_b), 0.0)
+    return O, L
+
+
+def block_self_attention(q: np.ndarray, kb: np.ndarray, vb: np.ndarray, scale: float):
+    """Attention of the block's R rows over the block's own R keys, in both
+    directions (a block-wise diffusion LM denoises all tokens of the block
+    together; READING: no causal mask inside the block).
+    q [B, Hq, R, D]; kb, vb [B, Hkv, R, D] -> O [B, Hq, R, D], LSE [B, Hq, R]."""
+    B, Hq, R, D = q.shape
+    G = Hq // kb.shape[1]
+    O = np.zeros((B, Hq, R, vb.shape[3]))
+    LSE = np.zeros((B, Hq, R))
+    toks = np.arange(kb.shape[2])
+    for b in range(B):
+        for h in range(Hq):
+            O[b, h], LSE[b, h] = attend_tokens(q[b, h], kb[b, h // G], vb[b, h // G], toks, scale)
+    return O, LSE
+
+
+def denoise_step(p: dict, q: np.ndarray, k: np.ndarray, v: np.ndarray, kb: np.ndarray, vb: np.ndarray, lists,
+                 row_mask, cache_O: np.ndarray, cache_L: np.ndarray):
+    """One denoising step of a block ([LoSA] sec. 2).
+
+    Rows with row_mask set (all rows when it is None: the dense first step,
+    whose lists hold every prefix block) recompute their prefix attention over
+    their block's list; the others keep the cached prefix state.  Every row
+    then merges its prefix state with the attention over the block's own keys.
+    Returns O, LSE (the step's output) and the updated prefix cache.
+    """
+    O_p, L_p = sparse_attention(p, q, k, v, lists, row_mask=row_mask)
+    upd = np.ones(q.shape[2], dtype=bool)[None, :].repeat(q.shape[0], 0) if row_mask is None else row_mask
+    cO = np.where(upd[:, None, :, None], O_p, cache_O)
+    cL = np.where(upd[:, None, :], L_p, cache_L)
+    O_b, L_b = block_self_attention(q, kb, vb, p["scale"])
+    O, L = merge_states(cO, cL, O_b, L_b)
+    return O, L, cO, cL
+
+
 # ---------------------------------------------------- threshold attention ---
 def threshold_walk(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows_pos: np.ndarray, tile: int, lam: float,
                    scale: float, causal: bool = True, decisions: dict | None = None):

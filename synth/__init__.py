@@ -13,6 +13,7 @@ from .workloads import (  # noqa: F401
     tiny_decode,
     gqa_decode,
     dlm_denoise,
+    dlm_denoise_steps,
     sparse_prefill,
     threshold_prefill,
 )

@@ -228,6 +228,52 @@ def dlm_denoise(seed: int = 3, L: int = 32768, R: int = 32, Hq: int = 32, Hkv: i
                     dict(q_prev=_store(q_prev, "bf16")[None], active=active, needles=needles))
 
 
+def dlm_denoise_steps(seed: int = 6, L: int = 32768, R: int = 32, Hq: int = 32, Hkv: int = 8, D: int = 128,
+                      block: int = 64, n_steps: int = 8, per_step: int = 4, n_needles: int = 8,
+                      theta: float = 0.1) -> Workload:
+    """Several denoising steps of one 32-token block over a cached prefix.
+
+    The prefix K/V, needles and step-0 queries come from ``dlm_denoise`` (its
+    previous-step queries are the queries of step 0).  The block's own keys
+    and values sit at positions L .. L+R-1: step 0 draws RoPE'd N(0, 1) keys and
+    N(0, 1) values.  At each later step ``per_step`` seeded rows that have not
+    changed before are unmasked: their query vectors (all heads) change by
+    N(0, 1) and their block keys/values are drawn afresh; every other row
+    drifts by N(0, 0.01^2).  extra holds per-step lists ``q_steps``
+    [1, Hq, R, D], ``kb_steps``/``vb_steps`` [1, Hkv, R, D] (bf16 bits) and the
+    unmasked rows ``changed`` of each step (empty at step 0).
+    """
+    base = dlm_denoise(seed=seed, L=L, R=R, Hq=Hq, Hkv=Hkv, D=D, block=block, n_active=per_step,
+                       n_needles=n_needles, theta=theta)
+    rpos = L + np.arange(R)
+    q = storage_to_f64(base.extra["q_prev"], "bf16")[0]
+    kb = np.stack([rope(_rng(seed, 70, g).standard_normal((R, D)), rpos) for g in range(Hkv)])
+    vb = np.stack([_rng(seed, 71, g).standard_normal((R, D)) for g in range(Hkv)])
+    q_steps, kb_steps, vb_steps, changed = [_store(q, "bf16")[None]], [_store(kb, "bf16")[None]], \
+        [_store(vb, "bf16")[None]], [np.zeros(0, dtype=np.int64)]
+    fresh = np.ones(R, dtype=bool)
+    for s in range(1, n_steps):
+        cand = np.nonzero(fresh)[0]
+        rows = np.sort(_rng(seed, 72, s).choice(cand, size=min(per_step, len(cand)), replace=False))
+        fresh[rows] = False
+        act = np.zeros(R, dtype=bool)
+        act[rows] = True
+        for h in range(Hq):
+            d = _rng(seed, 73, s, h).standard_normal((R, D))
+            q[h] = q[h] + np.where(act[:, None], d, 0.01 * d)
+        for g in range(Hkv):
+            nk = rope(_rng(seed, 74, s, g).standard_normal((R, D)), rpos)
+            nv = _rng(seed, 75, s, g).standard_normal((R, D))
+            kb[g] = np.where(act[:, None], nk, kb[g] + 0.01 * nk)
+            vb[g] = np.where(act[:, None], nv, vb[g] + 0.01 * nv)
+        q_steps.append(_store(q, "bf16")[None])
+        kb_steps.append(_store(kb, "bf16")[None])
+        vb_steps.append(_store(vb, "bf16")[None])
+        changed.append(rows.astype(np.int64))
+    extra = dict(base.extra, q_steps=q_steps, kb_steps=kb_steps, vb_steps=vb_steps, changed=changed)
+    return Workload("dlm_denoise_steps", "bf16", q_steps[0], base.k, base.v, dict(base.params), extra)
+
+
 def sparse_prefill(seed: int = 4, L: int = 32768, Hq: int = 32, Hkv: int = 8, D: int = 128, block: int = 128,
                    n_topics: int = 16, topic_frac: float = 0.25, amp: float = 4.0, c_norm2: float = 64.0) -> Workload:
     """Causal prefill with both a positional (fast band) and a topical (slow band) signal.

@@ -176,6 +176,39 @@ def test_threshold_decode_rejects_bad_arguments(lib):
     assert st == L.BSA_ERR_UNSUPPORTED and "chunks" in _err(lib)
 
 
+def test_merge_rejects_bad_arguments(lib):
+    a, b = _t(H=32, Lq=32, dtype=L.BSA_F32), _t(H=32, Lq=31, dtype=L.BSA_F32)
+    st = lib.bsa_merge_attention_states(ctypes.byref(a), FAKE, ctypes.byref(b), FAKE, ctypes.byref(a), FAKE, None)
+    assert st == L.BSA_ERR_INVALID and "shape" in _err(lib)
+    st = lib.bsa_merge_attention_states(ctypes.byref(a), FAKE, ctypes.byref(a), None, ctypes.byref(a), FAKE, None)
+    assert st == L.BSA_ERR_INVALID and "lse" in _err(lib)
+    st = lib.bsa_merge_attention_states(ctypes.byref(_t(D=96)), FAKE, ctypes.byref(_t(D=96)), FAKE,
+                                        ctypes.byref(_t(D=96)), FAKE, None)
+    assert st == L.BSA_ERR_UNSUPPORTED
+    st = lib.bsa_merge_attention_states(ctypes.byref(a), FAKE, ctypes.byref(_t(H=32, Lq=32, data=FAKE + 8)), FAKE,
+                                        ctypes.byref(a), FAKE, None)
+    assert st == L.BSA_ERR_INVALID and "aligned" in _err(lib)
+    # no rows: nothing to do, nothing launched
+    e = _t(H=32, Lq=0)
+    assert lib.bsa_merge_attention_states(ctypes.byref(e), FAKE, ctypes.byref(e), FAKE, ctypes.byref(e), FAKE,
+                                          None) == L.BSA_OK
+
+
+def test_block_attention_merge_rejects_bad_arguments(lib):
+    q, kb, o = _t(H=32, Lq=32), _t(H=8, Lq=32), _t(H=32, Lq=32, dtype=L.BSA_F32)
+
+    def call(qq, kk, oo, scale=0.088, lse=FAKE):
+        return lib.bsa_block_attention_merge(ctypes.byref(qq), ctypes.byref(kk), ctypes.byref(kk), scale,
+                                             ctypes.byref(oo), lse, ctypes.byref(oo), FAKE, None)
+    assert call(_t(H=32, Lq=40), _t(H=8, Lq=40), _t(H=32, Lq=40)) == L.BSA_ERR_UNSUPPORTED   # 40 rows
+    assert call(q, _t(H=8, Lq=31), o) == L.BSA_ERR_INVALID and "incompatible" in _err(lib)
+    assert call(q, _t(H=7, Lq=32), o) == L.BSA_ERR_INVALID                                # 7 does not divide 32
+    assert call(q, kb, _t(H=32, Lq=16)) == L.BSA_ERR_INVALID and "shape" in _err(lib)
+    assert call(q, kb, o, lse=None) == L.BSA_ERR_INVALID and "lse" in _err(lib)
+    assert call(q, kb, o, scale=0.0) == L.BSA_ERR_INVALID and "scale" in _err(lib)
+    assert call(_t(H=32, Lq=32, dtype=L.BSA_F32), _t(H=8, Lq=32, dtype=L.BSA_F32), o) == L.BSA_ERR_UNSUPPORTED
+
+
 def test_active_rows_rejects_mismatch(lib):
     a, b = _t(H=32, Lq=32), _t(H=32, Lq=31)
     st = lib.bsa_active_rows(ctypes.byref(a), ctypes.byref(b), 0.1, FAKE, None, None)

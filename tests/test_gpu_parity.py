@@ -259,6 +259,142 @@ def test_dlm_no_active_rows_writes_nothing(bsa):
     assert (rp == -1).all()
 
 
+# ------------------------------------------------- merge and full denoise ---
+def test_merge_states(bsa):
+    """bsa_merge_attention_states against the oracle's union-of-key-sets merge:
+    mixed input dtypes, empty states (LSE -inf, O ignored), rows empty on both
+    sides, a ragged row count, in place into one of the inputs."""
+    rng = np.random.default_rng(21)
+    shape = (2, 3, 37, 128)
+    oa = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).cuda().to(torch.bfloat16)
+    ob = torch.from_numpy(rng.standard_normal(shape).astype(np.float32) * 3).cuda()
+    la = rng.uniform(-5, 25, shape[:3]).astype(np.float32)
+    lb = rng.uniform(-5, 25, shape[:3]).astype(np.float32)
+    la[0, 0, :5] = -np.inf
+    lb[1, 2, 3:9] = -np.inf
+    la[1, 1, 10:12] = lb[1, 1, 10:12] = -np.inf
+    lb[0, 1, 20] = la[0, 1, 20] + 40.0             # one side dominates
+    oa[0, 0, :5] = float("nan")                      # O of an empty state is never read into the result
+    ob[1, 2, 3:9] = float("nan")
+    lad, lbd = torch.from_numpy(la).cuda(), torch.from_numpy(lb).cuda()
+    o32, l32 = bsa.bsa_merge_attention_states(oa, lad, ob, lbd, o=torch.empty(shape, device="cuda"))
+    o16, l16 = bsa.bsa_merge_attention_states(oa, lad, ob, lbd, o=torch.empty(shape, device="cuda",
+                                                                               dtype=torch.bfloat16))
+    ob_in, lb_in = ob.clone(), lbd.clone()
+    bsa.bsa_merge_attention_states(oa, lad, ob_in, lb_in, o=ob_in, lse=lb_in)
+    _sync()
+    oa64 = oa.float().cpu().numpy().astype(np.float64)
+    ob64 = ob.cpu().numpy().astype(np.float64)
+    oa64[0, 0, :5] = 0.0                             # the oracle is given finite values where the GPU gets NaN
+    ob64[1, 2, 3:9] = 0.0
+    O_ref, L_ref = orc.merge_states(oa64, la.astype(np.float64), ob64, lb.astype(np.float64))
+    o_np, l_np = o32.cpu().numpy(), l32.cpu().numpy()
+    assert np.array_equal(np.isinf(l_np), np.isinf(L_ref))
+    fin = np.isfinite(L_ref)
+    assert np.abs(l_np[fin] - L_ref[fin]).max() < 1e-5
+    assert np.abs(o_np - O_ref).max() < 2e-5
+    assert np.all(o_np[1, 1, 10:12] == 0)
+    assert torch.equal(l16, l32)
+    _check_rounding(o16, o32)
+    assert torch.equal(ob_in, o32) and torch.equal(lb_in, l32), "in-place merge differs"
+
+
+def _denoise_loop(bsa, w, check=True):
+    """Run the denoising steps of ``w`` through the library: step 0 dense over
+    the prefix for every row, later steps sparse for the active rows only
+    (union over them), stable rows keeping their cached prefix state, and every
+    row merged with its attention over the block's own keys.  With ``check``
+    each step is compared with the oracle's step (lists first, with the tie
+    band).  Returns the per-step active-row counts and list sizes."""
+    p = w.params
+    B, Hq, R, D = w.q.shape
+    Hkv, L = w.k.shape[1], w.k.shape[2]
+    NB = -(-L // p["kv_block"])
+    kd, vd = to_dev(w.k, "bf16"), to_dev(w.v, "bf16")
+    kmean, _ = bsa.bsa_build_block_summaries(kd, p["kv_block"], p["layout"])
+    cache_o = torch.zeros((B, Hq, R, D), device="cuda")
+    cache_l = torch.zeros((B, Hq, R), device="cuda")
+    idx_in = torch.zeros((B, Hkv, 1, 1), dtype=torch.int32, device="cuda")
+    cnt_in = torch.ones((B, Hkv, 1), dtype=torch.int32, device="cuda")
+    ap_in = bsa.attn_params(kv_block=64, q_block=R, cap=1, q_pos0=0, causal=0, scale=p["scale"])
+    if check:
+        k64, v64 = w.f64("k"), w.f64("v")
+        km_ref, _ = orc.block_summaries(k64, p["kv_block"], p["layout"])
+        rO, rL = np.zeros((B, Hq, R, D)), np.zeros((B, Hq, R))
+    stats = []
+    qprev = None
+    for s, (qs, kbs, vbs) in enumerate(zip(w.extra["q_steps"], w.extra["kb_steps"], w.extra["vb_steps"])):
+        where = f"{w.name} step {s}"
+        qd, kbd, vbd = to_dev(qs, "bf16"), to_dev(kbs, "bf16"), to_dev(vbs, "bf16")
+        if s == 0:
+            mask = None
+            cnt = torch.full((B, Hkv, 1), NB, dtype=torch.int32, device="cuda")
+            idx = torch.arange(NB, dtype=torch.int32, device="cuda").view(1, 1, 1, NB).repeat(B, Hkv, 1, 1)
+            cap = NB
+        else:
+            mask, _ = bsa.bsa_active_rows(qd, qprev, p["theta_act"])
+            idx, cnt, rp, cap = _select_raw(bsa, w, qd, kmean, row_mask=mask)
+        ap = bsa.attn_params(kv_block=p["kv_block"], q_block=R, cap=cap, q_pos0=p["q_pos0"], causal=0,
+                             scale=p["scale"])
+        bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap, row_mask=mask, o=cache_o, lse=cache_l)
+        # the fused block attention + merge, and the same from the general pieces (the block as a
+        # one-block sparse attention, then the state merge)
+        o32, l32 = bsa.bsa_block_attention_merge(qd, kbd, vbd, cache_o, cache_l, scale=p["scale"], o=_f32_out(qd))
+        o16, l16 = bsa.bsa_block_attention_merge(qd, kbd, vbd, cache_o, cache_l, scale=p["scale"],
+                                                 o=torch.empty_like(qd))
+        o_in, l_in = bsa.bsa_sparse_attention_fwd(qd, kbd, vbd, idx_in, cnt_in, ap_in, o=_f32_out(qd))
+        o32b, l32b = bsa.bsa_merge_attention_states(cache_o, cache_l, o_in, l_in, o=_f32_out(qd))
+        o_ip, l_ip = cache_o.clone(), cache_l.clone()
+        bsa.bsa_block_attention_merge(qd, kbd, vbd, o_ip, l_ip, scale=p["scale"], o=o_ip, lse=l_ip)
+        _sync()
+        assert torch.equal(o_ip, o32) and torch.equal(l_ip, l32), f"{w.name} step {s}: in-place merge differs"
+        n_act = R if mask is None else int(mask.sum().item())
+        stats.append(dict(active=n_act, list_blocks=cnt[0, :, 0].cpu().tolist()))
+        if check:
+            q64 = synth.storage_to_f64(qs, "bf16")
+            kb64, vb64 = synth.storage_to_f64(kbs, "bf16"), synth.storage_to_f64(vbs, "bf16")
+            if s == 0:
+                m_ref, lists = None, [[[np.arange(NB)] for _ in range(Hkv)] for _ in range(B)]
+            else:
+                m_ref, _ = orc.active_rows(q64, synth.storage_to_f64(w.extra["q_steps"][s - 1], "bf16"),
+                                           p["theta_act"])
+                assert np.array_equal(mask.cpu().numpy().astype(bool), m_ref), where
+                assert np.array_equal(np.nonzero(m_ref[0])[0], w.extra["changed"][s]), where
+                sel = orc.select_blocks(p, km_ref, q=q64, row_mask=m_ref)
+                idx_np, cnt_np, _ = _check_selection(sel, idx, cnt, rp, lambda qb: range(qb * R, (qb + 1) * R),
+                                                     where)
+                lists = _reference_lists(sel, idx_np, cnt_np)
+            O_ref, L_ref, rO, rL = orc.denoise_step(p, q64, k64, v64, kb64, vb64, lists, m_ref, rO, rL)
+            check_outputs(from_dev(o32), O_ref, l32.cpu().numpy(), L_ref, where)
+            check_outputs(from_dev(o32b), O_ref, l32b.cpu().numpy(), L_ref, where + " (general pieces)")
+            assert torch.equal(l16, l32)
+            _check_rounding(o16, o32)
+        qprev = qd
+    return stats
+
+
+def test_denoise_steps_small(bsa):
+    """Four steps over a 2152-token prefix (34 blocks, the last ragged)."""
+    w = synth.dlm_denoise_steps(L=2048 + 64 + 40, n_needles=2, n_steps=4)
+    st = _denoise_loop(bsa, w)
+    assert st[0]["active"] == 32 and all(x["active"] == 4 for x in st[1:])
+
+
+@pytest.mark.parametrize("R,Hq,Hkv", [(20, 16, 4), (16, 16, 2)])
+def test_denoise_steps_short_block(bsa, R, Hq, Hkv):
+    """Blocks of fewer rows than the block attention's 32 key lanes; group sizes 4 and 8."""
+    w = synth.dlm_denoise_steps(L=1024 + 7, R=R, Hq=Hq, Hkv=Hkv, n_needles=2, n_steps=3, per_step=3)
+    st = _denoise_loop(bsa, w)
+    assert all(x["active"] == 3 for x in st[1:])
+
+
+def test_denoise_steps_full_size(bsa):
+    """The benchmark's 32K prefix, first three steps (dense, then two sparse)."""
+    w = synth.dlm_denoise_steps(n_steps=3)
+    st = _denoise_loop(bsa, w)
+    assert all(max(x["list_blocks"]) < 512 for x in st[1:])
+
+
 def _prefill_case(bsa, w, sample_qb=None):
     p = w.params
     qd, kd, vd = _dev_workload(w)

@@ -303,6 +303,62 @@ def test_lse_merge_of_disjoint_halves():
     assert np.allclose(np.exp(l1 - L)[:, None] * O1 + np.exp(l2 - L)[:, None] * O2, O)
 
 
+def test_merge_states_is_softmax_over_the_union():
+    """merge_states of the states over two disjoint key sets equals one pass over
+    their union (scipy's logsumexp and softmax for the one pass), including an
+    empty side (LSE -inf, garbage O) and both sides empty."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((6, 16))
+    k = rng.standard_normal((300, 16))
+    v = rng.standard_normal((300, 16))
+    for na in (0, 1, 120, 300):
+        perm = rng.permutation(300)
+        A, Bs = np.sort(perm[:na]), np.sort(perm[na:])
+        Oa, La = orc.attend_tokens(q, k, v, A, 0.4)
+        Ob, Lb = orc.attend_tokens(q, k, v, Bs, 0.4)
+        if na == 0:
+            Oa = np.full_like(Oa, 7.0)                 # ignored: the set is empty
+        if na == 300:
+            Ob = np.full_like(Ob, np.nan)
+        O, L = orc.merge_states(Oa, La, Ob, Lb)
+        S = 0.4 * q @ k.T
+        assert np.allclose(L, logsumexp(S, axis=1), atol=1e-12)
+        assert np.allclose(O, softmax(S, axis=1) @ v, atol=1e-12)
+    O, L = orc.merge_states(np.ones((2, 4)), np.full(2, -np.inf), np.ones((2, 4)), np.full(2, -np.inf))
+    assert np.all(O == 0) and np.all(L == -np.inf)
+
+
+def test_denoise_first_step_is_dense_over_prefix_and_block():
+    """The dense first step (every prefix block listed, every row) plus the
+    block's own keys is the full softmax over [prefix; block] (scipy)."""
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, R, D, L, blk = 1, 4, 2, 8, 16, 200, 64
+    q = rng.standard_normal((B, Hq, R, D))
+    k, v = rng.standard_normal((B, Hkv, L, D)), rng.standard_normal((B, Hkv, L, D))
+    kb, vb = rng.standard_normal((B, Hkv, R, D)), rng.standard_normal((B, Hkv, R, D))
+    p = dict(kv_block=blk, q_block=R, q_pos0=L, causal=0, scale=0.25)
+    lists = [[[np.arange(-(-L // blk))] for _ in range(Hkv)]]
+    cO, cL = np.zeros((B, Hq, R, D)), np.zeros((B, Hq, R))
+    O, Lse, cO2, cL2 = orc.denoise_step(p, q, k, v, kb, vb, lists, None, cO, cL)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        kk, vv = np.concatenate([k[0, g], kb[0, g]]), np.concatenate([v[0, g], vb[0, g]])
+        S = 0.25 * q[0, h] @ kk.T
+        assert np.allclose(Lse[0, h], logsumexp(S, axis=1), atol=1e-12)
+        assert np.allclose(O[0, h], softmax(S, axis=1) @ vv, atol=1e-12)
+        Sp = 0.25 * q[0, h] @ k[0, g].T                # the cache holds the prefix part alone
+        assert np.allclose(cL2[0, h], logsumexp(Sp, axis=1), atol=1e-12)
+    # a later step where no row is active: the cache is kept as is, and each
+    # row is its cached prefix state merged with the new block part
+    kb2 = rng.standard_normal(kb.shape)
+    O3, L3, cO3, cL3 = orc.denoise_step(p, q, k, v, kb2, vb, lists, np.zeros((B, R), dtype=bool), cO2, cL2)
+    assert np.array_equal(cO3, cO2) and np.array_equal(cL3, cL2)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        S = 0.25 * q[0, h] @ np.concatenate([k[0, g], kb2[0, g]]).T
+        assert np.allclose(L3[0, h], logsumexp(S, axis=1), atol=1e-12)
+
+
 def test_causal_row_with_no_visible_key():
     q = np.ones((1, 4))
     O, lse = orc.attend_tokens(q, np.ones((4, 4)), np.ones((4, 4)), np.arange(2, 4), 1.0, np.array([1]))
