@@ -35,6 +35,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # skipped at 64K on the synthetic GQA decode workload.
 THRESH_DECODE_A = 0.4 * 65536
 THRESH_DECODE_SPLIT = 1024     # keys per split-KV slice
+WINDOW = 512                   # NSA sliding window (tokens) for the selection + window decode
 
 
 def log(msg):
@@ -175,7 +176,11 @@ def bench_decode(torch, bsa, synth, steps, warmup, flush):
         select()
         attend()
 
-    # capture one step in a HIP graph (warm up on a side stream first)
+    # Capture the step in a HIP graph (warm up on a side stream first).  A graph
+    # holds `inner` consecutive steps (as a model's decode graph holds its
+    # layers' steps back to back), inner dividing the step count so that
+    # exactly `steps` steps are timed; a graph of one step is timed too (it
+    # adds one graph launch per step).
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -183,21 +188,27 @@ def bench_decode(torch, bsa, synth, steps, warmup, flush):
             step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / steps
+    inner = next(d for d in (8, 4, 2, 1) if steps % d == 0)
+
+    def timed(n_inner):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_inner):
+                step()
+        for _ in range(max(1, warmup // n_inner)):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps // n_inner):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+    ms_per_step_single, _ = timed(1)
+    ms_per_step, wall = timed(inner)
     # per entry point, eager (warm: the same blocks every step, as in the replayed graph)
     reps = max(50, steps)
     t_sum = time_calls(torch, summarize, reps)
@@ -205,8 +216,30 @@ def bench_decode(torch, bsa, synth, steps, warmup, flush):
     t_att = time_calls(torch, attend, reps)
     t_att_cold = time_cold(torch, attend, 30, flush) if flush is not None else None
     sel_bytes = int(cnt.sum().item()) * p["kv_block"] * D * 2 * 2            # K and V of the selected blocks
-    return dict(ms_per_step=ms_per_step, wall_s=wall, sel_bytes=sel_bytes, t_sum=t_sum, t_sel=t_sel, t_att=t_att,
-                t_att_cold=t_att_cold, summary_bytes=Hkv * NB * D * 4, cnt=cnt.cpu().tolist(), workload=w)
+    # the same step with the sliding-window branch (NSA: w = 512) in the attention pass
+    W = WINDOW
+    ws_win = torch.zeros(bsa.bsa_window_decode_workspace_bytes(q, k, ap, W), dtype=torch.uint8, device="cuda")
+    lse2 = torch.empty((1, q.shape[1], 1, 2), dtype=torch.float32, device="cuda")
+
+    def attend_win():
+        bsa.bsa_window_decode_fwd(q, k, v, idx, cnt, ap, W, o=o, lse=lse2, workspace=ws_win)
+
+    def step_win():
+        summarize()
+        select()
+        attend_win()
+
+    t_step_win = time_graph(torch, step_win, max(20, steps // 8), inner=8)
+    t_att_win = time_calls(torch, attend_win, reps)
+    t_att_win_cold = time_cold(torch, attend_win, 30, flush) if flush is not None else None
+    win_bytes = sel_bytes + Hkv * W * D * 2 * 2
+    window = dict(window=W, us_per_step=round(t_step_win, 2), attention_us=round(t_att_win, 2),
+                  attention_us_cold=None if t_att_win_cold is None else round(t_att_win_cold, 2),
+                  tokens_per_group=int(cnt[0, 0, 0].item()) * p["kv_block"] + W, kv_bytes=win_bytes,
+                  gbs=round(win_bytes / (t_att_win * 1e3), 1))
+    return dict(ms_per_step=ms_per_step, ms_per_step_single=ms_per_step_single, steps_per_graph=inner, wall_s=wall,
+                sel_bytes=sel_bytes, t_sum=t_sum, t_sel=t_sel, t_att=t_att, t_att_cold=t_att_cold,
+                summary_bytes=Hkv * NB * D * 4, cnt=cnt.cpu().tolist(), workload=w, window=window)
 
 
 # -------------------------------------------------------------------- dlm ---
@@ -525,6 +558,8 @@ def main():
         log(f"decode: {1000 * d['ms_per_step']:.2f} us/step; attention {d['t_att']:.2f} us warm, "
             f"{d['t_att_cold']:.2f} us cold")
         result["decode"] = d
+        secondary["select_window_decode_64k"] = d["window"]
+        log(f"window decode: {d['window']}")
     if args.only in ("all", "tdecode"):
         secondary["threshold_decode_64k"] = bench_threshold_decode(
             torch, bsa, synth, reps, flush, result["decode"]["workload"] if "decode" in result else None)
@@ -552,7 +587,9 @@ def main():
         line.update(value=round(us, 3), ms_per_step=round(d["ms_per_step"], 5))
         line["config"] = {"workload": "gqa_decode_64k", "batch": 1, "q_heads": 32, "kv_heads": 8, "head_dim": 128,
                           "context": 65536, "kv_block": 64, "selected_blocks_per_group": 16,
-                          "step": "summary refresh + block selection + sparse attention (HIP graph replay)"}
+                          "step": "summary refresh + block selection + sparse attention (HIP graph replay)",
+                          "steps_per_graph": d["steps_per_graph"]}
+        line["us_per_step_one_step_graphs"] = round(1000 * d["ms_per_step_single"], 3)
         line["selected_kv_gbps"] = round(d["sel_bytes"] / (d["t_att"] * 1e3), 1)
         line["selected_kv_gbps_cold"] = round(d["sel_bytes"] / (d["t_att_cold"] * 1e3), 1)
         line["entry_point_us"] = {"bsa_build_block_summaries": round(d["t_sum"], 2),

@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["bsa_build_block_summaries", "bsa_select_blocks", "bsa_active_rows", "bsa_merge_attention_states",
-           "bsa_block_attention_merge",
+           "bsa_block_attention_merge", "bsa_window_decode_fwd", "bsa_window_decode_workspace_bytes",
            "bsa_sparse_attention_fwd",
            "bsa_threshold_attention_fwd", "bsa_threshold_decode_fwd", "bsa_select_workspace_bytes",
            "bsa_attention_workspace_bytes", "bsa_threshold_decode_workspace_bytes",
@@ -185,6 +185,30 @@ def bsa_sparse_attention_fwd(q, k, v, idx, cnt, p: BsaAttnParams, row_mask=None,
                                          cnt.data_ptr(), ctypes.byref(p), _ptr(row_mask), ctypes.byref(od),
                                          lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
           "bsa_sparse_attention_fwd")
+    return o, lse
+
+
+def bsa_window_decode_workspace_bytes(q, k, p: BsaAttnParams, window: int) -> int:
+    qd, kd = tensor_desc(q), tensor_desc(k)
+    return lib().bsa_window_decode_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(p), window)
+
+
+def bsa_window_decode_fwd(q, k, v, idx, cnt, p: BsaAttnParams, window: int, gates=None, o=None, lse=None,
+                          workspace=None):
+    """Returns (o, lse [B,Hq,Lq,2]): selected blocks and the sliding window, o = g_sel O_sel + g_win O_win."""
+    B, Hq, Lq, D = q.shape
+    if o is None:
+        o = torch.zeros_like(q)
+    if lse is None:
+        lse = torch.zeros((B, Hq, Lq, 2), dtype=torch.float32, device=q.device)
+    qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
+    need = bsa_window_decode_workspace_bytes(q, k, p, window)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    check(lib().bsa_window_decode_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),
+                                      cnt.data_ptr(), ctypes.byref(p), window, _ptr(gates), ctypes.byref(od),
+                                      lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
+          "bsa_window_decode_fwd")
     return o, lse
 
 

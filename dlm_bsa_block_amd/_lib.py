@@ -51,6 +51,9 @@ _SIGS = {
     "bsa_merge_attention_states": (c_int32, [_T, c_void_p, _T, c_void_p, _T, c_void_p, c_void_p]),
     "bsa_block_attention_merge": (c_int32, [_T, _T, _T, c_float, _T, c_void_p, _T, c_void_p, c_void_p]),
     "bsa_attention_workspace_bytes": (c_size_t, [_T, _T, POINTER(BsaAttnParams)]),
+    "bsa_window_decode_workspace_bytes": (c_size_t, [_T, _T, POINTER(BsaAttnParams), c_int32]),
+    "bsa_window_decode_fwd": (c_int32, [_T, _T, _T, c_void_p, c_void_p, POINTER(BsaAttnParams), c_int32, c_void_p,
+                                        _T, c_void_p, c_void_p, c_size_t, c_void_p]),
     "bsa_sparse_attention_fwd": (c_int32, [_T, _T, _T, c_void_p, c_void_p, POINTER(BsaAttnParams), c_void_p, _T,
                                            c_void_p, c_void_p, c_size_t, c_void_p]),
     "bsa_threshold_attention_fwd": (c_int32, [_T, _T, _T, POINTER(BsaThreshParams), _T, c_void_p, c_void_p,

@@ -233,6 +233,44 @@ bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, co
   return check_launch("sparse attention");
 }
 
+// ------------------------------------------------ selection + sliding window ---
+static bsa_status validate_window_decode(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                         const bsa_attn_params* p, int32_t window, AttnPlan& pl) {
+  bsa_status st = validate_attention(q, k, v, p, pl);
+  if (st != BSA_OK) return st;
+  if (pl.kind != 0) return fail(BSA_ERR_UNSUPPORTED, "the sliding window joins decode rows only (q_block = 1)");
+  if (window <= 0) return fail(BSA_ERR_INVALID, "window %d must be positive", window);
+  plan_attention(*q, *k, *p, pl, window);
+  return BSA_OK;
+}
+
+size_t bsa_window_decode_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, const bsa_attn_params* p,
+                                         int32_t window) {
+  AttnPlan pl;
+  if (!k || validate_window_decode(q, k, k, p, window, pl) != BSA_OK) return 0;
+  return pl.part_bytes;
+}
+
+bsa_status bsa_window_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const int32_t* idx,
+                                 const int32_t* cnt, const bsa_attn_params* p, int32_t window, const float* gates,
+                                 const bsa_tensor* o, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  AttnPlan pl;
+  bsa_status st = validate_window_decode(q, k, v, p, window, pl);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(o, "o", true)) != BSA_OK) return st;
+  if (!same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
+    return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
+  if (!idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "idx, cnt and lse are required");
+  if (!workspace || workspace_bytes < pl.part_bytes)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, pl.part_bytes);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  if (q->L == 0) { g_err[0] = 0; return BSA_OK; }
+  launch_attention(*q, *k, *v, idx, cnt, *p, pl, nullptr, *o, lse, workspace, static_cast<hipStream_t>(stream),
+                   window, gates);
+  return check_launch("selection + window decode");
+}
+
 // ----------------------------------------------------- threshold attention ---
 bsa_status bsa_threshold_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
                                        const bsa_thresh_params* p, const bsa_tensor* o, float* lse,

@@ -61,9 +61,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     for (int e = 0; e < 8; ++e) qx[h][e] *= a.c2;
   }
   const int64_t ntok = (int64_t)n_list * a.kv_block;
-  if (ntok == 0) return;                                // the combine writes O = 0, LSE = -inf
-  if (t_begin >= ntok) return;                          // no slice of the list for this workgroup
-  const int64_t t_end = min(ntok, t_begin + a.tok_per_item);
+  // With a sliding window (NSA structure section), the items after the list's
+  // own walk the row's window instead: the a.win keys ending at the row's
+  // position, key = key0 + t.  The combine merges the two runs of items apart.
+  int64_t t_lo = t_begin, t_end, key0 = -1;
+  const int sel_items = (int)((ntok + a.tok_per_item - 1) / a.tok_per_item);
+  if (a.win > 0 && item >= sel_items) {
+    const int64_t hi = min((int64_t)a.L, (int64_t)qpos + 1), lo = max((int64_t)0, hi - a.win);
+    t_lo = (int64_t)(item - sel_items) * a.tok_per_item;
+    if (t_lo >= hi - lo) return;                        // past the window
+    t_end = min(hi - lo, t_lo + a.tok_per_item);
+    key0 = lo;
+  } else {
+    if (ntok == 0) return;                              // the combine writes O = 0, LSE = -inf
+    if (t_begin >= ntok) return;                        // no slice of the list for this workgroup
+    t_end = min(ntok, t_begin + a.tok_per_item);
+  }
   float wm[G], wl[G], wacc[G][8];                       // this wave's running state
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -75,15 +88,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + d0) * ES;
   const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + d0) * ES;
 
-  for (int64_t c0 = t_begin; c0 < t_end; c0 += kDecTok) {
-    if (c0 != t_begin) load_blocks(c0);
+  for (int64_t c0 = t_lo; c0 < t_end; c0 += kDecTok) {
+    if (c0 != t_begin && key0 < 0) load_blocks(c0);
     int pos[PASSES];
     bool ok[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int64_t t = c0 + w * TPW + p * TPP + tg;
-      const int64_t key = (int64_t)blk[p] * a.kv_block + off[p];
-      ok[p] = t < t_end && blk[p] >= 0 && key < a.L && (!a.causal || key <= qpos);
+      const int64_t key = key0 >= 0 ? key0 + t : (int64_t)blk[p] * a.kv_block + off[p];
+      ok[p] = t < t_end && (key0 >= 0 || blk[p] >= 0) && key < a.L && (!a.causal || key <= qpos);
       pos[p] = ok[p] ? (int)key : 0;
     }
     float kx[PASSES][8], vx[PASSES][8];
@@ -210,33 +223,57 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
   const int64_t nunits = a.cnt ? (int64_t)a.cnt[li] * a.unit_num : (int64_t)a.items * a.unit_den;
   load_batch(0);
   const int nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
-  float M = -INFINITY, L = 0.f, acc = 0.f;
-  for (int it0 = 0; it0 < nvalid; it0 += BATCH) {
-    if (it0 > 0) load_batch(it0);
-    float bm = M;
+  // merge items [first, first + n) in order; the batch at `first` is loaded already
+  auto merge = [&](int first, int n, float& M, float& L, float& acc) __attribute__((always_inline)) {
+    M = -INFINITY;
+    L = 0.f;
+    acc = 0.f;
+    for (int it0 = 0; it0 < n; it0 += BATCH) {
+      if (it0 > 0) load_batch(first + it0);
+      float bm = M;
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u)
-      if (it0 + u < nvalid) bm = fmaxf(bm, mv[u]);
-    if (bm == -INFINITY) continue;                    // nothing visible so far
-    const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - bm);
-    L *= alpha;
-    acc *= alpha;
+      for (int u = 0; u < BATCH; ++u)
+        if (it0 + u < n) bm = fmaxf(bm, mv[u]);
+      if (bm == -INFINITY) continue;                  // nothing visible so far
+      const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+      L *= alpha;
+      acc *= alpha;
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      if (it0 + u < nvalid && mv[u] != -INFINITY) {
-        const float wgt = fast_exp2(mv[u] - bm);
-        L = fmaf(lv[u], wgt, L);
-        acc = fmaf(ov[u], wgt, acc);
+      for (int u = 0; u < BATCH; ++u) {
+        if (it0 + u < n && mv[u] != -INFINITY) {
+          const float wgt = fast_exp2(mv[u] - bm);
+          L = fmaf(lv[u], wgt, L);
+          acc = fmaf(ov[u], wgt, acc);
+        }
       }
+      M = bm;
     }
-    M = bm;
-  }
-  const float out = L > 0.f ? acc / L : 0.f;
+  };
+  float M, L, acc;
+  merge(0, nvalid, M, L, acc);
   const int h = g * G + hl;
   const int64_t oi = (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl + d;
+  float out = L > 0.f ? acc / L : 0.f;
+  if (a.win > 0) {
+    // the window's items follow the list's: O = g_sel O_sel + g_win O_win, one LSE per branch
+    const int64_t qpos = (int64_t)a.q_pos0 + row;
+    const int64_t hi = min((int64_t)a.L, qpos + 1), nwin = hi - max((int64_t)0, hi - a.win);
+    const int nw = (int)((nwin + a.unit_den - 1) / a.unit_den);
+    load_batch(nvalid);
+    float Mw, Lw, accw;
+    merge(nvalid, nw, Mw, Lw, accw);
+    const int64_t gi = (((int64_t)b * Hq + h) * a.Lq + row) * 2;
+    const float g0 = a.gates ? a.gates[gi] : 1.f, g1 = a.gates ? a.gates[gi + 1] : 1.f;
+    out = g0 * out + g1 * (Lw > 0.f ? accw / Lw : 0.f);
+    if (d == 0) {
+      a.lse[gi] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+      a.lse[gi + 1] = Lw > 0.f ? (Mw + log2f(Lw)) * kLn2 : -INFINITY;
+    }
+  } else if (d == 0) {
+    a.lse[((int64_t)b * Hq + h) * a.Lq + row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
   if (ODT == BSA_BF16) reinterpret_cast<uint16_t*>(a.o)[oi] = (uint16_t)f32_to_bf16(out);
   else reinterpret_cast<float*>(a.o)[oi] = out;
-  if (d == 0) a.lse[((int64_t)b * Hq + h) * a.Lq + row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Batches of 32: the first batch is loaded whatever the valid count (so it

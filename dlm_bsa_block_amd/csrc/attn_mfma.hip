@@ -554,7 +554,7 @@ void launch_gather(const GatherArgs& a, int kv_block, bool split, hipStream_t s)
 }
 
 // ------------------------------------------------------------------- host ---
-bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_params& p, AttnPlan& pl) {
+bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_params& p, AttnPlan& pl, int win) {
   pl.B = q.B;
   pl.Hq = q.H;
   pl.Hkv = k.H;
@@ -569,7 +569,7 @@ bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_par
     // slices of at least kDecMinSlice tokens (whole chunks), at most kDecMaxItems of them
     const int64_t per = std::max<int64_t>(kDecMinSlice / kDecTok, ceil_div(ceil_div(toks, kDecTok), kDecMaxItems));
     pl.tok_per_item = (int)(per * kDecTok);
-    pl.items = (int)ceil_div(toks, pl.tok_per_item);
+    pl.items = (int)ceil_div(toks, pl.tok_per_item) + (win > 0 ? (int)ceil_div(win, pl.tok_per_item) : 0);
     pl.qv = pl.G;
   } else if (p.q_block * pl.G <= 128 && p.q_block <= 64) {
     pl.kind = 2;
@@ -590,7 +590,7 @@ bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_par
 
 void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, const int32_t* idx,
                       const int32_t* cnt, const bsa_attn_params& p, const AttnPlan& pl, const uint8_t* row_mask,
-                      const bsa_tensor& o, float* lse, void* ws, hipStream_t s) {
+                      const bsa_tensor& o, float* lse, void* ws, hipStream_t s, int win, const float* gates) {
   const float c2 = p.scale * kLog2e;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = nullptr;
@@ -610,6 +610,7 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
     a.kv_block = p.kv_block; a.causal = p.causal; a.q_pos0 = p.q_pos0; a.Lq = pl.Lq; a.items = pl.items;
     a.tok_per_item = pl.tok_per_item;
     a.c2 = c2; a.row_mask = row_mask; a.part_o = part_o; a.part_ml = part_ml;
+    a.win = win;
     launch_decode(a, q.dtype, pl.D, pl.G, pl.B, s);
   } else {
     GatherArgs a;
@@ -634,6 +635,7 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
     c.qvc = 256 / pl.D;                          // one thread per (query vector, dim)
     c.Hkv = pl.Hkv; c.G = pl.G; c.NQB = pl.NQB; c.q_block = p.q_block; c.Lq = pl.Lq; c.D = pl.D; c.QV = pl.qv;
     c.row_mask = row_mask; c.o = o.data; c.osb = o.stride_b; c.osh = o.stride_h; c.osl = o.stride_l; c.lse = lse;
+    c.win = win; c.q_pos0 = p.q_pos0; c.L = pl.L; c.gates = gates;
     launch_combine(c, o.dtype, pl.B, s);
   }
 }

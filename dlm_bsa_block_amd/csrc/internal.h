@@ -75,10 +75,13 @@ struct AttnPlan {
   int qv;                   // query vectors per (b, g, q-block) in split mode
   size_t part_bytes;
 };
-bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_params& p, AttnPlan& pl);
+// win > 0 (decode only): a sliding window of win keys per row joins the list
+// (NSA sliding-window branch); gates [B][Hq][Lq][2] or null; lse then [B][Hq][Lq][2].
+bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_params& p, AttnPlan& pl, int win = 0);
 void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, const int32_t* idx,
                       const int32_t* cnt, const bsa_attn_params& p, const AttnPlan& pl, const uint8_t* row_mask,
-                      const bsa_tensor& o, float* lse, void* ws, hipStream_t s);
+                      const bsa_tensor& o, float* lse, void* ws, hipStream_t s, int win = 0,
+                      const float* gates = nullptr);
 
 bool plan_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, int kv_split, size_t& bytes);
 void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, float scale,

@@ -28,6 +28,7 @@ struct DecArgs {
   const uint8_t* row_mask;
   float* part_o;
   float* part_ml;
+  int win = 0;                    // > 0: items past the list's walk the win keys ending at the row
 };
 
 struct CombArgs {
@@ -40,7 +41,10 @@ struct CombArgs {
   const uint8_t* row_mask;
   void* o;
   int64_t osb, osh, osl;
-  float* lse;
+  float* lse;                     // [B][Hq][Lq], or [B][Hq][Lq][2] (list, window) when win > 0
+  int win = 0;                    // sliding window: its items follow the list's (decode only)
+  int q_pos0 = 0, L = 0;
+  const float* gates = nullptr;   // [B][Hq][Lq][2] branch gates, or null for 1 and 1
 };
 
 void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s);

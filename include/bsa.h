@@ -264,6 +264,30 @@ bsa_status bsa_threshold_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, co
                                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Selected blocks plus a sliding window in one decode pass (NSA structure
+ * section: parallel branches over the selected blocks and a sliding window of
+ * the newest w tokens, w = 512 on the page; the learned compression branch is
+ * not here).  Arguments as bsa_sparse_attention_fwd for decode rows
+ * (q_block = 1, any Lq rows, row r at position q_pos0 + r), no row mask, plus
+ * window w > 0: row r's window is the w keys ending at its position (fewer
+ * near the start).  Each branch is an exact softmax of its own; gates
+ * [B, Hq, Lq, 2] f32 (the branch weights a model's gate would give) or NULL
+ * for weights 1 and 1.  Writes o = g_sel O_sel + g_win O_win (q's dtype or
+ * f32) and lse [B, Hq, Lq, 2] (natural log of each branch's softmax
+ * denominator; -inf for an empty list).  K/V of the two branches stream in
+ * the same launch.  workspace: bsa_window_decode_workspace_bytes() bytes.
+ * Errors as bsa_sparse_attention_fwd; BSA_ERR_UNSUPPORTED for q_block > 1;
+ * BSA_ERR_INVALID for w <= 0.
+ * ------------------------------------------------------------------------ */
+size_t bsa_window_decode_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, const bsa_attn_params* p,
+                                         int32_t window);
+
+bsa_status bsa_window_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const int32_t* idx,
+                                 const int32_t* cnt, const bsa_attn_params* p, int32_t window, const float* gates,
+                                 const bsa_tensor* o, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Merge of two attention states over disjoint key sets (LoSA sec. 2: a stable
  * token of a denoising block reuses its cached prefix-attention output and
  * statistics; the full attention combines that state with the one over the

@@ -328,6 +328,35 @@ def sparse_attention(p: dict, q: np.ndarray, k: np.ndarray, v: np.ndarray, lists
     return O, LSE
 
 
+def window_decode(p: dict, q: np.ndarray, k: np.ndarray, v: np.ndarray, lists, window: int, gates=None):
+    """Selected blocks plus a sliding window ([NSA] structure section: parallel
+    branches over the selected blocks and a sliding window of w tokens, w = 512;
+    the compression branch needs learned weights and is left out).
+
+    Decode rows (q_block = 1): row r sits at position q_pos0 + r; its window is
+    the ``window`` keys ending there (fewer near the start).  Each branch is its
+    own exact softmax; READING: the branch outputs are summed with the given
+    gates [B, Hq, Lq, 2] (a model's gate values; 1 and 1 when None).
+    Returns O [B, Hq, Lq, D] and LSE [B, Hq, Lq, 2] (list branch, window branch).
+    """
+    B, Hq, Lq, D = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    O_sel, L_sel = sparse_attention(p, q, k, v, lists)
+    O_win = np.zeros_like(O_sel)
+    L_win = np.zeros_like(L_sel)
+    for b in range(B):
+        for h in range(Hq):
+            for r in range(Lq):
+                hi = min(L, p["q_pos0"] + r + 1)
+                toks = np.arange(max(0, hi - window), hi)
+                o, l = attend_tokens(q[b, h, [r]], k[b, h // G], v[b, h // G], toks, p["scale"])
+                O_win[b, h, r], L_win[b, h, r] = o[0], l[0]
+    g = np.ones((B, Hq, Lq, 2)) if gates is None else gates
+    O = g[..., 0:1] * O_sel + g[..., 1:2] * O_win
+    return O, np.stack([L_sel, L_win], axis=-1)
+
+
 # ------------------------------------------------------- locality pruning ---
 def active_rows(q_cur: np.ndarray, q_prev: np.ndarray, theta: float):
     """[LoSA] sec. 2, locality pruning: a row is active when the mean squared

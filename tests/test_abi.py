@@ -209,6 +209,21 @@ def test_block_attention_merge_rejects_bad_arguments(lib):
     assert call(_t(H=32, Lq=32, dtype=L.BSA_F32), _t(H=8, Lq=32, dtype=L.BSA_F32), o) == L.BSA_ERR_UNSUPPORTED
 
 
+def test_window_decode_rejects_bad_arguments(lib):
+    q, k = _t(H=32, Lq=1), _t(H=8, Lq=4096)
+    p = bsa.attn_params(kv_block=64, q_block=1, cap=16)
+    need = lib.bsa_window_decode_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(p), 512)
+    assert need > lib.bsa_attention_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(p)) > 0
+
+    def call(qq, pp, window, ws=need):
+        return lib.bsa_window_decode_fwd(ctypes.byref(qq), ctypes.byref(k), ctypes.byref(k), FAKE, FAKE,
+                                         ctypes.byref(pp), window, None, ctypes.byref(qq), FAKE, FAKE, ws, None)
+    assert call(q, p, 512, need - 1) == L.BSA_ERR_WORKSPACE
+    assert call(q, p, 0) == L.BSA_ERR_INVALID and "window" in _err(lib)
+    p32 = bsa.attn_params(kv_block=64, q_block=32, cap=16)
+    assert call(_t(H=32, Lq=32), p32, 512) == L.BSA_ERR_UNSUPPORTED and "decode" in _err(lib)
+
+
 def test_active_rows_rejects_mismatch(lib):
     a, b = _t(H=32, Lq=32), _t(H=32, Lq=31)
     st = lib.bsa_active_rows(ctypes.byref(a), ctypes.byref(b), 0.1, FAKE, None, None)

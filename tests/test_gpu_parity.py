@@ -193,6 +193,47 @@ def test_decode_select_everything_is_dense(bsa):
     assert (cnt == 32).all()
 
 
+def _window_case(bsa, w, window, with_gates=True):
+    """Selected blocks plus a sliding window of ``window`` keys in one pass,
+    against the oracle's two branches on the same lists (checked first)."""
+    p = w.params
+    qd, kd, vd = _dev_workload(w)
+    kmean, _ = bsa.bsa_build_block_summaries(kd, p["kv_block"], p["layout"])
+    idx, cnt, rp, cap = _select_raw(bsa, w, qd, kmean)
+    ap = bsa.attn_params(kv_block=p["kv_block"], q_block=1, cap=cap, q_pos0=p["q_pos0"], causal=p["causal"],
+                         scale=p["scale"])
+    B, Hq, Lq, _ = qd.shape
+    gates = None
+    if with_gates:
+        rng = np.random.default_rng(window)
+        gates = torch.from_numpy(rng.uniform(0.1, 1.2, (B, Hq, Lq, 2)).astype(np.float32)).cuda()
+    o32, lse = bsa.bsa_window_decode_fwd(qd, kd, vd, idx, cnt, ap, window, gates=gates, o=_f32_out(qd))
+    o16, lse16 = bsa.bsa_window_decode_fwd(qd, kd, vd, idx, cnt, ap, window, gates=gates, o=torch.empty_like(qd))
+    _sync()
+    _check_rounding(o16, o32)
+    assert torch.equal(lse, lse16)
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    km_ref, _ = orc.block_summaries(k, p["kv_block"], p["layout"])
+    sel = orc.select_blocks(p, km_ref, q=q)
+    idx_np, cnt_np, _ = _check_selection(sel, idx, cnt, rp, lambda qb: [qb], w.name)
+    g_np = None if gates is None else gates.cpu().numpy().astype(np.float64)
+    O_ref, L_ref = orc.window_decode(p, q, k, v, _reference_lists(sel, idx_np, cnt_np), window, g_np)
+    return check_outputs(from_dev(o32), O_ref, lse.cpu().numpy(), L_ref, f"{w.name} window {window}")
+
+
+@pytest.mark.parametrize("L,window,gates", [(4096 + 37, 512, True), (4096 + 37, 300, False), (700, 5000, True),
+                                            (2048, 64, True)])
+def test_window_decode_small(bsa, L, window, gates):
+    """Windows aligned and not to the blocks, longer than the prefix, one block long."""
+    w = synth.gqa_decode(L=L, n_needles=2)
+    _window_case(bsa, w, window, gates)
+
+
+def test_window_decode_full_size(bsa):
+    """64K decode with the page's window of 512 keys."""
+    _window_case(bsa, synth.gqa_decode(), 512)
+
+
 def _dlm_case(bsa, w, union_active: bool, full_check_rows=None):
     p = w.params
     qd, kd, vd = _dev_workload(w)

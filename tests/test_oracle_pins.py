@@ -359,6 +359,38 @@ def test_denoise_first_step_is_dense_over_prefix_and_block():
         assert np.allclose(L3[0, h], logsumexp(S, axis=1), atol=1e-12)
 
 
+def test_window_decode_branches():
+    """Selection + sliding window: the window branch is scipy's softmax over the
+    w keys ending at the row (clipped at the start); with w = L and gates
+    (0, 1) the result is dense attention; with gates (1, 0) it is the list
+    branch alone."""
+    rng = np.random.default_rng(14)
+    B, Hq, Hkv, Lq, D, L, blk = 1, 4, 2, 3, 16, 300, 64
+    q = rng.standard_normal((B, Hq, Lq, D))
+    k, v = rng.standard_normal((B, Hkv, L, D)), rng.standard_normal((B, Hkv, L, D))
+    p = dict(kv_block=blk, q_block=1, q_pos0=100, causal=1, scale=0.3)
+    lists = [[[np.array([0, 1]), np.array([1]), np.array([0])] for _ in range(Hkv)]]
+    gates = rng.uniform(0.2, 1.5, (B, Hq, Lq, 2))
+    O, LSE = orc.window_decode(p, q, k, v, lists, 40, gates)
+    O_sel, L_sel = orc.sparse_attention(p, q, k, v, lists)
+    for h in range(Hq):
+        g = h // 2
+        for r in range(Lq):
+            pos = 100 + r
+            S = 0.3 * k[0, g, pos - 39:pos + 1] @ q[0, h, r]
+            o_w = softmax(S) @ v[0, g, pos - 39:pos + 1]
+            assert np.isclose(LSE[0, h, r, 1], logsumexp(S))
+            assert np.allclose(O[0, h, r], gates[0, h, r, 0] * O_sel[0, h, r] + gates[0, h, r, 1] * o_w)
+    # a window longer than the prefix before the row is clipped at key 0
+    O2, L2 = orc.window_decode(p, q, k, v, lists, 5000, np.stack([np.zeros((B, Hq, Lq)), np.ones((B, Hq, Lq))], -1))
+    for h in range(Hq):
+        for r in range(Lq):
+            S = 0.3 * k[0, h // 2, :101 + r] @ q[0, h, r]
+            assert np.allclose(O2[0, h, r], softmax(S) @ v[0, h // 2, :101 + r])
+    O3, _ = orc.window_decode(p, q, k, v, lists, 7, np.stack([np.ones((B, Hq, Lq)), np.zeros((B, Hq, Lq))], -1))
+    assert np.allclose(O3, O_sel)
+
+
 def test_causal_row_with_no_visible_key():
     q = np.ones((1, 4))
     O, lse = orc.attend_tokens(q, np.ones((4, 4)), np.ones((4, 4)), np.arange(2, 4), 1.0, np.array([1]))
