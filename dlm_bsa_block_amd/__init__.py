@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = ["bsa_build_block_summaries", "bsa_select_blocks", "bsa_active_rows", "bsa_merge_attention_states",
            "bsa_block_attention_merge", "bsa_window_decode_fwd", "bsa_window_decode_workspace_bytes",
+           "bsa_token_select", "bsa_token_attention_fwd",
            "bsa_sparse_attention_fwd",
            "bsa_threshold_attention_fwd", "bsa_threshold_decode_fwd", "bsa_select_workspace_bytes",
            "bsa_attention_workspace_bytes", "bsa_threshold_decode_workspace_bytes",
@@ -209,6 +210,45 @@ def bsa_window_decode_fwd(q, k, v, idx, cnt, p: BsaAttnParams, window: int, gate
                                       cnt.data_ptr(), ctypes.byref(p), window, _ptr(gates), ctypes.byref(od),
                                       lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
           "bsa_window_decode_fwd")
+    return o, lse
+
+
+def bsa_token_select(q, k, fc_mask, budget: int, layout: int = BSA_ROPE_HALF, idx=None, cnt=None, workspace=None):
+    """Returns (idx [B,Hq,budget] int32 ascending, cnt [B,Hq] int32): each head's best tokens by q . k over
+    the frequency chunks marked in fc_mask [Hq, D/2] (uint8, on the device)."""
+    B, Hq = q.shape[:2]
+    if idx is None:
+        idx = torch.empty((B, Hq, budget), dtype=torch.int32, device=q.device)
+    if cnt is None:
+        cnt = torch.empty((B, Hq), dtype=torch.int32, device=q.device)
+    qd, kd = tensor_desc(q), tensor_desc(k)
+    need = lib().bsa_token_select_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    check(lib().bsa_token_select(ctypes.byref(qd), ctypes.byref(kd), fc_mask.data_ptr(), layout, budget,
+                                 idx.data_ptr(), cnt.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
+          "bsa_token_select")
+    return idx, cnt
+
+
+def bsa_token_attention_fwd(q, k, v, idx, cnt, scale=None, o=None, lse=None, workspace=None):
+    """Returns (o, lse): each query head over its own tokens (idx [B,Hq,Lq,cap] or [B,Hq,cap] for Lq = 1)."""
+    B, Hq, Lq, D = q.shape
+    cap = idx.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if o is None:
+        o = torch.zeros_like(q)
+    if lse is None:
+        lse = torch.zeros((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
+    need = lib().bsa_token_attention_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), cap)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    check(lib().bsa_token_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),
+                                        cnt.data_ptr(), cap, scale, ctypes.byref(od), lse.data_ptr(),
+                                        workspace.data_ptr(), workspace.numel(), _stream()),
+          "bsa_token_attention_fwd")
     return o, lse
 
 

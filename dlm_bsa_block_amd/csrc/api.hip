@@ -271,6 +271,83 @@ bsa_status bsa_window_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, const
   return check_launch("selection + window decode");
 }
 
+// ------------------------------------------------ token-level importance ---
+static bsa_status validate_token_select(const bsa_tensor* q, const bsa_tensor* k, const uint8_t* fc_mask,
+                                        int32_t layout, int32_t budget) {
+  bsa_status st = check_tensor(q, "q", false);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(k, "k", false)) != BSA_OK) return st;
+  if (q->dtype != k->dtype || q->B != k->B || q->D != k->D || q->H % k->H)
+    return fail(BSA_ERR_INVALID, "q/k shapes are incompatible");
+  if (q->L != 1) return fail(BSA_ERR_INVALID, "token selection takes one query row (q.L = %d)", q->L);
+  if (q->dtype != BSA_BF16 || q->D != 128) return fail(BSA_ERR_UNSUPPORTED, "token selection needs bf16, D = 128");
+  const int64_t G = q->H / k->H;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(BSA_ERR_UNSUPPORTED, "group size %d (supported: 1, 2, 4, 8)", (int)G);
+  if (k->L > 65536) return fail(BSA_ERR_UNSUPPORTED, "L = %d > 65536 keys", (int)k->L);
+  if (layout != BSA_ROPE_HALF && layout != BSA_ROPE_INTERLEAVED) return fail(BSA_ERR_INVALID, "layout %d", layout);
+  if (!fc_mask) return fail(BSA_ERR_INVALID, "fc_mask is required");
+  if (budget <= 0) return fail(BSA_ERR_INVALID, "budget %d must be positive", budget);
+  return BSA_OK;
+}
+
+size_t bsa_token_select_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k) {
+  if (!q || !k || q->H <= 0 || k->H <= 0 || k->L <= 0) return 0;
+  return token_select_workspace(*q, *k);
+}
+
+bsa_status bsa_token_select(const bsa_tensor* q, const bsa_tensor* k, const uint8_t* fc_mask, int32_t layout,
+                            int32_t budget, int32_t* idx, int32_t* cnt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  bsa_status st = validate_token_select(q, k, fc_mask, layout, budget);
+  if (st != BSA_OK) return st;
+  if (!idx || !cnt) return fail(BSA_ERR_INVALID, "idx and cnt are required");
+  const size_t need = token_select_workspace(*q, *k);
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  launch_token_select(*q, *k, fc_mask, layout, budget, idx, cnt, nullptr, workspace, static_cast<hipStream_t>(stream));
+  return check_launch("token selection");
+}
+
+static bsa_status validate_token_attention(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, int32_t cap,
+                                           float scale) {
+  bsa_status st = check_tensor(q, "q", false);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(k, "k", false)) != BSA_OK) return st;
+  if ((st = check_tensor(v, "v", false)) != BSA_OK) return st;
+  if (!same_shape(k, v)) return fail(BSA_ERR_INVALID, "k and v differ in shape or dtype");
+  if (q->dtype != k->dtype || q->B != k->B || q->D != k->D || q->H % k->H)
+    return fail(BSA_ERR_INVALID, "q/k shapes are incompatible");
+  if (cap <= 0) return fail(BSA_ERR_INVALID, "cap %d must be positive", cap);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(BSA_ERR_INVALID, "scale must be finite and > 0");
+  return BSA_OK;
+}
+
+size_t bsa_token_attention_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, int32_t cap) {
+  if (!q || !k || q->H <= 0 || k->H <= 0 || cap <= 0) return 0;
+  AttnPlan pl;
+  plan_token_attention(*q, *k, cap, pl);
+  return pl.part_bytes;
+}
+
+bsa_status bsa_token_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const int32_t* idx,
+                                   const int32_t* cnt, int32_t cap, float scale, const bsa_tensor* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  bsa_status st = validate_token_attention(q, k, v, cap, scale);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(o, "o", false)) != BSA_OK) return st;
+  if (!same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
+    return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
+  if (!idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "idx, cnt and lse are required");
+  AttnPlan pl;
+  plan_token_attention(*q, *k, cap, pl);
+  if (!workspace || workspace_bytes < pl.part_bytes)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, pl.part_bytes);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  launch_token_attention(*q, *k, *v, idx, cnt, cap, scale, pl, *o, lse, workspace, static_cast<hipStream_t>(stream));
+  return check_launch("token attention");
+}
+
 // ----------------------------------------------------- threshold attention ---
 bsa_status bsa_threshold_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
                                        const bsa_thresh_params* p, const bsa_tensor* o, float* lse,

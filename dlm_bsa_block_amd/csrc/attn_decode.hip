@@ -85,8 +85,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) wacc[h][e] = 0.f;
   }
-  const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + d0) * ES;
-  const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + d0) * ES;
+  const int gk = g / a.kv_div;                          // the K/V head of this list
+  const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)gk * a.ksh + d0) * ES;
+  const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)gk * a.vsh + d0) * ES;
 
   for (int64_t c0 = t_lo; c0 < t_end; c0 += kDecTok) {
     if (c0 != t_begin && key0 < 0) load_blocks(c0);

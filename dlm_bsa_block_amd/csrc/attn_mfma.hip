@@ -588,6 +588,48 @@ bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_par
   return true;
 }
 
+// Attention of each query head over its own token list (FASA technical summary
+// sec. 2, focused attention: all dims, original positions): the decode split
+// with one list per query head (G = 1 per list, blocks of one token), the K/V
+// head found by dividing the list's head by the group size.
+void plan_token_attention(const bsa_tensor& q, const bsa_tensor& k, int cap, AttnPlan& pl) {
+  pl.kind = 0;
+  pl.B = q.B; pl.Hq = q.H; pl.Hkv = q.H; pl.G = 1; pl.D = q.D; pl.Lq = q.L; pl.L = k.L; pl.NQB = q.L;
+  const int64_t per = std::max<int64_t>(kDecMinSlice / kDecTok, ceil_div(ceil_div(cap, kDecTok), kDecMaxItems));
+  pl.tok_per_item = (int)(per * kDecTok);
+  pl.items = (int)ceil_div(cap, pl.tok_per_item);
+  pl.qv = 1;
+  const size_t n = (size_t)pl.B * pl.Hkv * pl.NQB * pl.items * pl.qv;
+  pl.part_bytes = align256(n * pl.D * 4) + align256(n * 2 * 4);
+}
+
+void launch_token_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, const int32_t* idx,
+                            const int32_t* cnt, int cap, float scale, const AttnPlan& pl, const bsa_tensor& o,
+                            float* lse, void* ws, hipStream_t s) {
+  const size_t n = (size_t)pl.B * pl.Hkv * pl.NQB * pl.items * pl.qv;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(n * pl.D * 4));
+  DecArgs a;
+  a.q = static_cast<const uint8_t*>(q.data);
+  a.k = static_cast<const uint8_t*>(k.data);
+  a.v = static_cast<const uint8_t*>(v.data);
+  a.qsb = q.stride_b; a.qsh = q.stride_h; a.qsl = q.stride_l;
+  a.ksb = k.stride_b; a.ksh = k.stride_h; a.ksl = k.stride_l;
+  a.vsb = v.stride_b; a.vsh = v.stride_h; a.vsl = v.stride_l;
+  a.idx = idx; a.cnt = cnt; a.cap = cap; a.NQB = pl.NQB; a.Hkv = pl.Hkv; a.L = pl.L;
+  a.kv_block = 1; a.causal = 0; a.q_pos0 = 0; a.Lq = pl.Lq; a.items = pl.items; a.tok_per_item = pl.tok_per_item;
+  a.c2 = scale * kLog2e; a.row_mask = nullptr; a.part_o = part_o; a.part_ml = part_ml;
+  a.kv_div = (int)(q.H / k.H);
+  launch_decode(a, q.dtype, pl.D, 1, pl.B, s);
+  CombArgs c;
+  c.part_o = part_o; c.part_ml = part_ml; c.cnt = cnt; c.items = pl.items;
+  c.unit_num = 1; c.unit_den = pl.tok_per_item;
+  c.qvc = 256 / pl.D;
+  c.Hkv = pl.Hkv; c.G = 1; c.NQB = pl.NQB; c.q_block = 1; c.Lq = pl.Lq; c.D = pl.D; c.QV = 1;
+  c.row_mask = nullptr; c.o = o.data; c.osb = o.stride_b; c.osh = o.stride_h; c.osl = o.stride_l; c.lse = lse;
+  launch_combine(c, o.dtype, pl.B, s);
+}
+
 void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, const int32_t* idx,
                       const int32_t* cnt, const bsa_attn_params& p, const AttnPlan& pl, const uint8_t* row_mask,
                       const bsa_tensor& o, float* lse, void* ws, hipStream_t s, int win, const float* gates) {

@@ -83,6 +83,17 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
                       const bsa_tensor& o, float* lse, void* ws, hipStream_t s, int win = 0,
                       const float* gates = nullptr);
 
+// Token importance on a subset of frequency chunks, top-N tokens per query head, and the
+// attention of each head over its own token list.
+size_t token_select_workspace(const bsa_tensor& q, const bsa_tensor& k);
+void launch_token_select(const bsa_tensor& q, const bsa_tensor& k, const uint8_t* fc_mask, int layout, int budget,
+                         int32_t* idx, int32_t* cnt, float* scores_out, void* ws, hipStream_t s);
+void plan_token_attention(const bsa_tensor& q, const bsa_tensor& k, int cap, AttnPlan& pl);
+void launch_token_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, const int32_t* idx,
+                            const int32_t* cnt, int cap, float scale, const AttnPlan& pl, const bsa_tensor& o,
+                            float* lse, void* ws, hipStream_t s);
+
+
 bool plan_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, int kv_split, size_t& bytes);
 void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, float scale,
                              float lambda, int kv_split, const bsa_tensor& o, float* lse, int32_t* kept,

@@ -29,6 +29,7 @@ struct DecArgs {
   float* part_o;
   float* part_ml;
   int win = 0;                    // > 0: items past the list's walk the win keys ending at the row
+  int kv_div = 1;                 // lists per K/V head (per-query-head token lists: the group size)
 };
 
 struct CombArgs {

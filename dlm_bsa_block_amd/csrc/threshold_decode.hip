@@ -47,6 +47,8 @@ struct TDecArgs {
   int32_t* part_cnt;                    // [B][Hkv][nchunk][G] kept tiles
   int32_t* kept;                        // [B][Hq] kept tiles per head, or null
   uint8_t* keep_map;                    // [B][Hq][ntiles] or null
+  const uint8_t* fc_mask;               // token scoring: [Hq][64] frequency chunks in use (D = 128), or null
+  int layout;                           // RoPE layout naming the two dims of each chunk
   void* o;                              // [B][Hq][1][D], bf16 or f32
   int64_t osb, osh;
   float* lse;                           // [B][Hq][1]
@@ -82,6 +84,17 @@ __global__ __launch_bounds__(512) void tdec_scores_kernel(TDecArgs a) {
     if (col < G)
       v4 = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.qsb + (int64_t)(g * G + col) * a.qsh +
                                                   32 * ks + 8 * kq) * 2);
+    if (a.fc_mask && col < G) {
+      // token scoring on a subset of frequency chunks: zero the query dims of the other chunks
+      const uint8_t* fm = a.fc_mask + (int64_t)(g * G + col) * 64;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 32 * ks + 8 * kq + 2 * e;             // dims d, d + 1 of word e
+        const int f0 = a.layout == BSA_ROPE_HALF ? (d & 63) : (d >> 1);
+        const int f1 = a.layout == BSA_ROPE_HALF ? ((d + 1) & 63) : (d >> 1);
+        v4[e] &= (fm[f0] ? 0x0000FFFFu : 0u) | (fm[f1] ? 0xFFFF0000u : 0u);
+      }
+    }
     qb[ks] = __builtin_bit_cast(bf16x8, v4);
   }
   const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + (int64_t)s0 * a.ksl) * 2;
@@ -544,6 +557,8 @@ void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa
   a.smax = reinterpret_cast<float*>(p);
   a.kept = kept;
   a.keep_map = keep_map;
+  a.fc_mask = nullptr;
+  a.layout = 0;
   a.o = o.data; a.osb = o.stride_b; a.osh = o.stride_h;
   a.lse = lse;
   const dim3 gs(a.nsplit, q.B * k.H), gp(a.nchunk, q.B * k.H);
@@ -559,6 +574,172 @@ void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa
 #undef BSA_TDEC
   if (o.dtype == BSA_BF16) hipLaunchKernelGGL(tdec_combine_kernel<BSA_BF16>, dim3(q.B * q.H), dim3(512), 0, s, a);
   else hipLaunchKernelGGL(tdec_combine_kernel<BSA_F32>, dim3(q.B * q.H), dim3(512), 0, s, a);
+}
+
+// ----------------------------------------------------------------------------
+// Token importance on a subset of frequency chunks (FASA technical summary
+// sec. 2, token importance prediction: q.k over the dims of a head's dominant
+// chunks only) and the top-N tokens of each head.
+//
+// Scores come from the scores kernel above with the other chunks' query dims
+// zeroed.  The top N of a head's L scores (ties to the lower token) come from
+// one workgroup of 1024 threads holding 64 scores each (32 in registers, 32
+// in LDS): four
+// 8-bit radix passes on order-preserving keys (per-wave LDS histograms, one
+// wave scans the 256 bins) find the N-th key, then two block scans place the
+// chosen tokens in ascending order.
+constexpr int kTokThreads = 1024, kTokPer = 64;     // L <= 65536
+
+__global__ __launch_bounds__(1024) void token_topk_kernel(const float* __restrict__ scores, int Lpad, int L, int N,
+                                                          int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
+  constexpr int NT = kTokThreads, NW = NT / 64, PER = kTokPer, PR = PER / 2;   // PR keys in registers
+  __shared__ uint32_t kl[PER - PR][NT];            // the other keys, [e][thread]: conflict-free
+  __shared__ uint32_t hist[NW][256];
+  __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t sel_digit, sel_above;
+  const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const float* sr = scores + (int64_t)row * Lpad;
+  const int t0 = tid * PER;
+  uint32_t key[PR];
+  const int lim = L - t0;                            // this thread's token e is in the row iff e < lim
+  auto to_key = [&](float x, int e) __attribute__((always_inline)) {
+    const uint32_t u = __float_as_uint(x);
+    // order-preserving: larger float, larger key; 0 is below every score (and marks tokens >= L)
+    return e < lim ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
+  };
+#pragma unroll
+  for (int c = 0; c < PER / 4; ++c) {
+    const int t = t0 + 4 * c;
+    // clamped, so every load is in the row (keys past L are set to 0 below)
+    const f32x4 x = *reinterpret_cast<const f32x4*>(sr + min(t, Lpad - 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ei = 4 * c + e;
+      if (ei < PR) key[ei] = to_key(x[e], ei);
+      else kl[ei - PR][tid] = to_key(x[e], ei);
+    }
+  }
+  auto key_at = [&](int e) __attribute__((always_inline)) { return e < PR ? key[e] : kl[e - PR][tid]; };
+  const int Ne = min(N, L);
+  uint32_t prefix = 0u, mask = 0u, need = (uint32_t)Ne;
+  // block-wide exclusive scan of one value per thread (wave scans + wave totals)
+  auto block_excl = [&](uint32_t v) __attribute__((always_inline)) {
+    const uint32_t inc = wave_incl_scan_dpp(v);
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    uint32_t before = 0u;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww)
+      if (ww < w) before += wsum[ww];
+    __syncthreads();
+    return before + inc - v;
+  };
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < NW * 256 / NT; ++i) (&hist[0][0])[tid + NT * i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const uint32_t kk = key_at(e);
+      if ((kk & mask) == prefix) atomicAdd(&hist[w][(kk >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (w == 0) {
+      // lane l holds digits 255 - 4l - j (j = 0..3): descending digits across the wave
+      uint32_t c[4], sum = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int dg = 255 - 4 * lane - j;
+        c[j] = 0u;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) c[j] += hist[ww][dg];
+        sum += c[j];
+      }
+      uint32_t before = wave_incl_scan_dpp(sum) - sum;       // keys with larger digits
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (before < need && need <= before + c[j]) {
+          sel_digit = (uint32_t)(255 - 4 * lane - j);
+          sel_above = before;
+        }
+        before += c[j];
+      }
+    }
+    __syncthreads();
+    prefix |= sel_digit << shift;
+    mask |= 0xFFu << shift;
+    need -= sel_above;
+    __syncthreads();                                 // sel_* are rewritten by the next pass
+  }
+  // prefix is the N-th largest key; take every larger key and the first `need` ties
+  uint32_t n_gt = 0u, n_eq = 0u;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const uint32_t kk = key_at(e);
+    n_gt += kk > prefix;
+    n_eq += kk == prefix;
+  }
+  const uint32_t eq_before = block_excl(n_eq);
+  const uint32_t take = need > eq_before ? min(need - eq_before, n_eq) : 0u;
+  uint32_t pos = block_excl(n_gt + take);
+  int32_t* out = idx + (int64_t)row * N;
+  uint32_t taken = 0u;
+  int tok = t0;
+  asm volatile("" : "+v"(tok));                      // one running token index, not 64 precomputed ones
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const uint32_t kk = key_at(e);
+    const bool eq = kk == prefix && taken < take;
+    if (kk > prefix || eq) out[pos++] = tok;
+    taken += eq;
+    ++tok;
+  }
+  if (tid == 0) cnt[row] = Ne;
+}
+
+static size_t tok_sizes(const bsa_tensor& q, const bsa_tensor& k, size_t (&sz)[3]) {
+  const size_t heads = (size_t)q.B * q.H;
+  sz[0] = align256(heads * ((k.L + 3) & ~3LL) * 4);                 // scores
+  sz[1] = align256(heads * ceil_div(k.L, kTDecTile) * 4);           // tile maxima (written, unused)
+  sz[2] = align256(heads * ceil_div(k.L, kTDecMaxSplit) * 4);       // slice maxima (written, unused)
+  return sz[0] + sz[1] + sz[2];
+}
+
+size_t token_select_workspace(const bsa_tensor& q, const bsa_tensor& k) {
+  size_t sz[3];
+  return tok_sizes(q, k, sz);
+}
+
+void launch_token_select(const bsa_tensor& q, const bsa_tensor& k, const uint8_t* fc_mask, int layout, int budget,
+                         int32_t* idx, int32_t* cnt, float* scores_out, void* ws, hipStream_t s) {
+  const int G = (int)(q.H / k.H);
+  TDecArgs a{};
+  a.q = static_cast<const uint8_t*>(q.data);
+  a.k = static_cast<const uint8_t*>(k.data);
+  a.qsb = q.stride_b; a.qsh = q.stride_h;
+  a.ksb = k.stride_b; a.ksh = k.stride_h; a.ksl = k.stride_l;
+  a.Hkv = (int)k.H; a.G = G; a.L = (int)k.L; a.Lpad = (int)((k.L + 3) & ~3LL); a.split = kTDecMaxSplit;
+  a.nsplit = (int)ceil_div(k.L, kTDecMaxSplit);
+  a.ntiles = (int)ceil_div(k.L, kTDecTile);
+  a.c2 = 1.f;                                        // plain q.k
+  size_t sz[3];
+  tok_sizes(q, k, sz);
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  a.scores = scores_out ? scores_out : reinterpret_cast<float*>(p);
+  a.tmax = reinterpret_cast<float*>(p + sz[0]);
+  a.smax = reinterpret_cast<float*>(p + sz[0] + sz[1]);
+  a.fc_mask = fc_mask;
+  a.layout = layout;
+  const dim3 gs(a.nsplit, q.B * k.H);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(tdec_scores_kernel<1>, gs, dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(tdec_scores_kernel<2>, gs, dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(tdec_scores_kernel<4>, gs, dim3(512), 0, s, a); break;
+    default: hipLaunchKernelGGL(tdec_scores_kernel<8>, gs, dim3(512), 0, s, a); break;
+  }
+  hipLaunchKernelGGL(token_topk_kernel, dim3(q.B * q.H), dim3(kTokThreads), 0, s, a.scores, a.Lpad, a.L, budget,
+                     idx, cnt);
 }
 
 }  // namespace bsa

@@ -288,6 +288,43 @@ bsa_status bsa_window_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, const
                                  void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Token importance on a caller-given set of frequency chunks (FASA sec. 2,
+ * token importance prediction; the offline calibration that finds a head's
+ * dominant chunks is not here).  q [B, Hq, 1, D], k [B, Hkv, L, D], bf16,
+ * D = 128, Hq / Hkv in {1, 2, 4, 8}, L <= 65536.  fc_mask [Hq, D/2] uint8
+ * (device): 1 marks a chunk whose two dims (i, i + D/2 for BSA_ROPE_HALF;
+ * 2i, 2i + 1 for BSA_ROPE_INTERLEAVED) count.  Each head's score of token t
+ * is q . k_t over the marked dims only; idx [B, Hq, budget] int32 gets the
+ * min(budget, L) best tokens in ascending order (ties: lower token first),
+ * cnt [B, Hq] their number.  workspace: bsa_token_select_workspace_bytes()
+ * bytes, no initial contents.  Errors: BSA_ERR_INVALID for shapes, layout,
+ * a null mask or output, budget <= 0 or a misaligned workspace;
+ * BSA_ERR_UNSUPPORTED outside the supported set; BSA_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------ */
+size_t bsa_token_select_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k);
+
+bsa_status bsa_token_select(const bsa_tensor* q, const bsa_tensor* k, const uint8_t* fc_mask, int32_t layout,
+                            int32_t budget, int32_t* idx, int32_t* cnt, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Attention of every query head over its own token list (FASA sec. 2,
+ * focused attention: all dims, tokens at their original positions).  q
+ * [B, Hq, Lq, D], k/v [B, Hkv, L, D] (bf16 or f32, D 64 or 128), idx
+ * [B, Hq, Lq, cap] int32 token indices < L (any order, no repeats) and cnt
+ * [B, Hq, Lq] their number (<= cap): the layout bsa_token_select writes for
+ * Lq = 1.  Writes o (q's dtype or f32) and lse [B, Hq, Lq] (natural log;
+ * -inf and O = 0 for an empty list).  workspace:
+ * bsa_token_attention_workspace_bytes() bytes.  Errors as
+ * bsa_sparse_attention_fwd.
+ * ------------------------------------------------------------------------ */
+size_t bsa_token_attention_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, int32_t cap);
+
+bsa_status bsa_token_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const int32_t* idx,
+                                   const int32_t* cnt, int32_t cap, float scale, const bsa_tensor* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Merge of two attention states over disjoint key sets (LoSA sec. 2: a stable
  * token of a denoising block reuses its cached prefix-attention output and
  * statistics; the full attention combines that state with the one over the

@@ -357,6 +357,53 @@ def window_decode(p: dict, q: np.ndarray, k: np.ndarray, v: np.ndarray, lists, w
     return O, np.stack([L_sel, L_win], axis=-1)
 
 
+# ------------------------------------------------- token-level importance ---
+def fc_dims(f: int, D: int, layout: int) -> np.ndarray:
+    """The two dims of frequency chunk f ([FASA] sec. 2: RoPE rotates each
+    chunk's pair of dims together): (f, f + D/2) in the rotate-half layout,
+    (2f, 2f + 1) in the interleaved one."""
+    return np.array([f, f + D // 2]) if layout == ROPE_HALF else np.array([2 * f, 2 * f + 1])
+
+
+def token_scores(q: np.ndarray, k: np.ndarray, fc_mask: np.ndarray, layout: int) -> np.ndarray:
+    """[FASA] sec. 2, token importance prediction: each head scores every token
+    by q . k over the dims of its dominant chunks only (fc_mask [Hq, D/2],
+    given; the offline calibration that picks them is out of scope).
+    q [B, Hq, 1, D], k [B, Hkv, L, D] -> scores [B, Hq, L]."""
+    B, Hq, _, D = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    S = np.zeros((B, Hq, L))
+    for h in range(Hq):
+        fs = np.nonzero(fc_mask[h])[0]
+        dims = np.concatenate([fc_dims(f, D, layout) for f in fs]) if len(fs) else np.zeros(0, dtype=np.int64)
+        for b in range(B):
+            S[b, h] = k[b, h // G][:, dims] @ q[b, h, 0, dims]
+    return S
+
+
+def top_tokens(s: np.ndarray, budget: int):
+    """The min(budget, L) best tokens of one head by score, ties to the lower
+    token, in ascending token order; also the score of the last one taken."""
+    n = min(budget, len(s))
+    order = sorted(range(len(s)), key=lambda t: (-s[t], t))[:n]
+    return np.sort(np.array(order, dtype=np.int64)), s[order[-1]]
+
+
+def token_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, lists, scale: float):
+    """[FASA] sec. 2, focused attention: each head attends with all dims to its
+    own tokens at their original positions.  lists[b][h] -> token array.
+    Returns O [B, Hq, 1, D], LSE [B, Hq, 1]."""
+    B, Hq, _, D = q.shape
+    G = Hq // k.shape[1]
+    O = np.zeros((B, Hq, 1, v.shape[3]))
+    LSE = np.zeros((B, Hq, 1))
+    for b in range(B):
+        for h in range(Hq):
+            O[b, h], LSE[b, h] = attend_tokens(q[b, h], k[b, h // G], v[b, h // G], np.asarray(lists[b][h]), scale)
+    return O, LSE
+
+
 # ------------------------------------------------------- locality pruning ---
 def active_rows(q_cur: np.ndarray, q_prev: np.ndarray, theta: float):
     """[LoSA] sec. 2, locality pruning: a row is active when the mean squared

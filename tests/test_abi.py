@@ -224,6 +224,33 @@ def test_window_decode_rejects_bad_arguments(lib):
     assert call(_t(H=32, Lq=32), p32, 512) == L.BSA_ERR_UNSUPPORTED and "decode" in _err(lib)
 
 
+def test_token_select_and_attention_reject_bad_arguments(lib):
+    q, k = _t(H=32, Lq=1), _t(H=8, Lq=4096)
+    need = lib.bsa_token_select_workspace_bytes(ctypes.byref(q), ctypes.byref(k))
+    assert need >= 32 * 4096 * 4
+
+    def sel(qq, kk, mask=FAKE, layout=0, budget=256, ws=need):
+        return lib.bsa_token_select(ctypes.byref(qq), ctypes.byref(kk), mask, layout, budget, FAKE, FAKE, FAKE, ws,
+                                    None)
+    assert sel(q, k, ws=need - 1) == L.BSA_ERR_WORKSPACE
+    assert sel(q, k, mask=None) == L.BSA_ERR_INVALID and "fc_mask" in _err(lib)
+    assert sel(q, k, layout=2) == L.BSA_ERR_INVALID
+    assert sel(q, k, budget=0) == L.BSA_ERR_INVALID and "budget" in _err(lib)
+    assert sel(q, _t(H=8, Lq=65537)) == L.BSA_ERR_UNSUPPORTED
+    assert sel(_t(H=32, Lq=2), k) == L.BSA_ERR_INVALID and "one query row" in _err(lib)
+    assert sel(_t(H=32, Lq=1, D=64), _t(H=8, Lq=4096, D=64)) == L.BSA_ERR_UNSUPPORTED
+    wa = lib.bsa_token_attention_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 256)
+    assert wa > 0
+
+    def att(cap=256, scale=0.088, ws=wa, o=q):
+        return lib.bsa_token_attention_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), FAKE, FAKE, cap, scale,
+                                           ctypes.byref(o), FAKE, FAKE, ws, None)
+    assert att(ws=wa - 1) == L.BSA_ERR_WORKSPACE
+    assert att(cap=0) == L.BSA_ERR_INVALID
+    assert att(scale=float("inf")) == L.BSA_ERR_INVALID
+    assert att(o=_t(H=32, Lq=2)) == L.BSA_ERR_INVALID and "o must match" in _err(lib)
+
+
 def test_active_rows_rejects_mismatch(lib):
     a, b = _t(H=32, Lq=32), _t(H=32, Lq=31)
     st = lib.bsa_active_rows(ctypes.byref(a), ctypes.byref(b), 0.1, FAKE, None, None)

@@ -234,6 +234,71 @@ def test_window_decode_full_size(bsa):
     _window_case(bsa, synth.gqa_decode(), 512)
 
 
+TOKEN_EPS = 1e-4        # |score - N-th score| within this: either choice is correct (fp32 vs fp64 sums)
+
+
+def _fc_mask(Hq, n_fc, seed):
+    rng = np.random.default_rng(seed)
+    m = np.zeros((Hq, 64), dtype=np.uint8)
+    for h in range(Hq):
+        m[h, rng.choice(64, n_fc, replace=False)] = 1
+    return m
+
+
+def _token_case(bsa, w, budget, n_fc, layout, seed=0):
+    """Token scores on a subset of frequency chunks, top-N per head, then each
+    head's attention over its own tokens, against the oracle."""
+    p = w.params
+    qd, kd, vd = _dev_workload(w)
+    B, Hq = qd.shape[:2]
+    L = kd.shape[2]
+    mask = _fc_mask(Hq, n_fc, seed)
+    idx, cnt = bsa.bsa_token_select(qd, kd, torch.from_numpy(mask).cuda(), budget, layout=layout)
+    o32, lse = bsa.bsa_token_attention_fwd(qd, kd, vd, idx, cnt, scale=p["scale"], o=_f32_out(qd))
+    o16, lse16 = bsa.bsa_token_attention_fwd(qd, kd, vd, idx, cnt, scale=p["scale"], o=torch.empty_like(qd))
+    _sync()
+    _check_rounding(o16, o32)
+    assert torch.equal(lse, lse16)
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    S = orc.token_scores(q, k, mask, layout)
+    idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
+    n = min(budget, L)
+    lists = [[None] * Hq for _ in range(B)]
+    n_amb = 0
+    for b in range(B):
+        for h in range(Hq):
+            assert cnt_np[b, h] == n
+            got = idx_np[b, h, :n].astype(np.int64)
+            assert np.all(np.diff(got) > 0) and got.min() >= 0 and got.max() < L, f"head {h}: list not ascending"
+            ref, kth = orc.top_tokens(S[b, h], budget)
+            amb = set(np.nonzero(np.abs(S[b, h] - kth) <= TOKEN_EPS * max(1.0, abs(kth)))[0].tolist())
+            n_amb += len(amb)
+            assert set(got.tolist()) - amb == set(ref.tolist()) - amb, f"head {h}: token sets differ"
+            lists[b][h] = got
+    O_ref, L_ref = orc.token_attention(q, k, v, lists, p["scale"])
+    check_outputs(from_dev(o32), O_ref, lse.cpu().numpy(), L_ref, f"{w.name} tokens {budget}")
+    return idx_np, n_amb
+
+
+@pytest.mark.parametrize("L,budget,n_fc,layout", [(4096, 256, 8, 0), (3000 + 3, 100, 4, 1), (500, 1000, 64, 0),
+                                                  (8192, 1, 16, 0)])
+def test_token_select_small(bsa, L, budget, n_fc, layout):
+    """Budgets below and above L (all tokens), one token, all chunks, both layouts, a ragged L."""
+    w = synth.gqa_decode(L=L, n_needles=2)
+    _token_case(bsa, w, budget, n_fc, layout, seed=L)
+
+
+def test_token_select_group_size_8(bsa):
+    w = synth.gqa_decode(L=2048, Hq=16, Hkv=2, n_needles=2)
+    _token_case(bsa, w, 128, 8, 0, seed=3)
+
+
+def test_token_select_full_size(bsa):
+    """64K decode, 8 of 64 chunks per head, 256 tokens per head (the page's LongBench budget)."""
+    idx, _ = _token_case(bsa, synth.gqa_decode(), 256, 8, 0, seed=64)
+    assert idx.shape == (1, 32, 256)
+
+
 def _dlm_case(bsa, w, union_active: bool, full_check_rows=None):
     p = w.params
     qd, kd, vd = _dev_workload(w)

@@ -391,6 +391,52 @@ def test_window_decode_branches():
     assert np.allclose(O3, O_sel)
 
 
+@pytest.mark.parametrize("layout", [ROPE_HALF, ROPE_INTERLEAVED])
+def test_token_scores_follow_the_rope_chunks(layout):
+    """Per-chunk scores add up to q . k, and one chunk's score depends only on
+    the distance between the two positions once q and k are rotated with RoPE
+    (synth.rope in the same layout): a wrong dim pairing breaks it."""
+    rng = np.random.default_rng(15)
+    D, L = 32, 40
+    q0, k0 = rng.standard_normal((1, D)), rng.standard_normal((L, D))
+    allm = np.ones((1, D // 2), dtype=np.uint8)
+    q, k = q0[None, None], k0[None, None]
+    full = orc.token_scores(q, k, allm, layout)
+    assert np.allclose(full[0, 0], k0 @ q0[0])
+    parts = sum(orc.token_scores(q, k, np.eye(D // 2, dtype=np.uint8)[[f]], layout) for f in range(D // 2))
+    assert np.allclose(parts, full)
+    for f in (0, 5, D // 2 - 1):
+        m = np.eye(D // 2, dtype=np.uint8)[[f]]
+        sc = []
+        for shift in (0, 17, 300):
+            qr = synth.rope(q0, np.array([50 + shift]), layout)
+            kr = synth.rope(k0, np.arange(L) + shift, layout)
+            sc.append(orc.token_scores(qr[None, None], kr[None, None], m, layout)[0, 0])
+        assert np.allclose(sc[0], sc[1]) and np.allclose(sc[0], sc[2])
+
+
+def test_top_tokens_brute_force_with_ties():
+    rng = np.random.default_rng(16)
+    s = rng.integers(0, 6, 50).astype(float)           # many ties
+    for budget in (1, 7, 20, 50, 80):
+        toks, kth = orc.top_tokens(s, budget)
+        n = min(budget, 50)
+        assert len(toks) == n and np.all(np.diff(toks) > 0)
+        best = [t for _, t in sorted((-s[t], t) for t in range(50))][:n]
+        assert set(best) == set(toks.tolist()) and kth == min(s[best])
+
+
+def test_token_attention_with_every_token_is_dense():
+    rng = np.random.default_rng(17)
+    q = rng.standard_normal((1, 4, 1, 16))
+    k, v = rng.standard_normal((1, 2, 90, 16)), rng.standard_normal((1, 2, 90, 16))
+    lists = [[np.arange(90) for _ in range(4)]]
+    O, L = orc.token_attention(q, k, v, lists, 0.25)
+    for h in range(4):
+        S = 0.25 * k[0, h // 2] @ q[0, h, 0]
+        assert np.allclose(O[0, h, 0], softmax(S) @ v[0, h // 2]) and np.isclose(L[0, h, 0], logsumexp(S))
+
+
 def test_causal_row_with_no_visible_key():
     q = np.ones((1, 4))
     O, lse = orc.attend_tokens(q, np.ones((4, 4)), np.ones((4, 4)), np.arange(2, 4), 1.0, np.array([1]))
