@@ -36,6 +36,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 THRESH_DECODE_A = 0.4 * 65536
 THRESH_DECODE_SPLIT = 1024     # keys per split-KV slice
 WINDOW = 512                   # NSA sliding window (tokens) for the selection + window decode
+TOKEN_FCS = 8                  # frequency chunks per head for token importance (of 64)
+TOKEN_BUDGET = 256             # tokens per head (the FASA page's LongBench budget)
 
 
 def log(msg):
@@ -65,7 +67,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", default="all", choices=["all", "decode", "dlm", "prefill", "threshold", "tdecode"],
+    ap.add_argument("--only", default="all", choices=["all", "decode", "dlm", "prefill", "threshold", "tdecode", "tokens"],
                     help="which workloads to run (the headline line needs decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
@@ -506,6 +508,53 @@ def bench_threshold_decode(torch, bsa, synth, reps, flush, w=None):
                 speedup_vs_lambda0=round(t0_cold / t_cold, 3), other_lengths=other)
 
 
+# ----------------------------------------------------- token importance ---
+def bench_token_decode(torch, bsa, synth, reps, flush, w=None):
+    """Token-level selection on 8 of 64 frequency chunks per head (a seeded,
+    caller-given set) with 256 tokens per head, then each head's attention
+    over its tokens, on the 64K decode workload."""
+    import numpy as np
+    if w is None:
+        log("tokens: generating the 64K GQA workload")
+        w = synth.gqa_decode()
+    p = w.params
+    q, k, v = (to_dev(torch, x, "bf16") for x in (w.q, w.k, w.v))
+    B, Hkv, L, D = k.shape
+    Hq = q.shape[1]
+    rng = np.random.default_rng(64)
+    m = np.zeros((Hq, D // 2), dtype=np.uint8)
+    for h in range(Hq):
+        m[h, rng.choice(D // 2, TOKEN_FCS, replace=False)] = 1
+    mask = torch.from_numpy(m).cuda()
+    idx = torch.empty((B, Hq, TOKEN_BUDGET), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Hq), dtype=torch.int32, device="cuda")
+    ws_sel = torch.empty(bsa.bsa_token_select_workspace_bytes(q, k, TOKEN_BUDGET), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+    ws_att = torch.empty(bsa.bsa_token_attention_workspace_bytes(q, k, TOKEN_BUDGET), dtype=torch.uint8,
+                         device="cuda")
+
+    def select():
+        bsa.bsa_token_select(q, k, mask, TOKEN_BUDGET, idx=idx, cnt=cnt, workspace=ws_sel)
+
+    def attend():
+        bsa.bsa_token_attention_fwd(q, k, v, idx, cnt, scale=p["scale"], o=o, lse=lse, workspace=ws_att)
+
+    def step():
+        select()
+        attend()
+
+    t_step = time_graph(torch, step, reps)
+    t_sel = time_calls(torch, select, reps)
+    t_att = time_calls(torch, attend, reps)
+    t_step_cold = time_cold(torch, step, reps, flush) if flush is not None else None
+    tok_bytes = B * Hq * TOKEN_BUDGET * D * 2 * 2                      # each head's own K and V rows
+    return dict(fcs_per_head=TOKEN_FCS, budget=TOKEN_BUDGET, us_per_step=round(t_step, 2),
+                us_per_step_cold=None if t_step_cold is None else round(t_step_cold, 2),
+                select_us=round(t_sel, 2), attention_us=round(t_att, 2), scored_k_bytes=B * Hkv * L * D * 2,
+                attended_kv_bytes=tok_bytes, attention_gbs=round(tok_bytes / (t_att * 1e3), 1))
+
+
 # ------------------------------------------------------------ cpu baseline ---
 def cpu_baseline(w, seconds):
     """The fp64 oracle's decode step on the host, repeated for about `seconds`."""
@@ -564,6 +613,10 @@ def main():
         secondary["threshold_decode_64k"] = bench_threshold_decode(
             torch, bsa, synth, reps, flush, result["decode"]["workload"] if "decode" in result else None)
         log(f"tdecode: {secondary['threshold_decode_64k']}")
+    if args.only in ("all", "tokens"):
+        secondary["token_decode_64k"] = bench_token_decode(
+            torch, bsa, synth, reps, flush, result["decode"]["workload"] if "decode" in result else None)
+        log(f"tokens: {secondary['token_decode_64k']}")
     if args.only in ("all", "dlm"):
         secondary["dlm_denoise_32k"] = bench_dlm(torch, bsa, synth, reps)
         log(f"dlm: {secondary['dlm_denoise_32k']}")

@@ -213,6 +213,16 @@ def bsa_window_decode_fwd(q, k, v, idx, cnt, p: BsaAttnParams, window: int, gate
     return o, lse
 
 
+def bsa_token_select_workspace_bytes(q, k, budget: int) -> int:
+    qd, kd = tensor_desc(q), tensor_desc(k)
+    return lib().bsa_token_select_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), budget)
+
+
+def bsa_token_attention_workspace_bytes(q, k, cap: int) -> int:
+    qd, kd = tensor_desc(q), tensor_desc(k)
+    return lib().bsa_token_attention_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), cap)
+
+
 def bsa_token_select(q, k, fc_mask, budget: int, layout: int = BSA_ROPE_HALF, idx=None, cnt=None, workspace=None):
     """Returns (idx [B,Hq,budget] int32 ascending, cnt [B,Hq] int32): each head's best tokens by q . k over
     the frequency chunks marked in fc_mask [Hq, D/2] (uint8, on the device)."""
@@ -222,7 +232,7 @@ def bsa_token_select(q, k, fc_mask, budget: int, layout: int = BSA_ROPE_HALF, id
     if cnt is None:
         cnt = torch.empty((B, Hq), dtype=torch.int32, device=q.device)
     qd, kd = tensor_desc(q), tensor_desc(k)
-    need = lib().bsa_token_select_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd))
+    need = bsa_token_select_workspace_bytes(q, k, budget)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     check(lib().bsa_token_select(ctypes.byref(qd), ctypes.byref(kd), fc_mask.data_ptr(), layout, budget,
@@ -242,7 +252,7 @@ def bsa_token_attention_fwd(q, k, v, idx, cnt, scale=None, o=None, lse=None, wor
     if lse is None:
         lse = torch.zeros((B, Hq, Lq), dtype=torch.float32, device=q.device)
     qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
-    need = lib().bsa_token_attention_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), cap)
+    need = bsa_token_attention_workspace_bytes(q, k, cap)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     check(lib().bsa_token_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),

@@ -287,12 +287,15 @@ static bsa_status validate_token_select(const bsa_tensor* q, const bsa_tensor* k
   if (layout != BSA_ROPE_HALF && layout != BSA_ROPE_INTERLEAVED) return fail(BSA_ERR_INVALID, "layout %d", layout);
   if (!fc_mask) return fail(BSA_ERR_INVALID, "fc_mask is required");
   if (budget <= 0) return fail(BSA_ERR_INVALID, "budget %d must be positive", budget);
+  if (!token_select_supported(*k, budget))
+    return fail(BSA_ERR_UNSUPPORTED, "budget %d with L = %d: at most 2048 and at most 16384 / ceil(L / 4096)", budget,
+                (int)k->L);
   return BSA_OK;
 }
 
-size_t bsa_token_select_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k) {
-  if (!q || !k || q->H <= 0 || k->H <= 0 || k->L <= 0) return 0;
-  return token_select_workspace(*q, *k);
+size_t bsa_token_select_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, int32_t budget) {
+  if (!q || !k || q->H <= 0 || k->H <= 0 || k->L <= 0 || budget <= 0) return 0;
+  return token_select_workspace(*q, *k, budget);
 }
 
 bsa_status bsa_token_select(const bsa_tensor* q, const bsa_tensor* k, const uint8_t* fc_mask, int32_t layout,
@@ -301,7 +304,7 @@ bsa_status bsa_token_select(const bsa_tensor* q, const bsa_tensor* k, const uint
   bsa_status st = validate_token_select(q, k, fc_mask, layout, budget);
   if (st != BSA_OK) return st;
   if (!idx || !cnt) return fail(BSA_ERR_INVALID, "idx and cnt are required");
-  const size_t need = token_select_workspace(*q, *k);
+  const size_t need = token_select_workspace(*q, *k, budget);
   if (!workspace || workspace_bytes < need)
     return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");

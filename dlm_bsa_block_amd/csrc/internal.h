@@ -85,7 +85,8 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
 
 // Token importance on a subset of frequency chunks, top-N tokens per query head, and the
 // attention of each head over its own token list.
-size_t token_select_workspace(const bsa_tensor& q, const bsa_tensor& k);
+size_t token_select_workspace(const bsa_tensor& q, const bsa_tensor& k, int budget);
+bool token_select_supported(const bsa_tensor& k, int budget);
 void launch_token_select(const bsa_tensor& q, const bsa_tensor& k, const uint8_t* fc_mask, int layout, int budget,
                          int32_t* idx, int32_t* cnt, float* scores_out, void* ws, hipStream_t s);
 void plan_token_attention(const bsa_tensor& q, const bsa_tensor& k, int cap, AttnPlan& pl);

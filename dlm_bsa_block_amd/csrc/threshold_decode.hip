@@ -582,133 +582,166 @@ void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa
 // chunks only) and the top-N tokens of each head.
 //
 // Scores come from the scores kernel above with the other chunks' query dims
-// zeroed.  The top N of a head's L scores (ties to the lower token) come from
-// one workgroup of 1024 threads holding 64 scores each (32 in registers, 32
-// in LDS): four
-// 8-bit radix passes on order-preserving keys (per-wave LDS histograms, one
-// wave scans the 256 bins) find the N-th key, then two block scans place the
-// chosen tokens in ascending order.
-constexpr int kTokThreads = 1024, kTokPer = 64;     // L <= 65536
+// zeroed.  The top N of a head's L scores (ties to the lower token) take two
+// passes of one selection kernel, so that many CUs share a head:
+//   1. each of P parts of kTokPart tokens keeps its own top N (a global top-N
+//      token is in its part's top N under the same tie rule);
+//   2. one workgroup per head selects the top N of the P x N candidates.
+// A workgroup holds its elements in registers as order-preserving keys
+// (larger score, larger key; 0 marks no token), finds the N-th largest key
+// bit by bit with 32 counting steps, and places the chosen elements in their
+// original order (ascending tokens) with two block scans.
+constexpr int kTokPart = 4096;          // tokens per first-pass part
+constexpr int kTokMaxBudget = 2048;     // tokens per head, at most
+constexpr int kTokMaxCand = 16384;      // first-pass candidates per head, at most
 
-__global__ __launch_bounds__(1024) void token_topk_kernel(const float* __restrict__ scores, int Lpad, int L, int N,
-                                                          int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
-  constexpr int NT = kTokThreads, NW = NT / 64, PER = kTokPer, PR = PER / 2;   // PR keys in registers
-  __shared__ uint32_t kl[PER - PR][NT];            // the other keys, [e][thread]: conflict-free
-  __shared__ uint32_t hist[NW][256];
-  __shared__ uint32_t wsum[NW];
-  __shared__ uint32_t sel_digit, sel_above;
-  const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const float* sr = scores + (int64_t)row * Lpad;
-  const int t0 = tid * PER;
-  uint32_t key[PR];
-  const int lim = L - t0;                            // this thread's token e is in the row iff e < lim
-  auto to_key = [&](float x, int e) __attribute__((always_inline)) {
-    const uint32_t u = __float_as_uint(x);
-    // order-preserving: larger float, larger key; 0 is below every score (and marks tokens >= L)
-    return e < lim ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
-  };
+struct TopkArgs {
+  const float* scores;                  // pass 1: [rows][Lpad]
+  const uint32_t* in_keys;              // pass 2: [rows][P * N] candidates (0: none)
+  const int32_t* in_toks;
+  uint32_t* out_keys;                   // pass 1 output: [rows][P][N]
+  int32_t* out_toks;
+  int32_t* idx;                         // pass 2 output: [rows][N] and counts [rows]
+  int32_t* cnt;
+  int Lpad, L, N, P;
+};
+
+template <int NT, int PER, bool FIRST>
+__global__ __launch_bounds__(NT) void token_topk_kernel(TopkArgs a) {
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t wsum[2][NW];                   // double-buffered: one barrier per counting step
+  const int part = blockIdx.x, row = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int e0 = tid * PER;                          // this thread's first element
+  uint32_t key[PER];
+  int32_t tk[FIRST ? 1 : PER];
+  int n_elem, Ne;
+  if (FIRST) {
+    const int t0 = part * kTokPart;                  // first token of the part
+    n_elem = min(kTokPart, a.L - t0);
+    Ne = min(a.N, n_elem);
+    const float* sr = a.scores + (int64_t)row * a.Lpad + t0;
+    const int lim = n_elem - e0;                     // element e is in the part iff e < lim
+    const int cl = a.Lpad - t0 - 4;                  // last 16-byte chunk of the row from the part's start
 #pragma unroll
-  for (int c = 0; c < PER / 4; ++c) {
-    const int t = t0 + 4 * c;
-    // clamped, so every load is in the row (keys past L are set to 0 below)
-    const f32x4 x = *reinterpret_cast<const f32x4*>(sr + min(t, Lpad - 4));
+    for (int c = 0; c < PER / 4; ++c) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(sr + min(e0 + 4 * c, cl));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ei = 4 * c + e;
-      if (ei < PR) key[ei] = to_key(x[e], ei);
-      else kl[ei - PR][tid] = to_key(x[e], ei);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = __float_as_uint(x[e]);
+        key[4 * c + e] = 4 * c + e < lim ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
+      }
+    }
+  } else {
+    n_elem = a.P * a.N;
+    Ne = min(a.N, a.L);
+    const uint32_t* kr = a.in_keys + (int64_t)row * n_elem;
+    const int32_t* tr = a.in_toks + (int64_t)row * n_elem;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = min(e0 + e, n_elem - 1);
+      const uint32_t kk = kr[i];
+      key[e] = e0 + e < n_elem ? kk : 0u;
+      tk[e] = tr[i];
     }
   }
-  auto key_at = [&](int e) __attribute__((always_inline)) { return e < PR ? key[e] : kl[e - PR][tid]; };
-  const int Ne = min(N, L);
-  uint32_t prefix = 0u, mask = 0u, need = (uint32_t)Ne;
-  // block-wide exclusive scan of one value per thread (wave scans + wave totals)
+  // Block-wide sum (exact: counts stay far below 2^24) and exclusive scan of one
+  // value per thread.  Call k uses wsum[k & 1]: a wave can only write a buffer
+  // again two calls later, after every wave has passed the barrier between.
+  int call = 0;
+  auto block_sum = [&](uint32_t v) __attribute__((always_inline)) {
+    const float ws = wave_sum_dpp((float)v);
+    uint32_t* buf = wsum[call++ & 1];
+    if (lane == 0) buf[w] = (uint32_t)ws;
+    __syncthreads();
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) tot += buf[ww];
+    return tot;
+  };
   auto block_excl = [&](uint32_t v) __attribute__((always_inline)) {
     const uint32_t inc = wave_incl_scan_dpp(v);
-    if (lane == 63) wsum[w] = inc;
+    uint32_t* buf = wsum[call++ & 1];
+    if (lane == 63) buf[w] = inc;
     __syncthreads();
     uint32_t before = 0u;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww)
-      if (ww < w) before += wsum[ww];
-    __syncthreads();
+      if (ww < w) before += buf[ww];
     return before + inc - v;
   };
+  // the N-th largest key: the largest x with at least N keys >= x, bit by bit
+  uint32_t tau = 0u;
 #pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    uint32_t c = 0u;
 #pragma unroll
-    for (int i = 0; i < NW * 256 / NT; ++i) (&hist[0][0])[tid + NT * i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const uint32_t kk = key_at(e);
-      if ((kk & mask) == prefix) atomicAdd(&hist[w][(kk >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (w == 0) {
-      // lane l holds digits 255 - 4l - j (j = 0..3): descending digits across the wave
-      uint32_t c[4], sum = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int dg = 255 - 4 * lane - j;
-        c[j] = 0u;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) c[j] += hist[ww][dg];
-        sum += c[j];
-      }
-      uint32_t before = wave_incl_scan_dpp(sum) - sum;       // keys with larger digits
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (before < need && need <= before + c[j]) {
-          sel_digit = (uint32_t)(255 - 4 * lane - j);
-          sel_above = before;
-        }
-        before += c[j];
-      }
-    }
-    __syncthreads();
-    prefix |= sel_digit << shift;
-    mask |= 0xFFu << shift;
-    need -= sel_above;
-    __syncthreads();                                 // sel_* are rewritten by the next pass
+    for (int e = 0; e < PER; ++e) c += key[e] >= cand;
+    if (block_sum(c) >= (uint32_t)Ne) tau = cand;
   }
-  // prefix is the N-th largest key; take every larger key and the first `need` ties
   uint32_t n_gt = 0u, n_eq = 0u;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const uint32_t kk = key_at(e);
-    n_gt += kk > prefix;
-    n_eq += kk == prefix;
+    n_gt += key[e] > tau;
+    n_eq += key[e] == tau;
   }
+  const uint32_t need = (uint32_t)Ne - block_sum(n_gt);   // ties at the N-th key still to take
   const uint32_t eq_before = block_excl(n_eq);
   const uint32_t take = need > eq_before ? min(need - eq_before, n_eq) : 0u;
   uint32_t pos = block_excl(n_gt + take);
-  int32_t* out = idx + (int64_t)row * N;
   uint32_t taken = 0u;
-  int tok = t0;
-  asm volatile("" : "+v"(tok));                      // one running token index, not 64 precomputed ones
+  if (FIRST) {
+    const int64_t ob = ((int64_t)row * a.P + part) * a.N;
+    int tok = part * kTokPart + e0;
+    asm volatile("" : "+v"(tok));                    // one running token index, not PER precomputed ones
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const uint32_t kk = key_at(e);
-    const bool eq = kk == prefix && taken < take;
-    if (kk > prefix || eq) out[pos++] = tok;
-    taken += eq;
-    ++tok;
+    for (int e = 0; e < PER; ++e) {
+      const bool eq = key[e] == tau && taken < take;
+      if (key[e] > tau || eq) {
+        a.out_keys[ob + pos] = key[e];
+        a.out_toks[ob + pos] = tok;
+        ++pos;
+      }
+      taken += eq;
+      ++tok;
+    }
+    for (int i = Ne + tid; i < a.N; i += NT) a.out_keys[ob + i] = 0u;   // unused slots: no token
+  } else {
+    int32_t* out = a.idx + (int64_t)row * a.N;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const bool eq = key[e] == tau && taken < take;
+      if (key[e] > tau || eq) out[pos++] = tk[e];
+      taken += eq;
+    }
+    if (tid == 0) a.cnt[row] = Ne;
   }
-  if (tid == 0) cnt[row] = Ne;
 }
 
-static size_t tok_sizes(const bsa_tensor& q, const bsa_tensor& k, size_t (&sz)[3]) {
+static void tok_plan(const bsa_tensor& k, int budget, int& P) { P = (int)ceil_div(k.L, kTokPart); (void)budget; }
+
+static size_t tok_sizes(const bsa_tensor& q, const bsa_tensor& k, int budget, size_t (&sz)[5]) {
   const size_t heads = (size_t)q.B * q.H;
+  int P;
+  tok_plan(k, budget, P);
   sz[0] = align256(heads * ((k.L + 3) & ~3LL) * 4);                 // scores
   sz[1] = align256(heads * ceil_div(k.L, kTDecTile) * 4);           // tile maxima (written, unused)
   sz[2] = align256(heads * ceil_div(k.L, kTDecMaxSplit) * 4);       // slice maxima (written, unused)
-  return sz[0] + sz[1] + sz[2];
+  sz[3] = align256(heads * (size_t)P * budget * 4);                 // first-pass keys
+  sz[4] = align256(heads * (size_t)P * budget * 4);                 // first-pass tokens
+  return sz[0] + sz[1] + sz[2] + sz[3] + sz[4];
 }
 
-size_t token_select_workspace(const bsa_tensor& q, const bsa_tensor& k) {
-  size_t sz[3];
-  return tok_sizes(q, k, sz);
+bool token_select_supported(const bsa_tensor& k, int budget) {
+  int P;
+  tok_plan(k, budget, P);
+  return budget <= kTokMaxBudget && (int64_t)P * budget <= kTokMaxCand;
+}
+
+size_t token_select_workspace(const bsa_tensor& q, const bsa_tensor& k, int budget) {
+  size_t sz[5];
+  return tok_sizes(q, k, budget, sz);
 }
 
 void launch_token_select(const bsa_tensor& q, const bsa_tensor& k, const uint8_t* fc_mask, int layout, int budget,
@@ -723,8 +756,8 @@ void launch_token_select(const bsa_tensor& q, const bsa_tensor& k, const uint8_t
   a.nsplit = (int)ceil_div(k.L, kTDecMaxSplit);
   a.ntiles = (int)ceil_div(k.L, kTDecTile);
   a.c2 = 1.f;                                        // plain q.k
-  size_t sz[3];
-  tok_sizes(q, k, sz);
+  size_t sz[5];
+  tok_sizes(q, k, budget, sz);
   uint8_t* p = static_cast<uint8_t*>(ws);
   a.scores = scores_out ? scores_out : reinterpret_cast<float*>(p);
   a.tmax = reinterpret_cast<float*>(p + sz[0]);
@@ -738,8 +771,22 @@ void launch_token_select(const bsa_tensor& q, const bsa_tensor& k, const uint8_t
     case 4: hipLaunchKernelGGL(tdec_scores_kernel<4>, gs, dim3(512), 0, s, a); break;
     default: hipLaunchKernelGGL(tdec_scores_kernel<8>, gs, dim3(512), 0, s, a); break;
   }
-  hipLaunchKernelGGL(token_topk_kernel, dim3(q.B * q.H), dim3(kTokThreads), 0, s, a.scores, a.Lpad, a.L, budget,
-                     idx, cnt);
+  TopkArgs t{};
+  t.scores = a.scores;
+  t.in_keys = reinterpret_cast<const uint32_t*>(p + sz[0] + sz[1] + sz[2]);
+  t.in_toks = reinterpret_cast<const int32_t*>(p + sz[0] + sz[1] + sz[2] + sz[3]);
+  t.out_keys = reinterpret_cast<uint32_t*>(p + sz[0] + sz[1] + sz[2]);
+  t.out_toks = reinterpret_cast<int32_t*>(p + sz[0] + sz[1] + sz[2] + sz[3]);
+  t.idx = idx; t.cnt = cnt;
+  t.Lpad = a.Lpad; t.L = a.L; t.N = budget;
+  tok_plan(k, budget, t.P);
+  const int rows = (int)(q.B * q.H);
+  // pass 1: 256 threads x 16 tokens per part; pass 2: 16 candidates per thread, 256 or 1024 threads
+  hipLaunchKernelGGL((token_topk_kernel<256, kTokPart / 256, true>), dim3(t.P, rows), dim3(256), 0, s, t);
+  if (t.P * t.N <= 4096)
+    hipLaunchKernelGGL((token_topk_kernel<256, 16, false>), dim3(1, rows), dim3(256), 0, s, t);
+  else
+    hipLaunchKernelGGL((token_topk_kernel<1024, kTokMaxCand / 1024, false>), dim3(1, rows), dim3(1024), 0, s, t);
 }
 
 }  // namespace bsa

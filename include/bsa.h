@@ -296,12 +296,13 @@ bsa_status bsa_window_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, const
  * 2i, 2i + 1 for BSA_ROPE_INTERLEAVED) count.  Each head's score of token t
  * is q . k_t over the marked dims only; idx [B, Hq, budget] int32 gets the
  * min(budget, L) best tokens in ascending order (ties: lower token first),
- * cnt [B, Hq] their number.  workspace: bsa_token_select_workspace_bytes()
- * bytes, no initial contents.  Errors: BSA_ERR_INVALID for shapes, layout,
+ * cnt [B, Hq] their number; budget at most 2048 and at most
+ * 16384 / ceil(L / 4096) (1024 at 64K).  workspace:
+ * bsa_token_select_workspace_bytes() bytes, no initial contents.  Errors: BSA_ERR_INVALID for shapes, layout,
  * a null mask or output, budget <= 0 or a misaligned workspace;
  * BSA_ERR_UNSUPPORTED outside the supported set; BSA_ERR_WORKSPACE.
  * ------------------------------------------------------------------------ */
-size_t bsa_token_select_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k);
+size_t bsa_token_select_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, int32_t budget);
 
 bsa_status bsa_token_select(const bsa_tensor* q, const bsa_tensor* k, const uint8_t* fc_mask, int32_t layout,
                             int32_t budget, int32_t* idx, int32_t* cnt, void* workspace, size_t workspace_bytes,

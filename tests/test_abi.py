@@ -226,7 +226,7 @@ def test_window_decode_rejects_bad_arguments(lib):
 
 def test_token_select_and_attention_reject_bad_arguments(lib):
     q, k = _t(H=32, Lq=1), _t(H=8, Lq=4096)
-    need = lib.bsa_token_select_workspace_bytes(ctypes.byref(q), ctypes.byref(k))
+    need = lib.bsa_token_select_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 256)
     assert need >= 32 * 4096 * 4
 
     def sel(qq, kk, mask=FAKE, layout=0, budget=256, ws=need):
@@ -237,6 +237,8 @@ def test_token_select_and_attention_reject_bad_arguments(lib):
     assert sel(q, k, layout=2) == L.BSA_ERR_INVALID
     assert sel(q, k, budget=0) == L.BSA_ERR_INVALID and "budget" in _err(lib)
     assert sel(q, _t(H=8, Lq=65537)) == L.BSA_ERR_UNSUPPORTED
+    assert sel(q, k, budget=4096) == L.BSA_ERR_UNSUPPORTED and "budget" in _err(lib)
+    assert sel(q, _t(H=8, Lq=65536), budget=2048) == L.BSA_ERR_UNSUPPORTED         # 16 parts x 2048 > 16384
     assert sel(_t(H=32, Lq=2), k) == L.BSA_ERR_INVALID and "one query row" in _err(lib)
     assert sel(_t(H=32, Lq=1, D=64), _t(H=8, Lq=4096, D=64)) == L.BSA_ERR_UNSUPPORTED
     wa = lib.bsa_token_attention_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 256)
