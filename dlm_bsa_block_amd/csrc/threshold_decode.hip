@@ -589,7 +589,7 @@ void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa
 //   2. one workgroup per head selects the top N of the P x N candidates.
 // A workgroup holds its elements in registers as order-preserving keys
 // (larger score, larger key; 0 marks no token), finds the N-th largest key
-// bit by bit with 32 counting steps, and places the chosen elements in their
+// two bits at a time with 16 counting steps, and places the chosen elements in their
 // original order (ascending tokens) with two block scans.
 constexpr int kTokPart = 4096;          // tokens per first-pass part
 constexpr int kTokMaxBudget = 2048;     // tokens per head, at most
@@ -609,7 +609,8 @@ struct TopkArgs {
 template <int NT, int PER, bool FIRST>
 __global__ __launch_bounds__(NT) void token_topk_kernel(TopkArgs a) {
   constexpr int NW = NT / 64;
-  __shared__ uint32_t wsum[2][NW];                   // double-buffered: one barrier per counting step
+  __shared__ uint32_t wsum[2][NW];                   // double-buffered: one barrier per block sum
+  __shared__ uint32_t wsum3[2][3][NW];               // the same for the three counts of a 2-bit step
   const int part = blockIdx.x, row = blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int e0 = tid * PER;                          // this thread's first element
@@ -670,15 +671,37 @@ __global__ __launch_bounds__(NT) void token_topk_kernel(TopkArgs a) {
       if (ww < w) before += buf[ww];
     return before + inc - v;
   };
-  // the N-th largest key: the largest x with at least N keys >= x, bit by bit
+  // The N-th largest key: the largest x with at least N keys >= x, two bits a
+  // step (the counts at the three candidates x | 1, 2, 3 << shift, reduced
+  // together: their latencies overlap).
   uint32_t tau = 0u;
+  int call3 = 0;
 #pragma unroll 1
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    uint32_t c = 0u;
+  for (int shift = 30; shift >= 0; shift -= 2) {
+    uint32_t c[3] = {0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < PER; ++e) c += key[e] >= cand;
-    if (block_sum(c) >= (uint32_t)Ne) tau = cand;
+    for (int e = 0; e < PER; ++e) {
+      c[0] += key[e] >= (tau | (1u << shift));
+      c[1] += key[e] >= (tau | (2u << shift));
+      c[2] += key[e] >= (tau | (3u << shift));
+    }
+    float ws[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) ws[j] = wave_sum_dpp((float)c[j]);
+    uint32_t (*buf)[NW] = wsum3[call3++ & 1];
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) buf[j][w] = (uint32_t)ws[j];
+    }
+    __syncthreads();
+    uint32_t tot[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) tot[j] += buf[j][ww];
+    // counts fall with the candidate: take the largest one that still has N keys
+    const uint32_t dg = tot[2] >= (uint32_t)Ne ? 3u : tot[1] >= (uint32_t)Ne ? 2u : tot[0] >= (uint32_t)Ne ? 1u : 0u;
+    tau |= dg << shift;
   }
   uint32_t n_gt = 0u, n_eq = 0u;
 #pragma unroll
