@@ -208,10 +208,12 @@ def _window_case(bsa, w, window, with_gates=True):
         rng = np.random.default_rng(window)
         gates = torch.from_numpy(rng.uniform(0.1, 1.2, (B, Hq, Lq, 2)).astype(np.float32)).cuda()
     o32, lse = bsa.bsa_window_decode_fwd(qd, kd, vd, idx, cnt, ap, window, gates=gates, o=_f32_out(qd))
-    o16, lse16 = bsa.bsa_window_decode_fwd(qd, kd, vd, idx, cnt, ap, window, gates=gates, o=torch.empty_like(qd))
+    if qd.dtype == torch.bfloat16:
+        o16, lse16 = bsa.bsa_window_decode_fwd(qd, kd, vd, idx, cnt, ap, window, gates=gates, o=torch.empty_like(qd))
+        _sync()
+        _check_rounding(o16, o32)
+        assert torch.equal(lse, lse16)
     _sync()
-    _check_rounding(o16, o32)
-    assert torch.equal(lse, lse16)
     q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
     km_ref, _ = orc.block_summaries(k, p["kv_block"], p["layout"])
     sel = orc.select_blocks(p, km_ref, q=q)
@@ -227,6 +229,38 @@ def test_window_decode_small(bsa, L, window, gates):
     """Windows aligned and not to the blocks, longer than the prefix, one block long."""
     w = synth.gqa_decode(L=L, n_needles=2)
     _window_case(bsa, w, window, gates)
+
+
+def test_window_decode_tiny_f32(bsa):
+    """fp32 inputs, head dim 64, one head: the window branch through the fp32 decode path."""
+    _window_case(bsa, synth.tiny_decode(), 100, True)
+
+
+def test_token_attention_f32_lists(bsa):
+    """Per-head token attention with fp32 inputs, head dim 64, group size 2, unsorted seeded lists of
+    different lengths (one empty) -- the lists need not come from the token selection."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, L, D, cap = 2, 4, 2, 700, 64, 90
+    q = rng.standard_normal((B, Hq, 1, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    idx = np.zeros((B, Hq, 1, cap), dtype=np.int32)
+    cnt = np.zeros((B, Hq, 1), dtype=np.int32)
+    lists = [[None] * Hq for _ in range(B)]
+    for b in range(B):
+        for h in range(Hq):
+            n = 0 if (b, h) == (1, 2) else int(rng.integers(1, cap + 1))
+            t = rng.choice(L, n, replace=False)
+            idx[b, h, 0, :n] = t
+            cnt[b, h, 0] = n
+            lists[b][h] = t.astype(np.int64)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    o, lse = bsa.bsa_token_attention_fwd(qd, kd, vd, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
+                                         scale=0.125)
+    _sync()
+    O_ref, L_ref = orc.token_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), lists, 0.125)
+    check_outputs(o.cpu().numpy(), O_ref, lse.cpu().numpy(), L_ref, "token attention f32")
+    assert torch.all(o[1, 2] == 0) and lse[1, 2, 0].item() == float("-inf")
 
 
 def test_window_decode_full_size(bsa):
