@@ -20,6 +20,9 @@
 //      chunks spread that work over many compute units;
 //   3. combine_kernel: per head, the chunks' maxima in one round trip, then
 //      the partial sums of the chunks that kept anything, merged in order.
+//
+// The end of the file holds the token selection on a subset of frequency
+// chunks (FASA), which reuses the scores kernel with a chunk mask.
 #include "common.cuh"
 #include "internal.h"
 #include "split.h"
