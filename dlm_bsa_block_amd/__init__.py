@@ -20,7 +20,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = ["bsa_build_block_summaries", "bsa_select_blocks", "bsa_active_rows", "bsa_merge_attention_states",
            "bsa_block_attention_merge", "bsa_window_decode_fwd", "bsa_window_decode_workspace_bytes",
-           "bsa_token_select", "bsa_token_attention_fwd",
+           "bsa_token_select", "bsa_token_attention_fwd", "bsa_select_blocks_refresh",
            "bsa_sparse_attention_fwd",
            "bsa_threshold_attention_fwd", "bsa_threshold_decode_fwd", "bsa_select_workspace_bytes",
            "bsa_attention_workspace_bytes", "bsa_threshold_decode_workspace_bytes",
@@ -187,6 +187,32 @@ def bsa_sparse_attention_fwd(q, k, v, idx, cnt, p: BsaAttnParams, row_mask=None,
                                          lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
           "bsa_sparse_attention_fwd")
     return o, lse
+
+
+def bsa_select_blocks_refresh(k, refresh_block: int, q, k_mean, p: BsaSelectParams, k_energy=None, row_mask=None,
+                              want_row_picks=False, workspace=None, idx=None, cnt=None):
+    """bsa_build_block_summaries of block `refresh_block` (into k_mean / k_energy) and bsa_select_blocks, in
+    the selection's launches.  Returns (idx, cnt, row_picks or None)."""
+    B, Hkv, NB, D = k_mean.shape
+    Lq = q.shape[2]
+    NQB = -(-Lq // p.q_block)
+    if p.cap <= 0:
+        p.cap = list_capacity(NB, min(p.q_block, Lq), p)
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((B, Hkv, NQB, p.cap), dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv, NQB), dtype=torch.int32, device=dev)
+    rp = torch.empty((B, Hkv, Lq, p.cap), dtype=torch.int32, device=dev) if want_row_picks else None
+    qd, kd = tensor_desc(q), tensor_desc(k)
+    need = lib().bsa_select_workspace_bytes(ctypes.byref(qd), Hkv, NB, ctypes.byref(p))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    check(lib().bsa_select_blocks_refresh(ctypes.byref(kd), refresh_block, ctypes.byref(qd), k_mean.data_ptr(),
+                                          _ptr(k_energy), Hkv, NB, ctypes.byref(p), _ptr(row_mask), idx.data_ptr(),
+                                          cnt.data_ptr(), _ptr(rp), workspace.data_ptr(), workspace.numel(),
+                                          _stream()), "bsa_select_blocks_refresh")
+    return idx, cnt, rp
 
 
 def bsa_window_decode_workspace_bytes(q, k, p: BsaAttnParams, window: int) -> int:

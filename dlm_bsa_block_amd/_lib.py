@@ -52,6 +52,9 @@ _SIGS = {
     "bsa_block_attention_merge": (c_int32, [_T, _T, _T, c_float, _T, c_void_p, _T, c_void_p, c_void_p]),
     "bsa_attention_workspace_bytes": (c_size_t, [_T, _T, POINTER(BsaAttnParams)]),
     "bsa_window_decode_workspace_bytes": (c_size_t, [_T, _T, POINTER(BsaAttnParams), c_int32]),
+    "bsa_select_blocks_refresh": (c_int32, [_T, c_int32, _T, c_void_p, c_void_p, c_int32, c_int32,
+                                            POINTER(BsaSelectParams), c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_size_t, c_void_p]),
     "bsa_token_select_workspace_bytes": (c_size_t, [_T, _T, c_int32]),
     "bsa_token_select": (c_int32, [_T, _T, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
                                    c_void_p]),

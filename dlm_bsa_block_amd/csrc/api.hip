@@ -161,6 +161,40 @@ bsa_status bsa_select_blocks(const bsa_tensor* q, const float* q_energy, const f
   return check_launch("block selection");
 }
 
+bsa_status bsa_select_blocks_refresh(const bsa_tensor* k, int32_t refresh_block, const bsa_tensor* q, float* k_mean,
+                                     float* k_energy, int32_t num_kv_heads, int32_t num_kv_blocks,
+                                     const bsa_select_params* p, const uint8_t* row_mask, int32_t* idx, int32_t* cnt,
+                                     int32_t* row_picks, void* workspace, size_t workspace_bytes, void* stream) {
+  SelectPlan pl;
+  bsa_status st = validate_select(q, num_kv_heads, num_kv_blocks, p, pl);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(k, "k", false)) != BSA_OK) return st;
+  if (p->pooled_q || p->dual_band)
+    return fail(BSA_ERR_UNSUPPORTED, "the in-selection refresh takes raw query rows and one band");
+  if (k->dtype != q->dtype || k->B != q->B || k->H != num_kv_heads || k->D != q->D)
+    return fail(BSA_ERR_INVALID, "k does not match q and num_kv_heads");
+  if (ceil_div(k->L, p->kv_block) != num_kv_blocks)
+    return fail(BSA_ERR_INVALID, "num_kv_blocks %d != ceil(L / kv_block) = %lld", num_kv_blocks,
+                (long long)ceil_div(k->L, p->kv_block));
+  if (refresh_block < 0 || refresh_block >= num_kv_blocks)
+    return fail(BSA_ERR_INVALID, "refresh_block %d outside [0, %d)", refresh_block, num_kv_blocks);
+  if (p->causal && (int64_t)refresh_block * p->kv_block > p->q_pos0)
+    return fail(BSA_ERR_INVALID, "refresh_block %d is not visible to the first query row", refresh_block);
+  if (!k_mean || !idx || !cnt) return fail(BSA_ERR_INVALID, "k_mean, idx and cnt are required");
+  if (!aligned16(k_mean)) return fail(BSA_ERR_INVALID, "k_mean not 16-byte aligned");
+  const size_t need = pl.z_bytes + pl.tau_bytes + pl.bits_bytes + pl.cnt_bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  RefreshArgs ra;
+  ra.k = static_cast<const uint8_t*>(k->data);
+  ra.ksb = k->stride_b; ra.ksh = k->stride_h; ra.ksl = k->stride_l;
+  ra.L = (int)k->L; ra.block = refresh_block; ra.mean = k_mean; ra.energy = k_energy;
+  launch_select(*q, nullptr, k_mean, k_energy, *p, pl, row_mask, idx, cnt, row_picks, nullptr, workspace,
+                static_cast<hipStream_t>(stream), ra);
+  return check_launch("block selection with refresh");
+}
+
 // ------------------------------------------------------------- active rows ---
 bsa_status bsa_active_rows(const bsa_tensor* q_cur, const bsa_tensor* q_prev, float theta, uint8_t* row_mask,
                            float* mse, void* stream) {

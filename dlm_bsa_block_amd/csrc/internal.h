@@ -31,9 +31,19 @@ struct SelectPlan {
   size_t z_bytes, tau_bytes, bits_bytes, cnt_bytes;   // workspace regions, in this order
 };
 bool plan_select(const bsa_tensor& q, int NB, const bsa_select_params& p, SelectPlan& pl);
+// Optional refresh of one block's summary inside the selection (the newest decode block): the logits
+// workgroup that holds the block pools it from K, uses it and writes it out.  block < 0: none.
+struct RefreshArgs {
+  const uint8_t* k = nullptr;        // [B, Hkv, L, D], the selection's dtype
+  int64_t ksb = 0, ksh = 0, ksl = 0;
+  int L = 0, block = -1;
+  float* mean = nullptr;             // the k_mean array (written at `block`)
+  float* energy = nullptr;           // the k_energy array, or null
+};
 void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_mean, const float* k_energy,
                    const bsa_select_params& p, const SelectPlan& pl, const uint8_t* row_mask,
-                   int32_t* idx, int32_t* cnt, int32_t* row_picks, float* tau_out, void* ws, hipStream_t s);
+                   int32_t* idx, int32_t* cnt, int32_t* row_picks, float* tau_out, void* ws, hipStream_t s,
+                   const RefreshArgs& ra = RefreshArgs());
 
 void launch_active_rows(const bsa_tensor& a, const bsa_tensor& b, float theta, uint8_t* mask, float* mse,
                         hipStream_t s);

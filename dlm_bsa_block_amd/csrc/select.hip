@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
                                                      int64_t qsl, const float* __restrict__ k_mean, int NB, int Rtot,
                                                      int G, int Hkv, float scale, const float* __restrict__ tau,
                                                      int layout, int causal, int q_block, int kv_block, int q_pos0,
-                                                     int pooled, int Lq, float* __restrict__ Z) {
+                                                     int pooled, int Lq, float* __restrict__ Z, RefreshArgs ra) {
   constexpr int TM = TY * RPT, TJ = TX * CPT;
   const int NBp = (NB + 3) & ~3;          // row stride of Z, a multiple of 4 floats
   constexpr int ES = DT == BSA_BF16 ? 2 : 4;
@@ -459,13 +459,64 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
     for (int e = 0; e < 8; ++e) Qs[mm][d8 + e] = v[e];
   }
   const float* kb = k_mean + ((int64_t)b * Hkv + g) * NB * D;
+  // the block being refreshed (the newest, whose tokens change every decode
+  // step) is pooled here from K instead of read back, and written out
+  const int jr = ra.block - j0;
+  const bool refresh = ra.block >= 0 && jr >= 0 && jr < TJ;     // uniform over the workgroup
   for (int i = tid; i < TJ * (D / 4); i += 256) {
     const int jj = i / (D / 4), d4 = (i - jj * (D / 4)) * 4;
     const int j = j0 + jj;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (j < NB) v = *reinterpret_cast<const f32x4*>(kb + (int64_t)j * D + d4);
+    if (j < NB && !(refresh && jj == jr)) v = *reinterpret_cast<const f32x4*>(kb + (int64_t)j * D + d4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) Ks[jj][d4 + e] = v[e];
+  }
+  if (refresh) {
+    // one pass of 16 lanes x 8 dims per row, 16 rows per pass, fixed-order sums (as the summaries kernel)
+    constexpr int LPR = D / 8, RPP = 256 / LPR;
+    __shared__ float red[RPP][D + 4];
+    __shared__ float ered[4][2];
+    const int c = tid % LPR, rg = tid / LPR;
+    const int t0 = ra.block * kv_block, n = min(kv_block, ra.L - t0);
+    const uint8_t* kp = ra.k + ((int64_t)b * ra.ksb + (int64_t)g * ra.ksh + (int64_t)t0 * ra.ksl) * ES + c * 8 * ES;
+    float sum[8], e2 = 0.f;
+#pragma unroll
+    for (int q8 = 0; q8 < 8; ++q8) sum[q8] = 0.f;
+    for (int r0 = 0; r0 < n; r0 += 4 * RPP) {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + u * RPP + rg;
+        if (r < n) load8<DT>(kp + (int64_t)r * ra.ksl * ES, v[u]);
+        else {
+#pragma unroll
+          for (int q8 = 0; q8 < 8; ++q8) v[u][q8] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) { sum[q8] += v[u][q8]; e2 = fmaf(v[u][q8], v[u][q8], e2); }
+    }
+#pragma unroll
+    for (int q8 = 0; q8 < 8; ++q8) red[rg][c * 8 + q8] = sum[q8];
+    const int band = band_of_dim(c * 8, D, layout);
+    float ef = band == 0 ? e2 : 0.f, es = band == 0 ? 0.f : e2;
+    ef = wave_sum(ef);
+    es = wave_sum(es);
+    if ((tid & 63) == 0) { ered[tid >> 6][0] = ef; ered[tid >> 6][1] = es; }
+    __syncthreads();
+    const float inv = 1.0f / (float)n;
+    const int64_t row = ((int64_t)b * Hkv + g) * NB + ra.block;
+    for (int d = tid; d < D; d += 256) {
+      float t = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < RPP; ++rr) t += red[rr][d];
+      t *= inv;
+      Ks[jr][d] = t;
+      if (blockIdx.y == 0) ra.mean[row * D + d] = t;
+    }
+    if (ra.energy && blockIdx.y == 0 && tid < 2) ra.energy[row * 2 + tid] = (ered[0][tid] + ered[1][tid] + ered[2][tid] + ered[3][tid]) * inv;
   }
   __syncthreads();
 
@@ -547,7 +598,7 @@ bool plan_select(const bsa_tensor& q, int NB, const bsa_select_params& p, Select
 
 void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_mean, const float* k_energy,
                    const bsa_select_params& p, const SelectPlan& pl, const uint8_t* row_mask, int32_t* idx,
-                   int32_t* cnt, int32_t* row_picks, float* tau_out, void* ws, hipStream_t s) {
+                   int32_t* cnt, int32_t* row_picks, float* tau_out, void* ws, hipStream_t s, const RefreshArgs& ra) {
   const int G = pl.G, Hkv = pl.Hkv, NB = pl.NB;
   const int Rtot = p.pooled_q ? pl.NQB : pl.Lq;
   const int nb = p.dual_band ? 2 : 1;
@@ -598,7 +649,7 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
     dim3 grid((unsigned)ceil_div(NB, TX * CPT), (unsigned)ceil_div(M, TY * RPT), (unsigned)(pl.B * Hkv)); \
     hipLaunchKernelGGL((logits_kernel<DT, DD, TX, TY, RPT, CPT, DUAL>), grid, dim3(256), 0, s, qd,        \
                        q.stride_b, q.stride_h, q.stride_l, k_mean, NB, Rtot, G, Hkv, scale2, tau, p.layout, \
-                       p.causal, p.q_block, p.kv_block, p.q_pos0, p.pooled_q, pl.Lq, Z);                 \
+                       p.causal, p.q_block, p.kv_block, p.q_pos0, p.pooled_q, pl.Lq, Z, ra);             \
   } while (0)
 #define BSA_LOGITS_SHAPE(DT, DD, DUAL)                                   \
   do {                                                                   \

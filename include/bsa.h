@@ -160,6 +160,22 @@ bsa_status bsa_select_blocks(const bsa_tensor* q, const float* q_energy,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * bsa_build_block_summaries for one block followed by bsa_select_blocks, in
+ * the selection's launches: a decode step's newest block changes with every
+ * token, and its summary (mean and, if k_energy is non-NULL, band energies;
+ * Prism sec. 1-2, as the summaries entry point) is pooled from k by the
+ * scoring workgroup that needs it, used, and written to k_mean / k_energy at
+ * refresh_block.  k [B, Hkv, L, D] as q's dtype; num_kv_blocks must be
+ * ceil(L / kv_block).  Raw query rows and one band only (pooled_q = 0,
+ * dual_band = 0); with causal = 1 the block must start at or before q_pos0.
+ * Other arguments and errors as bsa_select_blocks (the same workspace size).
+ * ------------------------------------------------------------------------ */
+bsa_status bsa_select_blocks_refresh(const bsa_tensor* k, int32_t refresh_block, const bsa_tensor* q, float* k_mean,
+                                     float* k_energy, int32_t num_kv_heads, int32_t num_kv_blocks,
+                                     const bsa_select_params* p, const uint8_t* row_mask, int32_t* idx, int32_t* cnt,
+                                     int32_t* row_picks, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Locality pruning (LoSA sec. 2): row r of a denoising block is active when
  * the mean over heads and dims of (q_cur - q_prev)^2 exceeds theta (taken in
  * fp32).  q_cur/q_prev [B, H, R, D] bf16/f32 of the same shape; writes

@@ -253,6 +253,23 @@ def test_token_select_and_attention_reject_bad_arguments(lib):
     assert att(o=_t(H=32, Lq=2)) == L.BSA_ERR_INVALID and "o must match" in _err(lib)
 
 
+def test_select_refresh_rejects_bad_arguments(lib):
+    q, k = _t(H=32, Lq=1), _t(H=8, Lq=4096)
+    p = bsa.select_params(kv_block=64, q_block=1, topk=13, n_first=1, n_last=2, cap=16, q_pos0=4095)
+
+    def call(kk, blk, pp=p, nb=64):
+        return lib.bsa_select_blocks_refresh(ctypes.byref(kk), blk, ctypes.byref(q), FAKE, None, 8, nb,
+                                             ctypes.byref(pp), None, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert call(k, 64) == L.BSA_ERR_INVALID and "refresh_block" in _err(lib)
+    assert call(k, -1) == L.BSA_ERR_INVALID
+    assert call(_t(H=8, Lq=4000), 62, nb=64) == L.BSA_ERR_INVALID and "num_kv_blocks" in _err(lib)
+    assert call(_t(H=4, Lq=4096), 63) == L.BSA_ERR_INVALID
+    pd = bsa.select_params(kv_block=64, q_block=1, topk=13, dual_band=1, cap=16)
+    assert call(k, 63, pp=pd) == L.BSA_ERR_UNSUPPORTED
+    pc = bsa.select_params(kv_block=64, q_block=1, topk=13, causal=1, q_pos0=100, cap=16)
+    assert call(k, 63, pp=pc) == L.BSA_ERR_INVALID and "visible" in _err(lib)
+
+
 def test_active_rows_rejects_mismatch(lib):
     a, b = _t(H=32, Lq=32), _t(H=32, Lq=31)
     st = lib.bsa_active_rows(ctypes.byref(a), ctypes.byref(b), 0.1, FAKE, None, None)

@@ -193,6 +193,36 @@ def test_decode_select_everything_is_dense(bsa):
     assert (cnt == 32).all()
 
 
+def _refresh_case(bsa, w):
+    """Selection with the newest block's summary pooled inside it: the stored
+    summary of that block is stale (zeros) before the call."""
+    p = w.params
+    qd, kd, vd = _dev_workload(w)
+    NB = -(-kd.shape[2] // p["kv_block"])
+    kmean, kenergy = bsa.bsa_build_block_summaries(kd, p["kv_block"], p["layout"])
+    kmean[:, :, NB - 1] = 0.0
+    kenergy[:, :, NB - 1] = 0.0
+    sp = bsa.select_params(kv_block=p["kv_block"], q_block=1, q_pos0=p["q_pos0"], causal=p["causal"], topk=p["topk"],
+                           n_first=p["n_first"], n_last=p["n_last"], layout=p["layout"], scale=p["scale"])
+    idx, cnt, rp = bsa.bsa_select_blocks_refresh(kd, NB - 1, qd, kmean, sp, k_energy=kenergy, want_row_picks=True)
+    _sync()
+    q, k = w.f64("q"), w.f64("k")
+    km_ref, ke_ref = orc.block_summaries(k, p["kv_block"], p["layout"])
+    assert np.allclose(from_dev(kmean), km_ref, rtol=1e-5, atol=2e-6)
+    assert np.allclose(from_dev(kenergy), ke_ref, rtol=1e-5, atol=2e-6)
+    sel = orc.select_blocks(p, km_ref, q=q)
+    _check_selection(sel, idx, cnt, rp, lambda qb: [qb], w.name + " refresh")
+
+
+@pytest.mark.parametrize("L", [4096 + 37, 8192])
+def test_select_refresh_small(bsa, L):
+    _refresh_case(bsa, synth.gqa_decode(L=L, n_needles=3))
+
+
+def test_select_refresh_full_size(bsa):
+    _refresh_case(bsa, synth.gqa_decode())
+
+
 def _window_case(bsa, w, window, with_gates=True):
     """Selected blocks plus a sliding window of ``window`` keys in one pass,
     against the oracle's two branches on the same lists (checked first)."""
