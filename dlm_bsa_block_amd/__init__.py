@@ -115,7 +115,7 @@ def bsa_select_blocks(q: torch.Tensor, k_mean: torch.Tensor, p: BsaSelectParams,
     qd = tensor_desc(q)
     need = lib().bsa_select_workspace_bytes(ctypes.byref(qd), Hkv, NB, ctypes.byref(p))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)   # counters start at zero
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)   # no initial contents needed
     check(lib().bsa_select_blocks(ctypes.byref(qd), _ptr(q_energy), k_mean.data_ptr(), _ptr(k_energy), Hkv, NB,
                                   ctypes.byref(p), _ptr(row_mask), idx.data_ptr(), cnt.data_ptr(), _ptr(rp),
                                   _ptr(tau), workspace.data_ptr(), workspace.numel(), _stream()),
@@ -181,7 +181,7 @@ def bsa_sparse_attention_fwd(q, k, v, idx, cnt, p: BsaAttnParams, row_mask=None,
     qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
     need = lib().bsa_attention_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(p))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)   # counters start at zero
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)   # no initial contents needed
     check(lib().bsa_sparse_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),
                                          cnt.data_ptr(), ctypes.byref(p), _ptr(row_mask), ctypes.byref(od),
                                          lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),

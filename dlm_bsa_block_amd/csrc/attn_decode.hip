@@ -11,7 +11,7 @@
 // so the result does not depend on scheduling.  (Merging inside the last
 // workgroup to finish would need a device-scope fence per workgroup, which
 // costs far more than the extra kernel boundary on this chip.)
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 #include "split.h"
 

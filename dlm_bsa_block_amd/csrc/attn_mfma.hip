@@ -12,11 +12,11 @@
 // K/V tiles are copied straight from global memory into LDS (double-buffered)
 // and shared by the waves of a workgroup; each wave owns 32 query vectors.
 // Online softmax in fp32 with exp2; the running max and sum are lane-local
-// (see mfma_tile.cuh).
+// (see mfma_tile.h).
 #include <algorithm>
 
 #include "internal.h"
-#include "mfma_tile.cuh"
+#include "mfma_tile.h"
 #include "split.h"
 
 namespace bsa {
@@ -191,6 +191,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   const float l_tot = pair_sum(l_run);
   if (!SPLIT) {
     if (!valid) return;
+    if (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) return;   // stable row: cached O/LSE stay
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t oi = (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl;
     store_o_row(a.o_f32 ? (void*)(static_cast<float*>(a.o) + oi) : (void*)(static_cast<uint16_t*>(a.o) + oi),
@@ -348,6 +349,8 @@ __global__ __launch_bounds__(512, 1) void gather_stream_kernel(GatherArgs a) {
     const int ln = lane_id();
     const int row = c.wmin - a.q_pos0 + (ln & 31);
     if (32 * wr + (ln & 31) >= a.q_block || row >= a.Lq) return;
+    // a stable row (row_mask 0) keeps its cached O/LSE; the load is made only when a mask is given
+    if (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t oi = (int64_t)b * a.osb + (int64_t)c.h * a.osh + (int64_t)row * a.osl;
     store_o_row(a.o_f32 ? (void*)(static_cast<float*>(a.o) + oi) : (void*)(static_cast<uint16_t*>(a.o) + oi),

@@ -6,7 +6,7 @@
 // One workgroup per (row, batch).  Each thread accumulates a fixed strided
 // subset in fp32, then a fixed-order tree reduction, so the decision is
 // repeatable bit for bit.
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace bsa {

@@ -10,7 +10,7 @@
 //
 // One wave per (batch, head, row), each lane a fixed set of dims: elementwise
 // over HBM, every element read once and written once.
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace bsa {

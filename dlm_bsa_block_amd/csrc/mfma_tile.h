@@ -26,7 +26,7 @@
 // consecutive LDS, i.e. four rows, each lane fetching the chunk that belongs
 // in its slot.
 #pragma once
-#include "common.cuh"
+#include "common.h"
 
 namespace bsa {
 

@@ -6,23 +6,27 @@
 // forced initial/newest blocks follow the NSA page's selection setting; the
 // union over a query block follows the LoSA page (sec. 1-2).
 //
-// Three kernels:
-//   tau_kernel     per (query head, batch): retained band energy of the pooled
-//                  keys (and pooled queries) -> tau[b][h][band]
-//   logits_kernel  LDS-tiled fp32 products z = scale * q.kmean (/ tau), written
-//                  to workspace Z[b][g][row][head-in-group][band][block]
-//   pick_kernel    one wavefront per (selection row, KV group, batch): stages the
-//                  row's logits in LDS, takes the per-head (per-band) softmax over
-//                  the candidates, sums the group score, and runs a wavefront
-//                  radix select of the k' best non-forced blocks (ties -> lower
-//                  index) into an LDS bitmap.  A query block with one selection
-//                  row compacts its bitmap straight into the sorted index list;
-//                  otherwise every row publishes its bitmap and the last row of
-//                  the block to finish (a self-resetting counter) ORs them and
-//                  compacts the union.
+// Kernels:
+//   tau_partial_kernel  per (chunk of pooled vectors, head): band sums of the
+//                       pooled vectors' squared norms and of the mean energies
+//   tau_final_kernel    per (query head, batch): chunk sums in order ->
+//                       tau[b][h][band]
+//   logits_kernel       LDS-tiled fp32 products z = scale * q.kmean (/ tau),
+//                       written to workspace Z[b][g][row][head-in-group][band][block]
+//   pick_kernel         one workgroup per (selection row, KV group, batch):
+//                       per-head (per-band) softmax over the candidates, group
+//                       score, radix select of the k' best non-forced blocks
+//                       (ties -> lower index) into an LDS bitmap.  With one
+//                       selection row per query block the bitmap is compacted
+//                       straight into the sorted index list; otherwise every
+//                       row writes its bitmap to the workspace
+//   union_kernel        per (query block, KV group, batch): OR of the rows'
+//                       bitmaps and an ordered compaction into the list
+// LDS integer atomics (histogram counts, bitmap ORs) are used inside a
+// workgroup; they are order-independent, so the lists are deterministic.
 #include <algorithm>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace bsa {
@@ -121,6 +125,7 @@ struct PickArgs {
   const float* Z;
   int NB, NBp, Rtot, G, Hkv, nbands, NQB;
   int q_block, kv_block, q_pos0, Lq, causal, pooled;
+  int multi_row;           // raw rows with more than one row per query block: rows publish bitmaps
   int topk, topk_num, topk_den, n_first, n_last, cap;
   const uint8_t* row_mask;
   int32_t* idx;
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
   if (w == 0) {
     if (a.row_picks)
       wave_compact(bits, NBW, a.row_picks + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * a.cap, a.cap);
-    if (rp.rows == 1) {
+    if (!a.multi_row) {
       const int n = wave_compact(bits, NBW, a.idx + li * a.cap, 0);
       if (lane == 0) a.cnt[li] = n;
     } else {
@@ -436,8 +441,10 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
 
   if (causal) {
     // highest selection row of the tile -> its last visible block
+    // (the candidates of a raw row are those of its whole query block, as in the pick)
     const int rmax = min(M - 1, m0 + TM - 1) / G;
-    const int last_row = pooled ? min((rmax + 1) * q_block, Lq) - 1 : rmax;
+    const int qbmax = pooled ? rmax : rmax / q_block;
+    const int last_row = min((qbmax + 1) * q_block, Lq) - 1;
     const int jmax = (q_pos0 + last_row) / kv_block;
     if (j0 > jmax) return;
   }
@@ -632,6 +639,7 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
   a.Lq = pl.Lq;
   a.causal = p.causal;
   a.pooled = p.pooled_q;
+  a.multi_row = (!p.pooled_q && std::min(p.q_block, pl.Lq) > 1) ? 1 : 0;
   a.topk = p.topk;
   a.topk_num = p.topk_num;
   a.topk_den = p.topk_den;
@@ -676,7 +684,7 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
   else if (U <= 4) hipLaunchKernelGGL(pick_kernel<4>, pgrid, dim3(kPickThreads), 0, s, a);
   else if (U <= 8) hipLaunchKernelGGL(pick_kernel<8>, pgrid, dim3(kPickThreads), 0, s, a);
   else hipLaunchKernelGGL(pick_kernel<16>, pgrid, dim3(kPickThreads), 0, s, a);
-  if (!p.pooled_q && std::min(p.q_block, pl.Lq) > 1)
+  if (a.multi_row)
     hipLaunchKernelGGL(union_kernel, dim3(pl.NQB, Hkv, pl.B), dim3(64), 0, s, a);
 }
 

@@ -5,7 +5,7 @@
 // D/8 lanes with 16-byte (bf16) or 32-byte (f32) loads, so each wave streams
 // whole contiguous rows; up to four passes of loads are in flight per thread.
 // Reductions run in a fixed order, so results are bitwise repeatable.
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace bsa {

@@ -18,7 +18,7 @@
 #include <cmath>
 
 #include "internal.h"
-#include "mfma_tile.cuh"
+#include "mfma_tile.h"
 
 namespace bsa {
 

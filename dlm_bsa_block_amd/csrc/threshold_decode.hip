@@ -23,7 +23,7 @@
 //
 // The end of the file holds the token selection on a subset of frequency
 // chunks (FASA), which reuses the scores kernel with a chunk mask.
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 #include "split.h"
 

@@ -854,3 +854,96 @@ def test_workspace_reuse(bsa):
             ref = cur
         else:
             assert all(torch.equal(a, b) for a, b in zip(ref, cur)), f"call {it} differs"
+
+
+# ------------------------------------------------ ragged raw query blocks ---
+def _raw_block_case(bsa, w, row_mask_np=None, stale_workspace=False):
+    """Raw multi-row selection and attention on ``w`` (q_block from its params):
+    lists against the oracle (tie band), then every unmasked row's output and
+    LSE; rows with mask 0 must keep their cached values bit for bit.  With
+    ``stale_workspace`` the selection runs on a workspace filled with 0xFF (as
+    left by some other call), which must not leak into any list."""
+    p = w.params
+    qd, kd, vd = _dev_workload(w)
+    B, Hq, Lq, D = qd.shape
+    kmean, _ = bsa.bsa_build_block_summaries(kd, p["kv_block"], p["layout"])
+    mask = None if row_mask_np is None else torch.from_numpy(row_mask_np.astype(np.uint8)).cuda()
+    sp = bsa.select_params(kv_block=p["kv_block"], q_block=p["q_block"], q_pos0=p["q_pos0"], causal=p["causal"],
+                           topk=p["topk"], n_first=p["n_first"], n_last=p["n_last"], layout=p["layout"],
+                           scale=p["scale"], D=D)
+    ws = None
+    if stale_workspace:
+        sp.cap = bsa.list_capacity(kmean.shape[2], min(p["q_block"], Lq), sp)
+        ws = torch.full((bsa.bsa_select_workspace_bytes(qd, kd.shape[1], kmean.shape[2], sp),), 255,
+                        dtype=torch.uint8, device="cuda")
+    idx, cnt, rp, _ = bsa.bsa_select_blocks(qd, kmean, sp, row_mask=mask, want_row_picks=True, workspace=ws)
+    ap = bsa.attn_params(kv_block=p["kv_block"], q_block=p["q_block"], cap=sp.cap, q_pos0=p["q_pos0"],
+                         causal=p["causal"], scale=p["scale"])
+    cache_o = torch.randn(qd.shape, device="cuda")
+    cache_l = torch.randn(qd.shape[:3], device="cuda")
+    o, lse = bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap, row_mask=mask, o=cache_o.clone(),
+                                          lse=cache_l.clone())
+    _sync()
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    km_ref, _ = orc.block_summaries(k, p["kv_block"], p["layout"])
+    m_ref = None if row_mask_np is None else row_mask_np.astype(bool)
+    sel = orc.select_blocks(p, km_ref, q=q, row_mask=m_ref)
+    R = p["q_block"]
+    idx_np, cnt_np, _ = _check_selection(sel, idx, cnt, rp, lambda qb: range(qb * R, min((qb + 1) * R, Lq)),
+                                         w.name)
+    O_ref, L_ref = orc.sparse_attention(p, q, k, v, _reference_lists(sel, idx_np, cnt_np), row_mask=m_ref)
+    act = np.arange(Lq) if m_ref is None else np.nonzero(m_ref[0])[0]
+    o_np, l_np = from_dev(o), lse.cpu().numpy()
+    check_outputs(o_np[:, :, act], O_ref[:, :, act], l_np[:, :, act], L_ref[:, :, act], w.name)
+    if m_ref is not None:
+        stable = np.nonzero(~m_ref[0])[0]
+        assert torch.equal(o[:, :, stable], cache_o[:, :, stable]), "a stable row's output was written"
+        assert torch.equal(lse[:, :, stable], cache_l[:, :, stable]), "a stable row's LSE was written"
+    return cnt_np
+
+
+@pytest.mark.parametrize("Lq,masked,stale", [(33, False, False), (33, True, True), (65, True, False),
+                                             (33, False, True)])
+def test_select_one_row_last_block(bsa, Lq, masked, stale):
+    """Lq % q_block == 1: the last query block has a single row and its list is that row's picks
+    (raw rows, q_block 32), with and without a row mask, on a fresh or a stale workspace."""
+    w = synth.dlm_denoise(L=2048 + 40, R=Lq, n_needles=3)
+    w.params.update(q_block=32)
+    mask = None
+    if masked:
+        rng = np.random.default_rng(Lq)
+        mask = (rng.random((1, Lq)) < 0.4)
+        mask[0, Lq - 1] = True                      # the one-row block is active
+        mask[0, 0] = True
+    cnt = _raw_block_case(bsa, w, mask, stale)
+    assert cnt[0, :, -1].min() > 0
+
+
+def test_select_one_row_last_block_masked_out(bsa):
+    """The single row of the last query block is masked: its list is empty and the row keeps its cache."""
+    w = synth.dlm_denoise(L=1024, R=33, n_needles=2)
+    w.params.update(q_block=32)
+    mask = np.ones((1, 33), dtype=bool)
+    mask[0, 32] = False
+    cnt = _raw_block_case(bsa, w, mask, True)
+    assert (cnt[0, :, 1] == 0).all()
+
+
+@pytest.mark.parametrize("q_pos0,Lq", [(4080, 64), (4090, 45), (4032, 64)])
+def test_select_causal_raw_rows_unaligned(bsa, q_pos0, Lq):
+    """Causal raw multi-row selection where query blocks straddle a KV-block edge: every candidate
+    of a block (up to the block of its last row) is scored for every row of the block."""
+    w = synth.dlm_denoise(L=4160, R=Lq, n_needles=3)
+    w.params.update(q_block=32, q_pos0=q_pos0, causal=1)
+    _raw_block_case(bsa, w)
+
+
+@pytest.mark.parametrize("Hq,Hkv,R", [(16, 2, 32), (6, 2, 64), (8, 1, 48)])
+def test_row_mask_direct_mfma_paths(bsa, Hq, Hkv, R):
+    """Row masks on the direct (non-split) MFMA paths -- group size 8 with 32 rows, odd group size 3
+    with 64 rows, group size 8 with 48 rows: stable rows keep their cached O and LSE bit for bit."""
+    w = synth.dlm_denoise(L=2048 + 64, R=R, Hq=Hq, Hkv=Hkv, n_needles=2, n_active=R // 4)
+    rng = np.random.default_rng(Hq * 100 + R)
+    mask = rng.random((1, R)) < 0.5
+    mask[0, 0] = True
+    _raw_block_case(bsa, w, mask)

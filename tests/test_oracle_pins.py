@@ -580,6 +580,77 @@ def test_threshold_workload_skip_fraction_on_sample():
         assert set(r["kept"]) == window
 
 
+def test_threshold_rule_matches_the_blasst_golden():
+    """The stored skip rule (BLASST technical summary sec. 2, with the prefill workload's
+    "running max - ln(1e3)"): lambda = 1e-3, ln(lambda) as stored; a tile whose max trails the
+    running max by just less than ln(1/lambda) is kept, by just more is skipped."""
+    g = _golden("blasst_rule.txt")
+    assert g["lambda"] == 1e-3 and g["ln_lambda"] == pytest.approx(math.log(g["lambda"]), abs=1e-15)
+    assert synth.threshold_prefill(L=256, Hq=1, Hkv=1, D=16, tile=32, seg_tiles=2, n_needles=1).params["lam"] \
+        == g["lambda"]
+    v = np.random.default_rng(3).standard_normal((4, 4))
+    for delta, kept in ((1e-6, [0, 1]), (-1e-6, [1])):
+        # tile 1 (visited first) has max 0; tile 0's max trails it by |ln lambda| - delta
+        a = np.array([g["ln_lambda"] + delta, g["ln_lambda"] - 5.0, 0.0, -1.0])
+        q = np.zeros((1, 4)); q[0, 0] = 1.0
+        k = np.zeros((4, 4)); k[:, 0] = a
+        r = orc.threshold_walk(q, k, v, np.array([3]), 2, g["lambda"], 1.0, causal=False)
+        assert r["kept"] == kept, (delta, r["kept"])
+        assert r["margin"][0] == pytest.approx(delta, abs=1e-12)
+
+
+@pytest.mark.parametrize("L", [64 * 5 + 19, 64 * 5, 64 * 4 + 1])
+def test_decode_step_refreshes_only_the_newest_block(L):
+    """decode_step pools exactly block (L - 1) // b from K (mean and both band energies), writes no
+    other summary, and then equals selection + attention on the complete summaries.  L is ragged,
+    an exact multiple of b, and one token into a new block."""
+    rng = np.random.default_rng(L)
+    B, Hq, Hkv, D, b = 1, 4, 2, 16, 64
+    q = rng.standard_normal((B, Hq, 1, D))
+    k = rng.standard_normal((B, Hkv, L, D))
+    v = rng.standard_normal((B, Hkv, L, D))
+    p = dict(kv_block=b, q_block=1, q_pos0=L - 1, causal=0, topk=2, topk_num=0, topk_den=1, n_first=1,
+             n_last=1, dual_band=0, layout=ROPE_HALF, scale=1.0 / math.sqrt(D))
+    NB = -(-L // b)
+    j = (L - 1) // b
+    t0 = j * b
+    # the newest block's summary by its definition, written out here: mean and per-band mean energy
+    fast = np.zeros(D, dtype=bool)
+    fast[:D // 4] = True
+    fast[D // 2:D // 2 + D // 4] = True
+    seg = k[:, :, t0:L, :]
+    mean_j = seg.sum(axis=2) / (L - t0)
+    en_j = np.stack([(seg[..., fast] ** 2).sum(axis=(2, 3)), (seg[..., ~fast] ** 2).sum(axis=(2, 3))], -1) / (L - t0)
+    # stale newest block; sentinel values elsewhere must come back untouched
+    km = rng.standard_normal((B, Hkv, NB, D)) + 100.0
+    ke = rng.standard_normal((B, Hkv, NB, 2)) + 100.0
+    km_in, ke_in = km.copy(), ke.copy()
+    orc.decode_step(p, q, k, v, km, ke)
+    others = np.arange(NB) != j
+    assert np.array_equal(km[:, :, others], km_in[:, :, others])
+    assert np.array_equal(ke[:, :, others], ke_in[:, :, others])
+    assert np.allclose(km[:, :, j], mean_j, atol=1e-12) and np.allclose(ke[:, :, j], en_j, atol=1e-12)
+    # with correct older summaries the step equals the separate pieces on the full summaries
+    km_full, ke_full = orc.block_summaries(k, b, ROPE_HALF)
+    km2, ke2 = km_full.copy(), ke_full.copy()
+    km2[:, :, j] = 0.0
+    ke2[:, :, j] = 0.0
+    O, LSE, lists = orc.decode_step(p, q, k, v, km2, ke2)
+    assert np.allclose(km2, km_full, atol=1e-12) and np.allclose(ke2, ke_full, atol=1e-12)
+    sel = orc.select_blocks(p, km_full, q=q)
+    O2, L2 = orc.sparse_attention(p, q, k, v, sel["lists"])
+    for g in range(Hkv):
+        assert np.array_equal(lists[0][g][0], sel["lists"][0][g][0])
+        assert len(lists[0][g][0]) == min(NB, 4) and {0, NB - 1} <= set(lists[0][g][0].tolist())
+    assert np.allclose(O, O2, atol=1e-12) and np.allclose(LSE, L2, atol=1e-12)
+    # and with every block listed it is dense attention over all L keys
+    p_all = dict(p, topk=NB)
+    O3, L3, _ = orc.decode_step(p_all, q, k, v, km_full.copy(), ke_full.copy())
+    for h in range(Hq):
+        o_d, l_d = _dense(q[0, h], k[0, h // 2], v[0, h // 2], p["scale"])
+        assert np.allclose(O3[0, h], o_d, atol=1e-12) and np.allclose(L3[0, h], l_d)
+
+
 # --------------------------------------------------------------- generators ---
 def test_bf16_rounding_matches_torch():
     torch = pytest.importorskip("torch")
