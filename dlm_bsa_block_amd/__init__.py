@@ -21,7 +21,7 @@ from ._lib import (  # noqa: F401
 __all__ = ["bsa_build_block_summaries", "bsa_select_blocks", "bsa_active_rows", "bsa_merge_attention_states",
            "bsa_block_attention_merge", "bsa_window_decode_fwd", "bsa_window_decode_workspace_bytes",
            "bsa_token_select", "bsa_token_attention_fwd", "bsa_select_blocks_refresh",
-           "bsa_sparse_attention_fwd",
+           "bsa_sparse_attention_fwd", "bsa_sparse_attention_fwd_noalloc",
            "bsa_threshold_attention_fwd", "bsa_threshold_decode_fwd", "bsa_select_workspace_bytes",
            "bsa_attention_workspace_bytes", "bsa_threshold_decode_workspace_bytes",
            "BsaError", "tensor_desc", "select_params", "attn_params", "lib"]
@@ -186,6 +186,17 @@ def bsa_sparse_attention_fwd(q, k, v, idx, cnt, p: BsaAttnParams, row_mask=None,
                                          cnt.data_ptr(), ctypes.byref(p), _ptr(row_mask), ctypes.byref(od),
                                          lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
           "bsa_sparse_attention_fwd")
+    return o, lse
+
+
+def bsa_sparse_attention_fwd_noalloc(q, k, v, idx, cnt, p: BsaAttnParams, o, lse, row_mask=None):
+    """bsa_sparse_attention_fwd with its partials in the library's static device scratch: nothing is
+    allocated, so o and lse must be given.  Returns (o, lse)."""
+    qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
+    check(lib().bsa_sparse_attention_fwd_noalloc(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+                                                 idx.data_ptr(), cnt.data_ptr(), ctypes.byref(p), _ptr(row_mask),
+                                                 ctypes.byref(od), lse.data_ptr(), _stream()),
+          "bsa_sparse_attention_fwd_noalloc")
     return o, lse
 
 

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 
@@ -265,6 +266,66 @@ bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, co
   if (q->L == 0) { g_err[0] = 0; return BSA_OK; }
   launch_attention(*q, *k, *v, idx, cnt, *p, pl, row_mask, *o, lse, workspace, static_cast<hipStream_t>(stream));
   return check_launch("sparse attention");
+}
+
+// ------------------------------------------ attention without a workspace ---
+// bsa_sparse_attention_fwd_noalloc keeps its split-KV partials in this array
+// instead of a caller's workspace.  Each GPU the library runs on holds its own
+// copy until the process ends.  Host code never passes the array's name to a
+// kernel: it asks for the device address once per device and uses that.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kScratchDevices];
+
+// Device address of `scratch` on the device that runs `stream` (which must be
+// the current device); looked up on the first call for that device.
+static bsa_status scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (sdev != dev) return fail(BSA_ERR_INVALID, "stream belongs to device %d, the current device is %d", sdev, dev);
+  }
+  if (dev < 0 || dev >= kScratchDevices) return fail(BSA_ERR_UNSUPPORTED, "device ordinal %d >= %d", dev, kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(BSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return BSA_OK;
+}
+
+size_t bsa_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+bsa_status bsa_sparse_attention_fwd_noalloc(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                            const int32_t* idx, const int32_t* cnt, const bsa_attn_params* p,
+                                            const uint8_t* row_mask, const bsa_tensor* o, float* lse, void* stream) {
+  AttnPlan pl;
+  bsa_status st = validate_attention(q, k, v, p, pl);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(o, "o", true)) != BSA_OK) return st;
+  if (!same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
+    return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
+  if (!idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "idx, cnt and lse are required");
+  if (pl.part_bytes > kScratchBytes)
+    return fail(BSA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu",
+                pl.part_bytes, kScratchBytes);
+  if (q->L == 0) { g_err[0] = 0; return BSA_OK; }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (pl.part_bytes && (st = scratch_for_stream(s, &ws)) != BSA_OK) return st;
+  launch_attention(*q, *k, *v, idx, cnt, *p, pl, row_mask, *o, lse, ws, s);
+  return check_launch("sparse attention (static scratch)");
 }
 
 // ------------------------------------------------ selection + sliding window ---

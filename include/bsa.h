@@ -221,6 +221,28 @@ bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, co
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * bsa_sparse_attention_fwd without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, results and errors as
+ * bsa_sparse_attention_fwd; the split-KV partials go to a static device
+ * array of bsa_noalloc_scratch_bytes() bytes (64 MiB) that each GPU the
+ * library runs on holds until the process ends (its address is looked up
+ * once per device, on the first call there).  The call allocates and frees
+ * nothing.  Errors besides those of bsa_sparse_attention_fwd:
+ * BSA_ERR_WORKSPACE when the call needs more scratch than that (the size
+ * bsa_attention_workspace_bytes reports); BSA_ERR_INVALID when `stream`
+ * belongs to a device other than the current one.  The array keeps the last
+ * call's contents (no call needs them cleared); calls that overlap on one GPU
+ * share it and race, so keep them on one stream or order them.
+ * ------------------------------------------------------------------------ */
+size_t bsa_noalloc_scratch_bytes(void);
+
+bsa_status bsa_sparse_attention_fwd_noalloc(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                            const int32_t* idx, const int32_t* cnt, const bsa_attn_params* p,
+                                            const uint8_t* row_mask, const bsa_tensor* o, float* lse,
+                                            void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Softmax-threshold attention (BLASST sec. 2).  Per head and query tile of
  * `tile` rows, KV tiles are visited from the last one the tile can see down
  * to tile 0.  For a visited tile, S = scale * q k^T (causal-masked) and

@@ -139,6 +139,26 @@ def test_attention_rejects_bad_arguments(lib):
     assert st == L.BSA_ERR_INVALID and "o must match q" in _err(lib)
 
 
+def test_attention_noalloc_rejects_on_the_host(lib):
+    """The no-workspace attention validates like the workspace form and refuses a call whose
+    partials would not fit its static scratch, before touching the device."""
+    assert lib.bsa_noalloc_scratch_bytes() == 64 << 20
+    q, k = _t(H=32, Lq=4096), _t(H=8, Lq=4096)
+    p = bsa.attn_params(kv_block=64, q_block=32, cap=64)
+    need = lib.bsa_attention_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(p))
+    assert need > lib.bsa_noalloc_scratch_bytes()
+    st = lib.bsa_sparse_attention_fwd_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), FAKE, FAKE,
+                                              ctypes.byref(p), None, ctypes.byref(q), FAKE, None)
+    assert st == L.BSA_ERR_WORKSPACE and "static scratch" in _err(lib)
+    p96 = bsa.attn_params(kv_block=96, q_block=32, cap=64)
+    st = lib.bsa_sparse_attention_fwd_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), FAKE, FAKE,
+                                              ctypes.byref(p96), None, ctypes.byref(q), FAKE, None)
+    assert st == L.BSA_ERR_UNSUPPORTED
+    st = lib.bsa_sparse_attention_fwd_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), None, FAKE,
+                                              ctypes.byref(p), None, ctypes.byref(q), FAKE, None)
+    assert st == L.BSA_ERR_INVALID
+
+
 def test_threshold_rejects_bad_arguments(lib):
     q, k = _t(H=32, Lq=1024), _t(H=8, Lq=1024)
     for lam, tile, want in ((1.5, 128, L.BSA_ERR_INVALID), (-0.1, 128, L.BSA_ERR_INVALID),
