@@ -28,6 +28,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "wave_select.h"
 
 namespace bsa {
 
@@ -243,25 +244,22 @@ __device__ int wave_compact(const uint32_t* bits, int nw, int32_t* out, int pad_
 // candidates j = t + 256*u.  Per (head, band) channel: block-wide max, sum of
 // exp2 (logits are in log2 units), then the group score s[j] = sum over
 // channels of w * exp2(z - M) / S in a fixed channel order, kept in registers.
-// The k' best free candidates (ties -> lower index) come from a workgroup
-// radix select (four 8-bit passes over the score bits, LDS histogram); forced
-// blocks are always taken.  Blocks with one selection row write their sorted
-// list directly; otherwise the row's bitmap goes to the workspace for the
-// union kernel.
+// The scores go to LDS as order-preserving keys and one wavefront takes the k'
+// best free candidates (ties -> lower index; wave_topk) and adds the forced
+// blocks.  Blocks with one selection row write their sorted list directly;
+// otherwise the row's bitmap goes to the workspace for the union kernel.
 template <int U>
 __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t bits[kPickMaxWords];
+  constexpr int KPL = 4 * U;                          // keys per lane of the selecting wave
+  __shared__ uint32_t keys_sh[kPickThreads * U];
   __shared__ float red[2 * kPickChanBatch * 4];
-  __shared__ int misc[2];
-  __shared__ int eqcnt[U][4];
+  __shared__ __attribute__((aligned(16))) uint32_t cand_sh[64];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const RowPlan rp = row_plan(a, row);
   const int NBW = (a.NB + 31) / 32, nC = rp.nC, NBp = a.NBp;
   const int nchan = a.G * a.nbands;
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + rp.qb;
-  if (tid < kPickMaxWords) bits[tid] = 0u;
   const bool active = a.pooled || !a.row_mask || a.row_mask[(int64_t)b * a.Lq + row] != 0;
   if (active) {
     const float* zrow = a.Z + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * (int64_t)nchan * NBp;
@@ -309,85 +307,34 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
       }
       __syncthreads();                                  // red[] is reused by the next batch
     }
-    // ---- keys: free candidates only; scores are >= 0, so float bits order like values
-    uint32_t key[U];
+    // keys: free candidates only; scores are >= 0, so float bits order like values
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = tid + kPickThreads * u;
-      key[u] = (j < nC && j >= rp.nf_first && j < rp.last_lo) ? __float_as_uint(s[u]) + 1u : 0u;
-    }
-    uint32_t T = 0xFFFFFFFFu;
-    int need_eq = 0;
-    if (rp.kp > 0 && rp.kp < rp.n_free) {
-      uint32_t prefix = 0, pmask = 0;
-      int remaining = rp.kp;
-      for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        hist[tid] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (key[u] != 0u && (key[u] & pmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255u], 1u);
-        __syncthreads();
-        if (w == 0) {
-          // lane owns digits 255-4*lane .. 252-4*lane; prefix sum in descending digit order
-          uint32_t c[4], tot = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; tot += c[i]; }
-          const uint32_t incl = wave_incl_scan_dpp(tot);
-          uint32_t run = incl - tot;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (run < (uint32_t)remaining && run + c[i] >= (uint32_t)remaining) {
-              misc[0] = 255 - 4 * lane - i;
-              misc[1] = (int)run;
-            }
-            run += c[i];
-          }
-        }
-        __syncthreads();
-        remaining -= misc[1];
-        prefix |= (uint32_t)misc[0] << shift;
-        pmask |= 0xFFu << shift;
-      }
-      T = prefix;
-      need_eq = remaining;
-    } else if (rp.kp > 0) {
-      T = 1u;                       // every free candidate
-      need_eq = 1 << 30;
-    }
-    // ---- ties at T go to the lowest indices: rank equal keys in j order
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const unsigned long long m = __ballot(key[u] != 0u && key[u] == T);
-      if (lane == 0) eqcnt[u][w] = __popcll(m);
-    }
-    __syncthreads();
-    int before = 0;                                     // equal keys at smaller j
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool eq = key[u] != 0u && key[u] == T;
-      const unsigned long long m = __ballot(eq);
-      int rank = before + __popcll(m & ((1ull << lane) - 1ull));
-      for (int ww = 0; ww < w; ++ww) rank += eqcnt[u][ww];
-      const int j = tid + kPickThreads * u;
-      const bool forced = j < nC && (j < rp.nf_first || j >= rp.last_lo);
-      const bool take = forced || (key[u] != 0u && key[u] > T) || (eq && rank < need_eq);
-      if (take) atomicOr(&bits[j >> 5], 1u << (j & 31));
-      before += eqcnt[u][0] + eqcnt[u][1] + eqcnt[u][2] + eqcnt[u][3];
+      keys_sh[j] = (j < nC && j >= rp.nf_first && j < rp.last_lo) ? __float_as_uint(s[u]) + 1u : 0u;
     }
   }
   __syncthreads();
-  if (w == 0) {
-    if (a.row_picks)
-      wave_compact(bits, NBW, a.row_picks + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * a.cap, a.cap);
-    if (!a.multi_row) {
-      const int n = wave_compact(bits, NBW, a.idx + li * a.cap, 0);
-      if (lane == 0) a.cnt[li] = n;
-    } else {
-      uint32_t* mine = a.row_bits + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * kPickMaxWords;
-      for (int i = lane; i < NBW; i += 64) mine[i] = bits[i];
+  if (w != 0) return;
+  uint64_t flags = 0;
+  if (active) {
+    uint32_t k[KPL];                                  // lane l holds blocks KPL l .. KPL l + KPL - 1
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) k[i] = keys_sh[KPL * lane + i];
+    flags = wave_topk<KPL>(k, rp.kp, rp.n_free, cand_sh);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int j = KPL * lane + i;
+      if (j < nC && (j < rp.nf_first || j >= rp.last_lo)) flags |= 1ull << i;    // forced blocks
     }
+  }
+  if (a.row_picks)
+    wave_flags_to_list<KPL>(flags, a.row_picks + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * a.cap, a.cap);
+  if (!a.multi_row) {
+    const int n = wave_flags_to_list<KPL>(flags, a.idx + li * a.cap, 0);
+    if (lane == 0) a.cnt[li] = n;
+  } else {
+    wave_flags_to_bits<KPL>(flags, a.row_bits + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * kPickMaxWords, NBW);
   }
 }
 

@@ -947,3 +947,33 @@ def test_row_mask_direct_mfma_paths(bsa, Hq, Hkv, R):
     mask = rng.random((1, R)) < 0.5
     mask[0, 0] = True
     _raw_block_case(bsa, w, mask)
+
+
+def test_select_exact_ties_take_lower_blocks(bsa):
+    """21 copies of one needle block (bit-identical summaries, so equal scores in any precision)
+    compete for 13 scored picks: the selection takes the 13 lowest block indices among them."""
+    w = synth.gqa_decode(L=4096, Hq=8, Hkv=2, n_needles=1)
+    p = w.params
+    k = w.k.copy()
+    copies = {}
+    for g in range(2):
+        nd = int(w.extra["needles"][g, 0])
+        others = [j for j in range(1, 61) if j != nd][g * 3:g * 3 + 20]
+        for j in others:
+            k[0, g, 64 * j:64 * (j + 1)] = w.k[0, g, 64 * nd:64 * (nd + 1)]
+        copies[g] = sorted(others + [nd])
+    w.k = k
+    qd, kd, vd = _dev_workload(w)
+    kmean, _ = bsa.bsa_build_block_summaries(kd, 64, p["layout"])
+    idx, cnt, rp, cap = _select_raw(bsa, w, qd, kmean)
+    _sync()
+    idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
+    NB = 64
+    for g in range(2):
+        got = set(idx_np[0, g, 0, :cnt_np[0, g, 0]].tolist())
+        assert got == {0, NB - 2, NB - 1} | set(copies[g][:13]), (g, sorted(got))
+    # the oracle agrees (its exact fp64 ties also go to the lower index)
+    km_ref, _ = orc.block_summaries(w.f64("k"), 64, p["layout"])
+    sel = orc.select_blocks(p, km_ref, q=w.f64("q"))
+    for g in range(2):
+        assert set(sel["lists"][0][g][0].tolist()) == {0, NB - 2, NB - 1} | set(copies[g][:13])
