@@ -21,7 +21,8 @@ from ._lib import (  # noqa: F401
 __all__ = ["bsa_build_block_summaries", "bsa_select_blocks", "bsa_active_rows", "bsa_merge_attention_states",
            "bsa_block_attention_merge", "bsa_window_decode_fwd", "bsa_window_decode_workspace_bytes",
            "bsa_token_select", "bsa_token_attention_fwd", "bsa_select_blocks_refresh",
-           "bsa_sparse_attention_fwd", "bsa_sparse_attention_fwd_noalloc",
+           "bsa_sparse_attention_fwd", "bsa_sparse_attention_fwd_noalloc", "bsa_decode_step",
+           "bsa_decode_step_workspace_bytes",
            "bsa_threshold_attention_fwd", "bsa_threshold_decode_fwd", "bsa_select_workspace_bytes",
            "bsa_attention_workspace_bytes", "bsa_threshold_decode_workspace_bytes",
            "BsaError", "tensor_desc", "select_params", "attn_params", "lib"]
@@ -224,6 +225,39 @@ def bsa_select_blocks_refresh(k, refresh_block: int, q, k_mean, p: BsaSelectPara
                                           cnt.data_ptr(), _ptr(rp), workspace.data_ptr(), workspace.numel(),
                                           _stream()), "bsa_select_blocks_refresh")
     return idx, cnt, rp
+
+
+def bsa_decode_step_workspace_bytes(q, k, p: BsaSelectParams) -> int:
+    return int(lib().bsa_decode_step_workspace_bytes(ctypes.byref(tensor_desc(q)), ctypes.byref(tensor_desc(k)),
+                                                     ctypes.byref(p)))
+
+
+def bsa_decode_step(q, k, v, k_mean, p: BsaSelectParams, refresh_block: int = -1, k_energy=None, idx=None, cnt=None,
+                    o=None, lse=None, workspace=None):
+    """Selection (with the summary of block ``refresh_block`` pooled first, unless -1) and attention over the
+    selected blocks for decode rows.  Returns (idx [B,Hkv,Lq,cap], cnt [B,Hkv,Lq], o, lse [B,Hq,Lq])."""
+    B, Hq, Lq, D = q.shape
+    Hkv, NB = k_mean.shape[1], k_mean.shape[2]
+    if p.cap <= 0:
+        p.cap = list_capacity(NB, 1, p)
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((B, Hkv, Lq, p.cap), dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv, Lq), dtype=torch.int32, device=dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev)
+    need = bsa_decode_step_workspace_bytes(q, k, p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)   # zero before its first use
+    qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
+    check(lib().bsa_decode_step(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), k_mean.data_ptr(),
+                                _ptr(k_energy), refresh_block, ctypes.byref(p), idx.data_ptr(), cnt.data_ptr(),
+                                ctypes.byref(od), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _stream()), "bsa_decode_step")
+    return idx, cnt, o, lse
 
 
 def bsa_window_decode_workspace_bytes(q, k, p: BsaAttnParams, window: int) -> int:

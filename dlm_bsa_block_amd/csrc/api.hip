@@ -196,6 +196,71 @@ bsa_status bsa_select_blocks_refresh(const bsa_tensor* k, int32_t refresh_block,
   return check_launch("block selection with refresh");
 }
 
+// ------------------------------------------------------------- decode step ---
+static bsa_status validate_decode_step(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                       const bsa_select_params* p, DStepPlan& pl) {
+  if (!p) return fail(BSA_ERR_INVALID, "params: null");
+  bsa_status st = check_tensor(q, "q", false);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(k, "k", false)) != BSA_OK) return st;
+  if ((st = check_tensor(v, "v", false)) != BSA_OK) return st;
+  if (!same_shape(k, v)) return fail(BSA_ERR_INVALID, "k and v differ in shape or dtype");
+  if (q->dtype != k->dtype) return fail(BSA_ERR_INVALID, "q and k differ in dtype");
+  if (q->B != k->B || q->D != k->D || q->H % k->H) return fail(BSA_ERR_INVALID, "q/k shapes are incompatible");
+  const int G = q->H / k->H;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(BSA_ERR_UNSUPPORTED, "Hq/Hkv %d (supported: 1, 2, 4, 8)", G);
+  if (p->q_block != 1 || p->pooled_q || p->dual_band)
+    return fail(BSA_ERR_UNSUPPORTED, "the decode step takes decode rows (q_block 1), raw queries and one band");
+  if (p->kv_block <= 0) return fail(BSA_ERR_INVALID, "kv_block must be positive");
+  if (p->topk < 0 || p->topk_num < 0 || p->topk_den <= 0 || p->n_first < 0 || p->n_last < 0)
+    return fail(BSA_ERR_INVALID, "negative budget or topk_den <= 0");
+  if (p->layout != BSA_ROPE_HALF && p->layout != BSA_ROPE_INTERLEAVED) return fail(BSA_ERR_INVALID, "layout %d", p->layout);
+  if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(BSA_ERR_INVALID, "scale must be finite and > 0");
+  if (p->q_pos0 < 0) return fail(BSA_ERR_INVALID, "negative q_pos0");
+  const int64_t NB = ceil_div(k->L, p->kv_block);
+  if (NB > 4096) return fail(BSA_ERR_UNSUPPORTED, "%lld KV blocks > 4096", (long long)NB);
+  const int64_t kp = p->topk_num > 0 ? ceil_div((int64_t)p->topk_num * NB, p->topk_den) : p->topk;
+  const int64_t bound = std::min<int64_t>(NB, kp + p->n_first + p->n_last);
+  if (p->cap < bound)
+    return fail(BSA_ERR_CAPACITY, "cap %d < %lld (k' %lld + forced %d)", p->cap, (long long)bound, (long long)kp,
+                p->n_first + p->n_last);
+  if ((int64_t)p->cap * p->kv_block >= (int64_t(1) << 31)) return fail(BSA_ERR_UNSUPPORTED, "cap * kv_block too large");
+  plan_decode_step(*q, *k, *p, pl);
+  return BSA_OK;
+}
+
+size_t bsa_decode_step_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, const bsa_select_params* p) {
+  DStepPlan pl;
+  if (!k || validate_decode_step(q, k, k, p, pl) != BSA_OK) return 0;
+  return pl.z_bytes + pl.stats_bytes + pl.part_o_bytes + pl.part_ml_bytes + pl.arrival_bytes;
+}
+
+bsa_status bsa_decode_step(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, float* k_mean,
+                           float* k_energy, int32_t refresh_block, const bsa_select_params* p, int32_t* idx,
+                           int32_t* cnt, const bsa_tensor* o, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  DStepPlan pl;
+  bsa_status st = validate_decode_step(q, k, v, p, pl);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(o, "o", false)) != BSA_OK) return st;
+  if (!same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
+    return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
+  if (!k_mean || !idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "k_mean, idx, cnt and lse are required");
+  if (!aligned16(k_mean) || (k_energy && (reinterpret_cast<uintptr_t>(k_energy) & 7u)))
+    return fail(BSA_ERR_INVALID, "k_mean must be 16-byte and k_energy 8-byte aligned");
+  if (refresh_block < -1 || refresh_block >= pl.NB)
+    return fail(BSA_ERR_INVALID, "refresh_block %d outside [-1, %d)", refresh_block, pl.NB);
+  if (refresh_block >= 0 && p->causal && (int64_t)refresh_block * p->kv_block > p->q_pos0)
+    return fail(BSA_ERR_INVALID, "refresh_block %d is not visible to the first query row", refresh_block);
+  const size_t need = pl.z_bytes + pl.stats_bytes + pl.part_o_bytes + pl.part_ml_bytes + pl.arrival_bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  launch_decode_step(*q, *k, *v, k_mean, k_energy, refresh_block, *p, pl, idx, cnt, *o, lse, workspace,
+                     static_cast<hipStream_t>(stream));
+  return check_launch("decode step");
+}
+
 // ------------------------------------------------------------- active rows ---
 bsa_status bsa_active_rows(const bsa_tensor* q_cur, const bsa_tensor* q_prev, float theta, uint8_t* row_mask,
                            float* mse, void* stream) {

@@ -1,0 +1,565 @@
+// A decode step of selected-block attention in two launches.
+//
+//   dstep_logits_kernel   block logits of every decode row against the pooled
+//                         key summaries (Prism sec. 1: a block is scored by the
+//                         mean of its keys), with the newest block's summary
+//                         pooled from K first when asked (its tokens change
+//                         every step), plus each wavefront's softmax partials
+//                         (max and sum of exp2 over its 8 blocks) per head
+//   dstep_attend_kernel   per (slice of the list, row, KV group): the group
+//                         scores s[j] = sum over the group's heads of
+//                         softmax_h(z)[j] from the logits and the merged
+//                         partials, the k' best plus the forced blocks (NSA
+//                         structure section: block 0 and the newest ones) --
+//                         computed identically by every workgroup of the
+//                         group, so no launch sits between selection and
+//                         attention -- then the workgroup's slice of the
+//                         list's tokens, G query heads sharing each K/V load
+//                         (NSA implementation section).  The slice's partial
+//                         (m, l, o) is published with device-scope stores and
+//                         counted; the workgroup that counts last merges all
+//                         slices in order and writes O and LSE.
+//
+// Measured here: a kernel boundary costs about 4.5 us (the end-of-kernel cache
+// write-back plus the next dispatch), a device-scope release fence about
+// 10 us (it writes back the whole L2), a device-scope atomic or load 1-2 us.
+// The logits need every summary of the group, hence the one boundary; the
+// merge of the slices goes through device-scope stores and a counter, which
+// need no fence.
+//
+// The lists, outputs and LSE are those of bsa_select_blocks_refresh followed
+// by bsa_sparse_attention_fwd on the same arguments, up to fp32 rounding of the
+// scores (the normalisers are summed in another order).
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+#include "split.h"
+#include "wave_select.h"
+
+namespace bsa {
+
+struct DStepArgs {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  int64_t qsb, qsh, qsl, ksb, ksh, ksl, vsb, vsh, vsl;
+  float* k_mean;                  // [B][Hkv][NB][D]
+  float* k_energy;                // [B][Hkv][NB][2] or null
+  int refresh;                    // block pooled from K in this step, or -1
+  int B, Hkv, Lq, L, NB, NBp, kv_block, q_pos0, causal, layout;
+  int topk, topk_num, topk_den, n_first, n_last, cap;
+  float c2;                       // scale * log2(e)
+  float* Z;                       // [B][Hkv][Lq][G][NBp] logits (log2 units)
+  float* stats;                   // [B][Hkv][Lq][G][P][2] per-wavefront (max, sum of exp2)
+  int P;                          // wavefronts of the logits launch per row: 4 * ceil(NB / 32)
+  int32_t* idx;
+  int32_t* cnt;
+  float* part_o;                  // [B][Hkv][Lq][items][G][D]
+  float* part_ml;                 // [B][Hkv][Lq][items][G][2]
+  uint32_t* arrivals;             // [B][Hkv][Lq] x 32 words: slices finished (zeroed by the logits launch)
+  int items, tok_per_item;
+  void* o;                        // [B][Hq][Lq][D], bf16 or f32
+  int o_f32;
+  int64_t osb, osh, osl;
+  float* lse;                     // [B][Hq][Lq]
+};
+
+// Device-scope (coherent across the XCDs' L2 caches) stores and loads: the
+// partials a workgroup hands to the merging one go through these, so no cache
+// write-back or invalidation is needed.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev2(float* p, float lo, float hi) {
+  const uint64_t v = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 ld_dev2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+}
+
+// ------------------------------------------------------------------ logits ---
+// Workgroup = 4 waves x 8 blocks; 8 lanes per block, D / 8 dims per lane.
+template <int DT, int D, int G>
+__global__ __launch_bounds__(256) void dstep_logits_kernel(DStepArgs a) {
+  constexpr int ES = DT == BSA_BF16 ? 2 : 4;
+  constexpr int DPL = D / 8;
+  __shared__ float pooled[4][D];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int row = blockIdx.y, bg = blockIdx.z, b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int jw0 = blockIdx.x * 32 + w * 8;
+  const int j = jw0 + (lane >> 3), sub = lane & 7, d0 = sub * DPL;
+  const int qpos = a.q_pos0 + row;
+  const int nC = a.causal ? min(a.NB, qpos / a.kv_block + 1) : a.NB;
+  const bool valid = j < nC;
+
+  float qx[G][DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint8_t* qp = a.q + ((int64_t)b * a.qsb + (int64_t)(g * G + h) * a.qsh + (int64_t)row * a.qsl + d0) * ES;
+#pragma unroll
+    for (int c = 0; c < DPL / 8; ++c) {
+      float t[8];
+      load8<DT>(qp + c * 8 * ES, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qx[h][c * 8 + e] = t[e];
+    }
+  }
+  const int64_t mrow = ((int64_t)b * a.Hkv + g) * a.NB;
+  float km[DPL];
+  if (valid && j != a.refresh) {
+    const f32x4* mp = reinterpret_cast<const f32x4*>(a.k_mean + (mrow + j) * D + d0);
+#pragma unroll
+    for (int c = 0; c < DPL / 4; ++c) {
+      const f32x4 t = mp[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) km[4 * c + e] = t[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) km[e] = 0.f;
+  }
+  // the newest block: pooled here from K (Prism sec. 1-2 summary, as bsa_build_block_summaries), used and written out
+  if (a.refresh >= jw0 && a.refresh < jw0 + 8 && a.refresh < nC) {   // uniform over the wave
+    constexpr int LPR = D / 8, RPP = 64 / LPR;                         // lanes per K row, rows per pass
+    const int c = lane % LPR, rg = lane / LPR;
+    const int t0 = a.refresh * a.kv_block, n = min(a.kv_block, a.L - t0);
+    const uint8_t* kp = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + (int64_t)t0 * a.ksl + c * 8) * ES;
+    float sum[8], e2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] = 0.f;
+    constexpr int NP = 64 / RPP;                                       // 64 rows per round, all loads in flight
+    for (int r0 = 0; r0 < n; r0 += 64) {
+      float x[NP][8];
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const int r = r0 + u * RPP + rg;
+        if (r < n) load8<DT>(kp + (int64_t)r * a.ksl * ES, x[u]);
+        else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NP; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { sum[e] += x[u][e]; e2 = fmaf(x[u][e], x[u][e], e2); }
+    }
+    // fold the row groups: lanes c, c + LPR, ... (LPR = 16: two swaps; LPR = 8: three)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] = LPR == 16 ? groups_sum<16>(sum[e]) : groups_sum<8>(sum[e]);
+    const int band = band_of_dim(c * 8, D, a.layout);
+    const float ef = wave_sum_dpp(band == 0 ? e2 : 0.f), es = wave_sum_dpp(band == 0 ? 0.f : e2);
+    const float inv = 1.0f / (float)n;
+    if (rg == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pooled[w][c * 8 + e] = sum[e] * inv;
+    }
+    wave_sync_lds();
+    if (j == a.refresh) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) km[e] = pooled[w][d0 + e];
+    }
+    if (row == 0) {
+      if (rg == 0) {
+        f32x4* mo = reinterpret_cast<f32x4*>(a.k_mean + (mrow + a.refresh) * D + c * 8);
+        mo[0] = f32x4{pooled[w][c * 8], pooled[w][c * 8 + 1], pooled[w][c * 8 + 2], pooled[w][c * 8 + 3]};
+        mo[1] = f32x4{pooled[w][c * 8 + 4], pooled[w][c * 8 + 5], pooled[w][c * 8 + 6], pooled[w][c * 8 + 7]};
+      }
+      if (a.k_energy && lane == 0) {
+        a.k_energy[(mrow + a.refresh) * 2] = ef * inv;
+        a.k_energy[(mrow + a.refresh) * 2 + 1] = es * inv;
+      }
+    }
+  }
+
+  float z[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) dot = fmaf(qx[h][e], km[e], dot);
+    dot = group_sum<8>(dot);
+    z[h] = valid ? dot * a.c2 : -INFINITY;
+  }
+  const int64_t rowi = ((int64_t)b * a.Hkv + g) * a.Lq + row;
+  if (blockIdx.x == 0 && tid == 0) a.arrivals[rowi * 32] = 0u;   // the attention launch counts its slices here
+  if (valid) {
+    float mine = z[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) mine = sub == h ? z[h] : mine;
+    if (sub < G) a.Z[(rowi * G + sub) * a.NBp + j] = mine;
+  }
+  // this wave's softmax partial per head over its 8 blocks
+  const int wi = blockIdx.x * 4 + w;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float m = groups_max<8>(z[h]);
+    const float e = m == -INFINITY ? 0.f : fast_exp2(z[h] - m);
+    const float l = groups_sum<8>(e);
+    if (lane == h) {
+      float* st = a.stats + ((rowi * G + h) * a.P + wi) * 2;
+      st[0] = m;
+      st[1] = l;
+    }
+  }
+}
+
+// -------------------------------------------------------- select + attend ---
+template <int DT, int D, int G, int KPL>
+__global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
+  constexpr int ES = DT == BSA_BF16 ? 2 : 4;
+  constexpr int KPT = KPL / 4;          // keys per thread: blocks KPT t .. KPT t + KPT - 1
+  constexpr int SPL = KPL / 8;          // softmax partials per lane and head (P <= 64 * SPL)
+  constexpr int LPT = D / 8;            // lanes per token
+  constexpr int TPP = 64 / LPT;         // tokens per wave pass
+  constexpr int TPW = kDecTok / 4;      // tokens per wave and chunk
+  constexpr int PASSES = TPW / TPP;
+  __shared__ BlockTopkSmem topk_sh;
+  __shared__ int32_t lst[64 * KPL];                 // the row's list, ascending
+  __shared__ int last_sh;
+  __shared__ float sm_m[4][G], sm_l[4][G];
+  __shared__ float sm_acc[4][G][D];
+
+  const int item = blockIdx.x, row = blockIdx.y, bg = blockIdx.z;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tg = lane / LPT, d0 = (lane % LPT) * 8;
+  const int qpos = a.q_pos0 + row;
+  const int64_t rowi = ((int64_t)b * a.Hkv + g) * a.Lq + row;
+  // candidates, forced blocks and k' of this row (as the selection entry point)
+  const int nC = a.causal ? min(a.NB, qpos / a.kv_block + 1) : a.NB;
+  const int nf_first = min(a.n_first, nC);
+  const int last_lo = max(nf_first, nC - a.n_last);
+  const int n_free = last_lo - nf_first;
+  int kp = a.topk_num > 0 ? (int)(((int64_t)a.topk_num * nC + a.topk_den - 1) / a.topk_den) : a.topk;
+  kp = max(0, min(kp, n_free));
+
+  // ---- loads: queries (for the attention), softmax partials, logits
+  float qx[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    load8<DT>(a.q + ((int64_t)b * a.qsb + (int64_t)(g * G + h) * a.qsh + (int64_t)row * a.qsl + d0) * ES, qx[h]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qx[h][e] *= a.c2;
+  }
+  f32x2 st[G][SPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int r = 0; r < SPL; ++r) {
+      const int pi = lane + 64 * r;
+      st[h][r] = pi < a.P ? *reinterpret_cast<const f32x2*>(a.stats + ((rowi * G + h) * a.P + pi) * 2)
+                          : f32x2{-INFINITY, 0.f};
+    }
+  float zv[G][KPT];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < KPT; c += 4) {
+      const int j = KPT * tid + c;
+      f32x4 z4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (j < nC) z4 = *reinterpret_cast<const f32x4*>(a.Z + (rowi * G + h) * a.NBp + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zv[h][c + e] = j + e < nC ? z4[e] : -INFINITY;
+    }
+  // ---- per-head max and normaliser from the partials (fixed order: the same bits in every wave)
+  float Mh[G], invS[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m = st[h][0][0];
+#pragma unroll
+    for (int r = 1; r < SPL; ++r) m = fmaxf(m, st[h][r][0]);
+    m = wave_max_dpp(m);
+    float l = 0.f;
+#pragma unroll
+    for (int r = 0; r < SPL; ++r) l += st[h][r][0] == -INFINITY ? 0.f : st[h][r][1] * fast_exp2(st[h][r][0] - m);
+    l = wave_sum_dpp(l);
+    Mh[h] = m;
+    invS[h] = 1.0f / l;
+  }
+  // ---- group scores as keys (free candidates only; scores >= 0, so float bits order like values)
+  uint32_t keys[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const int j = KPT * tid + e;
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) s = fmaf(fast_exp2(zv[h][e] - Mh[h]), invS[h], s);
+    keys[e] = (j >= nf_first && j < last_lo) ? __float_as_uint(s) + 1u : 0u;
+  }
+  // the list: forced first blocks, the k' best free blocks (ascending), forced newest blocks
+  const int np = block_topk<KPT>(keys, kp, n_free, topk_sh, lst + nf_first);
+  const int n_list = nf_first + np + (nC - last_lo);
+  for (int i = tid; i < nf_first; i += 256) lst[i] = i;
+  for (int i = tid; i < nC - last_lo; i += 256) lst[nf_first + np + i] = last_lo + i;
+  __syncthreads();
+  if (item == 0) {
+    for (int i = tid; i < n_list; i += 256) a.idx[rowi * a.cap + i] = lst[i];
+    if (tid == 0) a.cnt[rowi] = n_list;
+  }
+
+  // ---- attention over this workgroup's slice of the list's tokens
+  const int64_t ntok = (int64_t)n_list * a.kv_block;
+  const int64_t t_begin = (int64_t)item * a.tok_per_item;
+  if (ntok == 0 && item == 0) {                         // nothing selected: O = 0, LSE = -inf
+    for (int i = tid; i < G * D; i += 256) {
+      const int h = i / D, d = i - h * D;
+      const int64_t oi = (int64_t)b * a.osb + (int64_t)(g * G + h) * a.osh + (int64_t)row * a.osl + d;
+      if (a.o_f32) static_cast<float*>(a.o)[oi] = 0.f;
+      else static_cast<uint16_t*>(a.o)[oi] = 0;
+      if (d == 0) a.lse[((int64_t)b * a.Hkv * G + g * G + h) * a.Lq + row] = -INFINITY;
+    }
+  }
+  if (t_begin >= ntok) return;                          // no slice of the list for this workgroup
+  const int64_t t_end = min(ntok, t_begin + a.tok_per_item);
+  float wm[G], wl[G], wacc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    wm[h] = -INFINITY;
+    wl[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wacc[h][e] = 0.f;
+  }
+  const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + d0) * ES;
+  const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + d0) * ES;
+  for (int64_t c0 = t_begin; c0 < t_end; c0 += kDecTok) {
+    int pos[PASSES];
+    bool ok[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int64_t t = c0 + w * TPW + p * TPP + tg;
+      const bool in = t < t_end;
+      const int e = in ? (int)(t / a.kv_block) : 0;
+      const int blk = in ? lst[e] : -1;
+      const int64_t key = (int64_t)blk * a.kv_block + (t - (int64_t)e * a.kv_block);
+      ok[p] = in && blk >= 0 && key < a.L && (!a.causal || key <= qpos);
+      pos[p] = ok[p] ? (int)key : 0;
+    }
+    float kx[PASSES][8], vx[PASSES][8];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      if (ok[p]) {
+        load8<DT>(kb + (int64_t)pos[p] * a.ksl * ES, kx[p]);
+        load8<DT>(vb + (int64_t)pos[p] * a.vsl * ES, vx[p]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kx[p][e] = 0.f; vx[p][e] = 0.f; }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float s[PASSES];
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = fmaf(qx[h][e], kx[p][e], dot);
+        dot = group_sum<LPT>(dot);
+        s[p] = ok[p] ? dot : -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int p = 1; p < PASSES; ++p) mx = fmaxf(mx, s[p]);
+      mx = groups_max<LPT>(mx);
+      const float m_new = fmaxf(wm[h], mx);
+      if (m_new == -INFINITY) continue;                  // nothing visible yet (wave-uniform)
+      const float alpha = fast_exp2(wm[h] - m_new);
+      float l = 0.f, acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const float pr = ok[p] ? fast_exp2(s[p] - m_new) : 0.f;
+        l += pr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(pr, vx[p][e], acc[e]);
+      }
+      l = groups_sum<LPT>(l);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = groups_sum<LPT>(acc[e]);
+      wm[h] = m_new;
+      wl[h] = fmaf(wl[h], alpha, l);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wacc[h][e] = fmaf(wacc[h][e], alpha, acc[e]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (lane < LPT) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_acc[w][h][d0 + e] = wacc[h][e];
+    }
+    if (lane == 0) { sm_m[w][h] = wm[h]; sm_l[w][h] = wl[h]; }
+  }
+  __syncthreads();
+  // merge the 4 waves into this workgroup's partial, stored at device scope (no cache holds it back)
+  const int64_t pbase = (rowi * a.items + item) * G;
+  for (int i = tid; i < G * D; i += 256) {
+    const int h = i / D, d = i - h * D;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][h]);
+    float o = 0.f, lsum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        if (sm_m[ww][h] == -INFINITY) continue;
+        const float wgt = fast_exp2(sm_m[ww][h] - M);
+        o = fmaf(sm_acc[ww][h][d], wgt, o);
+        lsum = fmaf(sm_l[ww][h], wgt, lsum);
+      }
+    }
+    __hip_atomic_store(a.part_o + (pbase + h) * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      const uint64_t ml = (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(lsum) << 32);
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(a.part_ml + (pbase + h) * 2), ml, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);                        // this wave's partial stores are done
+  __syncthreads();                                      // ... and every wave's
+  const int n_valid = (int)((ntok + a.tok_per_item - 1) / a.tok_per_item);
+  if (tid == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(a.arrivals + rowi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_sh = (int)before == n_valid - 1;
+  }
+  __syncthreads();
+  if (!last_sh) return;
+  // ---- the last slice to finish merges all slices in order: two dims of one head per thread
+  for (int i = tid; i < G * D / 2; i += 256) {
+    const int h = i / (D / 2), d = 2 * (i - h * (D / 2));
+    float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+    constexpr int BATCH = 32;
+    for (int it0 = 0; it0 < n_valid; it0 += BATCH) {
+      float mv[BATCH], lv[BATCH], o0[BATCH], o1[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int it = min(it0 + u, n_valid - 1);
+        const int64_t pi = (rowi * a.items + it) * G + h;
+        const uint64_t ml = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.part_ml + pi * 2), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t ov = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.part_o + pi * D + d),
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mv[u] = __uint_as_float((uint32_t)ml);
+        lv[u] = __uint_as_float((uint32_t)(ml >> 32));
+        o0[u] = __uint_as_float((uint32_t)ov);
+        o1[u] = __uint_as_float((uint32_t)(ov >> 32));
+      }
+      float bm = M;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (it0 + u < n_valid) bm = fmaxf(bm, mv[u]);
+      if (bm == -INFINITY) continue;
+      const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+      L *= alpha;
+      acc0 *= alpha;
+      acc1 *= alpha;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        if (it0 + u < n_valid && mv[u] != -INFINITY) {
+          const float wgt = fast_exp2(mv[u] - bm);
+          L = fmaf(lv[u], wgt, L);
+          acc0 = fmaf(o0[u], wgt, acc0);
+          acc1 = fmaf(o1[u], wgt, acc1);
+        }
+      }
+      M = bm;
+    }
+    const float r0 = L > 0.f ? acc0 / L : 0.f, r1 = L > 0.f ? acc1 / L : 0.f;
+    const int64_t oi = (int64_t)b * a.osb + (int64_t)(g * G + h) * a.osh + (int64_t)row * a.osl + d;
+    if (a.o_f32) {
+      static_cast<float*>(a.o)[oi] = r0;
+      static_cast<float*>(a.o)[oi + 1] = r1;
+    } else {
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.o) + oi) = pack_bf16x2(r0, r1);
+    }
+    if (d == 0) a.lse[((int64_t)b * a.Hkv * G + g * G + h) * a.Lq + row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------- host ---
+bool plan_decode_step(const bsa_tensor& q, const bsa_tensor& k, const bsa_select_params& p, DStepPlan& pl) {
+  pl.B = q.B;
+  pl.Hq = q.H;
+  pl.Hkv = k.H;
+  pl.G = q.H / k.H;
+  pl.D = q.D;
+  pl.Lq = q.L;
+  pl.L = k.L;
+  pl.NB = (int)ceil_div(k.L, p.kv_block);
+  pl.NBp = (pl.NB + 3) & ~3;
+  pl.KPL = pl.NB <= 1024 ? 16 : 64;
+  pl.P = 4 * (int)ceil_div(pl.NB, 32);
+  const int64_t toks = (int64_t)p.cap * p.kv_block;
+  const int64_t per = std::max<int64_t>(kDecMinSlice / kDecTok, ceil_div(ceil_div(toks, kDecTok), kDecMaxItems));
+  pl.tok_per_item = (int)(per * kDecTok);
+  pl.items = (int)ceil_div(toks, pl.tok_per_item);
+  const size_t rows = (size_t)pl.B * pl.Hkv * pl.Lq;
+  pl.z_bytes = align256(rows * pl.G * pl.NBp * 4);
+  pl.stats_bytes = align256(rows * pl.G * pl.P * 2 * 4);
+  pl.part_o_bytes = align256(rows * pl.items * pl.G * pl.D * 4);
+  pl.part_ml_bytes = align256(rows * pl.items * pl.G * 2 * 4);
+  pl.arrival_bytes = align256(rows * 32 * 4);
+  return true;
+}
+
+void launch_decode_step(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, float* k_mean,
+                        float* k_energy, int refresh, const bsa_select_params& p, const DStepPlan& pl, int32_t* idx,
+                        int32_t* cnt, const bsa_tensor& o, float* lse, void* ws, hipStream_t s) {
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  DStepArgs a;
+  a.q = static_cast<const uint8_t*>(q.data);
+  a.k = static_cast<const uint8_t*>(k.data);
+  a.v = static_cast<const uint8_t*>(v.data);
+  a.qsb = q.stride_b; a.qsh = q.stride_h; a.qsl = q.stride_l;
+  a.ksb = k.stride_b; a.ksh = k.stride_h; a.ksl = k.stride_l;
+  a.vsb = v.stride_b; a.vsh = v.stride_h; a.vsl = v.stride_l;
+  a.k_mean = k_mean; a.k_energy = k_energy; a.refresh = refresh;
+  a.B = pl.B; a.Hkv = pl.Hkv; a.Lq = pl.Lq; a.L = pl.L; a.NB = pl.NB; a.NBp = pl.NBp;
+  a.kv_block = p.kv_block; a.q_pos0 = p.q_pos0; a.causal = p.causal; a.layout = p.layout;
+  a.topk = p.topk; a.topk_num = p.topk_num; a.topk_den = p.topk_den; a.n_first = p.n_first; a.n_last = p.n_last;
+  a.cap = p.cap;
+  a.c2 = p.scale * kLog2e;
+  a.Z = reinterpret_cast<float*>(w8);
+  a.stats = reinterpret_cast<float*>(w8 + pl.z_bytes);
+  a.P = pl.P;
+  a.idx = idx; a.cnt = cnt;
+  a.part_o = reinterpret_cast<float*>(w8 + pl.z_bytes + pl.stats_bytes);
+  a.part_ml = reinterpret_cast<float*>(w8 + pl.z_bytes + pl.stats_bytes + pl.part_o_bytes);
+  a.arrivals = reinterpret_cast<uint32_t*>(w8 + pl.z_bytes + pl.stats_bytes + pl.part_o_bytes + pl.part_ml_bytes);
+  a.items = pl.items; a.tok_per_item = pl.tok_per_item;
+  a.o = o.data; a.o_f32 = o.dtype == BSA_F32; a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
+  a.lse = lse;
+
+  const dim3 g1((unsigned)ceil_div(pl.NB, 32), (unsigned)pl.Lq, (unsigned)(pl.B * pl.Hkv));
+  const dim3 g2((unsigned)pl.items, (unsigned)pl.Lq, (unsigned)(pl.B * pl.Hkv));
+#define BSA_DS(DT, DD, GG)                                                                                  \
+  do {                                                                                                     \
+    hipLaunchKernelGGL((dstep_logits_kernel<DT, DD, GG>), g1, dim3(256), 0, s, a);                          \
+    if (pl.KPL == 16) hipLaunchKernelGGL((dstep_attend_kernel<DT, DD, GG, 16>), g2, dim3(256), 0, s, a);    \
+    else hipLaunchKernelGGL((dstep_attend_kernel<DT, DD, GG, 64>), g2, dim3(256), 0, s, a);                 \
+  } while (0)
+#define BSA_DS_G(DT, DD)                       \
+  do {                                         \
+    switch (pl.G) {                            \
+      case 1: BSA_DS(DT, DD, 1); break;        \
+      case 2: BSA_DS(DT, DD, 2); break;        \
+      case 4: BSA_DS(DT, DD, 4); break;        \
+      default: BSA_DS(DT, DD, 8); break;       \
+    }                                          \
+  } while (0)
+  if (q.dtype == BSA_BF16) {
+    if (pl.D == 128) BSA_DS_G(BSA_BF16, 128); else BSA_DS_G(BSA_BF16, 64);
+  } else {
+    if (pl.D == 128) BSA_DS_G(BSA_F32, 128); else BSA_DS_G(BSA_F32, 64);
+  }
+#undef BSA_DS_G
+#undef BSA_DS
+
+}
+
+}  // namespace bsa

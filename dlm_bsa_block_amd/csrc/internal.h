@@ -105,6 +105,18 @@ void launch_token_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_
                             float* lse, void* ws, hipStream_t s);
 
 
+// One decode step (selection with an optional summary refresh, then attention over the lists) in
+// two launches: logits + softmax partials, then selection + split attention per workgroup with the
+// merge done by the workgroup that finishes last.
+struct DStepPlan {
+  int B, Hq, Hkv, G, D, Lq, L, NB, NBp, KPL, P, items, tok_per_item;
+  size_t z_bytes, stats_bytes, part_o_bytes, part_ml_bytes, arrival_bytes;   // workspace regions, in this order
+};
+bool plan_decode_step(const bsa_tensor& q, const bsa_tensor& k, const bsa_select_params& p, DStepPlan& pl);
+void launch_decode_step(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, float* k_mean,
+                        float* k_energy, int refresh, const bsa_select_params& p, const DStepPlan& pl, int32_t* idx,
+                        int32_t* cnt, const bsa_tensor& o, float* lse, void* ws, hipStream_t s);
+
 bool plan_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, int kv_split, size_t& bytes);
 void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, float scale,
                              float lambda, int kv_split, const bsa_tensor& o, float* lse, int32_t* kept,

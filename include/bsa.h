@@ -176,6 +176,43 @@ bsa_status bsa_select_blocks_refresh(const bsa_tensor* k, int32_t refresh_block,
                                      int32_t* row_picks, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * One GQA decode step: bsa_select_blocks_refresh followed by
+ * bsa_sparse_attention_fwd on the lists it selects (NSA
+ * structure section: selection block 64, block 0 and the newest blocks
+ * always kept; decode-speed section: the step reads only the selected
+ * blocks).
+ *
+ * q [B, Hq, Lq, D]: decode rows, row r at position q_pos0 + r, each its own
+ * query block (p->q_block must be 1; raw queries, one band: pooled_q = 0,
+ * dual_band = 0); k, v [B, Hkv, L, D] of q's dtype (bf16 or f32, D 64 or
+ * 128, Hq / Hkv in {1, 2, 4, 8}); NB = ceil(L / kv_block) <= 4096.
+ * k_mean [B, Hkv, NB, D] f32 (and k_energy [B, Hkv, NB, 2] or NULL) hold the
+ * summaries; when refresh_block >= 0 that block's summary is pooled from k
+ * (the newest block, whose tokens change every step), used, and written
+ * there (refresh_block = -1: none).  The scores, forced blocks, k', ties and
+ * causality follow bsa_select_blocks; the attention follows
+ * bsa_sparse_attention_fwd with the selection's scale, kv_block, q_pos0,
+ * causal and cap.  Writes idx [B, Hkv, Lq, cap] and cnt [B, Hkv, Lq] (as
+ * bsa_select_blocks), o (q's shape, q's dtype or f32) and lse [B, Hq, Lq].
+ * Two launches: the block logits (with per-wavefront softmax partials),
+ * then one workgroup per (slice of the list, row, KV group) that selects --
+ * every workgroup of a group computes the same list -- attends to its slice
+ * and publishes a split partial; the workgroup that finishes last merges the
+ * slices in order.  workspace: bsa_decode_step_workspace_bytes() bytes
+ * (logits, softmax partials, split-KV partials and a slice counter per row
+ * that the first launch clears; no initial contents needed; calls that
+ * overlap on one workspace race).  Errors: as the two entry points it
+ * combines; BSA_ERR_UNSUPPORTED for q_block != 1, pooled or dual-band
+ * selection, or NB > 4096.
+ * ------------------------------------------------------------------------ */
+size_t bsa_decode_step_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, const bsa_select_params* p);
+
+bsa_status bsa_decode_step(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, float* k_mean,
+                           float* k_energy, int32_t refresh_block, const bsa_select_params* p, int32_t* idx,
+                           int32_t* cnt, const bsa_tensor* o, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Locality pruning (LoSA sec. 2): row r of a denoising block is active when
  * the mean over heads and dims of (q_cur - q_prev)^2 exceeds theta (taken in
  * fp32).  q_cur/q_prev [B, H, R, D] bf16/f32 of the same shape; writes

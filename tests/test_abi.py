@@ -12,6 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bsa.h")
+PEAKS_HEADER = os.path.join(ROOT, "include", "bsa_peaks.h")
 
 bsa = pytest.importorskip("dlm_bsa_block_amd")
 from dlm_bsa_block_amd import _lib as L  # noqa: E402
@@ -19,8 +20,8 @@ from dlm_bsa_block_amd import _lib as L  # noqa: E402
 FAKE = 0x10000          # 16-byte aligned, never dereferenced
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(bsa_\w+)\s*\(", text)))
 
@@ -38,6 +39,27 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert hasattr(lib, n), n
         assert n in L._SIGS, f"binding has no signature for {n}"
+
+
+def test_peaks_library_exports_every_declared_function():
+    from dlm_bsa_block_amd import build as bb
+    if not os.path.exists(bb.PEAKS_LIB):
+        pytest.skip("libbsa_peaks.so not built")
+    plib = ctypes.CDLL(bb.PEAKS_LIB)
+    names = _declared_functions(PEAKS_HEADER)
+    assert names == ["bsa_peak_hbm_read", "bsa_peak_mfma_bf16", "bsa_peak_mfma_flops"]
+    for n in names:
+        assert hasattr(plib, n), n
+    plib.bsa_peak_mfma_flops.restype = ctypes.c_double
+    plib.bsa_peak_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    assert plib.bsa_peak_mfma_flops(10, 3) == 3 * 4 * 10 * 4 * 32 * 32 * 16 * 2
+    # host-side rejection only (nothing reaches the device)
+    plib.bsa_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    assert plib.bsa_peak_hbm_read(None, 1 << 20, 64, FAKE, None) == 1
+    assert plib.bsa_peak_hbm_read(FAKE, 8, 64, FAKE, None) == 1
+    plib.bsa_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert plib.bsa_peak_mfma_bf16(0, 64, FAKE, None) == 1
 
 
 def test_status_strings(lib):
