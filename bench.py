@@ -176,7 +176,14 @@ def bench_decode(torch, bsa, synth, steps, warmup, flush):
     def select_refresh():
         bsa.bsa_select_blocks_refresh(k, NB - 1, q, kmean, sp, k_energy=kenergy, workspace=ws_sel, idx=idx, cnt=cnt)
 
+    ws_step = torch.zeros(max(256, bsa.bsa_decode_step_workspace_bytes(q, k, sp)), dtype=torch.uint8, device="cuda")
+
     def step():
+        # the newest block's summary pooled, blocks selected and attended: one entry point, one launch
+        bsa.bsa_decode_step(q, k, v, kmean, sp, refresh_block=NB - 1, k_energy=kenergy, idx=idx, cnt=cnt, o=o,
+                            lse=lse, workspace=ws_step)
+
+    def step_separate():
         select_refresh()                         # the newest block's summary is pooled inside the selection
         attend()
 
@@ -213,6 +220,7 @@ def bench_decode(torch, bsa, synth, steps, warmup, flush):
 
     ms_per_step_single, _ = timed(1)
     ms_per_step, wall = timed(inner)
+    t_step_separate = time_graph(torch, step_separate, max(20, steps // inner), inner=inner)
     # per entry point, eager (warm: the same blocks every step, as in the replayed graph)
     reps = max(50, steps)
     t_sum = time_calls(torch, summarize, reps)
@@ -242,6 +250,7 @@ def bench_decode(torch, bsa, synth, steps, warmup, flush):
                   tokens_per_group=int(cnt[0, 0, 0].item()) * p["kv_block"] + W, kv_bytes=win_bytes,
                   gbs=round(win_bytes / (t_att_win * 1e3), 1))
     return dict(ms_per_step=ms_per_step, ms_per_step_single=ms_per_step_single, steps_per_graph=inner, wall_s=wall,
+                t_step_separate=t_step_separate,
                 sel_bytes=sel_bytes, t_sum=t_sum, t_sel=t_sel, t_selr=t_selr, t_att=t_att, t_att_cold=t_att_cold,
                 summary_bytes=Hkv * NB * D * 4, cnt=cnt.cpu().tolist(), workload=w, window=window)
 
@@ -381,9 +390,13 @@ def bench_dlm_steps(torch, bsa, synth, reps):
 
 
 # ---------------------------------------------------------------- prefill ---
+_WORKLOADS = {}          # generated workloads, reused by the CPU-baseline leg
+
+
 def bench_prefill(torch, bsa, synth, reps):
     log("prefill: generating the 32K causal prefill workload")
     w = synth.sparse_prefill()
+    _WORKLOADS["prefill"] = w
     p = w.params
     q, k, v = (to_dev(torch, x, "bf16") for x in (w.q, w.k, w.v))
     B, Hq, Lq, D = q.shape
@@ -431,6 +444,7 @@ def bench_prefill(torch, bsa, synth, reps):
 def bench_threshold(torch, bsa, synth, reps):
     log("threshold: generating the 128K threshold prefill workload")
     w = synth.threshold_prefill()
+    _WORKLOADS["threshold"] = w
     p = w.params
     q, k, v = (to_dev(torch, x, "bf16") for x in (w.q, w.k, w.v))
     B, Hq, L, D = q.shape
@@ -557,10 +571,76 @@ def bench_token_decode(torch, bsa, synth, reps, flush, w=None):
                 attended_kv_bytes=tok_bytes, attention_gbs=round(tok_bytes / (t_att * 1e3), 1))
 
 
+# ------------------------------------------------------- attainable peaks ---
+def measure_peaks(torch, flush):
+    """The repository's own microbenchmarks (libbsa_peaks.so): a streaming read of
+    a 4 GiB buffer (cold: twice the Infinity Cache and more) and a register-only
+    bf16 MFMA loop over every CU.  They give the measured denominators next to
+    the vendor figures."""
+    import ctypes
+    from dlm_bsa_block_amd import build as bb
+    lib = ctypes.CDLL(bb.PEAKS_LIB)
+    lib.bsa_peak_hbm_read.restype = ctypes.c_int32
+    lib.bsa_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.bsa_peak_mfma_bf16.restype = ctypes.c_int32
+    lib.bsa_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsa_peak_mfma_flops.restype = ctypes.c_double
+    lib.bsa_peak_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    buf = torch.empty(1 << 30, dtype=torch.float32, device="cuda")          # 4 GiB
+    buf.fill_(1.0)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    nbytes = buf.numel() * 4
+    best_read, wgs_read = 0.0, 0
+    for wgs in (1024, 2048, 4096):
+        for _ in range(2):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            if lib.bsa_peak_hbm_read(buf.data_ptr(), nbytes, wgs, sink.data_ptr(), s.cuda_stream) != 0:
+                raise RuntimeError("bsa_peak_hbm_read failed")
+            b.record(s)
+            torch.cuda.synchronize()
+            gbs = nbytes / (a.elapsed_time(b) * 1e6)
+            if gbs > best_read:
+                best_read, wgs_read = gbs, wgs
+    del buf
+    best_mfma, iters, wgs = 0.0, 20000, 1024
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        if lib.bsa_peak_mfma_bf16(iters, wgs, sink.data_ptr(), s.cuda_stream) != 0:
+            raise RuntimeError("bsa_peak_mfma_bf16 failed")
+        b.record(s)
+        torch.cuda.synchronize()
+        best_mfma = max(best_mfma, lib.bsa_peak_mfma_flops(iters, wgs) / (a.elapsed_time(b) * 1e9))
+    return dict(hbm_read_gbs=round(best_read, 1), hbm_read_workgroups=wgs_read, hbm_read_bytes=nbytes,
+                mfma_bf16_tflops=round(best_mfma, 1), mfma_loop="4 waves x 1024 workgroups x 20000 rounds of 4 "
+                "independent v_mfma_f32_32x32x16_bf16")
+
+
 # ------------------------------------------------------------ cpu baseline ---
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
+    except Exception:
+        return None
+
+
 def cpu_baseline(w, seconds):
     """The fp64 oracle's decode step on the host, repeated for about `seconds`."""
-    import numpy as np
     import oracle as orc
     from synth import storage_to_f64
     p = w.params
@@ -573,16 +653,98 @@ def cpu_baseline(w, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
-    except Exception:
-        pass
+    threads = _blas_threads()
     cores = len(os.sched_getaffinity(0))
     return dict(value=round(1e6 * el / n, 1), unit="us/step", cores=int(threads or cores), kind="oracle",
                 sample=f"{n} full 64K GQA decode steps (summary refresh + selection + attention, fp64 numpy) "
-                       f"in {el:.1f} s; host affinity {cores} cores, BLAS threads {threads}")
+                       f"in {el:.1f} s; host affinity {cores} cores, BLAS threads {threads}",
+                cpu_model=_cpu_model(), os_cpu_count=os.cpu_count())
+
+
+def cpu_baseline_other(synth, prefill_w=None, thr_w=None):
+    """The oracle on the other workloads, on the host cores: the tiny decode and
+    the denoising step in full; sparse prefill and threshold prefill on seeded
+    samples of query blocks (rows are independent, so a sample is exact for its
+    rows), with the full-size time extrapolated per (query block, head) and
+    labelled as such."""
+    import numpy as np
+    import oracle as orc
+    from synth import storage_to_f64
+    out = {}
+    # tiny decode, in full: median of 5
+    w = synth.tiny_decode()
+    p = w.params
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    ts = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        km, ke = orc.block_summaries(k, p["kv_block"], p["layout"])
+        sel = orc.select_blocks(p, km, q=q)
+        orc.sparse_attention(p, q, k, v, sel["lists"])
+        ts.append(time.perf_counter() - t0)
+    out["tiny_decode"] = dict(ms=round(1e3 * sorted(ts)[2], 3), kind="full")
+    # denoising step at 32K, in full, once (the prefix summaries are part of it)
+    w = synth.dlm_denoise()
+    p = w.params
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    t0 = time.perf_counter()
+    mask, _ = orc.active_rows(q, w.f64("q_prev"), p["theta_act"])
+    km, _ = orc.block_summaries(k, p["kv_block"], p["layout"])
+    sel = orc.select_blocks(p, km, q=q)
+    orc.sparse_attention(p, q, k, v, sel["lists"], row_mask=mask)
+    out["dlm_denoise_32k"] = dict(ms=round(1e3 * (time.perf_counter() - t0), 1), kind="full")
+    del q, k, v, w
+    # sparse prefill at 32K: summaries of every block (needed by any query block), then 2 query blocks x 32 heads
+    if prefill_w is not None:
+        w = prefill_w
+        p = w.params
+        q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+        t0 = time.perf_counter()
+        qm, qe = orc.block_summaries(q, p["kv_block"], p["layout"])
+        km, ke = orc.block_summaries(k, p["kv_block"], p["layout"])
+        tau = orc.band_temperatures(km, ke, p["layout"], q.shape[1] // k.shape[1], qm, qe)
+        t_sum = time.perf_counter() - t0
+        NQB = qm.shape[2]
+        qbs = [NQB // 2, NQB - 1]
+        t0 = time.perf_counter()
+        sel = orc.select_blocks(p, km, q_mean=qm, tau=tau, Lq=q.shape[2])
+        t_sel = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        orc.sparse_attention(p, q, k, v, sel["lists"], qblocks=qbs)
+        t_att = (time.perf_counter() - t0) / len(qbs)
+        out["sparse_prefill_32k"] = dict(
+            kind="sample", sample=f"query blocks {qbs} x 32 heads of attention; summaries, temperatures and the "
+                                  "selection of all 256 query blocks in full",
+            summaries_s=round(t_sum, 2), select_s=round(t_sel, 2), attention_s_per_query_block=round(t_att, 3),
+            extrapolated_full_s=round(t_sum + t_sel + t_att * NQB, 1))
+        del q, k, v
+    # threshold prefill at 128K: 2 query tiles x 2 heads walked (the last tile sees all 1024 KV tiles)
+    if thr_w is not None:
+        w = thr_w
+        p = w.params
+        T = p["tile"]
+        Lq = w.q.shape[2]
+        NQT = Lq // T
+        pairs = [(0, h, qt) for h in (0, 17) for qt in (NQT // 2, NQT - 1)]
+        G = w.q.shape[1] // w.k.shape[1]
+        t0 = time.perf_counter()
+        visited = 0
+        for (b, h, qt) in pairs:
+            rows = np.arange(qt * T, (qt + 1) * T)
+            qq = storage_to_f64(w.q[b, h, rows], "bf16")
+            kk = storage_to_f64(w.k[b, h // G], "bf16")
+            vv = storage_to_f64(w.v[b, h // G], "bf16")
+            orc.threshold_walk(qq, kk, vv, rows, T, p["lam"], p["scale"], True)
+            visited += qt + 1
+        el = time.perf_counter() - t0
+        total_visits = w.q.shape[1] * NQT * (NQT + 1) // 2
+        out["threshold_prefill_128k"] = dict(
+            kind="sample", sample=f"{len(pairs)} (head, query tile) walks, {visited} KV tiles visited",
+            s=round(el, 2), extrapolated_full_s=round(el / visited * total_visits, 1))
+    out["cpu_model"] = _cpu_model()
+    out["cores"] = len(os.sched_getaffinity(0))
+    out["blas_threads"] = _blas_threads()
+    return out
 
 
 def main():
@@ -630,6 +792,14 @@ def main():
     if args.only in ("all", "threshold"):
         secondary["threshold_prefill_128k"] = bench_threshold(torch, bsa, synth, max(3, reps // 8))
         log(f"threshold: {secondary['threshold_prefill_128k']}")
+    peaks = None
+    if args.only in ("all", "decode", "prefill", "threshold"):
+        log("peaks: HBM read and bf16 MFMA microbenchmarks")
+        peaks = measure_peaks(torch, flush)
+        log(f"peaks: {peaks}")
+        for key, frac_key in (("sparse_prefill_32k", "attention_tflops"), ("threshold_prefill_128k", "tflops")):
+            if key in secondary:
+                secondary[key]["mfma_frac_of_attainable"] = round(secondary[key][frac_key] / peaks["mfma_bf16_tflops"], 4)
     del flush
 
     line = {"metric": "decode µs/step + selected-KV HBM GB/s at 64K; sparse prefill TFLOP/s",
@@ -642,10 +812,11 @@ def main():
         line.update(value=round(us, 3), ms_per_step=round(d["ms_per_step"], 5))
         line["config"] = {"workload": "gqa_decode_64k", "batch": 1, "q_heads": 32, "kv_heads": 8, "head_dim": 128,
                           "context": 65536, "kv_block": 64, "selected_blocks_per_group": 16,
-                          "step": "summary refresh + block selection (one entry point) + sparse attention "
+                          "step": "bsa_decode_step: summary refresh + block selection + sparse attention "
                                   "(HIP graph replay)",
                           "steps_per_graph": d["steps_per_graph"]}
         line["us_per_step_one_step_graphs"] = round(1000 * d["ms_per_step_single"], 3)
+        line["us_per_step_separate_entry_points"] = round(d["t_step_separate"], 3)
         line["selected_kv_gbps"] = round(d["sel_bytes"] / (d["t_att"] * 1e3), 1)
         line["selected_kv_gbps_cold"] = round(d["sel_bytes"] / (d["t_att_cold"] * 1e3), 1)
         line["entry_point_us"] = {"bsa_build_block_summaries": round(d["t_sum"], 2),
@@ -653,15 +824,27 @@ def main():
                                   "bsa_select_blocks_refresh": round(d["t_selr"], 2),
                                   "bsa_sparse_attention_fwd": round(d["t_att"], 2),
                                   "bsa_sparse_attention_fwd_cold": round(d["t_att_cold"], 2)}
-        ach = d["sel_bytes"] / (d["t_att"] * 1e3)
-        line["roofline"] = {"kernel": "bsa_sparse_attention_fwd (decode split-KV + combine)", "bound": "hbm",
-                            "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        # roofline of the attention over the selected blocks, caches evicted before each call
+        ach = d["sel_bytes"] / (d["t_att_cold"] * 1e3)
+        line["roofline"] = {"kernel": "bsa_sparse_attention_fwd (decode split-KV + combine), cold caches",
+                            "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(ach / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic("gqa_decode_64k_hbm_counters.md"),
-                            "algorithmic_bytes": d["sel_bytes"]}
+                            "algorithmic_bytes": d["sel_bytes"],
+                            "achieved_warm": round(d["sel_bytes"] / (d["t_att"] * 1e3), 1)}
+        step_bytes = d["sel_bytes"] + d["summary_bytes"]
+        line["decode_step_bytes"] = {"selected_kv": d["sel_bytes"], "summaries_scanned": d["summary_bytes"],
+                                     "gbs": round(step_bytes / (us * 1e3), 1)}
+        if peaks is not None:
+            line["attainable_peaks"] = peaks
+            line["roofline"]["attainable_peak"] = peaks["hbm_read_gbs"]
+            line["roofline"]["frac_of_attainable"] = round(ach / peaks["hbm_read_gbs"], 4)
         if not args.no_cpu_baseline:
             log("cpu baseline: timing the fp64 oracle decode step")
             line["cpu_baseline"] = cpu_baseline(d["workload"], args.cpu_seconds)
+            log("cpu baseline: the oracle on the other workloads (samples where marked)")
+            line["cpu_baseline_other"] = cpu_baseline_other(synth, _WORKLOADS.get("prefill"),
+                                                            _WORKLOADS.get("threshold"))
     else:
         line.update(value=None, ms_per_step=None, config={"workload": args.only})
     if secondary:
