@@ -81,12 +81,20 @@ __device__ __forceinline__ f32x2 ld_dev2(const float* p) {
 }
 
 // ------------------------------------------------------------------ logits ---
-// Workgroup = 4 waves x 8 blocks; 8 lanes per block, D / 8 dims per lane.
+// Workgroup = 4 waves x 8 blocks; 8 lanes per block, D / 8 dims per lane.  The
+// workgroup that owns the newest block pools it from K with all four waves, in
+// the fixed order of the block-summary kernel (so the summary it writes has the
+// same bits): its K rows are requested before anything else, since that
+// workgroup finishes last.
 template <int DT, int D, int G>
 __global__ __launch_bounds__(256) void dstep_logits_kernel(DStepArgs a) {
   constexpr int ES = DT == BSA_BF16 ? 2 : 4;
   constexpr int DPL = D / 8;
-  __shared__ float pooled[4][D];
+  constexpr int LPR = D / 8, RPP = 256 / LPR;          // refresh: lanes per K row, rows per pass
+  constexpr int NV = ES / 2;                           // 16-byte words per lane and K row
+  __shared__ float red[RPP][D + 4];
+  __shared__ float ered[4][2];
+  __shared__ float pooled[D];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int row = blockIdx.y, bg = blockIdx.z, b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int jw0 = blockIdx.x * 32 + w * 8;
@@ -94,6 +102,25 @@ __global__ __launch_bounds__(256) void dstep_logits_kernel(DStepArgs a) {
   const int qpos = a.q_pos0 + row;
   const int nC = a.causal ? min(a.NB, qpos / a.kv_block + 1) : a.NB;
   const bool valid = j < nC;
+
+  // the newest block's first 4 * RPP rows, when this workgroup holds it (uniform over the workgroup)
+  const bool ref_wg = a.refresh >= (int)blockIdx.x * 32 && a.refresh < (int)blockIdx.x * 32 + 32 && a.refresh < nC;
+  const int rc = tid % LPR, rg = tid / LPR;
+  int n_ref = 0;
+  const uint8_t* kp = nullptr;
+  u32x4 kraw[4][NV];
+  if (ref_wg) {
+    const int t0 = a.refresh * a.kv_block;
+    n_ref = min(a.kv_block, a.L - t0);
+    kp = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + (int64_t)t0 * a.ksl + rc * 8) * ES;
+    // rows past the block's end load its last row (zeroed when used): no branch around a load
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = min(u * RPP + rg, n_ref - 1);
+#pragma unroll
+      for (int c = 0; c < NV; ++c) kraw[u][c] = reinterpret_cast<const u32x4*>(kp + (int64_t)r * a.ksl * ES)[c];
+    }
+  }
 
   float qx[G][DPL];
 #pragma unroll
@@ -121,57 +148,71 @@ __global__ __launch_bounds__(256) void dstep_logits_kernel(DStepArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) km[e] = 0.f;
   }
-  // the newest block: pooled here from K (Prism sec. 1-2 summary, as bsa_build_block_summaries), used and written out
-  if (a.refresh >= jw0 && a.refresh < jw0 + 8 && a.refresh < nC) {   // uniform over the wave
-    constexpr int LPR = D / 8, RPP = 64 / LPR;                         // lanes per K row, rows per pass
-    const int c = lane % LPR, rg = lane / LPR;
-    const int t0 = a.refresh * a.kv_block, n = min(a.kv_block, a.L - t0);
-    const uint8_t* kp = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + (int64_t)t0 * a.ksl + c * 8) * ES;
+  // the newest block: pooled here from K (Prism sec. 1-2 summary), used and written out
+  if (ref_wg) {
     float sum[8], e2 = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum[e] = 0.f;
-    constexpr int NP = 64 / RPP;                                       // 64 rows per round, all loads in flight
-    for (int r0 = 0; r0 < n; r0 += 64) {
-      float x[NP][8];
+    auto accumulate = [&](const float (&v)[4][8]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < NP; ++u) {
-        const int r = r0 + u * RPP + rg;
-        if (r < n) load8<DT>(kp + (int64_t)r * a.ksl * ES, x[u]);
-        else {
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
+        for (int e = 0; e < 8; ++e) { sum[e] += v[u][e]; e2 = fmaf(v[u][e], v[u][e], e2); }
+    };
+    {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool in = u * RPP + rg < n_ref;
+        if constexpr (DT == BSA_BF16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[u][2 * i] = in ? bf16lo(kraw[u][0][i]) : 0.f;
+            v[u][2 * i + 1] = in ? bf16hi(kraw[u][0][i]) : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[u][i] = in ? __uint_as_float(kraw[u][0][i]) : 0.f;
+            v[u][4 + i] = in ? __uint_as_float(kraw[u][NV - 1][i]) : 0.f;
+          }
         }
       }
-#pragma unroll
-      for (int u = 0; u < NP; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { sum[e] += x[u][e]; e2 = fmaf(x[u][e], x[u][e], e2); }
+      accumulate(v);
     }
-    // fold the row groups: lanes c, c + LPR, ... (LPR = 16: two swaps; LPR = 8: three)
+    for (int r0 = 4 * RPP; r0 < n_ref; r0 += 4 * RPP) {                // blocks longer than 4 * RPP rows
+      float v[4][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sum[e] = LPR == 16 ? groups_sum<16>(sum[e]) : groups_sum<8>(sum[e]);
-    const int band = band_of_dim(c * 8, D, a.layout);
-    const float ef = wave_sum_dpp(band == 0 ? e2 : 0.f), es = wave_sum_dpp(band == 0 ? 0.f : e2);
-    const float inv = 1.0f / (float)n;
-    if (rg == 0) {
+      for (int u = 0; u < 4; ++u) load8<DT>(kp + (int64_t)min(r0 + u * RPP + rg, n_ref - 1) * a.ksl * ES, v[u]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pooled[w][c * 8 + e] = sum[e] * inv;
+      for (int u = 0; u < 4; ++u) {
+        const bool in = r0 + u * RPP + rg < n_ref;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = in ? v[u][e] : 0.f;
+      }
+      accumulate(v);
     }
-    wave_sync_lds();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rg][rc * 8 + e] = sum[e];
+    const int band = band_of_dim(rc * 8, D, a.layout);
+    const float ef = wave_sum(band == 0 ? e2 : 0.f), es = wave_sum(band == 0 ? 0.f : e2);
+    if (lane == 0) { ered[w][0] = ef; ered[w][1] = es; }
+    __syncthreads();
+    const float inv = 1.0f / (float)n_ref;
+    for (int d = tid; d < D; d += 256) {
+      float t = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < RPP; ++rr) t += red[rr][d];
+      t *= inv;
+      pooled[d] = t;
+      if (row == 0) a.k_mean[(mrow + a.refresh) * D + d] = t;
+    }
+    if (a.k_energy && row == 0 && tid < 2)
+      a.k_energy[(mrow + a.refresh) * 2 + tid] = (ered[0][tid] + ered[1][tid] + ered[2][tid] + ered[3][tid]) * inv;
+    __syncthreads();
     if (j == a.refresh) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) km[e] = pooled[w][d0 + e];
-    }
-    if (row == 0) {
-      if (rg == 0) {
-        f32x4* mo = reinterpret_cast<f32x4*>(a.k_mean + (mrow + a.refresh) * D + c * 8);
-        mo[0] = f32x4{pooled[w][c * 8], pooled[w][c * 8 + 1], pooled[w][c * 8 + 2], pooled[w][c * 8 + 3]};
-        mo[1] = f32x4{pooled[w][c * 8 + 4], pooled[w][c * 8 + 5], pooled[w][c * 8 + 6], pooled[w][c * 8 + 7]};
-      }
-      if (a.k_energy && lane == 0) {
-        a.k_energy[(mrow + a.refresh) * 2] = ef * inv;
-        a.k_energy[(mrow + a.refresh) * 2 + 1] = es * inv;
-      }
+      for (int e = 0; e < DPL; ++e) km[e] = pooled[d0 + e];
     }
   }
 
@@ -220,6 +261,7 @@ __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
   __shared__ BlockTopkSmem topk_sh;
   __shared__ int32_t lst[64 * KPL];                 // the row's list, ascending
   __shared__ int last_sh;
+  __shared__ __attribute__((aligned(16))) uint64_t ml_sh[G * 32];   // the merge's (m, l): [head][slice of the batch]
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sm_acc[4][G][D];
 
@@ -338,17 +380,21 @@ __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
       ok[p] = in && blk >= 0 && key < a.L && (!a.causal || key <= qpos);
       pos[p] = ok[p] ? (int)key : 0;
     }
+    // every pass loads (row 0 stands in for a masked token, then zeroed): a load under a
+    // branch would make the compiler wait for one pass's rows before requesting the next
     float kx[PASSES][8], vx[PASSES][8];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      if (ok[p]) {
-        load8<DT>(kb + (int64_t)pos[p] * a.ksl * ES, kx[p]);
-        load8<DT>(vb + (int64_t)pos[p] * a.vsl * ES, vx[p]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { kx[p][e] = 0.f; vx[p][e] = 0.f; }
-      }
+      load8<DT>(kb + (int64_t)pos[p] * a.ksl * ES, kx[p]);
+      load8<DT>(vb + (int64_t)pos[p] * a.vsl * ES, vx[p]);
     }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kx[p][e] = ok[p] ? kx[p][e] : 0.f;
+        vx[p][e] = ok[p] ? vx[p][e] : 0.f;
+      }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float s[PASSES];
@@ -429,47 +475,86 @@ __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
   }
   __syncthreads();
   if (!last_sh) return;
-  // ---- the last slice to finish merges all slices in order: two dims of one head per thread
-  for (int i = tid; i < G * D / 2; i += 256) {
-    const int h = i / (D / 2), d = 2 * (i - h * (D / 2));
-    float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
-    constexpr int BATCH = 32;
-    for (int it0 = 0; it0 < n_valid; it0 += BATCH) {
-      float mv[BATCH], lv[BATCH], o0[BATCH], o1[BATCH];
+  // ---- the last slice to finish merges all slices in order: two dims of one head per thread.
+  // Per batch of 32 slices, every thread loads one (m, l) pair into LDS and its own dims of
+  // the 32 partial O's (at most 33 loads in flight per thread, so none waits for a free
+  // counter slot), then merges with a running maximum as the separate combine does.
+  constexpr int BATCH = 32;
+  static_assert(BATCH * G <= 256, "one (m, l) pair per thread and batch");
+  constexpr int NPOS = G * D / 2;                       // (head, dim pair) positions
+  constexpr int PPT = (NPOS + 255) / 256;
+  float M[PPT], L[PPT], acc0[PPT], acc1[PPT];
+#pragma unroll
+  for (int pp = 0; pp < PPT; ++pp) { M[pp] = -INFINITY; L[pp] = 0.f; acc0[pp] = 0.f; acc1[pp] = 0.f; }
+  for (int it0 = 0; it0 < n_valid; it0 += BATCH) {
+    if (it0 > 0) __syncthreads();                       // the previous batch's LDS reads are done
+    uint64_t mlv = 0;
+    if (tid < BATCH * G) {                              // entry tid = (head, slice of the batch)
+      const int h = tid / BATCH, u = tid - h * BATCH;
+      const int it = min(it0 + u, n_valid - 1);
+      mlv = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.part_ml + ((rowi * a.items + it) * G + h) * 2),
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int pp = 0; pp < PPT; ++pp) {
+      const int i = tid + 256 * pp;
+      // threads past the positions load a valid position too: loads under a branch would make
+      // the compiler wait for each one before the next
+      const int ic = min(i, NPOS - 1);
+      const int h = ic / (D / 2), d = 2 * (ic - h * (D / 2));
+      float o0[BATCH], o1[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int it = min(it0 + u, n_valid - 1);
         const int64_t pi = (rowi * a.items + it) * G + h;
-        const uint64_t ml = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.part_ml + pi * 2), __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
         const uint64_t ov = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.part_o + pi * D + d),
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        mv[u] = __uint_as_float((uint32_t)ml);
-        lv[u] = __uint_as_float((uint32_t)(ml >> 32));
         o0[u] = __uint_as_float((uint32_t)ov);
         o1[u] = __uint_as_float((uint32_t)(ov >> 32));
       }
-      float bm = M;
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u)
-        if (it0 + u < n_valid) bm = fmaxf(bm, mv[u]);
-      if (bm == -INFINITY) continue;
-      const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - bm);
-      L *= alpha;
-      acc0 *= alpha;
-      acc1 *= alpha;
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if (it0 + u < n_valid && mv[u] != -INFINITY) {
-          const float wgt = fast_exp2(mv[u] - bm);
-          L = fmaf(lv[u], wgt, L);
-          acc0 = fmaf(o0[u], wgt, acc0);
-          acc1 = fmaf(o1[u], wgt, acc1);
-        }
+      if (pp == 0) {
+        if (tid < BATCH * G) ml_sh[tid] = mlv;
+        __syncthreads();
       }
-      M = bm;
+      if (i < NPOS) {
+        // this head's (m, l) of the batch, read together (16-byte LDS reads)
+        uint64_t mlr[BATCH];
+#pragma unroll
+        for (int q = 0; q < BATCH / 2; ++q) {
+          const u32x4 t = *reinterpret_cast<const u32x4*>(&ml_sh[h * BATCH + 2 * q]);
+          mlr[2 * q] = (uint64_t)t[0] | ((uint64_t)t[1] << 32);
+          mlr[2 * q + 1] = (uint64_t)t[2] | ((uint64_t)t[3] << 32);
+        }
+        float bm = M[pp];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u)
+          if (it0 + u < n_valid) bm = fmaxf(bm, __uint_as_float((uint32_t)mlr[u]));
+        if (bm == -INFINITY) continue;
+        const float alpha = M[pp] == -INFINITY ? 0.f : fast_exp2(M[pp] - bm);
+        L[pp] *= alpha;
+        acc0[pp] *= alpha;
+        acc1[pp] *= alpha;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const uint64_t ml = mlr[u];
+          const float mv = __uint_as_float((uint32_t)ml);
+          if (it0 + u < n_valid && mv != -INFINITY) {
+            const float wgt = fast_exp2(mv - bm);
+            L[pp] = fmaf(__uint_as_float((uint32_t)(ml >> 32)), wgt, L[pp]);
+            acc0[pp] = fmaf(o0[u], wgt, acc0[pp]);
+            acc1[pp] = fmaf(o1[u], wgt, acc1[pp]);
+          }
+        }
+        M[pp] = bm;
+      }
     }
-    const float r0 = L > 0.f ? acc0 / L : 0.f, r1 = L > 0.f ? acc1 / L : 0.f;
+  }
+#pragma unroll
+  for (int pp = 0; pp < PPT; ++pp) {
+    const int i = tid + 256 * pp;
+    if (i >= NPOS) continue;
+    const int h = i / (D / 2), d = 2 * (i - h * (D / 2));
+    const float r0 = L[pp] > 0.f ? acc0[pp] / L[pp] : 0.f, r1 = L[pp] > 0.f ? acc1[pp] / L[pp] : 0.f;
     const int64_t oi = (int64_t)b * a.osb + (int64_t)(g * G + h) * a.osh + (int64_t)row * a.osl + d;
     if (a.o_f32) {
       static_cast<float*>(a.o)[oi] = r0;
@@ -477,7 +562,8 @@ __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
     } else {
       *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.o) + oi) = pack_bf16x2(r0, r1);
     }
-    if (d == 0) a.lse[((int64_t)b * a.Hkv * G + g * G + h) * a.Lq + row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    if (d == 0)
+      a.lse[((int64_t)b * a.Hkv * G + g * G + h) * a.Lq + row] = L[pp] > 0.f ? (M[pp] + log2f(L[pp])) * kLn2 : -INFINITY;
   }
 }
 

@@ -226,11 +226,13 @@ struct __attribute__((aligned(16))) BlockTopkSmem {
 // synchronises before reading out.
 template <int KPT>
 __device__ int block_topk(const uint32_t (&k)[KPT], int kp, int n_free, BlockTopkSmem& sm, int32_t* out) {
+  // one workgroup of 256 threads: thread t holds the keys of blocks KPT t .. KPT t + KPT - 1
   const int t = threadIdx.x, w = t >> 6, lane = t & 63;
   if (kp <= 0 || n_free <= 0) return 0;
   uint32_t T = 0;                                      // with T = 0 every free key is "above"
   if (kp < n_free) {
     if (t == 0) sm.n_cand = 0u;
+    sm.cand[t] = 0u;                                   // below every gathered key: the rank loop reads past n0
     uint32_t t0 = 1u;
     if (kp <= 64) {
       uint32_t mx = k[0];
@@ -262,11 +264,17 @@ __device__ int block_topk(const uint32_t (&k)[KPT], int kp, int n_free, BlockTop
       if (t < n0) {
         const uint64_t mine = sm.cand[t];
         int rank = 0;
-        for (int m0 = 0; m0 < n0; m0 += 2) {
-          const u32x4 q = *reinterpret_cast<const u32x4*>(&sm.cand[m0]);
-          const uint64_t a = (uint64_t)q[0] | ((uint64_t)q[1] << 32), b = (uint64_t)q[2] | ((uint64_t)q[3] << 32);
-          rank += a > mine ? 1 : 0;
-          rank += (m0 + 1 < n0 && b > mine) ? 1 : 0;
+        // eight keys per round, four 16-byte reads in flight; slots past n0 hold 0
+        for (int m0 = 0; m0 < n0; m0 += 8) {
+          u32x4 q[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) q[r] = *reinterpret_cast<const u32x4*>(&sm.cand[m0 + 2 * r]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint64_t a = (uint64_t)q[r][0] | ((uint64_t)q[r][1] << 32);
+            const uint64_t b = (uint64_t)q[r][2] | ((uint64_t)q[r][3] << 32);
+            rank += (a > mine ? 1 : 0) + (b > mine ? 1 : 0);
+          }
         }
         if (rank == kp - 1) sm.T = (uint32_t)(mine >> 32);
       }

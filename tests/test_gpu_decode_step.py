@@ -1,9 +1,9 @@
 """bsa_decode_step (selection with the newest block's summary refresh, then
-attention over the selected blocks, in three launches) against the fp64
+attention over the selected blocks, in two launches) against the fp64
 oracle, and against the separate entry points it combines.
 
 Per case: the refreshed summary (mean and band energies) against the oracle's
-summaries; the lists with the 1e-6 tie band; O and LSE against the oracle on
+summaries and bit for bit against the separate refresh; the lists with the 1e-6 tie band; O and LSE against the oracle on
 the lists the GPU chose (outside the tie band they are the oracle's).  Where
 the fused step and bsa_select_blocks_refresh + bsa_sparse_attention_fwd chose
 the same list, their outputs must be the same bits (the attention arithmetic
@@ -64,6 +64,8 @@ def _step_case(bsa, w, refresh=True, odtype=None):
         assert np.allclose(from_dev(kmean[:, :, rb]), km_ref[:, :, rb], rtol=1e-5, atol=2e-6)
         assert np.allclose(from_dev(kenergy[:, :, rb]), ke_ref[:, :, rb], rtol=1e-5, atol=1e-5)
         assert torch.equal(kmean[:, :, :rb], km2[:, :, :rb])        # nothing else written
+        # pooled in the block-summary kernel's fixed order, as the separate refresh: the same bits
+        assert torch.equal(kmean, km2) and torch.equal(kenergy, ke2)
     sel = orc.select_blocks(p, km_ref, q=qf)
     idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
     idx2_np, cnt2_np = idx2.cpu().numpy(), cnt2.cpu().numpy()
