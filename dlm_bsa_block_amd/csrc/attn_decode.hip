@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   const int tg = lane / LPT, d0 = (lane % LPT) * 8;
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
   const int row = qb;                                   // one query row per block
-  if (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) return;
+
   const int64_t t_begin = (int64_t)item * a.tok_per_item;
   const int qpos = a.q_pos0 + row;
   // The list count, the queries and the block indices of the first chunk are
@@ -52,6 +52,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   };
   const int n_list = a.cnt[li];
   load_blocks(t_begin);
+  // a stable row (mask 0) is skipped; its byte is read once the list's loads are out
+  if (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) return;
 
   float qx[G][8];
 #pragma unroll
@@ -100,17 +102,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
       ok[p] = t < t_end && (key0 >= 0 || blk[p] >= 0) && key < a.L && (!a.causal || key <= qpos);
       pos[p] = ok[p] ? (int)key : 0;
     }
+    // every pass loads (row 0 stands in for a masked token, then zeroed): a load under a
+    // branch would make the compiler wait for one pass's rows before requesting the next
     float kx[PASSES][8], vx[PASSES][8];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      if (ok[p]) {
-        load8<DT>(kb + (int64_t)pos[p] * a.ksl * ES, kx[p]);
-        load8<DT>(vb + (int64_t)pos[p] * a.vsl * ES, vx[p]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { kx[p][e] = 0.f; vx[p][e] = 0.f; }
-      }
+      load8<DT>(kb + (int64_t)pos[p] * a.ksl * ES, kx[p]);
+      load8<DT>(vb + (int64_t)pos[p] * a.vsl * ES, vx[p]);
     }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kx[p][e] = ok[p] ? kx[p][e] : 0.f;
+        vx[p][e] = ok[p] ? vx[p][e] : 0.f;
+      }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float s[PASSES];
@@ -184,95 +190,127 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 
 // Merge the split partials of active (row, head) pairs of a query block in
 // ascending slice order; write O (q's dtype) and the natural-log LSE.  One
-// thread per (query vector, dim): it loads the (m, l) of every slice and its
-// dim of every partial O together -- one round trip to memory, no exchange
-// between threads -- and merges them with a running maximum, BATCH slices at
-// a time.
+// thread per (query vector, dim).  Per batch of BATCH slices, the (m, l) pairs
+// of the workgroup's query vectors go through LDS (one load per thread) while
+// each thread loads its dim of every partial O, so a thread has at most
+// BATCH + 1 loads in flight and none waits for a free counter slot; the merge
+// then runs with a running maximum, BATCH slices at a time.
 template <int ODT, int BATCH>
 __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
-  const int QVC = a.qvc;
+  __shared__ __attribute__((aligned(16))) uint64_t ml_sh[2][4 * BATCH];   // [parity][query vector][slice]
+  const int QVC = a.qvc;                           // 256 / D <= 4
   const int nchunk = (a.QV + QVC - 1) / QVC;
   const int qb = blockIdx.x / nchunk, qv0 = (blockIdx.x % nchunk) * QVC;
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = a.G, QV = a.QV, D = a.D, Hq = a.Hkv * G;
   const int tid = threadIdx.x;
   const int c = tid / D, d = tid - c * D;          // 256 threads cover QVC * D <= 256 (D >= 64)
-  if (c >= QVC) return;
   const int qv = qv0 + c;
   const int rl = qv / G, hl = qv - rl * G;
   const int row = qb * a.q_block + rl;
-  if (qv >= QV || row >= a.Lq || (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0)) return;
+  // every thread takes part in the barriers; only live ones write.  The row-mask byte is loaded
+  // for a valid row whatever this thread's (no load under a branch) and looked at after the batch
+  const uint8_t* rmp = a.row_mask ? a.row_mask + (int64_t)b * a.Lq + min(row, a.Lq - 1)
+                                  : reinterpret_cast<const uint8_t*>(a.part_ml);   // any readable byte
+  const uint8_t rbyte = *rmp;
+  const bool in_range = c < QVC && qv < QV && row < a.Lq;
+  bool live = false;                               // set once the first batch is requested
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
   const int64_t p0 = li * a.items;
-  float mv[BATCH], lv[BATCH], ov[BATCH];
   // Slots are clamped to the workspace, not to the valid count, so the first
   // batch loads together with the count; slots past the count may hold stale
   // values and are excluded by selects (never multiplied by a zero weight).
-  // uniform slice bases, 32-bit lane offsets (one VGPR per load, not an address pair)
-  const uint32_t lo_ml = (uint32_t)qv * 2u, lo_o = (uint32_t)(qv * D + d);
-  auto load_batch = [&](int it0) __attribute__((always_inline)) {
+  const int qvo = min(qv, QV - 1);                 // a dead thread loads a valid slot too: no load under a branch
+  const uint32_t lo_o = (uint32_t)(qvo * D + d);
+  const int cs = tid / BATCH, us = tid - cs * BATCH;   // the (m, l) this thread stages: query vector qv0 + cs, slice us
+  const uint32_t lo_ml = (uint32_t)min(qv0 + cs, QV - 1) * 2u;
+  auto issue = [&](int it0, uint64_t& mlv, float (&ov)[BATCH]) __attribute__((always_inline)) {
+    mlv = 0;
+    if (tid < QVC * BATCH) {
+      const int64_t it = min(it0 + us, a.items - 1);
+      mlv = *reinterpret_cast<const uint64_t*>(a.part_ml + (p0 + it) * QV * 2 + lo_ml);
+    }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int64_t it = min(it0 + u, a.items - 1);
-      const float* bml = a.part_ml + (p0 + it) * QV * 2;
-      const float* bo = a.part_o + (p0 + it) * QV * D;
-      mv[u] = bml[lo_ml];
-      lv[u] = bml[lo_ml + 1u];
-      ov[u] = bo[lo_o];
+      ov[u] = a.part_o[(p0 + it) * QV * D + lo_o];
     }
   };
-  const int64_t nunits = a.cnt ? (int64_t)a.cnt[li] * a.unit_num : (int64_t)a.items * a.unit_den;
-  load_batch(0);
-  const int nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
-  // merge items [first, first + n) in order; the batch at `first` is loaded already
-  auto merge = [&](int first, int n, float& M, float& L, float& acc) __attribute__((always_inline)) {
+  int parity = 0;
+  // merge items [first, first + n) in order; the batch at `first` is issued already
+  auto merge = [&](int first, int n, uint64_t mlv, float (&ov)[BATCH], float& M, float& L, float& acc)
+      __attribute__((always_inline)) {
     M = -INFINITY;
     L = 0.f;
     acc = 0.f;
-    for (int it0 = 0; it0 < n; it0 += BATCH) {
-      if (it0 > 0) load_batch(first + it0);
-      float bm = M;
+    for (int it0 = 0; it0 < n; it0 += BATCH) {     // n is uniform over the workgroup
+      if (it0 > 0) issue(first + it0, mlv, ov);
+      if (tid < QVC * BATCH) ml_sh[parity][tid] = mlv;
+      __syncthreads();
+      if (live) {
+        uint64_t mlr[BATCH];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u)
-        if (it0 + u < n) bm = fmaxf(bm, mv[u]);
-      if (bm == -INFINITY) continue;                  // nothing visible so far
-      const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - bm);
-      L *= alpha;
-      acc *= alpha;
+        for (int q = 0; q < BATCH / 2; ++q) {
+          const u32x4 t = *reinterpret_cast<const u32x4*>(&ml_sh[parity][c * BATCH + 2 * q]);
+          mlr[2 * q] = (uint64_t)t[0] | ((uint64_t)t[1] << 32);
+          mlr[2 * q + 1] = (uint64_t)t[2] | ((uint64_t)t[3] << 32);
+        }
+        float bm = M;
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if (it0 + u < n && mv[u] != -INFINITY) {
-          const float wgt = fast_exp2(mv[u] - bm);
-          L = fmaf(lv[u], wgt, L);
-          acc = fmaf(ov[u], wgt, acc);
+        for (int u = 0; u < BATCH; ++u)
+          if (it0 + u < n) bm = fmaxf(bm, __uint_as_float((uint32_t)mlr[u]));
+        if (bm != -INFINITY) {                     // else nothing visible so far
+          const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+          L *= alpha;
+          acc *= alpha;
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const float mv = __uint_as_float((uint32_t)mlr[u]);
+            if (it0 + u < n && mv != -INFINITY) {
+              const float wgt = fast_exp2(mv - bm);
+              L = fmaf(__uint_as_float((uint32_t)(mlr[u] >> 32)), wgt, L);
+              acc = fmaf(ov[u], wgt, acc);
+            }
+          }
+          M = bm;
         }
       }
-      M = bm;
+      parity ^= 1;                                 // the next batch writes the other buffer
     }
   };
+  uint64_t mlv;
+  float ov[BATCH];
+  issue(0, mlv, ov);
+  live = in_range && !(a.row_mask && rbyte == 0);
+  const int64_t nunits = a.cnt ? (int64_t)a.cnt[li] * a.unit_num : (int64_t)a.items * a.unit_den;
+  const int nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
   float M, L, acc;
-  merge(0, nvalid, M, L, acc);
+  merge(0, nvalid, mlv, ov, M, L, acc);
   const int h = g * G + hl;
   const int64_t oi = (int64_t)b * a.osb + (int64_t)h * a.osh + (int64_t)row * a.osl + d;
   float out = L > 0.f ? acc / L : 0.f;
   if (a.win > 0) {
     // the window's items follow the list's: O = g_sel O_sel + g_win O_win, one LSE per branch
-    const int64_t qpos = (int64_t)a.q_pos0 + row;
+    // (decode only: one row per query block, so the window is uniform over the workgroup)
+    const int64_t qpos = (int64_t)a.q_pos0 + qb * a.q_block;
     const int64_t hi = min((int64_t)a.L, qpos + 1), nwin = hi - max((int64_t)0, hi - a.win);
     const int nw = (int)((nwin + a.unit_den - 1) / a.unit_den);
-    load_batch(nvalid);
+    issue(nvalid, mlv, ov);
     float Mw, Lw, accw;
-    merge(nvalid, nw, Mw, Lw, accw);
-    const int64_t gi = (((int64_t)b * Hq + h) * a.Lq + row) * 2;
-    const float g0 = a.gates ? a.gates[gi] : 1.f, g1 = a.gates ? a.gates[gi + 1] : 1.f;
-    out = g0 * out + g1 * (Lw > 0.f ? accw / Lw : 0.f);
-    if (d == 0) {
-      a.lse[gi] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-      a.lse[gi + 1] = Lw > 0.f ? (Mw + log2f(Lw)) * kLn2 : -INFINITY;
+    merge(nvalid, nw, mlv, ov, Mw, Lw, accw);
+    if (live) {
+      const int64_t gi = (((int64_t)b * Hq + h) * a.Lq + row) * 2;
+      const float g0 = a.gates ? a.gates[gi] : 1.f, g1 = a.gates ? a.gates[gi + 1] : 1.f;
+      out = g0 * out + g1 * (Lw > 0.f ? accw / Lw : 0.f);
+      if (d == 0) {
+        a.lse[gi] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+        a.lse[gi + 1] = Lw > 0.f ? (Mw + log2f(Lw)) * kLn2 : -INFINITY;
+      }
     }
-  } else if (d == 0) {
+  } else if (live && d == 0) {
     a.lse[((int64_t)b * Hq + h) * a.Lq + row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
+  if (!live) return;
   if (ODT == BSA_BF16) reinterpret_cast<uint16_t*>(a.o)[oi] = (uint16_t)f32_to_bf16(out);
   else reinterpret_cast<float*>(a.o)[oi] = out;
 }
