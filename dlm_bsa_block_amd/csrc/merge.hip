@@ -103,7 +103,7 @@ __device__ __forceinline__ float half_sum(float v) {
   return lo + hi;
 }
 
-template <int DO>
+template <int DO, bool PRE_F32>
 __global__ __launch_bounds__(256) void block_attn_merge_kernel(BlockMergeArgs a) {
   constexpr int D = 128, MAXR = 32, RW = MAXR / 4;   // rows per wave
   constexpr int KP = D + 4;                          // padded key rows: 16-byte reads, lanes spread over banks
@@ -120,6 +120,7 @@ __global__ __launch_bounds__(256) void block_attn_merge_kernel(BlockMergeArgs a)
   const int d0 = 2 * lane;                           // this lane's two dims in P V and the merge
 
   // ---- round trip 1: q, kb, vb (bf16) into LDS as f32; the cached prefix state into registers
+  float op[RW][2], lp[RW];
   {
     u32x4 qv[2], kv[2], vv[2];
 #pragma unroll
@@ -129,6 +130,23 @@ __global__ __launch_bounds__(256) void block_attn_merge_kernel(BlockMergeArgs a)
       qv[it] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)r * a.qsl + d) * 2);
       kv[it] = *reinterpret_cast<const u32x4*>(a.kb + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + (int64_t)r * a.ksl + d) * 2);
       vv[it] = *reinterpret_cast<const u32x4*>(a.vb + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + (int64_t)r * a.vsl + d) * 2);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+      const int r = min(w * RW + rr, R - 1);
+      const int64_t io = (int64_t)b * a.psb + (int64_t)h * a.psh + (int64_t)r * a.psl + d0;
+      // the cached state's dtype is a template argument: a branch around these loads would make
+      // each row's load wait for the previous one
+      if constexpr (PRE_F32) {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(reinterpret_cast<const float*>(a.o_pre) + io);
+        op[rr][0] = x[0];
+        op[rr][1] = x[1];
+      } else {
+        const uint32_t x = reinterpret_cast<const uint32_t*>(a.o_pre)[io / 2];
+        op[rr][0] = bf16lo(x);
+        op[rr][1] = bf16hi(x);
+      }
+      lp[rr] = a.lse_pre[((int64_t)b * a.Hq + h) * R + r];
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -149,22 +167,6 @@ __global__ __launch_bounds__(256) void block_attn_merge_kernel(BlockMergeArgs a)
         *reinterpret_cast<f32x4*>(&vs[r][d + 4]) = x1;
       }
     }
-  }
-  float op[RW][2], lp[RW];
-#pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    const int r = min(w * RW + rr, R - 1);
-    const int64_t io = (int64_t)b * a.psb + (int64_t)h * a.psh + (int64_t)r * a.psl + d0;
-    if (a.pre_f32) {
-      const f32x2 x = *reinterpret_cast<const f32x2*>(reinterpret_cast<const float*>(a.o_pre) + io);
-      op[rr][0] = x[0];
-      op[rr][1] = x[1];
-    } else {
-      const uint32_t x = reinterpret_cast<const uint32_t*>(a.o_pre)[io / 2];
-      op[rr][0] = bf16lo(x);
-      op[rr][1] = bf16hi(x);
-    }
-    lp[rr] = a.lse_pre[((int64_t)b * a.Hq + h) * R + r];
   }
   __syncthreads();
 
@@ -239,8 +241,13 @@ __global__ __launch_bounds__(256) void block_attn_merge_kernel(BlockMergeArgs a)
 
 void launch_block_attn_merge(const BlockMergeArgs& a, int dout, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.Hq));
-  if (dout == BSA_BF16) hipLaunchKernelGGL(block_attn_merge_kernel<BSA_BF16>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(block_attn_merge_kernel<BSA_F32>, grid, dim3(256), 0, s, a);
+  if (dout == BSA_BF16) {
+    if (a.pre_f32) hipLaunchKernelGGL((block_attn_merge_kernel<BSA_BF16, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((block_attn_merge_kernel<BSA_BF16, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.pre_f32) hipLaunchKernelGGL((block_attn_merge_kernel<BSA_F32, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((block_attn_merge_kernel<BSA_F32, false>), grid, dim3(256), 0, s, a);
+  }
 }
 
 }  // namespace bsa

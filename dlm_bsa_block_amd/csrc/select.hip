@@ -260,23 +260,42 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
   const int NBW = (a.NB + 31) / 32, nC = rp.nC, NBp = a.NBp;
   const int nchan = a.G * a.nbands;
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + rp.qb;
+  const float* zrow = a.Z + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * (int64_t)nchan * NBp;
+  constexpr int CC = kPickRegs / U > kPickChanBatch ? kPickChanBatch : (kPickRegs / U > 0 ? kPickRegs / U : 1);
+  // logits of a batch of channels: every load is requested (from a clamped, valid slot) before
+  // any is used, and slots past the channels or candidates become -inf afterwards
+  auto load_z = [&](int c0, float (&z)[CC][U]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < CC; ++cc)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = tid + kPickThreads * u;
+        z[cc][u] = zrow[(int64_t)min(c0 + cc, nchan - 1) * NBp + min(j, nC - 1)];
+      }
+#pragma unroll
+    for (int cc = 0; cc < CC; ++cc)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (!(c0 + cc < nchan && tid + kPickThreads * u < nC)) z[cc][u] = -INFINITY;
+  };
+  float z0[CC][U];
+  load_z(0, z0);                                      // requested before the row mask is looked at
   const bool active = a.pooled || !a.row_mask || a.row_mask[(int64_t)b * a.Lq + row] != 0;
   if (active) {
-    const float* zrow = a.Z + (((int64_t)b * a.Hkv + g) * a.Rtot + row) * (int64_t)nchan * NBp;
     const float wband = a.nbands == 2 ? 0.5f : 1.0f;
     float s[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) s[u] = 0.f;
-    constexpr int CC = kPickRegs / U > kPickChanBatch ? kPickChanBatch : (kPickRegs / U > 0 ? kPickRegs / U : 1);
     for (int c0 = 0; c0 < nchan; c0 += CC) {
       float z[CC][U];
+      if (c0 == 0) {
 #pragma unroll
-      for (int cc = 0; cc < CC; ++cc)
+        for (int cc = 0; cc < CC; ++cc)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = tid + kPickThreads * u;
-          z[cc][u] = (c0 + cc < nchan && j < nC) ? zrow[(int64_t)(c0 + cc) * NBp + j] : -INFINITY;
-        }
+          for (int u = 0; u < U; ++u) z[cc][u] = z0[cc][u];
+      } else {
+        load_z(c0, z);
+      }
       // all channels of the batch share the two barriers of their max and sum
       float mx[CC], sm[CC];
 #pragma unroll
@@ -396,34 +415,51 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
     if (j0 > jmax) return;
   }
 
-  // stage the query vectors (converted to f32) and the pooled keys
-  for (int i = tid; i < TM * (D / 8); i += 256) {
-    const int mm = i / (D / 8), d8 = (i - mm * (D / 8)) * 8;
-    const int m = m0 + mm;
-    float v[8];
-    if (m < M) {
-      const int row = m / G, hl = m - row * G;
-      const uint8_t* p = qdata + ((int64_t)b * qsb + (int64_t)(g * G + hl) * qsh + (int64_t)row * qsl + d8) * ES;
-      load8<DT>(p, v);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) Qs[mm][d8 + e] = v[e];
-  }
+  // stage the query vectors (converted to f32) and the pooled keys.  Every load of both is
+  // requested before the first LDS store, from clamped (valid) addresses, and out-of-range
+  // entries are zeroed afterwards: a load under a branch would make each wait for the last.
   const float* kb = k_mean + ((int64_t)b * Hkv + g) * NB * D;
   // the block being refreshed (the newest, whose tokens change every decode
   // step) is pooled here from K instead of read back, and written out
   const int jr = ra.block - j0;
   const bool refresh = ra.block >= 0 && jr >= 0 && jr < TJ;     // uniform over the workgroup
-  for (int i = tid; i < TJ * (D / 4); i += 256) {
-    const int jj = i / (D / 4), d4 = (i - jj * (D / 4)) * 4;
-    const int j = j0 + jj;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (j < NB && !(refresh && jj == jr)) v = *reinterpret_cast<const f32x4*>(kb + (int64_t)j * D + d4);
+  constexpr int QN = TM * (D / 8), KN = TJ * (D / 4);
+  constexpr int QIT = (QN + 255) / 256, KIT = (KN + 255) / 256;
+  float qv[QIT][8];
+  f32x4 kv[KIT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Ks[jj][d4 + e] = v[e];
+  for (int u = 0; u < QIT; ++u) {
+    const int i = min(tid + 256 * u, QN - 1);
+    const int mm = i / (D / 8), d8 = (i - mm * (D / 8)) * 8;
+    const int m = min(m0 + mm, M - 1);
+    const int row = m / G, hl = m - row * G;
+    load8<DT>(qdata + ((int64_t)b * qsb + (int64_t)(g * G + hl) * qsh + (int64_t)row * qsl + d8) * ES, qv[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < KIT; ++u) {
+    const int i = min(tid + 256 * u, KN - 1);
+    const int jj = i / (D / 4), d4 = (i - jj * (D / 4)) * 4;
+    kv[u] = *reinterpret_cast<const f32x4*>(kb + (int64_t)min(j0 + jj, NB - 1) * D + d4);
+  }
+#pragma unroll
+  for (int u = 0; u < QIT; ++u) {
+    const int i = tid + 256 * u;
+    if (i < QN) {
+      const int mm = i / (D / 8), d8 = (i - mm * (D / 8)) * 8;
+      const bool in = m0 + mm < M;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Qs[mm][d8 + e] = in ? qv[u][e] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < KIT; ++u) {
+    const int i = tid + 256 * u;
+    if (i < KN) {
+      const int jj = i / (D / 4), d4 = (i - jj * (D / 4)) * 4;
+      const bool in = j0 + jj < NB && !(refresh && jj == jr);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ks[jj][d4 + e] = in ? kv[u][e] : 0.f;
+    }
   }
   if (refresh) {
     // one pass of 16 lanes x 8 dims per row, 16 rows per pass, fixed-order sums (as the summaries kernel)
@@ -439,13 +475,12 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
     for (int r0 = 0; r0 < n; r0 += 4 * RPP) {
       float v[4][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = r0 + u * RPP + rg;
-        if (r < n) load8<DT>(kp + (int64_t)r * ra.ksl * ES, v[u]);
-        else {
+      for (int u = 0; u < 4; ++u) load8<DT>(kp + (int64_t)min(r0 + u * RPP + rg, n - 1) * ra.ksl * ES, v[u]);
 #pragma unroll
-          for (int q8 = 0; q8 < 8; ++q8) v[u][q8] = 0.f;
-        }
+      for (int u = 0; u < 4; ++u) {
+        const bool in = r0 + u * RPP + rg < n;
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) v[u][q8] = in ? v[u][q8] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)

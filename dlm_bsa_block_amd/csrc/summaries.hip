@@ -34,16 +34,16 @@ __global__ __launch_bounds__(256) void summaries_kernel(const uint8_t* __restric
   for (int i = 0; i < 8; ++i) sum[i] = 0.f;
   float e = 0.f;
   for (int r0 = 0; r0 < n; r0 += CH * RPP) {
+    // rows past the block's end load its last row and are zeroed: a load under a branch
+    // would make the compiler wait for each pass before requesting the next
     float v[CH][8];
 #pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int r = r0 + k * RPP + rg;
-      if (r < n) {
-        load8<DT>(p + (int64_t)r * sl * ES, v[k]);
-      } else {
+    for (int k = 0; k < CH; ++k) load8<DT>(p + (int64_t)min(r0 + k * RPP + rg, n - 1) * sl * ES, v[k]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[k][i] = 0.f;
-      }
+    for (int k = 0; k < CH; ++k) {
+      const bool in = r0 + k * RPP + rg < n;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[k][i] = in ? v[k][i] : 0.f;
     }
 #pragma unroll
     for (int k = 0; k < CH; ++k)

@@ -80,25 +80,35 @@ __global__ __launch_bounds__(512) void tdec_scores_kernel(TDecArgs a) {
   const int nt = (n + T - 1) / T;
 
   // Q^T operand: column = head (zero past G), k = dims 32 ks + 8 kq + 0..7
+  // (all loads of q and of the chunk mask are requested before any is used: loads under a
+  // branch, or used as they arrive, would each wait for the one before)
   bf16x8 qb[4];
+  u32x4 qw[4];
+  const int hq = g * G + min(col, G - 1);           // columns past G load a valid row, then zeroed
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    u32x4 v4 = {0u, 0u, 0u, 0u};
-    if (col < G)
-      v4 = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.qsb + (int64_t)(g * G + col) * a.qsh +
-                                                  32 * ks + 8 * kq) * 2);
-    if (a.fc_mask && col < G) {
-      // token scoring on a subset of frequency chunks: zero the query dims of the other chunks
-      const uint8_t* fm = a.fc_mask + (int64_t)(g * G + col) * 64;
+  for (int ks = 0; ks < 4; ++ks)
+    qw[ks] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.qsb + (int64_t)hq * a.qsh + 32 * ks + 8 * kq) * 2);
+  if (a.fc_mask) {                                  // uniform
+    // token scoring on a subset of frequency chunks: zero the query dims of the other chunks
+    const uint8_t* fm = a.fc_mask + (int64_t)hq * 64;
+    uint8_t mb[4][4][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d = 32 * ks + 8 * kq + 2 * e;             // dims d, d + 1 of word e
-        const int f0 = a.layout == BSA_ROPE_HALF ? (d & 63) : (d >> 1);
-        const int f1 = a.layout == BSA_ROPE_HALF ? ((d + 1) & 63) : (d >> 1);
-        v4[e] &= (fm[f0] ? 0x0000FFFFu : 0u) | (fm[f1] ? 0xFFFF0000u : 0u);
+        mb[ks][e][0] = fm[a.layout == BSA_ROPE_HALF ? (d & 63) : (d >> 1)];
+        mb[ks][e][1] = fm[a.layout == BSA_ROPE_HALF ? ((d + 1) & 63) : (d >> 1)];
       }
-    }
-    qb[ks] = __builtin_bit_cast(bf16x8, v4);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qw[ks][e] &= (mb[ks][e][0] ? 0x0000FFFFu : 0u) | (mb[ks][e][1] ? 0xFFFF0000u : 0u);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (col >= G) qw[ks] = u32x4{0u, 0u, 0u, 0u};
+    qb[ks] = __builtin_bit_cast(bf16x8, qw[ks]);
   }
   const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + (int64_t)s0 * a.ksl) * 2;
   const int nch = (nt * T) / CH;                    // chunks of the slice's tiles
