@@ -480,7 +480,7 @@ def denoise_step(p: dict, q: np.ndarray, k: np.ndarray, v: np.ndarray, kb: np.nd
 
 # ---------------------------------------------------- threshold attention ---
 def threshold_walk(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows_pos: np.ndarray, tile: int, lam: float,
-                   scale: float, causal: bool = True, decisions: dict | None = None):
+                   scale: float, causal: bool = True, decisions: dict | None = None, masses: bool = True):
     """One (head, query tile) of softmax-threshold attention ([BLASST] sec. 2).
 
     q: [T, D] rows of the tile at absolute positions rows_pos; k, v: [L, D].
@@ -499,7 +499,8 @@ def threshold_walk(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows_pos: np.nda
     the caller can check that every replayed choice agrees with fp64 except
     within a rounding band.
     Returns dict(O [T, D], lse [T], kept [tiles], order, margin {tile: float},
-    decision {tile: bool}, mass_kept, mass_skipped).
+    decision {tile: bool}, mass_kept, mass_skipped); ``masses=False`` leaves the
+    two masses None (a second pass over the keys, not needed for O and LSE).
     """
     L = k.shape[0]
     ln_lam = math.log(lam) if lam > 0 else -math.inf
@@ -531,6 +532,9 @@ def threshold_walk(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows_pos: np.nda
             kept.append(j)
     toks = block_tokens(np.array(sorted(kept), dtype=np.int64), tile, L)
     O, lse = attend_tokens(q, k, v, toks, scale, rows_pos if causal else None)
+    if not masses:
+        return dict(O=O, lse=lse, kept=sorted(kept), margin=margin, decision=decision, mass_kept=None,
+                    mass_skipped=None)
     # exp-mass kept vs skipped (for the skipped-mass bound), per row, relative to the final max
     all_toks = block_tokens(np.arange(jmax + 1), tile, L)
     S_all = scale * (q @ k[all_toks].T)

@@ -9,6 +9,8 @@ a ragged tail; the full-size cases use the shapes and launch configuration
 the benchmark times, checked on sampled rows.
 """
 import math
+import os
+import sys
 
 import numpy as np
 import pytest
@@ -16,7 +18,8 @@ import torch
 
 import oracle as orc
 import synth
-from parity import (THRESH_EPS, ambiguous, check_list, check_outputs, check_row_picks, from_dev, to_dev)
+from parity import (THRESH_EPS, ambiguous, check_list, check_outputs, check_row_picks, check_threshold_walk,
+                    from_dev, record_threshold, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -691,8 +694,11 @@ def _threshold_decode_case(bsa, w, lam, kv_split, where):
     gkeep = km.cpu().numpy().astype(bool)
     assert np.array_equal(gkeep.sum(axis=2), kept.cpu().numpy()), f"{where}: kept counts disagree with the map"
     O_ref, L_ref, _, margin = orc.threshold_decode(q, k, v, lam, scale, 64, decisions=gkeep)
-    bad = (gkeep != (margin >= 0)) & (np.abs(margin) > THRESH_EPS)
+    differ = gkeep != (margin >= 0)
+    bad = differ & (np.abs(margin) > THRESH_EPS)
     assert not bad.any(), f"{where}: {int(bad.sum())} keep/skip choices disagree with the fp64 walk"
+    record_threshold(gkeep.size, int(differ.sum()), gkeep.shape[0] * gkeep.shape[1], 0,
+                     float(np.abs(margin[differ]).max()) if differ.any() else 0.0)
     check_outputs(from_dev(o32), O_ref, lse.cpu().numpy(), L_ref, where)
     return float(1.0 - gkeep.mean())
 
@@ -728,12 +734,10 @@ def test_threshold_decode_full_size(bsa):
 
 # --------------------------------------------------------------- threshold ---
 def _threshold_case(bsa, w, lam, pairs):
-    """The oracle walks each sampled (head, query tile) with its own decisions.  If
-    the GPU's keep map matches, outputs are compared with that walk.  Otherwise
-    every differing decision must sit within THRESH_EPS of the fp64 threshold;
-    the walk is then replayed on the GPU's choices (each of which must agree with
-    the fp64 state along that path outside the band) and outputs are compared
-    with the replay."""
+    """The GPU's keep map and outputs for the sampled (batch, head, query tile)
+    triples, each checked against the fp64 walk (checks.check_threshold_walk:
+    the walk is replayed on the GPU's choices when they differ inside the
+    rounding band)."""
     p = w.params
     qd, kd, vd = _dev_workload(w)
     o, lse, kept, km = bsa.bsa_threshold_attention_fwd(qd, kd, vd, lam, scale=p["scale"], tile=p["tile"],
@@ -750,27 +754,17 @@ def _threshold_case(bsa, w, lam, pairs):
     G = w.q.shape[1] // w.k.shape[1]
     T = p["tile"]
     Lq = w.q.shape[2]
-    n_replayed = 0
+    tot = [0, 0, 0, 0.0]
     for (b, h, qt) in pairs:
         jmax = min(Lq - 1, (qt + 1) * T - 1) // T
         dec = {j: bool(km_np[b, h, qt, j]) for j in range(jmax + 1)}
         rows = np.arange(qt * T, min((qt + 1) * T, Lq))
-        args = (q[b, h, rows], k[b, h // G], v[b, h // G], rows, T, lam, p["scale"], bool(p["causal"]))
-        r = orc.threshold_walk(*args)
-        if r["decision"] != dec:
-            # tiles are visited from the highest index down: the first differing
-            # choice must sit in the rounding band of the fp64 walk
-            first = max(j for j in dec if dec[j] != r["decision"][j])
-            assert abs(r["margin"][first]) <= THRESH_EPS, \
-                f"h{h} qt{qt} tile {first}: gpu keep={dec[first]}, fp64 margin {r['margin'][first]:.4g}"
-            r = orc.threshold_walk(*args, decisions=dec)
-            n_replayed += 1
-            for j, mg in r["margin"].items():
-                if abs(mg) > THRESH_EPS:
-                    assert dec[j] == (mg >= 0), f"h{h} qt{qt} tile {j}: gpu keep={dec[j]}, fp64 margin {mg:.4g}"
-        assert kept_np[b, h, qt] == len(r["kept"])
-        check_outputs(o_np[b, h, rows], r["O"], l_np[b, h, rows], r["lse"], f"thr h{h} qt{qt}")
-    return kept_np, n_replayed
+        d, f, r, m = check_threshold_walk(q[b, h, rows], k[b, h // G], v[b, h // G], rows, T, lam, p["scale"],
+                                          bool(p["causal"]), dec, kept_np[b, h, qt], o_np[b, h, rows],
+                                          l_np[b, h, rows], f"thr h{h} qt{qt}")
+        tot = [tot[0] + d, tot[1] + f, tot[2] + r, max(tot[3], m)]
+    record_threshold(tot[0], tot[1], len(pairs), tot[2], tot[3])
+    return kept_np, tot[2]
 
 
 @pytest.mark.parametrize("L,lam", [(4096, 1e-3), (4000, 1e-3), (2048, 0.0), (4096, 0.3)])
@@ -792,14 +786,62 @@ def test_threshold_odd_group(bsa):
 
 
 def test_threshold_full_size_sampled(bsa):
-    """128K causal prefill with lambda = 1e-3: sampled query tiles of two heads."""
-    heads = [0, 13]
-    w = synth.threshold_prefill(heads=heads)
+    """128K causal prefill with lambda = 1e-3, every one of the 32 heads: 16 query
+    tiles per head (the last tile, which sees all 1024 KV tiles, and 15 drawn at
+    random), walked in the fp64 oracle by one spawned CPU worker per KV group."""
+    import multiprocessing as mp
+
+    import threshold_walks
+    w = synth.threshold_prefill()
+    p = w.params
+    T, lam = p["tile"], 1e-3
+    Hq, Hkv = w.q.shape[1], w.k.shape[1]
+    G, NQT = Hq // Hkv, -(-w.q.shape[2] // T)
+    qd, kd, vd = _dev_workload(w)
+    o, lse, kept, km = bsa.bsa_threshold_attention_fwd(qd, kd, vd, lam, scale=p["scale"], tile=T, causal=p["causal"],
+                                                       o=_f32_out(qd), want_keep_map=True)
+    _sync()
+    kept_np = kept.cpu().numpy()
+    sys.__stderr__.write("[threshold 128K] GPU pass done; gathering the sampled tiles\n")
+    sys.__stderr__.flush()
+    frac_skip = 1.0 - kept_np[0].sum() / (Hq * NQT * (NQT + 1) / 2)
+    assert 0.66 < frac_skip < 0.74, frac_skip
     rng = np.random.default_rng(5)
-    qts = sorted(set([0, 1023] + rng.choice(1024, 4, replace=False).tolist()))
-    kept, _ = _threshold_case(bsa, w, 1e-3, [(0, h, qt) for h in heads for qt in qts])
-    frac_skip = 1.0 - kept[0, heads].sum() / (len(heads) * 1024 * 1025 / 2)
-    assert 0.66 < frac_skip < 0.74
+    tasks = []
+    for g in range(Hkv):
+        items = []
+        for h in range(g * G, (g + 1) * G):
+            qts = [NQT - 1] + sorted(rng.choice(NQT - 1, 15, replace=False).tolist())
+            for qt in qts:
+                r0, r1 = qt * T, min((qt + 1) * T, w.q.shape[2])
+                items.append(dict(h=h, qt=qt, q=np.ascontiguousarray(w.q[0, h, r0:r1]),
+                                  dec={j: bool(x) for j, x in enumerate(km[0, h, qt, :qt + 1].cpu().numpy())},
+                                  kept=int(kept_np[0, h, qt]), o=o[0, h, r0:r1].cpu().numpy(),
+                                  lse=lse[0, h, r0:r1].cpu().numpy()))
+        tasks.append(dict(k=np.ascontiguousarray(w.k[0, g]), v=np.ascontiguousarray(w.v[0, g]), tile=T, lam=lam,
+                          scale=p["scale"], causal=bool(p["causal"]), items=items))
+    del o, lse, km
+    # one worker per KV group with two BLAS threads each: 16 threads, the CPU share of one GPU
+    nproc = min(Hkv, 8)
+    saved = {e: os.environ.get(e) for e in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for e in saved:
+        os.environ[e] = "2"
+    try:
+        with mp.get_context("spawn").Pool(nproc) as pool:
+            tot, walks = [0, 0, 0, 0.0], 0
+            for (d, f, r, m), n in pool.imap_unordered(threshold_walks.check_group, tasks):
+                tot = [tot[0] + d, tot[1] + f, tot[2] + r, max(tot[3], m)]
+                walks += n
+                sys.__stderr__.write(f"[threshold 128K] {walks} of {Hq * 16} walks checked\n")
+                sys.__stderr__.flush()
+    finally:
+        for e, val in saved.items():
+            if val is None:
+                os.environ.pop(e, None)
+            else:
+                os.environ[e] = val
+    assert walks == Hq * 16
+    record_threshold(tot[0], tot[1], walks, tot[2], tot[3])
 
 
 # ------------------------------------------------------------- determinism ---
