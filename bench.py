@@ -33,8 +33,19 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # Softmax-threshold decode: lambda = a / L (BLASST: one constant per model and
 # phase); with this a, 93% of the (head, tile) pairs and 81% of the V tiles are
 # skipped at 64K on the synthetic GQA decode workload.
-THRESH_DECODE_A = 0.4 * 65536
 THRESH_DECODE_SPLIT = 1024     # keys per split-KV slice
+# lambda = a / L for the threshold decode (BLASST page, section 2: one constant per
+# model and phase).  a is the largest of THRESH_DECODE_A_GRID whose output stays
+# within half the output tolerance of the dense result at every length of
+# THRESH_CALIB_LENGTHS, on both synthetic decode caches (the flat GQA decode one and
+# the one with the threshold-prefill structure); calibrate_threshold_decode()
+# repeats that sweep in every run and reports it.
+THRESH_DECODE_A = 1.0         # the calibrated value (structured cache at 16K is the binding case)
+THRESH_DECODE_A_GRID = tuple(2.0 ** e for e in range(-2, 16))    # 0.25 .. 32768
+THRESH_CALIB_LENGTHS = (16384, 32768, 65536)
+THRESH_CALIB_MAX_ABS = 5e-3    # half of the 1e-2 max-abs output tolerance
+THRESH_CALIB_REL_L2 = 2.5e-3   # half of the 5e-3 relative-L2 output tolerance
+THRESH_TINY_LAMBDA = 1e-30     # the skip test runs, and keeps every tile of these workloads
 WINDOW = 512                   # NSA sliding window (tokens) for the selection + window decode
 TOKEN_FCS = 8                  # frequency chunks per head for token importance (of 64)
 TOKEN_BUDGET = 256             # tokens per head (the FASA page's LongBench budget)
@@ -471,12 +482,59 @@ def bench_threshold(torch, bsa, synth, reps):
 
 
 # ------------------------------------------------------- threshold decode ---
-def bench_threshold_decode(torch, bsa, synth, reps, flush, w=None):
-    """Dense decode over the whole 64K cache with the softmax-threshold skip at
-    lambda = a / L: every K tile is read, V only for tiles some head keeps."""
-    if w is None:
-        log("tdecode: generating the 64K GQA workload")
-        w = synth.gqa_decode()
+def _tdec_errors(torch, bsa, w, lams):
+    """Threshold decode of workload w at each lambda against lambda = 0 (the same
+    kernels with the skip test compiled out: dense over all keys), fp32 outputs.
+    Returns [(max abs error, relative L2 error, skipped fraction of head tiles)]."""
+    p = w.params
+    q, k, v = (to_dev(torch, x, "bf16") for x in (w.q, w.k, w.v))
+    o32 = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    o0, _, _, _ = bsa.bsa_threshold_decode_fwd(q, k, v, 0.0, scale=p["scale"], kv_split=THRESH_DECODE_SPLIT,
+                                               o=o32.clone())
+    out = []
+    for lam in lams:
+        o, _, _, km = bsa.bsa_threshold_decode_fwd(q, k, v, lam, scale=p["scale"], kv_split=THRESH_DECODE_SPLIT,
+                                                   o=o32, want_keep_map=True)
+        out.append((float((o - o0).abs().max().item()), float(((o - o0).norm() / o0.norm()).item()),
+                    1.0 - km.float().mean().item()))
+    return out
+
+
+def calibrate_threshold_decode(torch, bsa, synth, cache=None):
+    """The sweep behind THRESH_DECODE_A: for each cache kind and length and each a
+    of the grid, the threshold decode at lambda = min(1, a / L) against the dense
+    result; the calibrated a is the largest whose max-abs and relative-L2 errors
+    stay within half the output tolerance everywhere.  cache: {(kind, L): workload}
+    already generated."""
+    cache = cache or {}
+    gens = {"flat": synth.gqa_decode, "structured": synth.threshold_decode}
+    sweep, ok = {}, {a: True for a in THRESH_DECODE_A_GRID}
+    for kind, gen in gens.items():
+        for L in THRESH_CALIB_LENGTHS:
+            w = cache.get((kind, L)) or gen(L=L)
+            errs = _tdec_errors(torch, bsa, w, [min(1.0, a / L) for a in THRESH_DECODE_A_GRID])
+            row = {}
+            for a, (e, r, sk) in zip(THRESH_DECODE_A_GRID, errs):
+                row[f"{a:g}"] = [float(f"{e:.3g}"), float(f"{r:.3g}"), round(sk, 4)]
+                ok[a] = ok[a] and e <= THRESH_CALIB_MAX_ABS and r <= THRESH_CALIB_REL_L2
+            sweep[f"{kind}_{L}"] = row
+    good = [a for a in THRESH_DECODE_A_GRID if ok[a]]
+    return dict(criterion=f"max|O_lambda - O_dense| <= {THRESH_CALIB_MAX_ABS:g} and relative L2 <= "
+                          f"{THRESH_CALIB_REL_L2:g} at L = {list(THRESH_CALIB_LENGTHS)} on the flat and the "
+                          "structured decode caches",
+                calibrated_a=max(good) if good else None,
+                sweep_columns="a: [max abs error, relative L2 error, skipped head tiles]", sweep=sweep)
+
+
+def bench_threshold_decode(torch, bsa, synth, reps, flush, w_flat=None):
+    """Threshold decode over the whole 64K cache with the threshold-prefill
+    structure (local segments and needles) at lambda = a / L: every K tile is
+    read, V only for tiles some head keeps.  Also: the error against the dense
+    result at that lambda, the same lambda on the flat GQA decode cache, the
+    calibration sweep, and the cost of the skip test where it skips nothing
+    (lambda = 1e-30) against the variant with the test compiled out (lambda = 0)."""
+    log("tdecode: generating the structured 64K decode cache")
+    w = synth.threshold_decode(L=65536)
     p = w.params
     q, k, v = (to_dev(torch, x, "bf16") for x in (w.q, w.k, w.v))
     B, Hkv, L, D = k.shape
@@ -495,33 +553,41 @@ def bench_threshold_decode(torch, bsa, synth, reps, flush, w=None):
 
     _, _, _, km = bsa.bsa_threshold_decode_fwd(q, k, v, lam, scale=p["scale"], kv_split=THRESH_DECODE_SPLIT,
                                                want_keep_map=True, workspace=ws)
+    _, _, kept_tiny, _ = bsa.bsa_threshold_decode_fwd(q, k, v, THRESH_TINY_LAMBDA, scale=p["scale"],
+                                                      kv_split=THRESH_DECODE_SPLIT, workspace=ws)
+    (err_max, err_rel, _), = _tdec_errors(torch, bsa, w, [lam])
     nt = km.shape[2]
     v_tiles = int(km.view(B, Hkv, G, nt).amax(dim=2).sum().item())        # tiles whose V is loaded
     head_kept = int(km.sum().item())
+    tiny_all_kept = int(kept_tiny.sum().item()) == B * Hq * nt
     t_warm = time_calls(torch, run(lam), reps)
     t_cold = time_cold(torch, run(lam), reps, flush)
     t0_cold = time_cold(torch, run(0.0), reps, flush)
+    tt_cold = time_cold(torch, run(THRESH_TINY_LAMBDA), reps, flush)
     k_bytes = B * Hkv * L * D * 2
     alg = k_bytes + v_tiles * 64 * D * 2 + 2 * B * Hq * D * 2            # all K, loaded V, q and o
     dense = 2 * k_bytes + 2 * B * Hq * D * 2
-    other = {}
-    for Ls in (16384, 32768):                                             # the same a at other lengths
-        ws_ = synth.gqa_decode(L=Ls)
-        qs, ks, vs = (to_dev(torch, x, "bf16") for x in (ws_.q, ws_.k, ws_.v))
-        lm = min(1.0, THRESH_DECODE_A / Ls)
-        _, _, _, kms = bsa.bsa_threshold_decode_fwd(qs, ks, vs, lm, scale=p["scale"], kv_split=THRESH_DECODE_SPLIT,
-                                                    want_keep_map=True)
-        vt = kms.view(B, Hkv, G, -1).amax(dim=2)
-        other[str(Ls)] = dict(lam=round(lm, 4), skip_head_tiles=round(1 - kms.float().mean().item(), 4),
-                              skip_v_tiles=round(1 - vt.float().mean().item(), 4))
-        del qs, ks, vs
+    del q, k, v
+    if w_flat is None:
+        w_flat = synth.gqa_decode()
+    (fe, fr, fs), = _tdec_errors(torch, bsa, w_flat, [lam])
+    log("tdecode: calibration sweep of lambda = a / L")
+    calib = calibrate_threshold_decode(torch, bsa, synth, {("structured", 65536): w, ("flat", 65536): w_flat})
     gbs = alg / (t_cold * 1e3)
-    return dict(us_cold=round(t_cold, 2), us_warm=round(t_warm, 2), lam=round(lam, 4), a=THRESH_DECODE_A,
+    return dict(cache="threshold-prefill structure (segments of 13824 keys, 8 needle tiles per KV head)",
+                us_cold=round(t_cold, 2), us_warm=round(t_warm, 2), lam=float(f"{lam:.4g}"), a=THRESH_DECODE_A,
                 kv_split=THRESH_DECODE_SPLIT, skip_head_tiles=round(1 - head_kept / (B * Hq * nt), 4),
                 skip_v_tiles=round(1 - v_tiles / (B * Hkv * nt), 4), algorithmic_bytes=alg,
                 gbs_cold=round(gbs, 1), hbm_frac_cold=round(gbs / HBM_PEAK_GBS, 4),
+                err_vs_dense=dict(max_abs=float(f"{err_max:.3g}"), rel_l2=float(f"{err_rel:.3g}")),
                 lambda0_us_cold=round(t0_cold, 2), lambda0_gbs_cold=round(dense / (t0_cold * 1e3), 1),
-                speedup_vs_lambda0=round(t0_cold / t_cold, 3), other_lengths=other)
+                speedup_vs_lambda0=round(t0_cold / t_cold, 3),
+                skip_test_overhead=dict(lam=THRESH_TINY_LAMBDA, us_cold=round(tt_cold, 2),
+                                        every_tile_kept=tiny_all_kept,
+                                        vs_test_compiled_out=round(tt_cold / t0_cold, 3)),
+                flat_cache_same_lambda=dict(skip_head_tiles=round(fs, 4), err_max=float(f"{fe:.3g}"),
+                                            rel_l2=float(f"{fr:.3g}")),
+                calibration=calib)
 
 
 # ----------------------------------------------------- token importance ---

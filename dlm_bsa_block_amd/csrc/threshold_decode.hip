@@ -196,7 +196,9 @@ __global__ __launch_bounds__(512) void tdec_scores_kernel(TDecArgs a) {
 // per key row, 8 keys per pass), so each wave walks every kept tile.  While
 // the loads are in flight the workgroup turns the kept scores into
 // p = 2^(s - m_c) in place (0 for a tile or key the head does not keep).
-template <int G>
+// CHECK = false (lambda = 0) compiles the skip test out: every finite tile is
+// kept and the newer tiles' maxima are not read.
+template <int G, bool CHECK>
 __global__ __launch_bounds__(256) void tdec_pv_kernel(TDecArgs a) {
   constexpr int D = 128, T = kTDecTile, NW = 4, NT = 256;
   constexpr int MAXT = kTDecMaxSplit / T;           // tiles per slice, at most 32
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(256) void tdec_pv_kernel(TDecArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       nv[h] = -INFINITY;
-      if (w == NW - 1)
+      if (CHECK && w == NW - 1)
         for (int q = sp + 1 + lane; q < a.nsplit; q += 64) nv[h] = fmaxf(nv[h], a.smax[(hb + h) * a.nsplit + q]);
     }
 #pragma unroll
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(256) void tdec_pv_kernel(TDecArgs a) {
       }
     }
     if (tid < G * MAXT) tmx[tid / MAXT][tid % MAXT] = tv;
-    if (w == NW - 1) {
+    if (CHECK && w == NW - 1) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float m = wave_max_dpp(nv[h]);
@@ -273,15 +275,18 @@ __global__ __launch_bounds__(256) void tdec_pv_kernel(TDecArgs a) {
     const int h = 2 * r + lane / 32, j = lane % 32;
     const bool valid = h < G && j < ntail;
     const float tm = valid ? tmx[h < G ? h : 0][j] : -INFINITY;
-    // max over the slice's tiles after j (shuffles stay inside each 32-lane half)
-    float incl = tm;
-#pragma unroll
-    for (int sft = 1; sft < 32; sft <<= 1) incl = fmaxf(incl, __shfl_down(incl, sft, 32));
-    float excl = __shfl_down(incl, 1, 32);
-    if (j == 31) excl = -INFINITY;
-    const float M = fmaxf(valid ? newer_sh[h] : -INFINITY, excl);
     const bool mine = valid && j < nt;                      // a tile of this chunk
-    const bool keep = mine && tm > -INFINITY && (M == -INFINITY || tm - M >= a.ln_lam2);
+    bool keep = mine && tm > -INFINITY;
+    if constexpr (CHECK) {
+      // max over the slice's tiles after j (shuffles stay inside each 32-lane half)
+      float incl = tm;
+#pragma unroll
+      for (int sft = 1; sft < 32; sft <<= 1) incl = fmaxf(incl, __shfl_down(incl, sft, 32));
+      float excl = __shfl_down(incl, 1, 32);
+      if (j == 31) excl = -INFINITY;
+      const float M = fmaxf(valid ? newer_sh[h] : -INFINITY, excl);
+      keep = keep && (M == -INFINITY || tm - M >= a.ln_lam2);
+    }
     const uint64_t bal = __ballot(keep);
     float x = keep ? tm : -INFINITY;
 #pragma unroll
@@ -577,7 +582,8 @@ void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa
   const dim3 gs(a.nsplit, q.B * k.H), gp(a.nchunk, q.B * k.H);
 #define BSA_TDEC(GG)                                                                  \
   hipLaunchKernelGGL(tdec_scores_kernel<GG>, gs, dim3(512), 0, s, a);                 \
-  hipLaunchKernelGGL(tdec_pv_kernel<GG>, gp, dim3(256), 0, s, a)
+  if (lambda > 0.f) hipLaunchKernelGGL((tdec_pv_kernel<GG, true>), gp, dim3(256), 0, s, a); \
+  else hipLaunchKernelGGL((tdec_pv_kernel<GG, false>), gp, dim3(256), 0, s, a)
   switch (G) {
     case 1: BSA_TDEC(1); break;
     case 2: BSA_TDEC(2); break;

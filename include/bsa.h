@@ -319,7 +319,8 @@ bsa_status bsa_threshold_attention_fwd(const bsa_tensor* q, const bsa_tensor* k,
  * head's kept tiles.  kv_split (keys per slice) sets how the work is cut:
  * each slice's kept keys are summed by one workgroup and the slices are
  * merged in order.  V of a tile is loaded only when some head of its KV
- * group keeps it.  lambda in [0, 1] (0 keeps all).
+ * group keeps it.  lambda in [0, 1]; lambda = 0 keeps every tile and runs a
+ * variant with the skip test compiled out (dense decode over all L keys).
  * Optional: kept_tiles [B, Hq] int32 (tiles kept per head) and keep_map
  * [B, Hq, ceil(L / 64)] uint8 (1 = kept).  Supported: bf16, D = 128, group
  * size 1, 2, 4 or 8, kv_split a multiple of 64 in [64, 2048], v row stride

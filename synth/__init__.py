@@ -16,4 +16,5 @@ from .workloads import (  # noqa: F401
     dlm_denoise_steps,
     sparse_prefill,
     threshold_prefill,
+    threshold_decode,
 )

@@ -374,3 +374,37 @@ def threshold_prefill(seed: int = 5, L: int = 131072, Hq: int = 32, Hkv: int = 8
     params = dict(tile=tile, causal=1, lam=lam, scale=1.0 / math.sqrt(D))
     return Workload("threshold_prefill", "bf16", qb[None], kb[None], vb[None], params,
                     dict(needles=needles, seg_tiles=seg_tiles, alpha=alpha))
+
+
+def threshold_decode(seed: int = 5, L: int = 65536, Hq: int = 32, Hkv: int = 8, D: int = 128, tile: int = 128,
+                     seg_tiles: int = 108, n_needles: int = 8, logit_gap: float = 24.0) -> Workload:
+    """One decode query per head over a cache with the threshold-prefill
+    structure (local segments and needles, no RoPE): the query, at position
+    L - 1, carries alpha*(e_seg(L-1) + w_g), so it sees its own and the
+    previous segment and the needles; the rest of the cache sits far below the
+    running max.  K and V are made exactly as threshold_prefill makes them; the
+    query's noise comes from its own stream."""
+    G = Hq // Hkv
+    NT = -(-L // tile)
+    nseg = -(-NT // seg_tiles) + 1
+    alpha = math.sqrt(logit_gap * math.sqrt(D))
+    seg = (np.arange(L) // tile) // seg_tiles
+    qb = np.zeros((Hq, 1, D), dtype=np.uint16)
+    kb = np.zeros((Hkv, L, D), dtype=np.uint16)
+    vb = np.zeros((Hkv, L, D), dtype=np.uint16)
+    needles = np.zeros((Hkv, n_needles), dtype=np.int64)
+    for g in range(Hkv):
+        e = _unit(_rng(seed, 50, g), nseg + 1, D)
+        nd = np.sort(_rng(seed, 51, g).choice(NT, size=min(n_needles, NT), replace=False))
+        w = _unit(_rng(seed, 52, g), 1, D)[0]
+        needles[g, :len(nd)] = nd
+        for h in range(g * G, (g + 1) * G):
+            qb[h] = _store(_normal(seed, _Q + 100, h, (1, D)) + alpha * (e[seg[L - 1]] + w)[None, :], "bf16")
+        kstruct = alpha * (e[seg] + e[seg + 1])
+        for t in nd:
+            kstruct[t * tile:min((t + 1) * tile, L)] = alpha * w
+        kb[g] = _store(_normal(seed, _K, g, (L, D)) + kstruct, "bf16")
+        vb[g] = _store(_normal(seed, _V, g, (L, D)), "bf16")
+    params = dict(q_pos0=L - 1, causal=1, scale=1.0 / math.sqrt(D))
+    return Workload("threshold_decode", "bf16", qb[None], kb[None], vb[None], params,
+                    dict(needles=needles, seg_tiles=seg_tiles, alpha=alpha))

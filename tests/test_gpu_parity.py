@@ -301,7 +301,11 @@ def test_window_decode_full_size(bsa):
     _window_case(bsa, synth.gqa_decode(), 512)
 
 
-TOKEN_EPS = 1e-4        # |score - N-th score| within this: either choice is correct (fp32 vs fp64 sums)
+def _fp32_dot_bound(n_terms: int) -> float:
+    """gamma_n = n u / (1 - n u), u = 2^-24: |fl(sum) - sum| <= gamma_n * sum |terms|
+    for a sum of n exact products accumulated in fp32 in any order."""
+    nu = n_terms * 2.0 ** -24
+    return nu / (1.0 - nu)
 
 
 def _fc_mask(Hq, n_fc, seed):
@@ -328,6 +332,10 @@ def _token_case(bsa, w, budget, n_fc, layout, seed=0):
     assert torch.equal(lse, lse16)
     q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
     S = orc.token_scores(q, k, mask, layout)
+    # per-token rounding bound of the GPU's fp32 score: the sum of |products| over the kept dims,
+    # times gamma_n, plus one rounding of the scaled result
+    A = orc.token_scores(np.abs(q), np.abs(k), mask, layout)
+    gam = _fp32_dot_bound(2 * n_fc)
     idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
     n = min(budget, L)
     lists = [[None] * Hq for _ in range(B)]
@@ -338,7 +346,10 @@ def _token_case(bsa, w, budget, n_fc, layout, seed=0):
             got = idx_np[b, h, :n].astype(np.int64)
             assert np.all(np.diff(got) > 0) and got.min() >= 0 and got.max() < L, f"head {h}: list not ascending"
             ref, kth = orc.top_tokens(S[b, h], budget)
-            amb = set(np.nonzero(np.abs(S[b, h] - kth) <= TOKEN_EPS * max(1.0, abs(kth)))[0].tolist())
+            # tokens whose exact score could fall on either side of the N-th one's after fp32 rounding
+            ki = ref[np.argmin(S[b, h][ref])]
+            band = gam * (A[b, h] + A[b, h][ki]) + 2.0 ** -23 * np.maximum(np.abs(S[b, h]), abs(kth))
+            amb = set(np.nonzero(np.abs(S[b, h] - kth) <= band)[0].tolist())
             n_amb += len(amb)
             assert set(got.tolist()) - amb == set(ref.tolist()) - amb, f"head {h}: token sets differ"
             lists[b][h] = got
@@ -723,13 +734,21 @@ def test_threshold_decode_group_sizes(bsa, Hq, Hkv):
     _threshold_decode_case(bsa, w, 0.4, 512, f"threshold decode G={Hq // Hkv}")
 
 
-def test_threshold_decode_full_size(bsa):
-    """64K GQA decode, every head, at the benchmark's lambda = a / L and slices."""
+@pytest.mark.parametrize("which", ["calibrated", "aggressive"])
+def test_threshold_decode_full_size(bsa, which):
+    """64K decode, every head, at the benchmark's slices: the cache with the
+    threshold-prefill structure at the calibrated lambda = a / L (the benchmark's
+    configuration), and the flat GQA decode cache at lambda = 0.4, which skips
+    most of its tiles (the skip path at full size)."""
     import bench
-    w = synth.gqa_decode()
-    lam = bench.THRESH_DECODE_A / w.k.shape[2]
-    skipped = _threshold_decode_case(bsa, w, lam, bench.THRESH_DECODE_SPLIT, "threshold decode 64K")
-    assert skipped > 0.3
+    if which == "calibrated":
+        w = synth.threshold_decode(L=65536)
+        lam = min(1.0, bench.THRESH_DECODE_A / w.k.shape[2])
+    else:
+        w, lam = synth.gqa_decode(), 0.4
+    skipped = _threshold_decode_case(bsa, w, lam, bench.THRESH_DECODE_SPLIT, f"threshold decode 64K lam={lam:g}")
+    if which == "aggressive":
+        assert skipped > 0.3
 
 
 # --------------------------------------------------------------- threshold ---
