@@ -282,8 +282,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
   float ov[BATCH];
   issue(0, mlv, ov);
   live = in_range && !(a.row_mask && rbyte == 0);
-  const int64_t nunits = a.cnt ? (int64_t)a.cnt[li] * a.unit_num : (int64_t)a.items * a.unit_den;
-  const int nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
+  int nvalid;
+  if (a.per_item_from_count) {
+    const int c_list = a.cnt[li];
+    const int per = max(1, (c_list + a.items - 1) / a.items);
+    nvalid = (c_list + per - 1) / per;
+  } else {
+    const int64_t nunits = a.cnt ? (int64_t)a.cnt[li] * a.unit_num : (int64_t)a.items * a.unit_den;
+    nvalid = (int)min((int64_t)a.items, (nunits + a.unit_den - 1) / a.unit_den);
+  }
   float M, L, acc;
   merge(0, nvalid, mlv, ov, M, L, acc);
   const int h = g * G + hl;

@@ -82,9 +82,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   const int n_list = a.cnt[li];
   int e0 = 0, e1 = n_list;
   if (SPLIT) {
-    e0 = item * kSplitBlocks;
+    // the list's entries are shared out over the launched items: a short list (a
+    // few active rows' union) gets one entry per workgroup, a full one kSplitBlocks
+    const int per = max(1, (n_list + a.items - 1) / a.items);
+    e0 = item * per;
     if (e0 >= n_list) return;
-    e1 = min(n_list, e0 + kSplitBlocks);
+    e1 = min(n_list, e0 + per);
   }
 
   // query vectors of this workgroup
@@ -676,7 +679,7 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
     CombArgs c;
     c.part_o = part_o; c.part_ml = part_ml; c.cnt = cnt; c.items = pl.items;
     if (pl.kind == 0) { c.unit_num = p.kv_block; c.unit_den = pl.tok_per_item; }
-    else { c.unit_num = 1; c.unit_den = kSplitBlocks; }
+    else { c.unit_num = 1; c.unit_den = 1; c.per_item_from_count = 1; }
     c.qvc = 256 / pl.D;                          // one thread per (query vector, dim)
     c.Hkv = pl.Hkv; c.G = pl.G; c.NQB = pl.NQB; c.q_block = p.q_block; c.Lq = pl.Lq; c.D = pl.D; c.QV = pl.qv;
     c.row_mask = row_mask; c.o = o.data; c.osb = o.stride_b; c.osh = o.stride_h; c.osl = o.stride_l; c.lse = lse;

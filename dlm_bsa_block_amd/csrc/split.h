@@ -46,6 +46,7 @@ struct CombArgs {
   int win = 0;                    // sliding window: its items follow the list's (decode only)
   int q_pos0 = 0, L = 0;
   const float* gates = nullptr;   // [B][Hq][Lq][2] branch gates, or null for 1 and 1
+  int per_item_from_count = 0;    // 1: each slice took max(1, ceil(cnt / items)) list entries
 };
 
 void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s);
