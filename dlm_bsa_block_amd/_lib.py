@@ -6,7 +6,8 @@ import os
 from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint8, c_void_p, c_char_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libbsa.so")
+# BSA_LIBRARY names another build of the same library (the sanitizer build of sanitize_check.py)
+LIB_PATH = os.environ.get("BSA_LIBRARY") or os.path.join(HERE, "libbsa.so")
 
 BSA_OK, BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_CAPACITY, BSA_ERR_WORKSPACE, BSA_ERR_HIP = range(6)
 BSA_BF16, BSA_F32 = 0, 1
