@@ -251,7 +251,7 @@ def bsa_decode_step(q, k, v, k_mean, p: BsaSelectParams, refresh_block: int = -1
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev)
     need = bsa_decode_step_workspace_bytes(q, k, p)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)   # zero before its first use
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)   # no initial contents needed
     qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
     check(lib().bsa_decode_step(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), k_mean.data_ptr(),
                                 _ptr(k_energy), refresh_block, ctypes.byref(p), idx.data_ptr(), cnt.data_ptr(),

@@ -15,15 +15,16 @@
 //                       written to workspace Z[b][g][row][head-in-group][band][block]
 //   pick_kernel         one workgroup per (selection row, KV group, batch):
 //                       per-head (per-band) softmax over the candidates, group
-//                       score, radix select of the k' best non-forced blocks
-//                       (ties -> lower index) into an LDS bitmap.  With one
-//                       selection row per query block the bitmap is compacted
-//                       straight into the sorted index list; otherwise every
-//                       row writes its bitmap to the workspace
+//                       score; then one wave selects the k' best non-forced
+//                       blocks (ties -> lower index; wave_select.h: a bitonic
+//                       sort of the lanes' maxima bounds the k'-th key, the
+//                       keys above the bound are ranked exactly).  With one
+//                       selection row per query block the picks go straight
+//                       into the sorted index list; otherwise every row
+//                       writes its bitmap to the workspace
 //   union_kernel        per (query block, KV group, batch): OR of the rows'
 //                       bitmaps and an ordered compaction into the list
-// LDS integer atomics (histogram counts, bitmap ORs) are used inside a
-// workgroup; they are order-independent, so the lists are deterministic.
+// No atomics are used: every list is a function of the inputs alone.
 #include <algorithm>
 
 #include "common.h"

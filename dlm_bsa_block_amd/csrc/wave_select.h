@@ -211,7 +211,9 @@ namespace bsa {
 // one of rank k' - 1 is T.  Block-order prefix counts of the keys above and
 // equal to T then place every pick directly at its position in the ascending
 // list.  Four barriers; no thread does more than KPT + the gathered count
-// compares.
+// compares.  The gathering appends with one LDS atomicAdd per wave; the order
+// in which the waves append does not matter, since the ranks come from the
+// unique (key, index) pairs.
 struct __attribute__((aligned(16))) BlockTopkSmem {
   uint64_t cand[256];                 // first: read 16 bytes at a time
   uint32_t offer[4];
