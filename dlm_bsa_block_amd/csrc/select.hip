@@ -368,12 +368,13 @@ __global__ __launch_bounds__(64) void union_kernel(PickArgs a) {
   const uint32_t* first = a.row_bits + (((int64_t)b * a.Hkv + g) * a.Rtot + (int64_t)qb * a.q_block) * kPickMaxWords;
   for (int i = lane; i < NBW; i += 64) {
     uint32_t u = 0u;
-    for (int r0 = 0; r0 < rows; r0 += 16) {
-      uint32_t v[16];
+    for (int r0 = 0; r0 < rows; r0 += 32) {
+      // rows past the block's end re-read its last row (OR is idempotent): no load under a branch
+      uint32_t v[32];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = r0 + k < rows ? first[(int64_t)(r0 + k) * kPickMaxWords + i] : 0u;
+      for (int k = 0; k < 32; ++k) v[k] = first[(int64_t)min(r0 + k, rows - 1) * kPickMaxWords + i];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) u |= v[k];
+      for (int k = 0; k < 32; ++k) u |= v[k];
     }
     bits[i] = u;
   }
