@@ -311,11 +311,13 @@ def bench_dlm(torch, bsa, synth, reps):
 def bench_dlm_steps(torch, bsa, synth, reps):
     """Denoising steps of one 32-token block over the 32K prefix: step 0 dense
     over the prefix for every row (builds the prefix cache), later steps with
-    locality pruning (4 rows change per step): active rows, selection for the
-    active rows, sparse prefix attention for them, attention over the block's
-    own keys for every row, and the merge.  Each step is also run with every
-    row recomputed (selection union over all rows), the form without pruning.
-    Steps are timed as HIP graph replays (GPU time, no host launch gaps)."""
+    locality pruning (4 rows change per step) through bsa_denoise_step: active
+    rows, selection for the active rows, sparse prefix attention for them,
+    attention over the block's own keys for every row, and the merge, in three
+    launches.  Each step is also run with every row recomputed (theta below
+    every change: the union over all rows), the form without pruning, and from
+    the separate entry points (seven launches).  Steps are timed as HIP graph
+    replays (GPU time, no host launch gaps)."""
     log("dlm steps: generating the multi-step denoising workload")
     w = synth.dlm_denoise_steps()
     p = w.params
@@ -364,12 +366,21 @@ def bench_dlm_steps(torch, bsa, synth, reps):
                                      workspace=ws_att)
         block_and_merge(qd, kbd, vbd)
 
+    ws_den = torch.empty(bsa.bsa_denoise_step_workspace_bytes(steps[0][0], kd, sp), dtype=torch.uint8,
+                         device="cuda")
+
     def sparse_step(s, pruned=True):
+        # the fused step; every row is active when theta lies below every row's change
+        qd, kbd, vbd = steps[s]
+        bsa.bsa_denoise_step(qd, steps[s - 1][0], p["theta_act"] if pruned else -1.0, kmean, kd, vd, kbd, vbd, sp,
+                             cache_o, cache_l, row_mask=mask, idx=idx, cnt=cnt, o=out, lse=lse, workspace=ws_den)
+
+    def sparse_step_pieces(s):
+        # the same step from the separate entry points
         qd, kbd, vbd = steps[s]
         bsa.bsa_active_rows(qd, steps[s - 1][0], p["theta_act"], want_mse=False, mask=mask)
-        rm = mask if pruned else None
-        bsa.bsa_select_blocks(qd, kmean, sp, row_mask=rm, workspace=ws_sel, idx=idx, cnt=cnt)
-        bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap, row_mask=rm, o=cache_o,
+        bsa.bsa_select_blocks(qd, kmean, sp, row_mask=mask, workspace=ws_sel, idx=idx, cnt=cnt)
+        bsa.bsa_sparse_attention_fwd(qd, kd, vd, idx, cnt, ap, row_mask=mask, o=cache_o,
                                      lse=cache_l, workspace=ws_att)
         block_and_merge(qd, kbd, vbd)
 
@@ -382,18 +393,24 @@ def bench_dlm_steps(torch, bsa, synth, reps):
         u_all = cnt.float().mean().item()
         cache_o.copy_(saved[0])
         cache_l.copy_(saved[1])
+        t_pc = time_graph(torch, lambda: sparse_step_pieces(s), reps)
+        cache_o.copy_(saved[0])
+        cache_l.copy_(saved[1])
         t = time_graph(torch, lambda: sparse_step(s), reps)
         per_step.append(dict(step=s, active_rows=int(mask.sum().item()), list_blocks_mean=round(cnt.float().mean().item(), 1),
-                             us=round(t, 2), all_rows_list_blocks_mean=round(u_all, 1), all_rows_us=round(t_all, 2)))
+                             us=round(t, 2), pieces_us=round(t_pc, 2), all_rows_list_blocks_mean=round(u_all, 1),
+                             all_rows_us=round(t_all, 2)))
     qd, kbd, vbd = steps[-1]
     t_fused = time_graph(torch, lambda: block_and_merge(qd, kbd, vbd), reps)
     t_pieces = time_graph(torch, lambda: block_and_merge_pieces(qd, kbd, vbd), reps)
     sp_steps = per_step[1:]
     mean_us = sum(x["us"] for x in sp_steps) / len(sp_steps)
     mean_all = sum(x["all_rows_us"] for x in sp_steps) / len(sp_steps)
+    mean_pc = sum(x["pieces_us"] for x in sp_steps) / len(sp_steps)
     dens = sum(x["list_blocks_mean"] for x in sp_steps) / len(sp_steps) / NB
     dens_all = sum(x["all_rows_list_blocks_mean"] for x in sp_steps) / len(sp_steps) / NB
     return dict(steps=len(steps), dense_first_step_us=round(t_dense, 2), pruned_step_us_mean=round(mean_us, 2),
+                pruned_over_dense=round(mean_us / t_dense, 3), pruned_step_pieces_us_mean=round(mean_pc, 2),
                 all_rows_step_us_mean=round(mean_all, 2), kv_density_pruned=round(dens, 4),
                 kv_density_all_rows=round(dens_all, 4), active_fraction_per_step=[x["active_rows"] / R for x in per_step],
                 block_attention_merge_us=round(t_fused, 2), block_attention_then_merge_us=round(t_pieces, 2),

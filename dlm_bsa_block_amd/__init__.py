@@ -260,6 +260,46 @@ def bsa_decode_step(q, k, v, k_mean, p: BsaSelectParams, refresh_block: int = -1
     return idx, cnt, o, lse
 
 
+def bsa_denoise_step_workspace_bytes(q, k, p: BsaSelectParams) -> int:
+    return int(lib().bsa_denoise_step_workspace_bytes(ctypes.byref(tensor_desc(q)), ctypes.byref(tensor_desc(k)),
+                                                      ctypes.byref(p)))
+
+
+def bsa_denoise_step(q, q_prev, theta: float, k_mean, k, v, kb, vb, p: BsaSelectParams, cache_o, cache_lse,
+                     row_mask=None, mse=None, want_mse=False, idx=None, cnt=None, o=None, lse=None, workspace=None):
+    """One locality-pruned denoising step: active rows, their block selection, prefix attention of the active
+    rows into (cache_o, cache_lse) and the block attention merged with the prefix state for every row.
+    Returns (row_mask [B,R], mse or None, idx [B,Hkv,1,cap], cnt [B,Hkv,1], o, lse [B,Hq,R])."""
+    B, Hq, R, D = q.shape
+    Hkv, NB = k_mean.shape[1], k_mean.shape[2]
+    if p.cap <= 0:
+        p.cap = list_capacity(NB, R, p)
+    dev = q.device
+    if row_mask is None:
+        row_mask = torch.empty((B, R), dtype=torch.uint8, device=dev)
+    if mse is None and want_mse:
+        mse = torch.empty((B, R), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((B, Hkv, 1, p.cap), dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv, 1), dtype=torch.int32, device=dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, R), dtype=torch.float32, device=dev)
+    need = bsa_denoise_step_workspace_bytes(q, k, p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)   # no initial contents needed
+    qd, pd, kd, vd = tensor_desc(q), tensor_desc(q_prev), tensor_desc(k), tensor_desc(v)
+    kbd, vbd, cd, od = tensor_desc(kb), tensor_desc(vb), tensor_desc(cache_o), tensor_desc(o)
+    check(lib().bsa_denoise_step(ctypes.byref(qd), ctypes.byref(pd), theta, k_mean.data_ptr(), ctypes.byref(kd),
+                                 ctypes.byref(vd), ctypes.byref(kbd), ctypes.byref(vbd), ctypes.byref(p),
+                                 ctypes.byref(cd), cache_lse.data_ptr(), row_mask.data_ptr(), _ptr(mse),
+                                 idx.data_ptr(), cnt.data_ptr(), ctypes.byref(od), lse.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), _stream()), "bsa_denoise_step")
+    return row_mask, mse, idx, cnt, o, lse
+
+
 def bsa_window_decode_workspace_bytes(q, k, p: BsaAttnParams, window: int) -> int:
     qd, kd = tensor_desc(q), tensor_desc(k)
     return lib().bsa_window_decode_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(p), window)

@@ -69,6 +69,10 @@ _SIGS = {
     "bsa_decode_step_workspace_bytes": (c_size_t, [_T, _T, POINTER(BsaSelectParams)]),
     "bsa_decode_step": (c_int32, [_T, _T, _T, c_void_p, c_void_p, c_int32, POINTER(BsaSelectParams), c_void_p,
                                   c_void_p, _T, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "bsa_denoise_step_workspace_bytes": (c_size_t, [_T, _T, POINTER(BsaSelectParams)]),
+    "bsa_denoise_step": (c_int32, [_T, _T, c_float, c_void_p, _T, _T, _T, _T, POINTER(BsaSelectParams), _T,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, _T, c_void_p, c_void_p,
+                                   c_size_t, c_void_p]),
     "bsa_noalloc_scratch_bytes": (c_size_t, []),
     "bsa_sparse_attention_fwd_noalloc": (c_int32, [_T, _T, _T, c_void_p, c_void_p, POINTER(BsaAttnParams), c_void_p,
                                                    _T, c_void_p, c_void_p]),

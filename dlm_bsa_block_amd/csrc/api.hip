@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "internal.h"
+#include "pick.h"
 
 namespace bsa {
 
@@ -611,6 +612,113 @@ bsa_status bsa_block_attention_merge(const bsa_tensor* q, const bsa_tensor* kb, 
   a.scale = scale;
   launch_block_attn_merge(a, o->dtype, static_cast<hipStream_t>(stream));
   return check_launch("block attention merge");
+}
+
+// ----------------------------------------------------------- denoise step ---
+static bsa_status validate_denoise_step(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                        const bsa_select_params* p, SelectPlan& sp, bsa_attn_params& ap,
+                                        AttnPlan& pl) {
+  if (!p) return fail(BSA_ERR_INVALID, "params: null");
+  bsa_status st = check_tensor(q, "q", false);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(k, "k", false)) != BSA_OK) return st;
+  if ((st = check_tensor(v, "v", false)) != BSA_OK) return st;
+  if (!same_shape(k, v)) return fail(BSA_ERR_INVALID, "k and v differ in shape or dtype");
+  if (q->dtype != BSA_BF16 || k->dtype != BSA_BF16 || q->D != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "the denoising step takes bf16 with D = 128");
+  if (q->B != k->B || q->D != k->D || q->H % k->H) return fail(BSA_ERR_INVALID, "q/k shapes are incompatible");
+  if (q->L > 32) return fail(BSA_ERR_UNSUPPORTED, "the denoising block has %d rows (at most 32)", (int)q->L);
+  if (p->q_block != q->L || p->pooled_q || p->dual_band)
+    return fail(BSA_ERR_UNSUPPORTED, "the denoising step takes one query block of raw rows (q_block = %d) and one band",
+                (int)q->L);
+  if (p->kv_block != 64 && p->kv_block != 128) return fail(BSA_ERR_UNSUPPORTED, "kv_block must be 64 or 128");
+  if ((int64_t)q->L * (q->H / k->H) > 128)
+    return fail(BSA_ERR_UNSUPPORTED, "rows x group size %d > 128", (int)(q->L * (q->H / k->H)));
+  const int64_t NB = ceil_div(k->L, p->kv_block);
+  if (NB > 4096) return fail(BSA_ERR_UNSUPPORTED, "%lld KV blocks > 4096", (long long)NB);
+  if ((st = validate_select(q, k->H, (int32_t)NB, p, sp)) != BSA_OK) return st;
+  ap.scale = p->scale;
+  ap.kv_block = p->kv_block;
+  ap.q_block = p->q_block;
+  ap.q_pos0 = p->q_pos0;
+  ap.causal = p->causal;
+  ap.cap = p->cap;
+  if ((st = validate_attention(q, k, v, &ap, pl)) != BSA_OK) return st;
+  if (pl.kind != 2) return fail(BSA_ERR_UNSUPPORTED, "the denoising block does not fit the split gather");
+  return BSA_OK;
+}
+
+size_t bsa_denoise_step_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, const bsa_select_params* p) {
+  SelectPlan sp;
+  bsa_attn_params ap;
+  AttnPlan pl;
+  if (!k || validate_denoise_step(q, k, k, p, sp, ap, pl) != BSA_OK) return 0;
+  return sp.z_bytes + pl.part_bytes;
+}
+
+bsa_status bsa_denoise_step(const bsa_tensor* q, const bsa_tensor* q_prev, float theta, const float* k_mean,
+                            const bsa_tensor* k, const bsa_tensor* v, const bsa_tensor* kb, const bsa_tensor* vb,
+                            const bsa_select_params* p, const bsa_tensor* cache_o, float* cache_lse,
+                            uint8_t* row_mask, float* mse, int32_t* idx, int32_t* cnt, const bsa_tensor* o, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  SelectPlan sp;
+  bsa_attn_params ap;
+  AttnPlan pl;
+  bsa_status st = validate_denoise_step(q, k, v, p, sp, ap, pl);
+  if (st != BSA_OK) return st;
+  if ((st = check_tensor(q_prev, "q_prev", false)) != BSA_OK) return st;
+  if (!same_shape(q, q_prev)) return fail(BSA_ERR_INVALID, "q and q_prev differ in shape or dtype");
+  if (!std::isfinite(theta)) return fail(BSA_ERR_INVALID, "theta must be finite");
+  if ((st = check_tensor(kb, "kb", false)) != BSA_OK) return st;
+  if ((st = check_tensor(vb, "vb", false)) != BSA_OK) return st;
+  if (!same_shape(kb, vb) || kb->dtype != BSA_BF16 || kb->B != q->B || kb->H != k->H || kb->L != q->L ||
+      kb->D != q->D)
+    return fail(BSA_ERR_INVALID, "kb and vb must be bf16 [B, Hkv, R, D]");
+  if ((st = check_tensor(cache_o, "cache_o", false)) != BSA_OK) return st;
+  if (!same_dims(q, cache_o) || cache_o->dtype != BSA_F32)
+    return fail(BSA_ERR_INVALID, "cache_o must be f32 with q's shape");
+  if ((st = check_tensor(o, "o", false)) != BSA_OK) return st;
+  if (!same_dims(q, o)) return fail(BSA_ERR_INVALID, "o must have q's shape");
+  if (!k_mean || !cache_lse || !row_mask || !idx || !cnt || !lse)
+    return fail(BSA_ERR_INVALID, "k_mean, cache_lse, row_mask, idx, cnt and lse are required");
+  if (!aligned16(k_mean)) return fail(BSA_ERR_INVALID, "k_mean not 16-byte aligned");
+  const size_t need = sp.z_bytes + pl.part_bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // 1: the block logits of every row, with the active-row test of every row in the same launch
+  launch_select_logits(*q, k_mean, *p, sp, workspace, s, active_rows_args(*q, *q_prev, theta, row_mask, mse));
+  // 2: per (slice, KV group): the active rows' picks, their union and the slice's split partials
+  void* part = static_cast<uint8_t*>(workspace) + sp.z_bytes;
+  const PickArgs pk = make_pick_args(*p, sp, workspace, row_mask, idx, cnt, nullptr);
+  launch_denoise_gather(*q, *k, *v, ap, pl, pk, row_mask, idx, cnt, part, s);
+  // 3: per (rows, head): combine of the active rows into the cache, block attention and merge
+  DenMergeArgs dm;
+  BlockMergeArgs& a = dm.m;
+  a.q = static_cast<const uint8_t*>(q->data);
+  a.kb = static_cast<const uint8_t*>(kb->data);
+  a.vb = static_cast<const uint8_t*>(vb->data);
+  a.o_pre = cache_o->data; a.lse_pre = cache_lse; a.o = o->data; a.lse = lse;
+  a.qsb = q->stride_b; a.qsh = q->stride_h; a.qsl = q->stride_l;
+  a.ksb = kb->stride_b; a.ksh = kb->stride_h; a.ksl = kb->stride_l;
+  a.vsb = vb->stride_b; a.vsh = vb->stride_h; a.vsl = vb->stride_l;
+  a.psb = cache_o->stride_b; a.psh = cache_o->stride_h; a.psl = cache_o->stride_l;
+  a.osb = o->stride_b; a.osh = o->stride_h; a.osl = o->stride_l;
+  a.B = (int)q->B; a.Hq = (int)q->H; a.G = (int)(q->H / k->H); a.R = (int)q->L;
+  a.pre_f32 = 1;
+  a.scale = p->scale;
+  const size_t n = (size_t)pl.B * pl.Hkv * pl.NQB * pl.items * pl.qv;
+  dm.part_o = static_cast<const float*>(part);
+  dm.part_ml = reinterpret_cast<const float*>(static_cast<uint8_t*>(part) + align256(n * pl.D * 4));
+  dm.cnt = cnt;
+  dm.row_mask = row_mask;
+  dm.cache_o = static_cast<float*>(cache_o->data);
+  dm.cache_lse = cache_lse;
+  dm.Hkv = (int)k->H;
+  dm.items = pl.items;
+  launch_den_merge(dm, o->dtype, s);
+  return check_launch("denoising step");
 }
 
 size_t bsa_threshold_decode_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, int32_t kv_split) {

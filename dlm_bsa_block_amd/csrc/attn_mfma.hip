@@ -8,7 +8,10 @@
 //   * the denoising step: one workgroup per (slice of the list, query block,
 //     KV group) holding the block's active (row, head) pairs as up to 128
 //     query vectors, writing split partials for the combine (LoSA sec. 2:
-//     only active rows recompute, over the block's union).
+//     only active rows recompute, over the block's union).  In the fused
+//     denoising step the workgroup first picks the blocks of every active
+//     row itself (one wavefront per row, from the logits) and takes the
+//     union, so no launch sits between the logits and the attention.
 // K/V tiles are copied straight from global memory into LDS (double-buffered)
 // and shared by the waves of a workgroup; each wave owns 32 query vectors.
 // Online softmax in fp32 with exp2; the running max and sum are lane-local
@@ -17,6 +20,7 @@
 
 #include "internal.h"
 #include "mfma_tile.h"
+#include "pick.h"
 #include "split.h"
 
 namespace bsa {
@@ -39,6 +43,7 @@ struct GatherArgs {
   float* part_ml;
   int items;
   int wpg;                        // streaming kernel: workgroups per (batch, KV group)
+  PickArgs pk;                    // in-kernel pick (split mode, one query block): Z, row plan inputs
 };
 
 // One workgroup = NW waves of 32 query vectors.  Direct mode: NW / 4 heads of
@@ -48,13 +53,25 @@ struct GatherArgs {
 // tile u is computed, so one barrier per tile suffices.  A list entry (a KV
 // block of SUB * KVB keys) is walked as SUB tiles of KVB keys: with 64-key
 // tiles two workgroups fit on a CU and their waves overlap freely.
-template <int KVB, int NW, bool SPLIT, int SUB = 1>
+// PU > 0 (split mode, one query block): the list is not read but picked here
+// -- wavefront w picks active rows w, w + NW, ... (wave_pick_row<PU>, the
+// keys staged in the tile buffers, which are free until the walk starts), the
+// flags are OR-ed over the waves and compacted; every workgroup of the group
+// computes the same list, keeps its own slice of it in LDS, and workgroup 0
+// writes the list and its length out.
+template <int KVB, int NW, bool SPLIT, int SUB = 1, int PU = 0>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gather_mfma_kernel(GatherArgs a) {
   constexpr int TILE = KVB * kRow;                 // elements of one K or V tile
   constexpr int HPW = SPLIT ? 1 : NW / 4;          // heads per workgroup
+  constexpr bool PICK = PU > 0;
+  static_assert(!PICK || (SPLIT && 256 * PU * NW * 4 <= 4 * TILE * 2), "pick keys fit in the tile buffers");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE];   // K0 V0 K1 V1
   __shared__ int qv_row[128], qv_head[128], qv_full[128];
   __shared__ int n_qv_sh;
+  __shared__ uint64_t pflags_sh[PICK ? NW : 1][64];
+  __shared__ __attribute__((aligned(16))) uint32_t pcand_sh[PICK ? NW : 1][64];
+  __shared__ int slice_sh[PICK ? kSplitBlocks : 1];
+  __shared__ int n_list_sh;
 
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -79,19 +96,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     g = bgi - b * a.Hkv;
   }
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
-  const int n_list = a.cnt[li];
-  int e0 = 0, e1 = n_list;
-  if (SPLIT) {
-    // the list's entries are shared out over the launched items: a short list (a
-    // few active rows' union) gets one entry per workgroup, a full one kSplitBlocks
-    const int per = max(1, (n_list + a.items - 1) / a.items);
-    e0 = item * per;
-    if (e0 >= n_list) return;
-    e1 = min(n_list, e0 + per);
-  }
-
   // query vectors of this workgroup
-  if (SPLIT) {
+  auto stage_qv = [&]() __attribute__((always_inline)) {
     if (w == 0) {
       const int row = qb * a.q_block + lane;
       const bool act = lane < a.q_block && row < a.Lq && (!a.row_mask || a.row_mask[(int64_t)b * a.Lq + row]);
@@ -107,6 +113,55 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
       if (lane == 0) n_qv_sh = __popcll(m) * a.G;
     }
     __syncthreads();
+  };
+  int n_list, e0 = 0, e1;
+  if constexpr (PICK) {
+    stage_qv();
+    const int n_act = n_qv_sh / a.G;
+    uint64_t fl = 0;
+    uint32_t* keys = reinterpret_cast<uint32_t*>(lds) + w * 256 * PU;
+    for (int k = w; k < n_act; k += NW) fl |= wave_pick_row<PU>(a.pk, b, g, qv_row[k * a.G], keys, pcand_sh[w]);
+    pflags_sh[w][lane] = fl;
+    __syncthreads();
+    if (w == 0) {
+      uint64_t f = pflags_sh[0][lane];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) f |= pflags_sh[ww][lane];
+      // ascending compaction (bit e of lane l = block 4 PU l + e); this workgroup keeps its slice
+      const uint32_t c = (uint32_t)__popcll(f);
+      const uint32_t incl = wave_incl_scan_dpp(c);
+      const int n = (int)lane_read(incl, 63);
+      const int per = max(1, (n + a.items - 1) / a.items);
+      const int s0 = item * per, s1 = min(n, s0 + per);
+      int pos = (int)(incl - c);
+      int32_t* out = a.pk.idx + li * a.cap;            // the pick writes the list (workgroup 0)
+      while (f) {
+        const int e = __ffsll((unsigned long long)f) - 1;
+        f &= f - 1;
+        const int j = 4 * PU * lane + e;
+        if (pos >= s0 && pos < s1 && pos - s0 < kSplitBlocks) slice_sh[pos - s0] = j;   // per <= kSplitBlocks
+        if (item == 0) out[pos] = j;
+        ++pos;
+      }
+      if (lane == 0) {
+        n_list_sh = n;
+        if (item == 0) a.pk.cnt[li] = n;
+      }
+    }
+    __syncthreads();
+    n_list = n_list_sh;
+  } else {
+    n_list = a.cnt[li];
+  }
+  e1 = n_list;
+  if (SPLIT) {
+    // the list's entries are shared out over the launched items: a short list (a
+    // few active rows' union) gets one entry per workgroup, a full one kSplitBlocks
+    const int per = max(1, (n_list + a.items - 1) / a.items);
+    e0 = item * per;
+    if (e0 >= n_list) return;
+    e1 = min(n_list, e0 + per);
+    if constexpr (!PICK) stage_qv();
   }
   const int n_qv = SPLIT ? n_qv_sh : 0;
   const int wr = w & 3;                            // wave within its head
@@ -146,7 +201,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   // rows of tile u (of list entry e0 + u / SUB) inside the KV sequence (0 for
   // an index outside it, or a part beyond the end: nothing is read)
   auto entry_rows = [&](int u, int& key0) {
-    const int j = list[e0 + u / SUB];
+    const int j = PICK ? slice_sh[u / SUB] : list[e0 + u / SUB];
     const int blk0 = j * (KVB * SUB);
     key0 = blk0 + (u % SUB) * KVB;
     return (j < 0 || blk0 >= a.L || key0 >= a.L) ? 0 : min(KVB, a.L - key0);
@@ -557,6 +612,50 @@ void launch_gather(const GatherArgs& a, int kv_block, bool split, hipStream_t s)
     if (kv_block == 128) hipLaunchKernelGGL((gather_mfma_kernel<64, 4, false, 2>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((gather_mfma_kernel<64, 4, false>), grid, dim3(256), 0, s, a);
   }
+}
+
+// The denoising step's gather with the picks inside (split mode, one query
+// block): pick width U (candidates per lane = 4 U) from the number of blocks.
+void launch_gather_pick(const GatherArgs& a, int kv_block, hipStream_t s) {
+  dim3 grid(a.items, 1, a.B * a.Hkv);
+  const int U = (int)ceil_div(a.pk.NBp, kPickThreads);
+#define BSA_GP(KVB, UU) hipLaunchKernelGGL((gather_mfma_kernel<KVB, 4, true, 1, UU>), grid, dim3(256), 0, s, a)
+#define BSA_GP_U(KVB)                 \
+  do {                                \
+    if (U <= 1) BSA_GP(KVB, 1);       \
+    else if (U <= 2) BSA_GP(KVB, 2);  \
+    else if (U <= 4) BSA_GP(KVB, 4);  \
+    else if (U <= 8) BSA_GP(KVB, 8);  \
+    else BSA_GP(KVB, 16);             \
+  } while (0)
+  if (kv_block == 128) BSA_GP_U(128);
+  else BSA_GP_U(64);
+#undef BSA_GP_U
+#undef BSA_GP
+}
+
+void launch_denoise_gather(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, const bsa_attn_params& p,
+                           const AttnPlan& pl, const PickArgs& pk, const uint8_t* row_mask, int32_t* idx,
+                           int32_t* cnt, void* ws, hipStream_t s) {
+  const size_t n = (size_t)pl.B * pl.Hkv * pl.NQB * pl.items * pl.qv;
+  GatherArgs a;
+  a.q = static_cast<const uint16_t*>(q.data);
+  a.k = static_cast<const uint16_t*>(k.data);
+  a.v = static_cast<const uint16_t*>(v.data);
+  a.qsb = q.stride_b; a.qsh = q.stride_h; a.qsl = q.stride_l;
+  a.ksb = k.stride_b; a.ksh = k.stride_h; a.ksl = k.stride_l;
+  a.vsb = v.stride_b; a.vsh = v.stride_h; a.vsl = v.stride_l;
+  a.idx = idx; a.cnt = cnt; a.B = pl.B; a.cap = p.cap; a.NQB = pl.NQB; a.Hkv = pl.Hkv; a.G = pl.G;
+  a.L = pl.L; a.Lq = pl.Lq; a.q_block = p.q_block; a.q_pos0 = p.q_pos0; a.causal = p.causal;
+  a.c2 = p.scale * kLog2e;
+  a.row_mask = row_mask;
+  a.o = nullptr; a.o_f32 = 0; a.osb = a.osh = a.osl = 0; a.lse = nullptr;
+  a.part_o = static_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(n * pl.D * 4));
+  a.items = pl.items;
+  a.wpg = 0;
+  a.pk = pk;
+  launch_gather_pick(a, p.kv_block, s);
 }
 
 // ------------------------------------------------------------------- host ---

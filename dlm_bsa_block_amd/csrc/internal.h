@@ -48,6 +48,24 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
 void launch_active_rows(const bsa_tensor& a, const bsa_tensor& b, float theta, uint8_t* mask, float* mse,
                         hipStream_t s);
 
+// The active-row test of a denoising block (row mean of (q_cur - q_prev)^2 over heads and dims
+// against theta); also run as extra workgroups of the denoising step's logits launch.
+struct ActiveRowsArgs {
+  const uint8_t* a = nullptr;        // q_cur [B, H, R, D]; null: no row jobs in the launch
+  const uint8_t* c = nullptr;        // q_prev, same shape and dtype
+  int64_t asb = 0, ash = 0, asl = 0, csb = 0, csh = 0, csl = 0;
+  int H = 0, R = 0, D = 0;
+  float theta = 0.f;
+  uint8_t* mask = nullptr;           // [B, R]
+  float* mse = nullptr;              // [B, R] or null
+  int z0 = 0, slices = 0;            // in a logits launch: first z index of the row jobs, z-slices per batch
+};
+ActiveRowsArgs active_rows_args(const bsa_tensor& x, const bsa_tensor& y, float theta, uint8_t* mask, float* mse);
+// The block logits of bsa_select_blocks alone (one band, no refresh) into the workspace's logit
+// region, with the active-row jobs `act` (if act.a is set) in the same launch.
+void launch_select_logits(const bsa_tensor& q, const float* k_mean, const bsa_select_params& p,
+                          const SelectPlan& pl, void* ws, hipStream_t s, const ActiveRowsArgs& act);
+
 // Merge of two attention states (o_x [B, H, L, D] any of bf16/f32, lse_x [B, H, L] natural log).
 struct MergeArgs {
   const void* o_a;
@@ -76,6 +94,21 @@ struct BlockMergeArgs {
   float scale;
 };
 void launch_block_attn_merge(const BlockMergeArgs& a, int dout, hipStream_t s);
+
+// The fused denoising step's last launch: combine of the split partials of the active rows into the
+// prefix cache (f32), then the block attention and merge of every row.
+constexpr int kDenRows = 4;          // rows per workgroup
+struct DenMergeArgs {
+  BlockMergeArgs m;                  // o_pre = the prefix cache (f32, pre_f32 = 1), lse_pre = its lse
+  const float* part_o;               // [B][Hkv][items][R * G][D] split partials (query block 0)
+  const float* part_ml;              // [B][Hkv][items][R * G][2]
+  const int32_t* cnt;                // [B][Hkv] list lengths
+  const uint8_t* row_mask;           // [B][R]
+  float* cache_o;                    // the prefix cache again, written for active rows
+  float* cache_lse;
+  int Hkv, items;
+};
+void launch_den_merge(const DenMergeArgs& a, int dout, hipStream_t s);
 
 struct AttnPlan {
   int kind;                 // 0 = VALU decode split, 1 = MFMA gather (direct), 2 = MFMA gather split

@@ -86,32 +86,28 @@ namespace bsa {
 // and V copied straight into LDS, the tile's max as the softmax reference).
 // The copies, the query fragments and the row's cached prefix (O, lse) are
 // all requested before the first product.
-template <int DO, bool PRE_F32>
-__global__ __launch_bounds__(64) void block_attn_merge_kernel(BlockMergeArgs a) {
+// The requests of one wave's block tile: the K and V tiles into LDS, the
+// query fragments of lane row r32 (rows past R load row R - 1 and are zeroed)
+// and that row's cached prefix state (O in the O^T layout: dims
+// 32 dt + 8 i4 + 4 hi .. + 3, and its lse).  Returns the lane's row.
+template <bool PRE_F32>
+__device__ __forceinline__ int block_tile_requests(const BlockMergeArgs& a, int b, int h, uint32_t l0, bf16x8 (&qf)[8],
+                                                   float (&op)[4][4][4], float& la) {
   constexpr int KVB = 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * KVB * kRow];   // K tile, then V tile
-  const int bh = blockIdx.x;
-  const int b = bh / a.Hq, h = bh - b * a.Hq, g = h / a.G;
-  const int lane = threadIdx.x, r32 = lane & 31, hi = lane >> 5;
+  const int g = h / a.G, lane = threadIdx.x & 63, r32 = lane & 31, hi = lane >> 5;
   const int R = a.R;
-  const uint32_t l0 = lds_addr(lds);
   // rows past R repeat row R - 1: their keys are masked and their V rows weighted by zero
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.kb);
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.vb);
   issue_tile<KVB, 1>(kb + (int64_t)b * a.ksb + (int64_t)g * a.ksh, a.ksl, R, l0);
   issue_tile<KVB, 1>(vb + (int64_t)b * a.vsb + (int64_t)g * a.vsh, a.vsl, R, l0 + KVB * kRow * 2);
-  // this lane's query row (rows past R load row R - 1 and are zeroed)
-  const bool valid = r32 < R;
   const int row = min(r32, R - 1);
-  bf16x8 qf[8];
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)b * a.qsb + (int64_t)h * a.qsh +
                            (int64_t)row * a.qsl;
 #pragma unroll
     for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st + 8 * hi);
   }
-  // the row's cached prefix state, in the O^T layout: dims 32 dt + 8 i4 + 4 hi .. + 3
-  float op[4][4][4];
   {
     const int64_t io = (int64_t)b * a.psb + (int64_t)h * a.psh + (int64_t)row * a.psl;
 #pragma unroll
@@ -132,30 +128,43 @@ __global__ __launch_bounds__(64) void block_attn_merge_kernel(BlockMergeArgs a) 
         }
       }
   }
-  const float la = a.lse_pre[((int64_t)b * a.Hq + h) * R + row];
-  if (!valid) {
+  la = a.lse_pre[((int64_t)b * a.Hq + h) * R + row];
+  if (r32 >= R) {
 #pragma unroll
     for (int st = 0; st < 8; ++st) qf[st] = bf16x8{};
   }
+  return row;
+}
+
+// The block tile once its inputs are in LDS: S^T = K Q^T masked to the R
+// keys, softmax with the tile's max, O^T = V^T P^T; returns the block part's
+// lse (natural log) and leaves its unnormalised O and row sum in o / l_tot.
+__device__ __forceinline__ float block_tile_compute(const BlockMergeArgs& a, const uint16_t* lds,
+                                                    const bf16x8 (&qf)[8], f32x16 (&o)[4], float& l_tot) {
+  constexpr int KVB = 32;
   int kofs[8], vofs[8];
   k_offsets(kofs);
   v_offsets(vofs);
   wait_tile_loads();                                 // the tiles are in LDS (one wave: no barrier)
-
   const float c2 = a.scale * kLog2e;
   f32x16 s[1];
   qk_tile<KVB>(lds, kofs, qf, s);
-  mask_tile<1>(s, R - 1);
-  f32x16 o[4];
+  mask_tile<1>(s, a.R - 1);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
   float m_ref = -INFINITY, l_run = 0.f;
   const float msub = softmax_rescale(tile_max<1>(s) * c2, m_ref, l_run, o);
   softmax_pv_tile<KVB>(lds + KVB * kRow, vofs, s, c2, msub, l_run, o);
-  const float l_tot = pair_sum(l_run);
+  l_tot = pair_sum(l_run);
+  return (m_ref + log2f(l_tot)) * kLn2;             // >= 1 key
+}
 
-  if (!valid) return;
-  const float lb = (m_ref + log2f(l_tot)) * kLn2;   // the block part's lse (natural log); >= 1 key
+// O and lse of lane row `row` from the prefix state (op, la) and the block part (o, lb, l_tot).
+template <int DO>
+__device__ __forceinline__ void block_merge_store(const BlockMergeArgs& a, int b, int h, int row,
+                                                  const float (&op)[4][4][4], float la, const f32x16 (&o)[4], float lb,
+                                                  float l_tot) {
+  const int hi = (threadIdx.x & 63) >> 5;
   const float m = fmaxf(la, lb);
   const float wa = la > -INFINITY ? fast_exp2((la - m) * kLog2e) : 0.f;
   const float wb = fast_exp2((lb - m) * kLog2e);
@@ -177,7 +186,164 @@ __global__ __launch_bounds__(64) void block_attn_merge_kernel(BlockMergeArgs a) 
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + io + d) = f32x4{y[0], y[1], y[2], y[3]};
       }
     }
-  if (hi == 0) a.lse[((int64_t)b * a.Hq + h) * R + row] = m + log2f(tot) * kLn2;
+  if (hi == 0) a.lse[((int64_t)b * a.Hq + h) * a.R + row] = m + log2f(tot) * kLn2;
+}
+
+// One wave per (batch, query head): the R <= 32 rows are one 32-query tile and
+// the block's keys one 32-key tile, so the step is one tile of the MFMA
+// attention (S^T = K Q^T and O^T = V^T P^T with v_mfma_f32_32x32x16_bf16, K
+// and V copied straight into LDS, the tile's max as the softmax reference).
+// The copies, the query fragments and the row's cached prefix (O, lse) are
+// all requested before the first product.
+template <int DO, bool PRE_F32>
+__global__ __launch_bounds__(64) void block_attn_merge_kernel(BlockMergeArgs a) {
+  constexpr int KVB = 32;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * KVB * kRow];   // K tile, then V tile
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  bf16x8 qf[8];
+  float op[4][4][4], la;
+  const int row = block_tile_requests<PRE_F32>(a, b, h, lds_addr(lds), qf, op, la);
+  f32x16 o[4];
+  float l_tot;
+  const float lb = block_tile_compute(a, lds, qf, o, l_tot);
+  if ((int)(threadIdx.x & 31) >= a.R) return;
+  block_merge_store<DO>(a, b, h, row, op, la, o, lb, l_tot);
+}
+
+// ------------------------------------------------------- denoising step ---
+// The last launch of the fused denoising step: the combine of the split
+// partials of the active rows (the prefix attention over the block's list;
+// written to the prefix cache, as the combine of the attention entry point
+// writes O and LSE), then the block tile and the merge of every row, as the
+// block-merge entry point.  One workgroup per (kDenRows rows, batch, query
+// head); wave 0 requests its tile inputs first, all four waves combine (one
+// row and two dims per thread, partial slices in batches of 32 with a running
+// maximum, the combine's arithmetic), the new prefix of the active rows is
+// handed to wave 0 through LDS, and wave 0 computes the tile (for all rows;
+// each workgroup writes only its own) and the merge.
+template <int DO>
+__global__ __launch_bounds__(256) void den_merge_kernel(DenMergeArgs a) {
+  constexpr int KVB = 32, BATCH = 32, RC = kDenRows;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * KVB * kRow];
+  __shared__ __attribute__((aligned(16))) uint64_t ml_sh[RC * BATCH];
+  __shared__ __attribute__((aligned(16))) float pre_sh[RC][kD];
+  __shared__ float pre_lse_sh[RC];
+  const BlockMergeArgs& m = a.m;
+  const int r0 = blockIdx.x * RC, bh = blockIdx.y;
+  const int b = bh / m.Hq, h = bh - b * m.Hq, g = h / m.G, hl = h - g * m.G;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int R = m.R;
+  bf16x8 qf[8];
+  float op[4][4][4], la = 0.f;
+  int trow = 0;
+  uint8_t tact = 0;
+  if (w == 0) {
+    trow = block_tile_requests<true>(m, b, h, lds_addr(lds), qf, op, la);
+    tact = a.row_mask[(int64_t)b * R + trow];
+  }
+  // ---- combine: thread = (row r0 + tid / 64, dims 2 (tid % 64), + 1)
+  const int rl = tid >> 6, d = 2 * (tid & 63);
+  const int row = r0 + rl, rowc = min(row, R - 1);
+  const uint8_t rbyte = a.row_mask[(int64_t)b * R + rowc];
+  const int64_t li = (int64_t)b * a.Hkv + g;
+  const int c_list = a.cnt[li];
+  const int QV = R * m.G, qv = rowc * m.G + hl;
+  const int64_t p0 = li * a.items;
+  const int sr = tid / BATCH, su = tid - sr * BATCH;        // the (m, l) this thread stages
+  const int sqv = min(r0 + sr, R - 1) * m.G + hl;
+  const int per = max(1, (c_list + a.items - 1) / a.items);
+  const int nvalid = (c_list + per - 1) / per;
+  const bool live = row < R && rbyte != 0;
+  float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int it0 = 0; it0 < nvalid; it0 += BATCH) {           // uniform over the workgroup
+    if (it0 > 0) __syncthreads();                           // the previous batch's LDS reads are done
+    uint64_t mlv = 0;
+    if (tid < RC * BATCH) {
+      const int64_t it = min(it0 + su, nvalid - 1);
+      mlv = *reinterpret_cast<const uint64_t*>(a.part_ml + ((p0 + it) * QV + sqv) * 2);
+    }
+    // slots past the valid count are clamped to a written one and excluded below
+    float o0[BATCH], o1[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int64_t it = min(it0 + u, nvalid - 1);
+      const f32x2 v = *reinterpret_cast<const f32x2*>(a.part_o + ((p0 + it) * QV + qv) * kD + d);
+      o0[u] = v[0];
+      o1[u] = v[1];
+    }
+    if (tid < RC * BATCH) ml_sh[tid] = mlv;
+    __syncthreads();
+    if (live) {
+      uint64_t mlr[BATCH];
+#pragma unroll
+      for (int q = 0; q < BATCH / 2; ++q) {
+        const u32x4 t = *reinterpret_cast<const u32x4*>(&ml_sh[rl * BATCH + 2 * q]);
+        mlr[2 * q] = (uint64_t)t[0] | ((uint64_t)t[1] << 32);
+        mlr[2 * q + 1] = (uint64_t)t[2] | ((uint64_t)t[3] << 32);
+      }
+      float bm = M;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (it0 + u < nvalid) bm = fmaxf(bm, __uint_as_float((uint32_t)mlr[u]));
+      if (bm != -INFINITY) {                                // else nothing visible so far
+        const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+        L *= alpha;
+        acc0 *= alpha;
+        acc1 *= alpha;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const float mv = __uint_as_float((uint32_t)mlr[u]);
+          if (it0 + u < nvalid && mv != -INFINITY) {
+            const float wgt = fast_exp2(mv - bm);
+            L = fmaf(__uint_as_float((uint32_t)(mlr[u] >> 32)), wgt, L);
+            acc0 = fmaf(o0[u], wgt, acc0);
+            acc1 = fmaf(o1[u], wgt, acc1);
+          }
+        }
+        M = bm;
+      }
+    }
+  }
+  if (live) {
+    const float y0 = L > 0.f ? acc0 / L : 0.f, y1 = L > 0.f ? acc1 / L : 0.f;
+    const float lp = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    float* co = a.cache_o + (int64_t)b * m.psb + (int64_t)h * m.psh + (int64_t)row * m.psl + d;
+    *reinterpret_cast<f32x2*>(co) = f32x2{y0, y1};
+    pre_sh[rl][d] = y0;
+    pre_sh[rl][d + 1] = y1;
+    if (d == 0) {
+      a.cache_lse[((int64_t)b * m.Hq + h) * R + row] = lp;
+      pre_lse_sh[rl] = lp;
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
+  f32x16 o[4];
+  float l_tot;
+  const float lb = block_tile_compute(m, lds, qf, o, l_tot);
+  const int r32 = threadIdx.x & 31;
+  if (r32 >= R || r32 < r0 || r32 >= r0 + RC) return;
+  if (tact) {
+    // an active row's prefix is the one just combined (the values written to the cache)
+    const int hi = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&pre_sh[r32 - r0][32 * dt + 8 * i4 + 4 * hi]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) op[dt][i4][e] = x[e];
+      }
+    la = pre_lse_sh[r32 - r0];
+  }
+  block_merge_store<DO>(m, b, h, trow, op, la, o, lb, l_tot);
+}
+
+void launch_den_merge(const DenMergeArgs& a, int dout, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(a.m.R, kDenRows), (unsigned)(a.m.B * a.m.Hq));
+  if (dout == BSA_BF16) hipLaunchKernelGGL((den_merge_kernel<BSA_BF16>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((den_merge_kernel<BSA_F32>), grid, dim3(256), 0, s, a);
 }
 
 void launch_block_attn_merge(const BlockMergeArgs& a, int dout, hipStream_t s) {

@@ -29,6 +29,8 @@
 
 #include "common.h"
 #include "internal.h"
+#include "locality.h"
+#include "pick.h"
 #include "wave_select.h"
 
 namespace bsa {
@@ -123,47 +125,6 @@ __global__ __launch_bounds__(64) void tau_final_kernel(const float* __restrict__
 }
 
 // -------------------------------------------------------------------- pick ---
-struct PickArgs {
-  const float* Z;
-  int NB, NBp, Rtot, G, Hkv, nbands, NQB;
-  int q_block, kv_block, q_pos0, Lq, causal, pooled;
-  int multi_row;           // raw rows with more than one row per query block: rows publish bitmaps
-  int topk, topk_num, topk_den, n_first, n_last, cap;
-  const uint8_t* row_mask;
-  int32_t* idx;
-  int32_t* cnt;
-  int32_t* row_picks;
-  uint32_t* row_bits;      // [B][Hkv][Rtot][128] row bitmaps (blocks with several rows)
-};
-
-constexpr int kPickMaxWords = 128;     // NB <= 4096
-constexpr int kPickThreads = 256;
-constexpr int kPickRegs = 32;          // logits held per thread at once
-constexpr int kPickChanBatch = 16;     // (head, band) channels reduced together, at most
-
-struct RowPlan {
-  int qb, rows, nC, nf_first, last_lo, kp, n_free;
-};
-
-__device__ __forceinline__ RowPlan row_plan(const PickArgs& a, int row) {
-  RowPlan r;
-  r.qb = a.pooled ? row : row / a.q_block;
-  r.rows = a.pooled ? 1 : min(a.q_block, a.Lq - r.qb * a.q_block);
-  int jmax = a.NB - 1;
-  if (a.causal) {
-    const int last_row = min((r.qb + 1) * a.q_block, a.Lq) - 1;
-    jmax = min(a.NB - 1, (a.q_pos0 + last_row) / a.kv_block);
-  }
-  r.nC = jmax + 1;
-  r.nf_first = min(a.n_first, r.nC);
-  r.last_lo = max(r.nf_first, r.nC - a.n_last);       // forced: j < nf_first or j >= last_lo
-  const int n_forced = r.nf_first + (r.nC - r.last_lo);
-  int kp = a.topk_num > 0 ? (int)(((int64_t)a.topk_num * r.nC + a.topk_den - 1) / a.topk_den) : a.topk;
-  r.kp = max(0, min(kp, r.nC - n_forced));
-  r.n_free = r.nC - n_forced;
-  return r;
-}
-
 // Sum of a value over the 256 threads, identical bits in every thread
 // (fixed DPP order inside each wave, then the 4 wave totals in order).
 __device__ __forceinline__ float block_sum(float v, float* red, int slot) {
@@ -394,7 +355,16 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
                                                      int64_t qsl, const float* __restrict__ k_mean, int NB, int Rtot,
                                                      int G, int Hkv, float scale, const float* __restrict__ tau,
                                                      int layout, int causal, int q_block, int kv_block, int q_pos0,
-                                                     int pooled, int Lq, float* __restrict__ Z, RefreshArgs ra) {
+                                                     int pooled, int Lq, float* __restrict__ Z, RefreshArgs ra,
+                                                     ActiveRowsArgs act) {
+  if (act.a != nullptr && (int)blockIdx.z >= act.z0) {
+    // the denoising step's active-row test rides in this launch: extra z-slices, one row per workgroup
+    __shared__ float sh4[4];
+    const int k = blockIdx.z - act.z0, b = k / act.slices;
+    const int r = (k - b * act.slices) * (gridDim.x * gridDim.y) + blockIdx.y * gridDim.x + blockIdx.x;
+    if (r < act.R) active_row_job<DT>(act, r, b, sh4);
+    return;
+  }
   constexpr int TM = TY * RPT, TJ = TX * CPT;
   const int NBp = (NB + 3) & ~3;          // row stride of Z, a multiple of 4 floats
   constexpr int ES = DT == BSA_BF16 ? 2 : 4;
@@ -587,35 +557,16 @@ bool plan_select(const bsa_tensor& q, int NB, const bsa_select_params& p, Select
 }
 
 
-void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_mean, const float* k_energy,
-                   const bsa_select_params& p, const SelectPlan& pl, const uint8_t* row_mask, int32_t* idx,
-                   int32_t* cnt, int32_t* row_picks, float* tau_out, void* ws, hipStream_t s, const RefreshArgs& ra) {
-  const int G = pl.G, Hkv = pl.Hkv, NB = pl.NB;
-  const int Rtot = p.pooled_q ? pl.NQB : pl.Lq;
-  const int nb = p.dual_band ? 2 : 1;
-  float* Z = static_cast<float*>(ws);
-  float* tau = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.z_bytes);
-  if (p.dual_band) {
-    const float* qm = p.pooled_q ? static_cast<const float*>(q.data) : nullptr;
-    const int nchunk = tau_chunks(NB, p.pooled_q ? pl.NQB : 0);
-    float* part = tau + align256((size_t)pl.B * pl.Hq * 2 * 4) / 4;
-    const int ids = Hkv + (qm ? pl.Hq : 0);
-    hipLaunchKernelGGL(tau_partial_kernel, dim3(nchunk, ids, pl.B), dim3(256), 0, s, k_mean, k_energy, NB, qm,
-                       q.stride_b, q.stride_h, q.stride_l, q_energy, pl.NQB, pl.D, Hkv, pl.Hq, p.layout, nchunk,
-                       part);
-    hipLaunchKernelGGL(tau_final_kernel, dim3(pl.Hq, pl.B), dim3(64), 0, s, part, Hkv, G, nchunk, qm ? 1 : 0, tau,
-                       tau_out);
-  }
-  const int M = Rtot * G;
-  const uint8_t* qd = static_cast<const uint8_t*>(q.data);
+PickArgs make_pick_args(const bsa_select_params& p, const SelectPlan& pl, void* ws, const uint8_t* row_mask,
+                        int32_t* idx, int32_t* cnt, int32_t* row_picks) {
   PickArgs a;
-  a.Z = Z;
-  a.NB = NB;
-  a.NBp = (NB + 3) & ~3;
-  a.Rtot = Rtot;
-  a.G = G;
-  a.Hkv = Hkv;
-  a.nbands = nb;
+  a.Z = static_cast<const float*>(ws);
+  a.NB = pl.NB;
+  a.NBp = (pl.NB + 3) & ~3;
+  a.Rtot = p.pooled_q ? pl.NQB : pl.Lq;
+  a.G = pl.G;
+  a.Hkv = pl.Hkv;
+  a.nbands = p.dual_band ? 2 : 1;
   a.NQB = pl.NQB;
   a.q_block = p.q_block;
   a.kv_block = p.kv_block;
@@ -635,13 +586,31 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
   a.cnt = cnt;
   a.row_picks = row_picks;
   a.row_bits = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + pl.z_bytes + pl.tau_bytes);
+  return a;
+}
+
+// The block logits (after the band temperatures when dual-band), with the
+// optional summary refresh and the optional active-row jobs in the same launch.
+static void launch_logits(const bsa_tensor& q, const float* k_mean, const bsa_select_params& p, const SelectPlan& pl,
+                          void* ws, hipStream_t s, const RefreshArgs& ra, ActiveRowsArgs act) {
+  const int G = pl.G, Hkv = pl.Hkv, NB = pl.NB;
+  const int Rtot = p.pooled_q ? pl.NQB : pl.Lq;
+  float* Z = static_cast<float*>(ws);
+  const float* tau = reinterpret_cast<const float*>(static_cast<uint8_t*>(ws) + pl.z_bytes);
+  const int M = Rtot * G;
+  const uint8_t* qd = static_cast<const uint8_t*>(q.data);
   const float scale2 = p.scale * kLog2e;
 #define BSA_LOGITS(DT, DD, TX, TY, RPT, CPT, DUAL)                                                        \
   do {                                                                                                    \
     dim3 grid((unsigned)ceil_div(NB, TX * CPT), (unsigned)ceil_div(M, TY * RPT), (unsigned)(pl.B * Hkv)); \
+    if (act.a) {                                                                                          \
+      act.z0 = (int)grid.z;                                                                               \
+      act.slices = (int)ceil_div(act.R, (int64_t)grid.x * grid.y);                                        \
+      grid.z += (unsigned)(pl.B * act.slices);                                                            \
+    }                                                                                                     \
     hipLaunchKernelGGL((logits_kernel<DT, DD, TX, TY, RPT, CPT, DUAL>), grid, dim3(256), 0, s, qd,        \
                        q.stride_b, q.stride_h, q.stride_l, k_mean, NB, Rtot, G, Hkv, scale2, tau, p.layout, \
-                       p.causal, p.q_block, p.kv_block, p.q_pos0, p.pooled_q, pl.Lq, Z, ra);             \
+                       p.causal, p.q_block, p.kv_block, p.q_pos0, p.pooled_q, pl.Lq, Z, ra, act);        \
   } while (0)
 #define BSA_LOGITS_SHAPE(DT, DD, DUAL)                                   \
   do {                                                                   \
@@ -661,6 +630,32 @@ void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_me
 #undef BSA_LOGITS_D
 #undef BSA_LOGITS_SHAPE
 #undef BSA_LOGITS
+}
+
+void launch_select_logits(const bsa_tensor& q, const float* k_mean, const bsa_select_params& p,
+                          const SelectPlan& pl, void* ws, hipStream_t s, const ActiveRowsArgs& act) {
+  launch_logits(q, k_mean, p, pl, ws, s, RefreshArgs(), act);
+}
+
+void launch_select(const bsa_tensor& q, const float* q_energy, const float* k_mean, const float* k_energy,
+                   const bsa_select_params& p, const SelectPlan& pl, const uint8_t* row_mask, int32_t* idx,
+                   int32_t* cnt, int32_t* row_picks, float* tau_out, void* ws, hipStream_t s, const RefreshArgs& ra) {
+  const int Hkv = pl.Hkv, NB = pl.NB;
+  float* tau = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.z_bytes);
+  if (p.dual_band) {
+    const float* qm = p.pooled_q ? static_cast<const float*>(q.data) : nullptr;
+    const int nchunk = tau_chunks(NB, p.pooled_q ? pl.NQB : 0);
+    float* part = tau + align256((size_t)pl.B * pl.Hq * 2 * 4) / 4;
+    const int ids = Hkv + (qm ? pl.Hq : 0);
+    hipLaunchKernelGGL(tau_partial_kernel, dim3(nchunk, ids, pl.B), dim3(256), 0, s, k_mean, k_energy, NB, qm,
+                       q.stride_b, q.stride_h, q.stride_l, q_energy, pl.NQB, pl.D, Hkv, pl.Hq, p.layout, nchunk,
+                       part);
+    hipLaunchKernelGGL(tau_final_kernel, dim3(pl.Hq, pl.B), dim3(64), 0, s, part, Hkv, pl.G, nchunk, qm ? 1 : 0, tau,
+                       tau_out);
+  }
+  launch_logits(q, k_mean, p, pl, ws, s, ra, ActiveRowsArgs());
+  const PickArgs a = make_pick_args(p, pl, ws, row_mask, idx, cnt, row_picks);
+  const int Rtot = a.Rtot;
   const int U = (int)ceil_div(a.NBp, kPickThreads);
   dim3 pgrid(Rtot, Hkv, pl.B);
   if (U <= 1) hipLaunchKernelGGL(pick_kernel<1>, pgrid, dim3(kPickThreads), 0, s, a);

@@ -438,6 +438,48 @@ bsa_status bsa_block_attention_merge(const bsa_tensor* q, const bsa_tensor* kb, 
                                      void* stream);
 
 /* Status text and the calling thread's last error detail. */
+/* ------------------------------------------------------------------------ *
+ * One denoising step of a block-wise diffusion LM with locality pruning, in
+ * three launches (LoSA sec. 2: only the rows whose queries changed since the
+ * previous step recompute their prefix attention, over the union of their
+ * selected blocks; every row then attends to the block's own keys and merges
+ * with its prefix state).  The results are those of, in order,
+ *   bsa_active_rows(q, q_prev, theta, row_mask, mse);
+ *   bsa_select_blocks(q, NULL, k_mean, NULL, Hkv, NB, p, row_mask, idx, cnt,
+ *                     NULL, NULL, ...);
+ *   bsa_sparse_attention_fwd(q, k, v, idx, cnt, {p->scale, p->kv_block, R,
+ *                     p->q_pos0, p->causal, p->cap}, row_mask, cache_o,
+ *                     cache_lse, ...);
+ *   bsa_block_attention_merge(q, kb, vb, p->scale, cache_o, cache_lse, o, lse);
+ * bit for bit: the same arithmetic in the same order.
+ * q, q_prev [B, Hq, R, D] bf16, D = 128, 1 <= R <= 32, R * Hq / Hkv <= 128;
+ * k, v [B, Hkv, L, D] bf16 (the prefix), NB = ceil(L / p->kv_block) <= 4096,
+ * kv_block 64 or 128; k_mean [B, Hkv, NB, D] f32 (bsa_build_block_summaries
+ * of k); kb, vb [B, Hkv, R, D] bf16 (the block's own keys and values).
+ * p: one query block of raw rows (q_block = R), one band; the budget, forced
+ * blocks, causality and cap as bsa_select_blocks.  cache_o [B, Hq, R, D] f32
+ * and cache_lse [B, Hq, R]: the prefix state, read for stable rows and
+ * rewritten for active ones.  Writes row_mask [B, R] (and mse [B, R] if not
+ * NULL), idx [B, Hkv, 1, cap] / cnt [B, Hkv, 1] (the union list), o [B, Hq,
+ * R, D] bf16 or f32 and lse [B, Hq, R].
+ * Launches: the block logits of every row with the active-row test as extra
+ * workgroups; per (slice of the list, KV group) the picks of the active rows
+ * (one wavefront per row; every workgroup of a group forms the same union),
+ * the slice's split partials; per (4 rows, query head) the combine of the
+ * partials into the cache, the block tile and the merge.
+ * workspace: bsa_denoise_step_workspace_bytes() bytes (logits, split
+ * partials; no initial contents needed; calls that overlap on one workspace
+ * race).  Errors: as the entry points it combines; BSA_ERR_UNSUPPORTED
+ * outside the shapes above.
+ * ------------------------------------------------------------------------ */
+size_t bsa_denoise_step_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, const bsa_select_params* p);
+
+bsa_status bsa_denoise_step(const bsa_tensor* q, const bsa_tensor* q_prev, float theta, const float* k_mean,
+                            const bsa_tensor* k, const bsa_tensor* v, const bsa_tensor* kb, const bsa_tensor* vb,
+                            const bsa_select_params* p, const bsa_tensor* cache_o, float* cache_lse,
+                            uint8_t* row_mask, float* mse, int32_t* idx, int32_t* cnt, const bsa_tensor* o,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 const char* bsa_status_string(int32_t status);
 const char* bsa_last_error(void);
 int32_t bsa_version(void);
