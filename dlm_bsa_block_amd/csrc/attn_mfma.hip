@@ -114,9 +114,30 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     }
     __syncthreads();
   };
+  // this lane's query vector and its fragments
+  const int wr = w & 3;                            // wave within its head
+  const int qv = 32 * wr + r32;
+  int n_qv = 0, row = 0, h = 0;
+  bool valid = false, wave_busy = false;
+  bf16x8 qf[8];
+  auto setup_q = [&]() __attribute__((always_inline)) {
+    if (SPLIT) {
+      n_qv = n_qv_sh;
+      valid = qv < n_qv;
+      row = valid ? qv_row[qv] : 0;
+      h = g * a.G + (valid ? qv_head[qv] : 0);
+    } else {
+      row = qb * a.q_block + qv;
+      valid = qv < a.q_block && row < a.Lq;
+      h = g * a.G + h0 + (w >> 2);
+    }
+    wave_busy = SPLIT ? (32 * wr < n_qv) : (32 * wr < a.q_block && qb * a.q_block + 32 * wr < a.Lq);
+    load_q_frag(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)row * a.qsl, valid, qf);
+  };
   int n_list, e0 = 0, e1;
   if constexpr (PICK) {
     stage_qv();
+    setup_q();                                     // the query loads overlap the picks
     const int n_act = n_qv_sh / a.G;
     uint64_t fl = 0;
     uint32_t* keys = reinterpret_cast<uint32_t*>(lds) + w * 256 * PU;
@@ -163,29 +184,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     e1 = min(n_list, e0 + per);
     if constexpr (!PICK) stage_qv();
   }
-  const int n_qv = SPLIT ? n_qv_sh : 0;
-  const int wr = w & 3;                            // wave within its head
-  const int qv = 32 * wr + r32;
-  bool valid;
-  int row, h;
-  if (SPLIT) {
-    valid = qv < n_qv;
-    row = valid ? qv_row[qv] : 0;
-    h = g * a.G + (valid ? qv_head[qv] : 0);
-  } else {
-    row = qb * a.q_block + qv;
-    valid = qv < a.q_block && row < a.Lq;
-    h = g * a.G + h0 + (w >> 2);
-  }
-  const bool wave_busy = SPLIT ? (32 * wr < n_qv) : (32 * wr < a.q_block && qb * a.q_block + 32 * wr < a.Lq);
+  if constexpr (!PICK) setup_q();
   const int qpos = a.q_pos0 + row;
   // smallest query position of the wave (for deciding whether a tile needs the causal mask)
   int wave_min_pos = valid ? qpos : 0x7FFFFFFF;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) wave_min_pos = min(wave_min_pos, wave_xor(wave_min_pos, m));
 
-  bf16x8 qf[8];
-  load_q_frag(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)row * a.qsl, valid, qf);
   int kofs[8], vofs[8];
   k_offsets(kofs);
   v_offsets(vofs);

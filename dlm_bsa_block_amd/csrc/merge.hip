@@ -89,7 +89,8 @@ namespace bsa {
 // The requests of one wave's block tile: the K and V tiles into LDS, the
 // query fragments of lane row r32 (rows past R load row R - 1 and are zeroed)
 // and that row's cached prefix state (O in the O^T layout: dims
-// 32 dt + 8 i4 + 4 hi .. + 3, and its lse).  Returns the lane's row.
+// 32 dt + 8 i4 + 4 hi .. + 3, and its lse).  Returns the lane's row.  Run by
+// wave 0 of its workgroup: the tile copies place LDS rows by wave index.
 template <bool PRE_F32>
 __device__ __forceinline__ int block_tile_requests(const BlockMergeArgs& a, int b, int h, uint32_t l0, bf16x8 (&qf)[8],
                                                    float (&op)[4][4][4], float& la) {
@@ -216,72 +217,89 @@ __global__ __launch_bounds__(64) void block_attn_merge_kernel(BlockMergeArgs a) 
 // partials of the active rows (the prefix attention over the block's list;
 // written to the prefix cache, as the combine of the attention entry point
 // writes O and LSE), then the block tile and the merge of every row, as the
-// block-merge entry point.  One workgroup per (kDenRows rows, batch, query
-// head); wave 0 requests its tile inputs first, all four waves combine (one
-// row and two dims per thread, partial slices in batches of 32 with a running
-// maximum, the combine's arithmetic), the new prefix of the active rows is
-// handed to wave 0 through LDS, and wave 0 computes the tile (for all rows;
-// each workgroup writes only its own) and the merge.
+// block-merge entry point.  One workgroup of five waves per (kDenRows rows,
+// batch, query head): wave 1 + r combines row r0 + r (two dims per lane,
+// partial slices in batches of 32 with a running maximum, the combine's
+// arithmetic; a stable row's wave has nothing to do), while wave 0 (the tile
+// copies address LDS rows by wave index) copies the block's K/V tile,
+// computes the block tile for all rows and then, once the combined prefix of
+// the active rows is in LDS, merges and writes its rows.
 template <int DO>
-__global__ __launch_bounds__(256) void den_merge_kernel(DenMergeArgs a) {
+__global__ __launch_bounds__(320) void den_merge_kernel(DenMergeArgs a) {
   constexpr int KVB = 32, BATCH = 32, RC = kDenRows;
+  static_assert(RC == 4, "one combining wave per row");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * KVB * kRow];
-  __shared__ __attribute__((aligned(16))) uint64_t ml_sh[RC * BATCH];
+  __shared__ __attribute__((aligned(16))) uint64_t ml_sh[RC][BATCH];
   __shared__ __attribute__((aligned(16))) float pre_sh[RC][kD];
   __shared__ float pre_lse_sh[RC];
   const BlockMergeArgs& m = a.m;
   const int r0 = blockIdx.x * RC, bh = blockIdx.y;
   const int b = bh / m.Hq, h = bh - b * m.Hq, g = h / m.G, hl = h - g * m.G;
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int R = m.R;
-  bf16x8 qf[8];
-  float op[4][4][4], la = 0.f;
-  int trow = 0;
-  uint8_t tact = 0;
   if (w == 0) {
-    trow = block_tile_requests<true>(m, b, h, lds_addr(lds), qf, op, la);
-    tact = a.row_mask[(int64_t)b * R + trow];
+    // ---- wave 0: the block tile, then (after the combine) the merge
+    bf16x8 qf[8];
+    float op[4][4][4], la;
+    const int trow = block_tile_requests<true>(m, b, h, lds_addr(lds), qf, op, la);
+    const uint8_t tact = a.row_mask[(int64_t)b * R + trow];
+    f32x16 o[4];
+    float l_tot;
+    const float lb = block_tile_compute(m, lds, qf, o, l_tot);
+    __syncthreads();                                        // the combined prefixes are in LDS
+    const int r32 = lane & 31;
+    if (r32 >= R || r32 < r0 || r32 >= r0 + RC) return;
+    if (tact) {
+      // an active row's prefix is the one just combined (the values written to the cache)
+      const int hi = lane >> 5;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&pre_sh[r32 - r0][32 * dt + 8 * i4 + 4 * hi]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) op[dt][i4][e] = x[e];
+        }
+      la = pre_lse_sh[r32 - r0];
+    }
+    block_merge_store<DO>(m, b, h, trow, op, la, o, lb, l_tot);
+    return;
   }
-  // ---- combine: thread = (row r0 + tid / 64, dims 2 (tid % 64), + 1)
-  const int rl = tid >> 6, d = 2 * (tid & 63);
+  // ---- waves 1..4: the combine of row r0 + rl (dims 2 lane, + 1)
+  const int rl = w - 1, d = 2 * lane;
   const int row = r0 + rl, rowc = min(row, R - 1);
-  const uint8_t rbyte = a.row_mask[(int64_t)b * R + rowc];
+  const uint8_t rbyte = (uint8_t)__builtin_amdgcn_readfirstlane(a.row_mask[(int64_t)b * R + rowc]);
   const int64_t li = (int64_t)b * a.Hkv + g;
   const int c_list = a.cnt[li];
   const int QV = R * m.G, qv = rowc * m.G + hl;
   const int64_t p0 = li * a.items;
-  const int sr = tid / BATCH, su = tid - sr * BATCH;        // the (m, l) this thread stages
-  const int sqv = min(r0 + sr, R - 1) * m.G + hl;
   const int per = max(1, (c_list + a.items - 1) / a.items);
   const int nvalid = (c_list + per - 1) / per;
-  const bool live = row < R && rbyte != 0;
-  float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int it0 = 0; it0 < nvalid; it0 += BATCH) {           // uniform over the workgroup
-    if (it0 > 0) __syncthreads();                           // the previous batch's LDS reads are done
-    uint64_t mlv = 0;
-    if (tid < RC * BATCH) {
-      const int64_t it = min(it0 + su, nvalid - 1);
-      mlv = *reinterpret_cast<const uint64_t*>(a.part_ml + ((p0 + it) * QV + sqv) * 2);
-    }
-    // slots past the valid count are clamped to a written one and excluded below
-    float o0[BATCH], o1[BATCH];
+  const bool live = row < R && rbyte != 0;                  // uniform over the wave
+  if (live) {
+    float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+    for (int it0 = 0; it0 < nvalid; it0 += BATCH) {
+      // slots past the valid count are clamped to a written one and excluded below
+      const int64_t itm = min(it0 + (lane & (BATCH - 1)), nvalid - 1);
+      const uint64_t mlv = *reinterpret_cast<const uint64_t*>(a.part_ml + ((p0 + itm) * QV + qv) * 2);
+      float o0[BATCH], o1[BATCH];
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int64_t it = min(it0 + u, nvalid - 1);
-      const f32x2 v = *reinterpret_cast<const f32x2*>(a.part_o + ((p0 + it) * QV + qv) * kD + d);
-      o0[u] = v[0];
-      o1[u] = v[1];
-    }
-    if (tid < RC * BATCH) ml_sh[tid] = mlv;
-    __syncthreads();
-    if (live) {
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t it = min(it0 + u, nvalid - 1);
+        const f32x2 v = *reinterpret_cast<const f32x2*>(a.part_o + ((p0 + it) * QV + qv) * kD + d);
+        o0[u] = v[0];
+        o1[u] = v[1];
+      }
+      if (lane < BATCH) ml_sh[rl][lane] = mlv;
+      wave_sync_lds();
       uint64_t mlr[BATCH];
 #pragma unroll
       for (int q = 0; q < BATCH / 2; ++q) {
-        const u32x4 t = *reinterpret_cast<const u32x4*>(&ml_sh[rl * BATCH + 2 * q]);
+        const u32x4 t = *reinterpret_cast<const u32x4*>(&ml_sh[rl][2 * q]);
         mlr[2 * q] = (uint64_t)t[0] | ((uint64_t)t[1] << 32);
         mlr[2 * q + 1] = (uint64_t)t[2] | ((uint64_t)t[3] << 32);
       }
+      wave_sync_lds();                                      // read before the next batch rewrites it
       float bm = M;
 #pragma unroll
       for (int u = 0; u < BATCH; ++u)
@@ -304,46 +322,24 @@ __global__ __launch_bounds__(256) void den_merge_kernel(DenMergeArgs a) {
         M = bm;
       }
     }
-  }
-  if (live) {
     const float y0 = L > 0.f ? acc0 / L : 0.f, y1 = L > 0.f ? acc1 / L : 0.f;
     const float lp = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
     float* co = a.cache_o + (int64_t)b * m.psb + (int64_t)h * m.psh + (int64_t)row * m.psl + d;
     *reinterpret_cast<f32x2*>(co) = f32x2{y0, y1};
     pre_sh[rl][d] = y0;
     pre_sh[rl][d + 1] = y1;
-    if (d == 0) {
+    if (lane == 0) {
       a.cache_lse[((int64_t)b * m.Hq + h) * R + row] = lp;
       pre_lse_sh[rl] = lp;
     }
   }
   __syncthreads();
-  if (w != 0) return;
-  f32x16 o[4];
-  float l_tot;
-  const float lb = block_tile_compute(m, lds, qf, o, l_tot);
-  const int r32 = threadIdx.x & 31;
-  if (r32 >= R || r32 < r0 || r32 >= r0 + RC) return;
-  if (tact) {
-    // an active row's prefix is the one just combined (the values written to the cache)
-    const int hi = (threadIdx.x & 63) >> 5;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&pre_sh[r32 - r0][32 * dt + 8 * i4 + 4 * hi]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) op[dt][i4][e] = x[e];
-      }
-    la = pre_lse_sh[r32 - r0];
-  }
-  block_merge_store<DO>(m, b, h, trow, op, la, o, lb, l_tot);
 }
 
 void launch_den_merge(const DenMergeArgs& a, int dout, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(a.m.R, kDenRows), (unsigned)(a.m.B * a.m.Hq));
-  if (dout == BSA_BF16) hipLaunchKernelGGL((den_merge_kernel<BSA_BF16>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((den_merge_kernel<BSA_F32>), grid, dim3(256), 0, s, a);
+  if (dout == BSA_BF16) hipLaunchKernelGGL((den_merge_kernel<BSA_BF16>), grid, dim3(64 * (kDenRows + 1)), 0, s, a);
+  else hipLaunchKernelGGL((den_merge_kernel<BSA_F32>), grid, dim3(64 * (kDenRows + 1)), 0, s, a);
 }
 
 void launch_block_attn_merge(const BlockMergeArgs& a, int dout, hipStream_t s) {

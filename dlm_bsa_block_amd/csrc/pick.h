@@ -103,9 +103,11 @@ __device__ uint64_t wave_pick_row(const PickArgs& a, int b, int g, int row, uint
 #pragma unroll
         for (int u = 0; u < U; ++u)
           if (64 * v + lane + 256 * u >= nC) z[cc][v][u] = -INFINITY;
+    // every channel of the batch is reduced (a channel past the last one only has its sum
+    // discarded): a branch here would let the compiler sink the later channels' loads below it
 #pragma unroll
     for (int cc = 0; cc < CW; ++cc) {
-      if (c0 + cc >= nchan) break;                   // uniform
+      const bool cv = c0 + cc < nchan;                 // uniform
       float r[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -129,7 +131,10 @@ __device__ uint64_t wave_pick_row(const PickArgs& a, int b, int g, int row, uint
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int u = 0; u < U; ++u) s[v][u] = fmaf(z[cc][v][u], inv, s[v][u]);
+        for (int u = 0; u < U; ++u) {
+          const float t = fmaf(z[cc][v][u], inv, s[v][u]);
+          s[v][u] = cv ? t : s[v][u];
+        }
     }
   }
   // keys in block order (free candidates only; scores are >= 0, so float bits order like values)

@@ -369,8 +369,10 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
   const int NBp = (NB + 3) & ~3;          // row stride of Z, a multiple of 4 floats
   constexpr int ES = DT == BSA_BF16 ? 2 : 4;
   constexpr int NBANDS = DUAL ? 2 : 1;
-  __shared__ float Qs[TM][D + 1];
-  __shared__ float Ks[TJ][D + 1];
+  // rows padded to D + 4 floats: 16-byte reads of 4 dims, and the 16 lanes of a row group hit
+  // distinct banks (row stride 132 words = 4 banks apart)
+  __shared__ __attribute__((aligned(16))) float Qs[TM][D + 4];
+  __shared__ __attribute__((aligned(16))) float Ks[TJ][D + 4];
   const int tid = threadIdx.x, tx = tid % TX, ty = tid / TX;
   const int j0 = blockIdx.x * TJ, m0 = blockIdx.y * TM;
   const int bg = blockIdx.z, b = bg / Hkv, g = bg - b * Hkv;
@@ -419,8 +421,10 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
     if (i < QN) {
       const int mm = i / (D / 8), d8 = (i - mm * (D / 8)) * 8;
       const bool in = m0 + mm < M;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Qs[mm][d8 + e] = in ? qv[u][e] : 0.f;
+      *reinterpret_cast<f32x4*>(&Qs[mm][d8]) =
+          in ? f32x4{qv[u][0], qv[u][1], qv[u][2], qv[u][3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(&Qs[mm][d8 + 4]) =
+          in ? f32x4{qv[u][4], qv[u][5], qv[u][6], qv[u][7]} : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 #pragma unroll
@@ -429,8 +433,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
     if (i < KN) {
       const int jj = i / (D / 4), d4 = (i - jj * (D / 4)) * 4;
       const bool in = j0 + jj < NB && !(refresh && jj == jr);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Ks[jj][d4 + e] = in ? kv[u][e] : 0.f;
+      *reinterpret_cast<f32x4*>(&Ks[jj][d4]) = in ? kv[u] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   if (refresh) {
@@ -493,24 +496,27 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
   for (int q4 = 0; q4 < 4; ++q4) {
     // a quarter of the dims always belongs to one band (either layout)
     const int bnd = DUAL ? ((layout == BSA_ROPE_HALF) ? (q4 & 1) : (q4 >> 1)) : 0;
-#pragma unroll 8
-    for (int d = q4 * (D / 4); d < (q4 + 1) * (D / 4); ++d) {
-      float qv[RPT], kv[CPT];
+    // four dims per LDS read; the products are still accumulated one dim at a time, in order
+#pragma unroll 2
+    for (int d4 = q4 * (D / 4); d4 < (q4 + 1) * (D / 4); d4 += 4) {
+      f32x4 qv[RPT], kv[CPT];
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) qv[r] = Qs[ty * RPT + r][d];
+      for (int r = 0; r < RPT; ++r) qv[r] = *reinterpret_cast<const f32x4*>(&Qs[ty * RPT + r][d4]);
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) kv[c] = Ks[tx + TX * c][d];
+      for (int c = 0; c < CPT; ++c) kv[c] = *reinterpret_cast<const f32x4*>(&Ks[tx + TX * c][d4]);
 #pragma unroll
-      for (int r = 0; r < RPT; ++r)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          if (DUAL) {
-            if (bnd == 0) acc[r][c][0] = fmaf(qv[r], kv[c], acc[r][c][0]);
-            else acc[r][c][NBANDS - 1] = fmaf(qv[r], kv[c], acc[r][c][NBANDS - 1]);
-          } else {
-            acc[r][c][0] = fmaf(qv[r], kv[c], acc[r][c][0]);
+        for (int r = 0; r < RPT; ++r)
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) {
+            if (DUAL) {
+              if (bnd == 0) acc[r][c][0] = fmaf(qv[r][e], kv[c][e], acc[r][c][0]);
+              else acc[r][c][NBANDS - 1] = fmaf(qv[r][e], kv[c][e], acc[r][c][NBANDS - 1]);
+            } else {
+              acc[r][c][0] = fmaf(qv[r][e], kv[c][e], acc[r][c][0]);
+            }
           }
-        }
     }
   }
 
