@@ -70,7 +70,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   __shared__ int n_qv_sh;
   __shared__ uint64_t pflags_sh[PICK ? NW : 1][64];
   __shared__ __attribute__((aligned(16))) uint32_t pcand_sh[PICK ? NW : 1][64];
-  __shared__ int slice_sh[PICK ? kSplitBlocks : 1];
+  __shared__ int slice_sh[PICK ? kDenSplitBlocks : 1];
   __shared__ int n_list_sh;
 
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31;
@@ -132,7 +132,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
       h = g * a.G + h0 + (w >> 2);
     }
     wave_busy = SPLIT ? (32 * wr < n_qv) : (32 * wr < a.q_block && qb * a.q_block + 32 * wr < a.Lq);
-    load_q_frag(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)row * a.qsl, valid, qf);
+    // an invalid lane reads a row inside the sequence (row 0 in split mode, else the last row);
+    // its fragments are zeroed where they are first needed, so nothing waits for the loads here
+    load_q_frag_raw(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)min(row, a.Lq - 1) * a.qsl, qf);
   };
   int n_list, e0 = 0, e1;
   if constexpr (PICK) {
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
         const int e = __ffsll((unsigned long long)f) - 1;
         f &= f - 1;
         const int j = 4 * PU * lane + e;
-        if (pos >= s0 && pos < s1 && pos - s0 < kSplitBlocks) slice_sh[pos - s0] = j;   // per <= kSplitBlocks
+        if (pos >= s0 && pos < s1 && pos - s0 < kDenSplitBlocks) slice_sh[pos - s0] = j;   // per <= kDenSplitBlocks
         if (item == 0) out[pos] = j;
         ++pos;
       }
@@ -185,6 +187,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     if constexpr (!PICK) stage_qv();
   }
   if constexpr (!PICK) setup_q();
+  zero_q_frag(valid, qf);
   const int qpos = a.q_pos0 + row;
   // smallest query position of the wave (for deciding whether a tile needs the causal mask)
   int wave_min_pos = valid ? qpos : 0x7FFFFFFF;

@@ -83,6 +83,42 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   v += dpp_f32<0x143, 0xc>(0.f, v);    // row_bcast:31 into rows 2, 3
   return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
+// wave_sum_dpp / wave_max_dpp of N independent values, stage by stage: the same
+// bits as N separate calls, with the DPP latencies of the values overlapping.
+template <int N>
+__device__ __forceinline__ void wave_sum_dpp_n(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<0xB1>(0.f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x4E>(0.f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x141>(0.f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x140>(0.f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x142, 0xa>(0.f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<0x143, 0xc>(0.f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v[i]), 63));
+}
+template <int N>
+__device__ __forceinline__ void wave_max_dpp_n(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<0xB1>(-INFINITY, v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<0x4E>(-INFINITY, v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<0x141>(-INFINITY, v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<0x140>(-INFINITY, v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<0x142, 0xa>(-INFINITY, v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f32<0x143, 0xc>(-INFINITY, v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v[i]), 63));
+}
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(-INFINITY, v));
   v = fmaxf(v, dpp_f32<0x4E>(-INFINITY, v));

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(320) void den_merge_kernel(DenMergeArgs a) {
   constexpr int KVB = 32, BATCH = 32, RC = kDenRows;
   static_assert(RC == 4, "one combining wave per row");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * KVB * kRow];
-  __shared__ __attribute__((aligned(16))) uint64_t ml_sh[RC][BATCH];
+  __shared__ __attribute__((aligned(16))) uint64_t ml_sh[RC][2 * BATCH];
   __shared__ __attribute__((aligned(16))) float pre_sh[RC][kD];
   __shared__ float pre_lse_sh[RC];
   const BlockMergeArgs& m = a.m;
@@ -278,28 +278,16 @@ __global__ __launch_bounds__(320) void den_merge_kernel(DenMergeArgs a) {
   const bool live = row < R && rbyte != 0;                  // uniform over the wave
   if (live) {
     float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
-    for (int it0 = 0; it0 < nvalid; it0 += BATCH) {
-      // slots past the valid count are clamped to a written one and excluded below
-      const int64_t itm = min(it0 + (lane & (BATCH - 1)), nvalid - 1);
-      const uint64_t mlv = *reinterpret_cast<const uint64_t*>(a.part_ml + ((p0 + itm) * QV + qv) * 2);
-      float o0[BATCH], o1[BATCH];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int64_t it = min(it0 + u, nvalid - 1);
-        const f32x2 v = *reinterpret_cast<const f32x2*>(a.part_o + ((p0 + it) * QV + qv) * kD + d);
-        o0[u] = v[0];
-        o1[u] = v[1];
-      }
-      if (lane < BATCH) ml_sh[rl][lane] = mlv;
-      wave_sync_lds();
+    // one batch of 32 slices: a running maximum, then the slices in order (the combine's arithmetic)
+    auto batch = [&](int it0, const float (&o0)[BATCH], const float (&o1)[BATCH], const uint64_t* mls)
+        __attribute__((always_inline)) {
       uint64_t mlr[BATCH];
 #pragma unroll
       for (int q = 0; q < BATCH / 2; ++q) {
-        const u32x4 t = *reinterpret_cast<const u32x4*>(&ml_sh[rl][2 * q]);
+        const u32x4 t = *reinterpret_cast<const u32x4*>(mls + 2 * q);
         mlr[2 * q] = (uint64_t)t[0] | ((uint64_t)t[1] << 32);
         mlr[2 * q + 1] = (uint64_t)t[2] | ((uint64_t)t[3] << 32);
       }
-      wave_sync_lds();                                      // read before the next batch rewrites it
       float bm = M;
 #pragma unroll
       for (int u = 0; u < BATCH; ++u)
@@ -321,6 +309,32 @@ __global__ __launch_bounds__(320) void den_merge_kernel(DenMergeArgs a) {
         }
         M = bm;
       }
+    };
+    // two batches are requested together (their loads overlap; the arithmetic stays per batch)
+    for (int it0 = 0; it0 < nvalid; it0 += 2 * BATCH) {
+      // slots past the valid count are clamped to a written one and excluded in batch()
+      const int64_t itm = min(it0 + lane, nvalid - 1);
+      const uint64_t mlv = *reinterpret_cast<const uint64_t*>(a.part_ml + ((p0 + itm) * QV + qv) * 2);
+      float oa0[BATCH], oa1[BATCH], ob0[BATCH], ob1[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t it = min(it0 + u, nvalid - 1);
+        const f32x2 v = *reinterpret_cast<const f32x2*>(a.part_o + ((p0 + it) * QV + qv) * kD + d);
+        oa0[u] = v[0];
+        oa1[u] = v[1];
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int64_t it = min(it0 + BATCH + u, nvalid - 1);
+        const f32x2 v = *reinterpret_cast<const f32x2*>(a.part_o + ((p0 + it) * QV + qv) * kD + d);
+        ob0[u] = v[0];
+        ob1[u] = v[1];
+      }
+      ml_sh[rl][lane] = mlv;
+      wave_sync_lds();
+      batch(it0, oa0, oa1, &ml_sh[rl][0]);
+      if (it0 + BATCH < nvalid) batch(it0 + BATCH, ob0, ob1, &ml_sh[rl][BATCH]);
+      wave_sync_lds();                                      // read before the next pair rewrites it
     }
     const float y0 = L > 0.f ? acc0 / L : 0.f, y1 = L > 0.f ? acc1 / L : 0.f;
     const float lp = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;

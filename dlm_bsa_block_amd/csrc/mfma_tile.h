@@ -408,13 +408,28 @@ __device__ __forceinline__ void settle(bf16x8 (&qf)[8]) {
 }
 
 // Load the lane's Q^T operand fragments: query row pointer (bf16, D = 128).
-__device__ __forceinline__ void load_q_frag(const uint16_t* qrow, bool valid, bf16x8 (&qf)[8]) {
+// The loads of load_q_frag alone (qrow readable); zero_q_frag applies the
+// validity afterwards, where the fragments are first needed.
+__device__ __forceinline__ void load_q_frag_raw(const uint16_t* qrow, bf16x8 (&qf)[8]) {
   const int hi = (threadIdx.x & 63) >> 5;
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    u32x4 w = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
-    qf[st] = __builtin_bit_cast(bf16x8, w);
-  }
+  for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st + 8 * hi);
+}
+__device__ __forceinline__ void zero_q_frag(bool valid, bf16x8 (&qf)[8]) {
+#pragma unroll
+  for (int st = 0; st < 8; ++st) qf[st] = valid ? qf[st] : bf16x8{};
+}
+
+// qrow must be a readable row (callers clamp it); a lane with valid = false gets
+// zeros.  The loads are made whatever valid is (a load under a branch would
+// make the compiler wait for it where the branch joins).
+__device__ __forceinline__ void load_q_frag(const uint16_t* qrow, bool valid, bf16x8 (&qf)[8]) {
+  const int hi = (threadIdx.x & 63) >> 5;
+  u32x4 w[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) w[st] = *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * hi);
+#pragma unroll
+  for (int st = 0; st < 8; ++st) qf[st] = __builtin_bit_cast(bf16x8, valid ? w[st] : u32x4{0, 0, 0, 0});
 }
 
 }  // namespace bsa

@@ -66,10 +66,10 @@ void launch_denoise_gather(const bsa_tensor& q, const bsa_tensor& k, const bsa_t
 // The picks of one selection row by a single wavefront, with the arithmetic of
 // the 256-thread pick of the selection entry point: lane l stands for the
 // threads 64 v + l (v < 4) of that workgroup, which own the candidates
-// j = 64 v + l + 256 u.  Each per-thread max and sum is formed in the same
-// order, reduced over the lanes per v with the same DPP network, and the four
-// totals are combined in order, so every score, and hence every pick, has the
-// same bits.  keys: 256 U words of LDS and cand: 64 words, both owned by this
+// j = 64 v + l + 256 u.  Each per-thread sum is formed in the same order, the
+// four of a lane are added in order of v and the lane sums go through the same
+// DPP network (block_sum_lanes_n there; the maxima, exact in any order, take
+// one reduction), so every score, and hence every pick, has the same bits.  keys: 256 U words of LDS and cand: 64 words, both owned by this
 // wavefront.  Returns the flags of blocks KPL lane + e (KPL = 4 U), forced
 // blocks included.
 template <int U>
@@ -103,31 +103,40 @@ __device__ uint64_t wave_pick_row(const PickArgs& a, int b, int g, int row, uint
 #pragma unroll
         for (int u = 0; u < U; ++u)
           if (64 * v + lane + 256 * u >= nC) z[cc][v][u] = -INFINITY;
-    // every channel of the batch is reduced (a channel past the last one only has its sum
-    // discarded): a branch here would let the compiler sink the later channels' loads below it
+    // Every channel of the batch is reduced (a channel past the last one only has its
+    // result discarded): a branch here would let the compiler sink the later channels' loads
+    // below it.  The maxima of all channels go through one interleaved reduction (a max is
+    // exact in any order), then the lane sums of all channels through another.
+    float mx[CW];
+#pragma unroll
+    for (int cc = 0; cc < CW; ++cc) {
+      mx[cc] = z[cc][0][0];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int u = 0; u < U; ++u) mx[cc] = fmaxf(mx[cc], z[cc][v][u]);
+    }
+    wave_max_dpp_n<CW>(mx);
+    float sm[CW];
+#pragma unroll
+    for (int cc = 0; cc < CW; ++cc) {
+      float t[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        t[v] = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          z[cc][v][u] = fast_exp2(z[cc][v][u] - mx[cc]);   // -inf (not a candidate) -> 0
+          t[v] += z[cc][v][u];
+        }
+      }
+      sm[cc] = ((t[0] + t[1]) + t[2]) + t[3];
+    }
+    wave_sum_dpp_n<CW>(sm);
 #pragma unroll
     for (int cc = 0; cc < CW; ++cc) {
       const bool cv = c0 + cc < nchan;                 // uniform
-      float r[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float m = z[cc][v][0];
-#pragma unroll
-        for (int u = 1; u < U; ++u) m = fmaxf(m, z[cc][v][u]);
-        r[v] = wave_max_dpp(m);
-      }
-      const float mx = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float sm = 0.f;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          z[cc][v][u] = fast_exp2(z[cc][v][u] - mx);   // -inf (not a candidate) -> 0
-          sm += z[cc][v][u];
-        }
-        r[v] = wave_sum_dpp(sm);
-      }
-      const float inv = wband / (r[0] + r[1] + r[2] + r[3]);
+      const float inv = wband / sm[cc];
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll

@@ -157,20 +157,20 @@ __device__ __forceinline__ void block_max_n(float (&v)[N], int n, float* red, in
     v[i] = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
   }
 }
+// Sum over the 256 threads in the order shared with the per-wave pick of the
+// denoising step: for each lane l the partials of threads l, 64 + l, 128 + l
+// and 192 + l are added in that order, then the 64 lane sums go through the
+// DPP network; every thread gets the same bits.  red: N * 256 floats.
 template <int N>
-__device__ __forceinline__ void block_sum_n(float (&v)[N], int n, float* red, int slot0) {
+__device__ __forceinline__ void block_sum_lanes_n(float (&v)[N], float* red) {
+  const int t = threadIdx.x, l = t & 63;
 #pragma unroll
-  for (int i = 0; i < N; ++i)
-    if (i < n) v[i] = wave_sum_dpp(v[i]);                   // n is uniform: unused values skip the reduction
-  if ((threadIdx.x & 63) == 0)
-#pragma unroll
-    for (int i = 0; i < N; ++i) red[(slot0 + i) * 4 + (threadIdx.x >> 6)] = v[i];
+  for (int i = 0; i < N; ++i) red[i * 256 + t] = v[i];
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float* r = red + (slot0 + i) * 4;
-    v[i] = r[0] + r[1] + r[2] + r[3];
-  }
+  for (int i = 0; i < N; ++i)
+    v[i] = ((red[i * 256 + l] + red[i * 256 + 64 + l]) + red[i * 256 + 128 + l]) + red[i * 256 + 192 + l];
+  wave_sum_dpp_n<N>(v);
 }
 
 // Ordered compaction of a bitmap (nw <= 128 words) into ascending indices,
@@ -204,8 +204,9 @@ __device__ int wave_compact(const uint32_t* bits, int nw, int32_t* out, int pad_
 
 // One workgroup per (selection row, KV group, batch).  Thread t owns the
 // candidates j = t + 256*u.  Per (head, band) channel: block-wide max, sum of
-// exp2 (logits are in log2 units), then the group score s[j] = sum over
-// channels of w * exp2(z - M) / S in a fixed channel order, kept in registers.
+// exp2 (logits are in log2 units; summed in the order block_sum_lanes_n
+// fixes), then the group score s[j] = sum over channels of w * exp2(z - M) / S
+// in a fixed channel order, kept in registers.
 // The scores go to LDS as order-preserving keys and one wavefront takes the k'
 // best free candidates (ties -> lower index; wave_topk) and adds the forced
 // blocks.  Blocks with one selection row write their sorted list directly;
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
   constexpr int KPL = 4 * U;                          // keys per lane of the selecting wave
   __shared__ uint32_t keys_sh[kPickThreads * U];
   __shared__ float red[2 * kPickChanBatch * 4];
+  __shared__ float red2[kPickChanBatch * kPickThreads];
   __shared__ __attribute__((aligned(16))) uint32_t cand_sh[64];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
           sm[cc] += z[cc][u];
         }
       }
-      block_sum_n<CC>(sm, nb, red, CC);
+      block_sum_lanes_n<CC>(sm, red2);
 #pragma unroll
       for (int cc = 0; cc < CC; ++cc) {
         if (c0 + cc >= nchan) continue;
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(PickArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) s[u] = fmaf(z[cc][u], inv, s[u]);
       }
-      __syncthreads();                                  // red[] is reused by the next batch
+      __syncthreads();                                  // red[] and red2[] are reused by the next batch
     }
     // keys: free candidates only; scores are >= 0, so float bits order like values
 #pragma unroll

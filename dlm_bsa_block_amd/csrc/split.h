@@ -14,6 +14,7 @@ constexpr int kDecTok = 32;         // list tokens per decode chunk (4 waves x 8
 constexpr int kDecMaxItems = 512;   // decode slices per (row, group)
 constexpr int kDecMinSlice = 32;    // list tokens per decode slice, at least
 constexpr int kSplitBlocks = 8;     // list entries per MFMA split workgroup
+constexpr int kDenSplitBlocks = 16; // the same in the fused denoising step (its workgroups also pick)
 constexpr int kCombMaxItems = 512;  // split slices the combine can merge
 
 struct DecArgs {

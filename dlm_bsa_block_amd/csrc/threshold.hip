@@ -71,7 +71,7 @@ __global__ __launch_bounds__(NW * 64, 1) void threshold_kernel(ThrArgs a) {
   const int jmax = a.causal ? min(a.NKT - 1, last_row / kTile) : a.NKT - 1;
 
   bf16x8 qf[8];
-  load_q_frag(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)row * a.qsl, valid, qf);
+  load_q_frag(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)min(row, a.Lq - 1) * a.qsl, valid, qf);
   int kofs[8], vofs[8];
   k_offsets(kofs);
   v_offsets(vofs);

@@ -111,20 +111,29 @@ __device__ uint64_t wave_topk(const uint32_t (&k)[KPL], int kp, int n_free, uint
     const int n0 = (int)lane_read(incl, 63);
     if (n0 <= 64) {
       int pos = (int)(incl - c);
+      cand[lane] = 0u;                       // slots past n0 stay 0: below every gathered key
+      wave_sync_lds();
 #pragma unroll
       for (int e = 0; e < KPL; ++e)
         if (k[e] >= t0) cand[pos++] = k[e];
       wave_sync_lds();
-      const uint32_t mine = lane < n0 ? cand[lane] : 0u;
-      // rank = keys that outrank this one: larger, or equal and earlier in block order
+      const uint32_t mine = cand[lane];
+      // rank = keys that outrank this one: larger, or equal and earlier in block order (a zero
+      // slot outranks no gathered key).  The slots are read 32 at a time, all requested before
+      // the first compare.
       int rank = 0;
-      for (int m0 = 0; m0 < n0; m0 += 4) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(cand + m0);
+      for (int m0 = 0; m0 < n0; m0 += 32) {
+        u32x4 q[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int m = m0 + t;
-          rank += (m < n0 && (q[t] > mine || (q[t] == mine && m < lane))) ? 1 : 0;
-        }
+        for (int i = 0; i < 8; ++i) q[i] = *reinterpret_cast<const u32x4*>(cand + m0 + 4 * i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int m = m0 + 4 * i + t;
+            rank += (q[i][t] > mine) ? 1 : 0;
+            rank += (q[i][t] == mine && m < lane) ? 1 : 0;
+          }
       }
       const uint64_t at = __ballot(lane < n0 && rank == kp - 1);
       T = lane_read(mine, __ffsll((unsigned long long)at) - 1);
