@@ -298,8 +298,9 @@ def bench_dlm(torch, bsa, synth, reps):
         def attend():
             bsa.bsa_sparse_attention_fwd(q, k, v, idx, cnt, ap, row_mask=mask, o=o, lse=lse, workspace=ws_att)
 
-        t_step = time_calls(torch, step, reps)
-        t_att = time_calls(torch, attend, reps)
+        # GPU time of the launches (graph replays): the host's launch gaps are not the kernels' cost
+        t_step = time_graph(torch, step, reps)
+        t_att = time_graph(torch, attend, reps)
         u = cnt.cpu().numpy()[0, :, 0]
         ubytes = int(u.sum()) * 64 * D * 2 * 2
         out[mode] = dict(us_per_step=round(t_step, 2), attention_us=round(t_att, 2),

@@ -219,7 +219,7 @@ def bsa_select_blocks_refresh(k, refresh_block: int, q, k_mean, p: BsaSelectPara
     qd, kd = tensor_desc(q), tensor_desc(k)
     need = lib().bsa_select_workspace_bytes(ctypes.byref(qd), Hkv, NB, ctypes.byref(p))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)   # no initial contents needed
     check(lib().bsa_select_blocks_refresh(ctypes.byref(kd), refresh_block, ctypes.byref(qd), k_mean.data_ptr(),
                                           _ptr(k_energy), Hkv, NB, ctypes.byref(p), _ptr(row_mask), idx.data_ptr(),
                                           cnt.data_ptr(), _ptr(rp), workspace.data_ptr(), workspace.numel(),
@@ -316,7 +316,7 @@ def bsa_window_decode_fwd(q, k, v, idx, cnt, p: BsaAttnParams, window: int, gate
     qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
     need = bsa_window_decode_workspace_bytes(q, k, p, window)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)   # no initial contents needed
     check(lib().bsa_window_decode_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),
                                       cnt.data_ptr(), ctypes.byref(p), window, _ptr(gates), ctypes.byref(od),
                                       lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),

@@ -646,10 +646,6 @@ static bsa_status validate_denoise_step(const bsa_tensor* q, const bsa_tensor* k
   ap.cap = p->cap;
   if ((st = validate_attention(q, k, v, &ap, pl)) != BSA_OK) return st;
   if (pl.kind != 2) return fail(BSA_ERR_UNSUPPORTED, "the denoising block does not fit the split gather");
-  // the fused gather's workgroups each pick the whole list: fewer of them, with longer slices
-  pl.items = (int)ceil_div(p->cap, kDenSplitBlocks);
-  const size_t n = (size_t)pl.B * pl.Hkv * pl.NQB * pl.items * pl.qv;
-  pl.part_bytes = align256(n * pl.D * 4) + align256(n * 2 * 4);
   return BSA_OK;
 }
 

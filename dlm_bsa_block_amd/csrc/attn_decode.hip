@@ -214,6 +214,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
                                   : reinterpret_cast<const uint8_t*>(a.part_ml);   // any readable byte
   const uint8_t rbyte = *rmp;
   const bool in_range = c < QVC && qv < QV && row < a.Lq;
+  // a workgroup whose rows are all stable has no partials to merge (none were written): it leaves
+  // before requesting any, rather than pulling unwritten slots from memory
+  if (a.row_mask && !__syncthreads_or(in_range && rbyte != 0)) return;
   bool live = false;                               // set once the first batch is requested
   const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + qb;
   const int64_t p0 = li * a.items;

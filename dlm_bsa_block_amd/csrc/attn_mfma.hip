@@ -70,7 +70,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   __shared__ int n_qv_sh;
   __shared__ uint64_t pflags_sh[PICK ? NW : 1][64];
   __shared__ __attribute__((aligned(16))) uint32_t pcand_sh[PICK ? NW : 1][64];
-  __shared__ int slice_sh[PICK ? kDenSplitBlocks : 1];
+  __shared__ int slice_sh[PICK ? kSplitBlocks : 1];
   __shared__ int n_list_sh;
 
   const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31;
@@ -136,7 +136,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     // its fragments are zeroed where they are first needed, so nothing waits for the loads here
     load_q_frag_raw(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)min(row, a.Lq - 1) * a.qsl, qf);
   };
-  int n_list, e0 = 0, e1;
+  int n_list = 0, e0 = 0, e1;
+  if constexpr (!PICK) n_list = a.cnt[li];         // requested before the row mask and the queries
   if constexpr (PICK) {
     stage_qv();
     setup_q();                                     // the query loads overlap the picks
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
         const int e = __ffsll((unsigned long long)f) - 1;
         f &= f - 1;
         const int j = 4 * PU * lane + e;
-        if (pos >= s0 && pos < s1 && pos - s0 < kDenSplitBlocks) slice_sh[pos - s0] = j;   // per <= kDenSplitBlocks
+        if (pos >= s0 && pos < s1 && pos - s0 < kSplitBlocks) slice_sh[pos - s0] = j;   // per <= kSplitBlocks
         if (item == 0) out[pos] = j;
         ++pos;
       }
@@ -173,8 +174,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     }
     __syncthreads();
     n_list = n_list_sh;
-  } else {
-    n_list = a.cnt[li];
+  } else if (SPLIT) {
+    // the active rows and their query loads do not depend on the list: both overlap its length's load
+    stage_qv();
+    setup_q();
   }
   e1 = n_list;
   if (SPLIT) {
@@ -184,9 +187,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     e0 = item * per;
     if (e0 >= n_list) return;
     e1 = min(n_list, e0 + per);
-    if constexpr (!PICK) stage_qv();
   }
-  if constexpr (!PICK) setup_q();
+  if (!SPLIT) setup_q();
   zero_q_frag(valid, qf);
   const int qpos = a.q_pos0 + row;
   // smallest query position of the wave (for deciding whether a tile needs the causal mask)

@@ -13,8 +13,7 @@ namespace bsa {
 constexpr int kDecTok = 32;         // list tokens per decode chunk (4 waves x 8 tokens)
 constexpr int kDecMaxItems = 512;   // decode slices per (row, group)
 constexpr int kDecMinSlice = 32;    // list tokens per decode slice, at least
-constexpr int kSplitBlocks = 8;     // list entries per MFMA split workgroup
-constexpr int kDenSplitBlocks = 16; // the same in the fused denoising step (its workgroups also pick)
+constexpr int kSplitBlocks = 16;    // list entries per MFMA split workgroup, at most
 constexpr int kCombMaxItems = 512;  // split slices the combine can merge
 
 struct DecArgs {

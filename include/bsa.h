@@ -451,11 +451,7 @@ bsa_status bsa_block_attention_merge(const bsa_tensor* q, const bsa_tensor* kb, 
  *                     p->q_pos0, p->causal, p->cap}, row_mask, cache_o,
  *                     cache_lse, ...);
  *   bsa_block_attention_merge(q, kb, vb, p->scale, cache_o, cache_lse, o, lse);
- * row_mask, mse, idx and cnt bit for bit (the same arithmetic in the same
- * order); the cache and O / LSE to the rounding of the probabilities (the
- * fused attention cuts the list into slices of up to 16 blocks rather than
- * 8, and P enters the P.V products in bf16 relative to each slice's running
- * maximum).
+ * bit for bit: the same arithmetic in the same order.
  * q, q_prev [B, Hq, R, D] bf16, D = 128, 1 <= R <= 32, R * Hq / Hkv <= 128;
  * k, v [B, Hkv, L, D] bf16 (the prefix), NB = ceil(L / p->kv_block) <= 4096,
  * kv_block 64 or 128; k_mean [B, Hkv, NB, D] f32 (bsa_build_block_summaries

@@ -6,10 +6,8 @@ Per sparse step, both paths start from the same prefix cache:
   * against bsa_active_rows + bsa_select_blocks(row_mask) +
     bsa_sparse_attention_fwd(row_mask, into the cache) +
     bsa_block_attention_merge: the row mask, the MSE and the list must be the
-    same bits (same arithmetic, same order); the rewritten cache and O / LSE
-    agree within the oracle's bounds (the fused gather cuts the list into
-    longer slices, and P enters the P.V products in bf16 relative to each
-    slice's running maximum), and stable rows' cache entries keep their bits;
+    same bits, and so must the rewritten cache and O / LSE (the same
+    arithmetic in the same order, the list cut into the same slices);
   * against the oracle, carrying the oracle's own cache across the steps: the
     mask exactly, the union list within the 1e-6 tie band of the active rows'
     picks, O and LSE within the fp32 bounds on the lists the GPU chose.
@@ -37,13 +35,6 @@ def bsa():
 
 def _sync():
     torch.cuda.synchronize()
-
-
-def _close(o_a, o_b, l_a, l_b, where):
-    """Two split-KV groupings of the same attention: P enters the P.V products in bf16, relative to
-    each slice's running maximum, so the groupings agree to that rounding (the oracle's bounds)."""
-    check_outputs(from_dev(o_a), from_dev(o_b).astype(np.float64), l_a.cpu().numpy(),
-                  l_b.cpu().numpy().astype(np.float64), where)
 
 
 def _select_params(bsa, p, R, D, causal=None):
@@ -112,11 +103,8 @@ def _run_steps(bsa, w, theta=None, o_f32=True, causal=None, oracle=True, steps=N
             for g in range(Hkv):
                 c = int(cnt_s[b, g, 0])
                 assert torch.equal(idx_f[b, g, 0, :c], idx_s[b, g, 0, :c]), f"{where}: list b{b} g{g}"
-        stable = mask_s == 0
-        assert torch.equal(fo[:, :, stable[0]], cache_o[:, :, stable[0]]), where + ": stable rows' cache"
-        assert torch.equal(fl[:, :, stable[0]], cache_l[:, :, stable[0]]), where + ": stable rows' cache lse"
-        _close(fo, cache_o, fl, cache_l, where + ": prefix cache")
-        _close(o_f.float(), o_s.float(), l_f, l_s, where + ": output")
+        assert torch.equal(fo, cache_o) and torch.equal(fl, cache_l), where + ": prefix cache"
+        assert torch.equal(o_f, o_s) and torch.equal(l_f, l_s), where + ": output"
         n_act = int(mask_f.sum().item())
         stats.append(dict(active=n_act, list_blocks=cnt_f[0, :, 0].cpu().tolist()))
         if oracle:
