@@ -542,6 +542,94 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
   }
 }
 
+// Block logits on the matrix cores (raw bf16 query rows, D = 128, one band):
+// Z = Q . Kmean^T per 32 x 32 tile with v_mfma_f32_32x32x16_bf16.  The query
+// rows are bf16 already; each f32 summary x is split exactly into three bf16
+// parts by truncation: hi = the top 8 significand bits of x, mid = the top 8 of
+// x - hi, lo = x - hi - mid (at most 8 bits left; both differences are exact
+// in fp32).  Every product is then exact and only the fp32 accumulation
+// rounds, as in the vector form.  One workgroup = 4 waves over 32 query vectors x 128 blocks, each wave
+// one 32 x 32 tile; the operands go straight from memory into registers (every
+// load requested before the first product), and no LDS is used.
+__global__ __launch_bounds__(256) void logits_mfma_kernel(const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh,
+                                                          int64_t qsl, const float* __restrict__ k_mean, int NB,
+                                                          int Rtot, int G, int Hkv, float scale, int causal,
+                                                          int q_block, int kv_block, int q_pos0, int Lq,
+                                                          float* __restrict__ Z, ActiveRowsArgs act) {
+  if (act.a != nullptr && (int)blockIdx.z >= act.z0) {
+    __shared__ float sh4[4];
+    const int k = blockIdx.z - act.z0, b = k / act.slices;
+    const int r = (k - b * act.slices) * (gridDim.x * gridDim.y) + blockIdx.y * gridDim.x + blockIdx.x;
+    if (r < act.R) active_row_job<BSA_BF16>(act, r, b, sh4);
+    return;
+  }
+  constexpr int D = 128;
+  const int NBp = (NB + 3) & ~3;
+  const int M = Rtot * G;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c32 = lane & 31, hi = lane >> 5;
+  const int m0 = blockIdx.y * 32, j0 = blockIdx.x * 128 + w * 32;
+  const int bg = blockIdx.z, b = bg / Hkv, g = bg - b * Hkv;
+  if (causal) {
+    // the tile's last row sees blocks up to jmax (the candidates of a raw row are its query block's)
+    const int rmax = min(M - 1, m0 + 31) / G;
+    const int last_row = min((rmax / q_block + 1) * q_block, Lq) - 1;
+    if (j0 > (q_pos0 + last_row) / kv_block) return;   // uniform over the wave
+  }
+  // operands: query vector m0 + c32 (row m / G, head g G + m % G) and block j0 + c32, dims 16 t + 8 hi ..
+  const int m = min(m0 + c32, M - 1), row = m / G, hl = m - row * G;
+  const uint16_t* qp = q + (int64_t)b * qsb + (int64_t)(g * G + hl) * qsh + (int64_t)row * qsl + 8 * hi;
+  const float* kp = k_mean + (((int64_t)b * Hkv + g) * NB + min(j0 + c32, NB - 1)) * D + 8 * hi;
+  bf16x8 qa[8];
+  f32x4 kv[8][2];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) qa[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    kv[t][0] = *reinterpret_cast<const f32x4*>(kp + 16 * t);
+    kv[t][1] = *reinterpret_cast<const f32x4*>(kp + 16 * t + 4);
+  }
+  // every load lands before the first product (left to itself the compiler issues the later k-steps'
+  // loads between the products, each then a round trip of its own)
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    asm volatile("" : "+v"(qa[t]));
+    asm volatile("" : "+v"(kv[t][0]), "+v"(kv[t][1]));
+  }
+  f32x16 acc_hi = f32x16{}, acc_lo = f32x16{};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    uint32_t xb[8], r1b[8], r2b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = kv[t][e >> 2][e & 3];
+      xb[e] = __float_as_uint(x);
+      const float r1 = x - __uint_as_float(xb[e] & 0xFFFF0000u);
+      r1b[e] = __float_as_uint(r1);
+      r2b[e] = __float_as_uint(r1 - __uint_as_float(r1b[e] & 0xFFFF0000u));
+    }
+    // bf16 pairs: the upper halves of two words (the truncations; r2 has no lower half)
+    u32x4 ph, pm, pl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ph[e] = __builtin_amdgcn_perm(xb[2 * e + 1], xb[2 * e], 0x07060302u);
+      pm[e] = __builtin_amdgcn_perm(r1b[2 * e + 1], r1b[2 * e], 0x07060302u);
+      pl[e] = __builtin_amdgcn_perm(r2b[2 * e + 1], r2b[2 * e], 0x07060302u);
+    }
+    acc_hi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], __builtin_bit_cast(bf16x8, ph), acc_hi, 0, 0, 0);
+    acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], __builtin_bit_cast(bf16x8, pm), acc_lo, 0, 0, 0);
+    acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], __builtin_bit_cast(bf16x8, pl), acc_lo, 0, 0, 0);
+  }
+  // lane: block j0 + c32; element i: query vector m0 + 8 (i / 4) + 4 hi + i % 4
+  const int j = j0 + c32;
+  if (j >= NB) return;
+  float* zb = Z + (((int64_t)b * Hkv + g) * Rtot * G) * NBp + j;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int mm = m0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+    if (mm < M) zb[(int64_t)mm * NBp] = (acc_hi[i] + acc_lo[i]) * scale;
+  }
+}
+
 // ------------------------------------------------------------------- host ---
 bool plan_select(const bsa_tensor& q, int NB, const bsa_select_params& p, SelectPlan& pl) {
   pl.B = q.B;
@@ -625,6 +713,19 @@ static void launch_logits(const bsa_tensor& q, const float* k_mean, const bsa_se
     if (M <= 8) BSA_LOGITS(DT, DD, 32, 8, 1, 1, DUAL);                   \
     else BSA_LOGITS(DT, DD, 16, 16, 2, 4, DUAL);                         \
   } while (0)
+  if (M > 8 && q.dtype == BSA_BF16 && pl.D == 128 && !p.dual_band && !p.pooled_q && ra.block < 0) {
+    // raw bf16 rows in tiles of 32: the matrix cores (one band, no refresh)
+    dim3 grid((unsigned)ceil_div(NB, 128), (unsigned)ceil_div(M, 32), (unsigned)(pl.B * Hkv));
+    if (act.a) {
+      act.z0 = (int)grid.z;
+      act.slices = (int)ceil_div(act.R, (int64_t)grid.x * grid.y);
+      grid.z += (unsigned)(pl.B * act.slices);
+    }
+    hipLaunchKernelGGL(logits_mfma_kernel, grid, dim3(256), 0, s, reinterpret_cast<const uint16_t*>(qd),
+                       q.stride_b, q.stride_h, q.stride_l, k_mean, NB, Rtot, G, Hkv, scale2, p.causal, p.q_block,
+                       p.kv_block, p.q_pos0, pl.Lq, Z, act);
+    return;
+  }
 #define BSA_LOGITS_D(DT, DUAL)                                              \
   do {                                                                      \
     if (pl.D == 128) BSA_LOGITS_SHAPE(DT, 128, DUAL);                       \

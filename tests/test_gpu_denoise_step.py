@@ -140,6 +140,24 @@ def test_denoise_step_small(bsa):
     assert all(x["active"] == 4 for x in st)
 
 
+def _stack(wa, wb):
+    """Two denoising workloads of the same shapes as one of batch 2."""
+    cat = lambda x, y: np.concatenate([x, y], axis=0)
+    extra = dict(q_steps=[cat(x, y) for x, y in zip(wa.extra["q_steps"], wb.extra["q_steps"])],
+                 kb_steps=[cat(x, y) for x, y in zip(wa.extra["kb_steps"], wb.extra["kb_steps"])],
+                 vb_steps=[cat(x, y) for x, y in zip(wa.extra["vb_steps"], wb.extra["vb_steps"])])
+    return synth.Workload("dlm_denoise_steps_b2", wa.dtype, cat(wa.q, wb.q), cat(wa.k, wb.k), cat(wa.v, wb.v),
+                          dict(wa.params), extra)
+
+
+def test_denoise_step_batch_two(bsa):
+    """Two sequences in one call: different prefixes, queries and active rows per batch entry."""
+    w = _stack(synth.dlm_denoise_steps(seed=6, L=1024 + 64 + 5, n_needles=2, n_steps=3),
+               synth.dlm_denoise_steps(seed=9, L=1024 + 64 + 5, n_needles=2, n_steps=3))
+    st = _run_steps(bsa, w)
+    assert all(x["active"] == 8 for x in st)
+
+
 def test_denoise_step_bf16_out_causal(bsa):
     """bf16 output and the causal flag (the prefix lies before the block: every key stays visible)."""
     w = synth.dlm_denoise_steps(L=1024 + 64 + 3, n_needles=2, n_steps=3)
