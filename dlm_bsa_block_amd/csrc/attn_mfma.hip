@@ -137,7 +137,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     load_q_frag_raw(a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)min(row, a.Lq - 1) * a.qsl, qf);
   };
   int n_list = 0, e0 = 0, e1;
-  if constexpr (!PICK) n_list = a.cnt[li];         // requested before the row mask and the queries
+  // requested before the row mask and the queries (a count above the capacity is cut to it)
+  if constexpr (!PICK) n_list = min(a.cnt[li], a.cap);
   if constexpr (PICK) {
     stage_qv();
     setup_q();                                     // the query loads overlap the picks
@@ -208,10 +209,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   const uint16_t* kbg = a.k + (int64_t)b * a.ksb + (int64_t)g * a.ksh;
   const uint16_t* vbg = a.v + (int64_t)b * a.vsb + (int64_t)g * a.vsh;
   const int32_t* list = a.idx + li * a.cap;
+  // a split slice's entries (at most kSplitBlocks), one per lane, read once: no list load inside the walk
+  int ent = -1;
+  if constexpr (SPLIT) {
+    if constexpr (PICK) ent = lane < e1 - e0 ? slice_sh[lane] : -1;
+    else ent = lane < e1 - e0 ? list[e0 + lane] : -1;
+  }
   // rows of tile u (of list entry e0 + u / SUB) inside the KV sequence (0 for
   // an index outside it, or a part beyond the end: nothing is read)
   auto entry_rows = [&](int u, int& key0) {
-    const int j = PICK ? slice_sh[u / SUB] : list[e0 + u / SUB];
+    const int j = SPLIT ? __builtin_amdgcn_readlane(ent, u / SUB) : list[e0 + u / SUB];
     const int blk0 = j * (KVB * SUB);
     key0 = blk0 + (u % SUB) * KVB;
     return (j < 0 || blk0 >= a.L || key0 >= a.L) ? 0 : min(KVB, a.L - key0);
@@ -224,6 +231,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
     issue_tile<KVB, NW>(kbg + (int64_t)key0 * a.ksl, a.ksl, nk, lds0 + (uint32_t)(buf * 2 * TILE * 2));
     issue_tile<KVB, NW>(vbg + (int64_t)key0 * a.vsl, a.vsl, nk, lds0 + (uint32_t)((buf * 2 + 1) * TILE * 2));
   };
+
 
   const int nt = (e1 - e0) * SUB;
   // largest query position of the wave: a tile wholly after it is skipped
