@@ -548,9 +548,12 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint8_t* __restrict__
 // parts by truncation: hi = the top 8 significand bits of x, mid = the top 8 of
 // x - hi, lo = x - hi - mid (at most 8 bits left; both differences are exact
 // in fp32).  Every product is then exact and only the fp32 accumulation
-// rounds, as in the vector form.  One workgroup = 4 waves over 32 query vectors x 128 blocks, each wave
-// one 32 x 32 tile; the operands go straight from memory into registers (every
-// load requested before the first product), and no LDS is used.
+// rounds, as in the vector form.  One workgroup = 4 waves over 128 query
+// vectors x 32 blocks, each wave one 32 x 32 tile: the waves share the blocks'
+// summaries (read from memory once per workgroup, the other waves hit the
+// cache) and each summary is read by one workgroup only.  The operands go
+// straight from memory into registers (every load requested before the first
+// product), and no LDS is used.
 __global__ __launch_bounds__(256) void logits_mfma_kernel(const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh,
                                                           int64_t qsl, const float* __restrict__ k_mean, int NB,
                                                           int Rtot, int G, int Hkv, float scale, int causal,
@@ -567,7 +570,8 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(const uint16_t* __rest
   const int NBp = (NB + 3) & ~3;
   const int M = Rtot * G;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c32 = lane & 31, hi = lane >> 5;
-  const int m0 = blockIdx.y * 32, j0 = blockIdx.x * 128 + w * 32;
+  const int m0 = blockIdx.y * 128 + w * 32, j0 = blockIdx.x * 32;
+  if (m0 >= M) return;                              // uniform over the wave; no barrier follows
   const int bg = blockIdx.z, b = bg / Hkv, g = bg - b * Hkv;
   if (causal) {
     // the tile's last row sees blocks up to jmax (the candidates of a raw row are its query block's)
@@ -715,7 +719,7 @@ static void launch_logits(const bsa_tensor& q, const float* k_mean, const bsa_se
   } while (0)
   if (M > 8 && q.dtype == BSA_BF16 && pl.D == 128 && !p.dual_band && !p.pooled_q && ra.block < 0) {
     // raw bf16 rows in tiles of 32: the matrix cores (one band, no refresh)
-    dim3 grid((unsigned)ceil_div(NB, 128), (unsigned)ceil_div(M, 32), (unsigned)(pl.B * Hkv));
+    dim3 grid((unsigned)ceil_div(NB, 32), (unsigned)ceil_div(M, 128), (unsigned)(pl.B * Hkv));
     if (act.a) {
       act.z0 = (int)grid.z;
       act.slices = (int)ceil_div(act.R, (int64_t)grid.x * grid.y);
