@@ -269,11 +269,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
 #pragma unroll
           for (int u = 0; u < BATCH; ++u) {
             const float mv = __uint_as_float((uint32_t)mlr[u]);
-            if (it0 + u < n && mv != -INFINITY) {
-              const float wgt = fast_exp2(mv - bm);
-              L = fmaf(__uint_as_float((uint32_t)(mlr[u] >> 32)), wgt, L);
-              acc = fmaf(ov[u], wgt, acc);
-            }
+            // selects, not a branch per slice (a skipped slot's stale values are never multiplied in)
+            const bool use = it0 + u < n && mv != -INFINITY;
+            const float wgt = fast_exp2(mv - bm);
+            const float l2 = fmaf(__uint_as_float((uint32_t)(mlr[u] >> 32)), wgt, L), a2 = fmaf(ov[u], wgt, acc);
+            L = use ? l2 : L;
+            acc = use ? a2 : acc;
           }
           M = bm;
         }

@@ -538,12 +538,15 @@ __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
         for (int u = 0; u < BATCH; ++u) {
           const uint64_t ml = mlr[u];
           const float mv = __uint_as_float((uint32_t)ml);
-          if (it0 + u < n_valid && mv != -INFINITY) {
-            const float wgt = fast_exp2(mv - bm);
-            L[pp] = fmaf(__uint_as_float((uint32_t)(ml >> 32)), wgt, L[pp]);
-            acc0[pp] = fmaf(o0[u], wgt, acc0[pp]);
-            acc1[pp] = fmaf(o1[u], wgt, acc1[pp]);
-          }
+          // selects, not a branch per slice: a slot past the count or with nothing visible keeps
+          // the sums as they are (its stale values are never multiplied in)
+          const bool use = it0 + u < n_valid && mv != -INFINITY;
+          const float wgt = fast_exp2(mv - bm);
+          const float l2 = fmaf(__uint_as_float((uint32_t)(ml >> 32)), wgt, L[pp]);
+          const float a0 = fmaf(o0[u], wgt, acc0[pp]), a1 = fmaf(o1[u], wgt, acc1[pp]);
+          L[pp] = use ? l2 : L[pp];
+          acc0[pp] = use ? a0 : acc0[pp];
+          acc1[pp] = use ? a1 : acc1[pp];
         }
         M[pp] = bm;
       }

@@ -300,12 +300,14 @@ __global__ __launch_bounds__(320) void den_merge_kernel(DenMergeArgs a) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
           const float mv = __uint_as_float((uint32_t)mlr[u]);
-          if (it0 + u < nvalid && mv != -INFINITY) {
-            const float wgt = fast_exp2(mv - bm);
-            L = fmaf(__uint_as_float((uint32_t)(mlr[u] >> 32)), wgt, L);
-            acc0 = fmaf(o0[u], wgt, acc0);
-            acc1 = fmaf(o1[u], wgt, acc1);
-          }
+          // selects, not a branch per slice (a skipped slot's stale values are never multiplied in)
+          const bool use = it0 + u < nvalid && mv != -INFINITY;
+          const float wgt = fast_exp2(mv - bm);
+          const float l2 = fmaf(__uint_as_float((uint32_t)(mlr[u] >> 32)), wgt, L);
+          const float a0 = fmaf(o0[u], wgt, acc0), a1 = fmaf(o1[u], wgt, acc1);
+          L = use ? l2 : L;
+          acc0 = use ? a0 : acc0;
+          acc1 = use ? a1 : acc1;
         }
         M = bm;
       }
