@@ -182,7 +182,8 @@ def bsa_sparse_attention_fwd(q, k, v, idx, cnt, p: BsaAttnParams, row_mask=None,
     qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
     need = lib().bsa_attention_workspace_bytes(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(p))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)   # no initial contents needed
+        # the arrival counters at its front must be zero on the first call (calls leave them zero)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     check(lib().bsa_sparse_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),
                                          cnt.data_ptr(), ctypes.byref(p), _ptr(row_mask), ctypes.byref(od),
                                          lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),

@@ -292,6 +292,7 @@ static bsa_status validate_attention(const bsa_tensor* q, const bsa_tensor* k, c
   if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(BSA_ERR_INVALID, "scale must be finite and > 0");
   if (p->q_pos0 < 0) return fail(BSA_ERR_INVALID, "negative q_pos0");
   plan_attention(*q, *k, *p, pl);
+  plan_attention_counters(pl);
   if (pl.kind == 0) {
     if (pl.G != 1 && pl.G != 2 && pl.G != 4 && pl.G != 8)
       return fail(BSA_ERR_UNSUPPORTED, "decode path needs Hq/Hkv in {1, 2, 4, 8}, got %d", pl.G);
@@ -313,7 +314,7 @@ static bsa_status validate_attention(const bsa_tensor* q, const bsa_tensor* k, c
 size_t bsa_attention_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, const bsa_attn_params* p) {
   AttnPlan pl;
   if (!k || validate_attention(q, k, k, p, pl) != BSA_OK) return 0;
-  return pl.part_bytes;
+  return pl.arrival_bytes + pl.part_bytes;
 }
 
 bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const int32_t* idx,
@@ -327,18 +328,20 @@ bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, co
   if (!same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
     return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
   if (!idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "idx, cnt and lse are required");
-  if (pl.part_bytes && (!workspace || workspace_bytes < pl.part_bytes))
-    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, pl.part_bytes);
-  if (pl.part_bytes && !aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
+  const size_t need = pl.arrival_bytes + pl.part_bytes;
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (need && !aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
   if (q->L == 0) { g_err[0] = 0; return BSA_OK; }
   launch_attention(*q, *k, *v, idx, cnt, *p, pl, row_mask, *o, lse, workspace, static_cast<hipStream_t>(stream));
   return check_launch("sparse attention");
 }
 
 // ------------------------------------------ attention without a workspace ---
-// bsa_sparse_attention_fwd_noalloc keeps its split-KV partials in this array
-// instead of a caller's workspace.  Each GPU the library runs on holds its own
-// copy until the process ends.  Host code never passes the array's name to a
+// bsa_sparse_attention_fwd_noalloc keeps its arrival counters and split-KV
+// partials in this array instead of a caller's workspace.  Each GPU the library
+// runs on holds its own copy until the process ends; it starts zeroed, and
+// every call leaves the counters zero.  Host code never passes the array's name to a
 // kernel: it asks for the device address once per device and uses that.
 constexpr size_t kScratchBytes = size_t(64) << 20;
 constexpr int kScratchDevices = 64;
@@ -384,13 +387,14 @@ bsa_status bsa_sparse_attention_fwd_noalloc(const bsa_tensor* q, const bsa_tenso
   if (!same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
     return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
   if (!idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "idx, cnt and lse are required");
-  if (pl.part_bytes > kScratchBytes)
-    return fail(BSA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu",
-                pl.part_bytes, kScratchBytes);
+  const size_t need = pl.arrival_bytes + pl.part_bytes;
+  if (need > kScratchBytes)
+    return fail(BSA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu", need,
+                kScratchBytes);
   if (q->L == 0) { g_err[0] = 0; return BSA_OK; }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   void* ws = nullptr;
-  if (pl.part_bytes && (st = scratch_for_stream(s, &ws)) != BSA_OK) return st;
+  if (need && (st = scratch_for_stream(s, &ws)) != BSA_OK) return st;
   launch_attention(*q, *k, *v, idx, cnt, *p, pl, row_mask, *o, lse, ws, s);
   return check_launch("sparse attention (static scratch)");
 }

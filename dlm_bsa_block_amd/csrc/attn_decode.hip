@@ -7,17 +7,20 @@
 // G query heads of the group share each K/V load (NSA implementation-challenges
 // section: GQA-aware access).  A thread's K and V loads are issued before any
 // arithmetic.  Each workgroup writes an unnormalised partial (m, l, acc) per
-// query head; a combine kernel merges the partials in ascending slice order,
-// so the result does not depend on scheduling.  (Merging inside the last
-// workgroup to finish would need a device-scope fence per workgroup, which
-// costs far more than the extra kernel boundary on this chip.)
+// query head; the partials are merged in ascending slice order, so the result
+// does not depend on scheduling.  Without a sliding window the merge runs in the
+// same launch: partials go out with device-scope stores and the workgroup that
+// finishes a (row, group)'s last slice merges them (a kernel boundary costs
+// more than the counter and the device-scope loads).  With the window's second
+// branch, or for token lists, a combine kernel merges them.
 #include "common.h"
 #include "internal.h"
 #include "split.h"
+#include "split_merge.h"
 
 namespace bsa {
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool MERGE>
 __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   constexpr int ES = DT == BSA_BF16 ? 2 : 4;
   constexpr int LPT = D / 8;            // lanes per token
@@ -26,6 +29,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   constexpr int PASSES = TPW / TPP;
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sm_acc[4][G][D];
+  __shared__ int last_sh;
+  __shared__ __attribute__((aligned(16))) uint64_t ml_sh[G * 32];   // the merge's (m, l): [head][slice of the batch]
 
   const int item = blockIdx.x, qb = blockIdx.y, bg = blockIdx.z;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
@@ -75,7 +80,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     t_end = min(hi - lo, t_lo + a.tok_per_item);
     key0 = lo;
   } else {
-    if (ntok == 0) return;                              // the combine writes O = 0, LSE = -inf
+    if (MERGE && ntok == 0 && item == 0) {              // nothing selected: O = 0, LSE = -inf
+      const int Hq = a.Hkv * G;
+      for (int i = tid; i < G * D; i += 256) {
+        const int h = i / D, d = i - h * D;
+        const int64_t oi = (int64_t)b * a.osb + (int64_t)(g * G + h) * a.osh + (int64_t)row * a.osl + d;
+        if (a.o_f32) static_cast<float*>(a.o)[oi] = 0.f;
+        else static_cast<uint16_t*>(a.o)[oi] = 0;
+        if (d == 0) a.lse[((int64_t)b * Hq + g * G + h) * a.Lq + row] = -INFINITY;
+      }
+    }
+    if (ntok == 0) return;                              // (split path: the combine writes O = 0, LSE = -inf)
     if (t_begin >= ntok) return;                        // no slice of the list for this workgroup
     t_end = min(ntok, t_begin + a.tok_per_item);
   }
@@ -180,12 +195,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
         lsum = fmaf(sm_l[ww][h], wgt, lsum);
       }
     }
-    a.part_o[(pbase + h) * D + d] = o;
-    if (d == 0) {
-      a.part_ml[(pbase + h) * 2] = M;
-      a.part_ml[(pbase + h) * 2 + 1] = lsum;
+    if (MERGE) {
+      st_dev(a.part_o + (pbase + h) * D + d, o);
+      if (d == 0) st_dev2(a.part_ml + (pbase + h) * 2, M, lsum);
+    } else {
+      a.part_o[(pbase + h) * D + d] = o;
+      if (d == 0) {
+        a.part_ml[(pbase + h) * 2] = M;
+        a.part_ml[(pbase + h) * 2 + 1] = lsum;
+      }
     }
   }
+  if (!MERGE) return;
+  // every workgroup past this point holds one of the list's sel_items slices (the others returned)
+  if (!arrive_last(a.arrivals + li * kArrivalStride, sel_items, last_sh)) return;
+  const int Hq = a.Hkv * G;
+  merge_published<G, D>(a.part_o + li * a.items * G * D, a.part_ml + li * a.items * G * 2, sel_items, ml_sh, a.o,
+                        a.o_f32, (int64_t)b * a.osb + (int64_t)(g * G) * a.osh + (int64_t)row * a.osl, a.osh,
+                        a.lse + ((int64_t)b * Hq + g * G) * a.Lq + row, a.Lq);
 }
 
 // Merge the split partials of active (row, head) pairs of a query block in
@@ -338,7 +365,11 @@ void launch_combine(const CombArgs& a, int odt, int B, hipStream_t s) {
 
 void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s) {
   dim3 grid(a.items, a.NQB, B * a.Hkv);
-#define BSA_DEC(DT, DD, GG) hipLaunchKernelGGL((decode_kernel<DT, DD, GG>), grid, dim3(256), 0, s, a)
+#define BSA_DEC(DT, DD, GG)                                                                           \
+  do {                                                                                                \
+    if (a.arrivals) hipLaunchKernelGGL((decode_kernel<DT, DD, GG, true>), grid, dim3(256), 0, s, a);  \
+    else hipLaunchKernelGGL((decode_kernel<DT, DD, GG, false>), grid, dim3(256), 0, s, a);            \
+  } while (0)
 #define BSA_DEC_G(DT, DD)                              \
   do {                                                 \
     switch (G) {                                       \

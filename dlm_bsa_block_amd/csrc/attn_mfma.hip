@@ -22,6 +22,7 @@
 #include "mfma_tile.h"
 #include "pick.h"
 #include "split.h"
+#include "split_merge.h"
 
 namespace bsa {
 
@@ -711,6 +712,11 @@ bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_par
   return true;
 }
 
+void plan_attention_counters(AttnPlan& pl) {
+  pl.arrival_bytes = pl.part_bytes ? kArrivalBytes : 0;
+  pl.merge_in_launch = pl.kind == 0 && pl.part_bytes && (int64_t)pl.B * pl.Hkv * pl.NQB <= kArrivalRows;
+}
+
 // Attention of each query head over its own token list (FASA technical summary
 // sec. 2, focused attention: all dims, original positions): the decode split
 // with one list per query head (G = 1 per list, blocks of one token), the K/V
@@ -757,6 +763,10 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
                       const int32_t* cnt, const bsa_attn_params& p, const AttnPlan& pl, const uint8_t* row_mask,
                       const bsa_tensor& o, float* lse, void* ws, hipStream_t s, int win, const float* gates) {
   const float c2 = p.scale * kLog2e;
+  // without a window, the counters (if any) come first; the window decode plans none
+  uint32_t* arrivals = win == 0 && pl.arrival_bytes ? static_cast<uint32_t*>(ws) : nullptr;
+  if (win == 0) ws = static_cast<uint8_t*>(ws) + pl.arrival_bytes;
+  const bool merged = arrivals && pl.merge_in_launch;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = nullptr;
   if (pl.kind != 1) {
@@ -776,6 +786,11 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
     a.tok_per_item = pl.tok_per_item;
     a.c2 = c2; a.row_mask = row_mask; a.part_o = part_o; a.part_ml = part_ml;
     a.win = win;
+    if (merged) {
+      a.arrivals = arrivals;
+      a.o = o.data; a.o_f32 = o.dtype == BSA_F32; a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
+      a.lse = lse;
+    }
     launch_decode(a, q.dtype, pl.D, pl.G, pl.B, s);
   } else {
     GatherArgs a;
@@ -792,7 +807,7 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
     a.lse = lse; a.part_o = part_o; a.part_ml = part_ml; a.items = pl.items;
     launch_gather(a, p.kv_block, pl.kind == 2, s);
   }
-  if (pl.kind != 1) {
+  if (pl.kind != 1 && !merged) {
     CombArgs c;
     c.part_o = part_o; c.part_ml = part_ml; c.cnt = cnt; c.items = pl.items;
     if (pl.kind == 0) { c.unit_num = p.kv_block; c.unit_den = pl.tok_per_item; }

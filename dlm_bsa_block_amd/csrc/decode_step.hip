@@ -35,6 +35,7 @@
 #include "common.h"
 #include "internal.h"
 #include "split.h"
+#include "split_merge.h"
 #include "wave_select.h"
 
 namespace bsa {
@@ -64,21 +65,6 @@ struct DStepArgs {
   int64_t osb, osh, osl;
   float* lse;                     // [B][Hq][Lq]
 };
-
-// Device-scope (coherent across the XCDs' L2 caches) stores and loads: the
-// partials a workgroup hands to the merging one go through these, so no cache
-// write-back or invalidation is needed.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev2(float* p, float lo, float hi) {
-  const uint64_t v = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ f32x2 ld_dev2(const float* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return f32x2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
-}
 
 // ------------------------------------------------------------------ logits ---
 // Workgroup = 4 waves x 8 blocks; 8 lanes per block, D / 8 dims per lane.  The
@@ -458,116 +444,15 @@ __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
         lsum = fmaf(sm_l[ww][h], wgt, lsum);
       }
     }
-    __hip_atomic_store(a.part_o + (pbase + h) * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == 0) {
-      const uint64_t ml = (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(lsum) << 32);
-      __hip_atomic_store(reinterpret_cast<uint64_t*>(a.part_ml + (pbase + h) * 2), ml, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
+    st_dev(a.part_o + (pbase + h) * D + d, o);
+    if (d == 0) st_dev2(a.part_ml + (pbase + h) * 2, M, lsum);
   }
-  __builtin_amdgcn_s_waitcnt(0);                        // this wave's partial stores are done
-  __syncthreads();                                      // ... and every wave's
   const int n_valid = (int)((ntok + a.tok_per_item - 1) / a.tok_per_item);
-  if (tid == 0) {
-    const uint32_t before =
-        __hip_atomic_fetch_add(a.arrivals + rowi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_sh = (int)before == n_valid - 1;
-  }
-  __syncthreads();
-  if (!last_sh) return;
-  // ---- the last slice to finish merges all slices in order: two dims of one head per thread.
-  // Per batch of 32 slices, every thread loads one (m, l) pair into LDS and its own dims of
-  // the 32 partial O's (at most 33 loads in flight per thread, so none waits for a free
-  // counter slot), then merges with a running maximum as the separate combine does.
-  constexpr int BATCH = 32;
-  static_assert(BATCH * G <= 256, "one (m, l) pair per thread and batch");
-  constexpr int NPOS = G * D / 2;                       // (head, dim pair) positions
-  constexpr int PPT = (NPOS + 255) / 256;
-  float M[PPT], L[PPT], acc0[PPT], acc1[PPT];
-#pragma unroll
-  for (int pp = 0; pp < PPT; ++pp) { M[pp] = -INFINITY; L[pp] = 0.f; acc0[pp] = 0.f; acc1[pp] = 0.f; }
-  for (int it0 = 0; it0 < n_valid; it0 += BATCH) {
-    if (it0 > 0) __syncthreads();                       // the previous batch's LDS reads are done
-    uint64_t mlv = 0;
-    if (tid < BATCH * G) {                              // entry tid = (head, slice of the batch)
-      const int h = tid / BATCH, u = tid - h * BATCH;
-      const int it = min(it0 + u, n_valid - 1);
-      mlv = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.part_ml + ((rowi * a.items + it) * G + h) * 2),
-                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-#pragma unroll
-    for (int pp = 0; pp < PPT; ++pp) {
-      const int i = tid + 256 * pp;
-      // threads past the positions load a valid position too: loads under a branch would make
-      // the compiler wait for each one before the next
-      const int ic = min(i, NPOS - 1);
-      const int h = ic / (D / 2), d = 2 * (ic - h * (D / 2));
-      float o0[BATCH], o1[BATCH];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int it = min(it0 + u, n_valid - 1);
-        const int64_t pi = (rowi * a.items + it) * G + h;
-        const uint64_t ov = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.part_o + pi * D + d),
-                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        o0[u] = __uint_as_float((uint32_t)ov);
-        o1[u] = __uint_as_float((uint32_t)(ov >> 32));
-      }
-      if (pp == 0) {
-        if (tid < BATCH * G) ml_sh[tid] = mlv;
-        __syncthreads();
-      }
-      if (i < NPOS) {
-        // this head's (m, l) of the batch, read together (16-byte LDS reads)
-        uint64_t mlr[BATCH];
-#pragma unroll
-        for (int q = 0; q < BATCH / 2; ++q) {
-          const u32x4 t = *reinterpret_cast<const u32x4*>(&ml_sh[h * BATCH + 2 * q]);
-          mlr[2 * q] = (uint64_t)t[0] | ((uint64_t)t[1] << 32);
-          mlr[2 * q + 1] = (uint64_t)t[2] | ((uint64_t)t[3] << 32);
-        }
-        float bm = M[pp];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u)
-          if (it0 + u < n_valid) bm = fmaxf(bm, __uint_as_float((uint32_t)mlr[u]));
-        if (bm == -INFINITY) continue;
-        const float alpha = M[pp] == -INFINITY ? 0.f : fast_exp2(M[pp] - bm);
-        L[pp] *= alpha;
-        acc0[pp] *= alpha;
-        acc1[pp] *= alpha;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-          const uint64_t ml = mlr[u];
-          const float mv = __uint_as_float((uint32_t)ml);
-          // selects, not a branch per slice: a slot past the count or with nothing visible keeps
-          // the sums as they are (its stale values are never multiplied in)
-          const bool use = it0 + u < n_valid && mv != -INFINITY;
-          const float wgt = fast_exp2(mv - bm);
-          const float l2 = fmaf(__uint_as_float((uint32_t)(ml >> 32)), wgt, L[pp]);
-          const float a0 = fmaf(o0[u], wgt, acc0[pp]), a1 = fmaf(o1[u], wgt, acc1[pp]);
-          L[pp] = use ? l2 : L[pp];
-          acc0[pp] = use ? a0 : acc0[pp];
-          acc1[pp] = use ? a1 : acc1[pp];
-        }
-        M[pp] = bm;
-      }
-    }
-  }
-#pragma unroll
-  for (int pp = 0; pp < PPT; ++pp) {
-    const int i = tid + 256 * pp;
-    if (i >= NPOS) continue;
-    const int h = i / (D / 2), d = 2 * (i - h * (D / 2));
-    const float r0 = L[pp] > 0.f ? acc0[pp] / L[pp] : 0.f, r1 = L[pp] > 0.f ? acc1[pp] / L[pp] : 0.f;
-    const int64_t oi = (int64_t)b * a.osb + (int64_t)(g * G + h) * a.osh + (int64_t)row * a.osl + d;
-    if (a.o_f32) {
-      static_cast<float*>(a.o)[oi] = r0;
-      static_cast<float*>(a.o)[oi + 1] = r1;
-    } else {
-      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.o) + oi) = pack_bf16x2(r0, r1);
-    }
-    if (d == 0)
-      a.lse[((int64_t)b * a.Hkv * G + g * G + h) * a.Lq + row] = L[pp] > 0.f ? (M[pp] + log2f(L[pp])) * kLn2 : -INFINITY;
-  }
+  if (!arrive_last(a.arrivals + rowi * 32, n_valid, last_sh)) return;
+  // the last slice to finish merges all slices in order
+  merge_published<G, D>(a.part_o + rowi * a.items * G * D, a.part_ml + rowi * a.items * G * 2, n_valid, ml_sh,
+                        a.o, a.o_f32, (int64_t)b * a.osb + (int64_t)(g * G) * a.osh + (int64_t)row * a.osl, a.osh,
+                        a.lse + ((int64_t)b * a.Hkv * G + g * G) * a.Lq + row, a.Lq);
 }
 
 // ------------------------------------------------------------------- host ---

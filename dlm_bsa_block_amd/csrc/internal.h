@@ -117,7 +117,14 @@ struct AttnPlan {
   int tok_per_item;         // decode: list tokens per item
   int qv;                   // query vectors per (b, g, q-block) in split mode
   size_t part_bytes;
+  // bsa_sparse_attention_fwd's workspace: arrival counters at the front (kArrivalBytes, or 0 for
+  // a call without partials), then the partials; merge_in_launch: the decode split merges its
+  // slices in its own launch (counters there) instead of a combine launch
+  size_t arrival_bytes = 0;
+  bool merge_in_launch = false;
 };
+// Sets the entry point's counter region and whether the decode split merges in its launch.
+void plan_attention_counters(AttnPlan& pl);
 // win > 0 (decode only): a sliding window of win keys per row joins the list
 // (NSA sliding-window branch); gates [B][Hq][Lq][2] or null; lse then [B][Hq][Lq][2].
 bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_params& p, AttnPlan& pl, int win = 0);

@@ -30,6 +30,14 @@ struct DecArgs {
   float* part_ml;
   int win = 0;                    // > 0: items past the list's walk the win keys ending at the row
   int kv_div = 1;                 // lists per K/V head (per-query-head token lists: the group size)
+  // Non-null (win == 0 only): the slices are merged in the same launch by the last workgroup of
+  // each (row, group) to finish, counted on arrivals[li * kArrivalStride] (zero on entry, left
+  // zero), and O / LSE are written here; null: the partials wait for combine_kernel.
+  uint32_t* arrivals = nullptr;
+  void* o = nullptr;
+  int o_f32 = 0;
+  int64_t osb = 0, osh = 0, osl = 0;
+  float* lse = nullptr;           // [B][Hq][Lq]
 };
 
 struct CombArgs {

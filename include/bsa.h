@@ -238,8 +238,15 @@ bsa_status bsa_active_rows(const bsa_tensor* q_cur, const bsa_tensor* q_prev, fl
  * result before rounding); lse is [B, Hq, Lq] f32
  * contiguous.  Supported: bf16 with D = 128 and kv_block in {64, 128}; f32
  * or D = 64 only for single-row query blocks (decode).  workspace:
- * bsa_attention_workspace_bytes() bytes (split-KV partial results; no
- * initial contents needed; calls that overlap on one workspace race).
+ * bsa_attention_workspace_bytes() bytes: when nonzero, its first 65536
+ * bytes hold arrival counters and the rest the split-KV partial results.
+ * The counters must be ZERO on the first call with a workspace (clear it
+ * once after allocating it); every call leaves them zero, for calls of any
+ * shape, so they need no clearing after that -- unless the buffer has served
+ * anything else in between.  (Single-row query blocks merge their split-KV
+ * slices in the attention launch: the workgroup that finishes a row's last
+ * slice, found with these counters, merges them.)  Counters that are not zero
+ * give wrong outputs, not an error.  Calls that overlap on one workspace race.
  * ------------------------------------------------------------------------ */
 typedef struct {
   float scale;
@@ -261,16 +268,18 @@ bsa_status bsa_sparse_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, co
  * bsa_sparse_attention_fwd without a workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Arguments, results and errors as
- * bsa_sparse_attention_fwd; the split-KV partials go to a static device
- * array of bsa_noalloc_scratch_bytes() bytes (64 MiB) that each GPU the
- * library runs on holds until the process ends (its address is looked up
- * once per device, on the first call there).  The call allocates and frees
- * nothing.  Errors besides those of bsa_sparse_attention_fwd:
- * BSA_ERR_WORKSPACE when the call needs more scratch than that (the size
- * bsa_attention_workspace_bytes reports); BSA_ERR_INVALID when `stream`
- * belongs to a device other than the current one.  The array keeps the last
- * call's contents (no call needs them cleared); calls that overlap on one GPU
- * share it and race, so keep them on one stream or order them.
+ * bsa_sparse_attention_fwd; the arrival counters and split-KV partials go
+ * to a static device array of bsa_noalloc_scratch_bytes() bytes (64 MiB)
+ * that each GPU the library runs on holds until the process ends (its
+ * address is looked up once per device, on the first call there).  The call
+ * allocates and frees nothing.  Errors besides those of
+ * bsa_sparse_attention_fwd: BSA_ERR_WORKSPACE when the call needs more
+ * scratch than that (the size bsa_attention_workspace_bytes reports);
+ * BSA_ERR_INVALID when `stream` belongs to a device other than the current
+ * one.  The array starts zeroed and keeps the last call's contents; every
+ * call leaves the counters zero, so nothing needs clearing.  Calls that
+ * overlap on one GPU share it and race, so keep them on one stream or order
+ * them.
  * ------------------------------------------------------------------------ */
 size_t bsa_noalloc_scratch_bytes(void);
 

@@ -17,4 +17,5 @@ from .workloads import (  # noqa: F401
     sparse_prefill,
     threshold_prefill,
     threshold_decode,
+    decode_rows,
 )

@@ -408,3 +408,27 @@ def threshold_decode(seed: int = 5, L: int = 65536, Hq: int = 32, Hkv: int = 8, 
     params = dict(q_pos0=L - 1, causal=1, scale=1.0 / math.sqrt(D))
     return Workload("threshold_decode", "bf16", qb[None], kb[None], vb[None], params,
                     dict(needles=needles, seg_tiles=seg_tiles, alpha=alpha))
+
+
+def decode_rows(seed: int = 7, Lq: int = 128, L: int = 4096, Hq: int = 32, Hkv: int = 8, D: int = 128,
+                block: int = 64, cap: int = 16) -> Workload:
+    """Many single-row query blocks at once (rows decoded together over one
+    shared prefix), each with its own given block list: per (KV head, row) a
+    count drawn uniformly from 0 .. cap (every seventh row of KV head 0 gets an
+    empty list), the blocks drawn without replacement from the NB blocks and
+    sorted.  No RoPE; N(0, 1) queries, keys and values.  extra: idx
+    [1, Hkv, Lq, cap] int32 (-1 past the count), cnt [1, Hkv, Lq] int32."""
+    NB = -(-L // block)
+    qb = np.stack([_store(_normal(seed, _Q, h, (Lq, D)), "bf16") for h in range(Hq)])
+    kb = np.stack([_store(_normal(seed, _K, g, (L, D)), "bf16") for g in range(Hkv)])
+    vb = np.stack([_store(_normal(seed, _V, g, (L, D)), "bf16") for g in range(Hkv)])
+    idx = np.full((1, Hkv, Lq, cap), -1, dtype=np.int32)
+    cnt = np.zeros((1, Hkv, Lq), dtype=np.int32)
+    for g in range(Hkv):
+        rng = _rng(seed, 60, g)
+        for r in range(Lq):
+            n = 0 if (g == 0 and r % 7 == 0) else int(rng.integers(0, min(cap, NB) + 1))
+            cnt[0, g, r] = n
+            idx[0, g, r, :n] = np.sort(rng.choice(NB, size=n, replace=False))
+    params = dict(kv_block=block, q_block=1, q_pos0=L - Lq, causal=0, cap=cap, scale=1.0 / math.sqrt(D))
+    return Workload("decode_rows", "bf16", qb[None], kb[None], vb[None], params, dict(idx=idx, cnt=cnt))

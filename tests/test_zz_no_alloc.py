@@ -1,5 +1,5 @@
 """bsa_sparse_attention_fwd_noalloc: the attention entry point that takes no
-workspace (its split-KV partials live in the library's static device scratch).
+workspace (its arrival counters and split-KV partials live in the library's static device scratch).
 Two calls in a row through the C ABI -- a denoising block (32 rows, split MFMA
 path) and then a smaller decode step -- each equal, bit for bit, to
 bsa_sparse_attention_fwd with a caller workspace on the same inputs; the
@@ -40,7 +40,7 @@ def _compare(bsa, q, k, v, idx, cnt, ap, row_mask=None, odtype=None):
     odtype = q.dtype if odtype is None else odtype
     base_o = torch.randn(q.shape, device="cuda").to(odtype)
     base_l = torch.randn(q.shape[:3], device="cuda")
-    ws = torch.empty(max(256, bsa.bsa_attention_workspace_bytes(q, k, ap)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(256, bsa.bsa_attention_workspace_bytes(q, k, ap)), dtype=torch.uint8, device="cuda")
     o_ref, l_ref = bsa.bsa_sparse_attention_fwd(q, k, v, idx, cnt, ap, row_mask=row_mask, o=base_o.clone(),
                                                 lse=base_l.clone(), workspace=ws)
     o, lse = bsa.bsa_sparse_attention_fwd_noalloc(q, k, v, idx, cnt, ap, base_o.clone(), base_l.clone(),
