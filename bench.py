@@ -631,7 +631,7 @@ def bench_token_decode(torch, bsa, synth, reps, flush, w=None):
     ws_sel = torch.empty(bsa.bsa_token_select_workspace_bytes(q, k, TOKEN_BUDGET), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
-    ws_att = torch.empty(bsa.bsa_token_attention_workspace_bytes(q, k, TOKEN_BUDGET), dtype=torch.uint8,
+    ws_att = torch.zeros(bsa.bsa_token_attention_workspace_bytes(q, k, TOKEN_BUDGET), dtype=torch.uint8,
                          device="cuda")
 
     def select():

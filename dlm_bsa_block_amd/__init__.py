@@ -317,7 +317,8 @@ def bsa_window_decode_fwd(q, k, v, idx, cnt, p: BsaAttnParams, window: int, gate
     qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
     need = bsa_window_decode_workspace_bytes(q, k, p, window)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)   # no initial contents needed
+        # the arrival counters at its front must be zero on the first call (calls leave them zero)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     check(lib().bsa_window_decode_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),
                                       cnt.data_ptr(), ctypes.byref(p), window, _ptr(gates), ctypes.byref(od),
                                       lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
@@ -366,7 +367,8 @@ def bsa_token_attention_fwd(q, k, v, idx, cnt, scale=None, o=None, lse=None, wor
     qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(o)
     need = bsa_token_attention_workspace_bytes(q, k, cap)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        # the arrival counters at its front must be zero on the first call (calls leave them zero)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     check(lib().bsa_token_attention_fwd(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), idx.data_ptr(),
                                         cnt.data_ptr(), cap, scale, ctypes.byref(od), lse.data_ptr(),
                                         workspace.data_ptr(), workspace.numel(), _stream()),

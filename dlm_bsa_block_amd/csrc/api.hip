@@ -407,6 +407,7 @@ static bsa_status validate_window_decode(const bsa_tensor* q, const bsa_tensor* 
   if (pl.kind != 0) return fail(BSA_ERR_UNSUPPORTED, "the sliding window joins decode rows only (q_block = 1)");
   if (window <= 0) return fail(BSA_ERR_INVALID, "window %d must be positive", window);
   plan_attention(*q, *k, *p, pl, window);
+  plan_attention_counters(pl);
   return BSA_OK;
 }
 
@@ -414,7 +415,7 @@ size_t bsa_window_decode_workspace_bytes(const bsa_tensor* q, const bsa_tensor* 
                                          int32_t window) {
   AttnPlan pl;
   if (!k || validate_window_decode(q, k, k, p, window, pl) != BSA_OK) return 0;
-  return pl.part_bytes;
+  return pl.arrival_bytes + pl.part_bytes;
 }
 
 bsa_status bsa_window_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const int32_t* idx,
@@ -428,8 +429,9 @@ bsa_status bsa_window_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, const
   if (!same_dims(q, o) || (o->dtype != q->dtype && o->dtype != BSA_F32))
     return fail(BSA_ERR_INVALID, "o must match q in shape, with q's dtype or f32");
   if (!idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "idx, cnt and lse are required");
-  if (!workspace || workspace_bytes < pl.part_bytes)
-    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, pl.part_bytes);
+  const size_t need = pl.arrival_bytes + pl.part_bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
   if (q->L == 0) { g_err[0] = 0; return BSA_OK; }
   launch_attention(*q, *k, *v, idx, cnt, *p, pl, nullptr, *o, lse, workspace, static_cast<hipStream_t>(stream),
@@ -496,7 +498,7 @@ size_t bsa_token_attention_workspace_bytes(const bsa_tensor* q, const bsa_tensor
   if (!q || !k || q->H <= 0 || k->H <= 0 || cap <= 0) return 0;
   AttnPlan pl;
   plan_token_attention(*q, *k, cap, pl);
-  return pl.part_bytes;
+  return pl.arrival_bytes + pl.part_bytes;
 }
 
 bsa_status bsa_token_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const int32_t* idx,
@@ -510,8 +512,9 @@ bsa_status bsa_token_attention_fwd(const bsa_tensor* q, const bsa_tensor* k, con
   if (!idx || !cnt || !lse) return fail(BSA_ERR_INVALID, "idx, cnt and lse are required");
   AttnPlan pl;
   plan_token_attention(*q, *k, cap, pl);
-  if (!workspace || workspace_bytes < pl.part_bytes)
-    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, pl.part_bytes);
+  const size_t need = pl.arrival_bytes + pl.part_bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   if (!aligned16(workspace)) return fail(BSA_ERR_INVALID, "workspace not 16-byte aligned");
   launch_token_attention(*q, *k, *v, idx, cnt, cap, scale, pl, *o, lse, workspace, static_cast<hipStream_t>(stream));
   return check_launch("token attention");

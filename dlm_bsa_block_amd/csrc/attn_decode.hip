@@ -207,12 +207,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     }
   }
   if (!MERGE) return;
-  // every workgroup past this point holds one of the list's sel_items slices (the others returned)
-  if (!arrive_last(a.arrivals + li * kArrivalStride, sel_items, last_sh)) return;
+  // every workgroup past this point holds one slice: one of the list's sel_items, or with a
+  // window one of its n_win after them (the others returned)
+  int n_win = 0;
+  if (a.win > 0) {
+    const int64_t hi = min((int64_t)a.L, (int64_t)qpos + 1), lo = max((int64_t)0, hi - a.win);
+    n_win = (int)((hi - lo + a.tok_per_item - 1) / a.tok_per_item);
+  }
+  if (!arrive_last(a.arrivals + li * kArrivalStride, sel_items + n_win, last_sh)) return;
   const int Hq = a.Hkv * G;
-  merge_published<G, D>(a.part_o + li * a.items * G * D, a.part_ml + li * a.items * G * 2, sel_items, ml_sh, a.o,
-                        a.o_f32, (int64_t)b * a.osb + (int64_t)(g * G) * a.osh + (int64_t)row * a.osl, a.osh,
-                        a.lse + ((int64_t)b * Hq + g * G) * a.Lq + row, a.Lq);
+  const float* po = a.part_o + li * a.items * G * D;
+  const float* pml = a.part_ml + li * a.items * G * 2;
+  const int64_t o_off = (int64_t)b * a.osb + (int64_t)(g * G) * a.osh + (int64_t)row * a.osl;
+  const int64_t r0 = ((int64_t)b * Hq + g * G) * a.Lq + row;     // head g G's (row) entry
+  if (a.win == 0) {
+    merge_published<G, D>(po, pml, sel_items, ml_sh, a.o, a.o_f32, o_off, a.osh, a.lse + r0, a.Lq);
+  } else {
+    merge_published_window<G, D>(po, pml, sel_items, n_win, ml_sh, a.o, a.o_f32, o_off, a.osh, a.lse + 2 * r0,
+                                 2 * (int64_t)a.Lq, a.gates ? a.gates + 2 * r0 : nullptr, 2 * (int64_t)a.Lq);
+  }
 }
 
 // Merge the split partials of active (row, head) pairs of a query block in
@@ -316,7 +329,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
   int nvalid;
   if (a.per_item_from_count) {
     const int c_list = a.cnt[li];
-    const int per = max(1, (c_list + a.items - 1) / a.items);
+    const int per = split_per(c_list, a.items);
     nvalid = (c_list + per - 1) / per;
   } else {
     const int64_t nunits = a.cnt ? (int64_t)a.cnt[li] * a.unit_num : (int64_t)a.items * a.unit_den;

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
       const uint32_t c = (uint32_t)__popcll(f);
       const uint32_t incl = wave_incl_scan_dpp(c);
       const int n = (int)lane_read(incl, 63);
-      const int per = max(1, (n + a.items - 1) / a.items);
+      const int per = split_per(n, a.items);
       const int s0 = item * per, s1 = min(n, s0 + per);
       int pos = (int)(incl - c);
       int32_t* out = a.pk.idx + li * a.cap;            // the pick writes the list (workgroup 0)
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && KVB == 64) ? 2 : 1) void gathe
   if (SPLIT) {
     // the list's entries are shared out over the launched items: a short list (a
     // few active rows' union) gets one entry per workgroup, a full one kSplitBlocks
-    const int per = max(1, (n_list + a.items - 1) / a.items);
+    const int per = split_per(n_list, a.items);
     e0 = item * per;
     if (e0 >= n_list) return;
     e1 = min(n_list, e0 + per);
@@ -730,12 +730,15 @@ void plan_token_attention(const bsa_tensor& q, const bsa_tensor& k, int cap, Att
   pl.qv = 1;
   const size_t n = (size_t)pl.B * pl.Hkv * pl.NQB * pl.items * pl.qv;
   pl.part_bytes = align256(n * pl.D * 4) + align256(n * 2 * 4);
+  plan_attention_counters(pl);
 }
 
 void launch_token_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v, const int32_t* idx,
                             const int32_t* cnt, int cap, float scale, const AttnPlan& pl, const bsa_tensor& o,
                             float* lse, void* ws, hipStream_t s) {
   const size_t n = (size_t)pl.B * pl.Hkv * pl.NQB * pl.items * pl.qv;
+  uint32_t* arrivals = static_cast<uint32_t*>(ws);    // the counters come first
+  ws = static_cast<uint8_t*>(ws) + pl.arrival_bytes;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(n * pl.D * 4));
   DecArgs a;
@@ -749,7 +752,13 @@ void launch_token_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_
   a.kv_block = 1; a.causal = 0; a.q_pos0 = 0; a.Lq = pl.Lq; a.items = pl.items; a.tok_per_item = pl.tok_per_item;
   a.c2 = scale * kLog2e; a.row_mask = nullptr; a.part_o = part_o; a.part_ml = part_ml;
   a.kv_div = (int)(q.H / k.H);
+  if (pl.merge_in_launch) {
+    a.arrivals = arrivals;
+    a.o = o.data; a.o_f32 = o.dtype == BSA_F32; a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
+    a.lse = lse;
+  }
   launch_decode(a, q.dtype, pl.D, 1, pl.B, s);
+  if (pl.merge_in_launch) return;
   CombArgs c;
   c.part_o = part_o; c.part_ml = part_ml; c.cnt = cnt; c.items = pl.items;
   c.unit_num = 1; c.unit_den = pl.tok_per_item;
@@ -763,9 +772,9 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
                       const int32_t* cnt, const bsa_attn_params& p, const AttnPlan& pl, const uint8_t* row_mask,
                       const bsa_tensor& o, float* lse, void* ws, hipStream_t s, int win, const float* gates) {
   const float c2 = p.scale * kLog2e;
-  // without a window, the counters (if any) come first; the window decode plans none
-  uint32_t* arrivals = win == 0 && pl.arrival_bytes ? static_cast<uint32_t*>(ws) : nullptr;
-  if (win == 0) ws = static_cast<uint8_t*>(ws) + pl.arrival_bytes;
+  // the counters (if the plan has any) come first
+  uint32_t* arrivals = pl.arrival_bytes ? static_cast<uint32_t*>(ws) : nullptr;
+  ws = static_cast<uint8_t*>(ws) + pl.arrival_bytes;
   const bool merged = arrivals && pl.merge_in_launch;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = nullptr;
@@ -790,6 +799,7 @@ void launch_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor
       a.arrivals = arrivals;
       a.o = o.data; a.o_f32 = o.dtype == BSA_F32; a.osb = o.stride_b; a.osh = o.stride_h; a.osl = o.stride_l;
       a.lse = lse;
+      a.gates = gates;
     }
     launch_decode(a, q.dtype, pl.D, pl.G, pl.B, s);
   } else {

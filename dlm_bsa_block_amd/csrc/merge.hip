@@ -13,6 +13,7 @@
 #include "common.h"
 #include "internal.h"
 #include "mfma_tile.h"
+#include "split.h"
 
 namespace bsa {
 
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(320) void den_merge_kernel(DenMergeArgs a) {
   const int c_list = a.cnt[li];
   const int QV = R * m.G, qv = rowc * m.G + hl;
   const int64_t p0 = li * a.items;
-  const int per = max(1, (c_list + a.items - 1) / a.items);
+  const int per = split_per(c_list, a.items);
   const int nvalid = (c_list + per - 1) / per;
   const bool live = row < R && rbyte != 0;                  // uniform over the wave
   if (live) {

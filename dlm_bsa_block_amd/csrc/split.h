@@ -15,6 +15,15 @@ constexpr int kDecMaxItems = 512;   // decode slices per (row, group)
 constexpr int kDecMinSlice = 32;    // list tokens per decode slice, at least
 constexpr int kSplitBlocks = 16;    // list entries per MFMA split workgroup, at most
 constexpr int kCombMaxItems = 512;  // split slices the combine can merge
+constexpr int kSplitMinBlocks = 1;  // list entries per MFMA split workgroup, at least
+
+// List entries per slice of the MFMA split over `items` launched workgroups:
+// an even share of the n entries, at least kSplitMinBlocks (at most
+// kSplitBlocks, since items = ceil(cap / kSplitBlocks)).  Every kernel that
+// walks or merges the slices uses this one rule.
+__host__ __device__ __forceinline__ int split_per(int n, int items) {
+  return max(kSplitMinBlocks, (n + items - 1) / items);
+}
 
 struct DecArgs {
   const uint8_t* q;
@@ -30,14 +39,15 @@ struct DecArgs {
   float* part_ml;
   int win = 0;                    // > 0: items past the list's walk the win keys ending at the row
   int kv_div = 1;                 // lists per K/V head (per-query-head token lists: the group size)
-  // Non-null (win == 0 only): the slices are merged in the same launch by the last workgroup of
-  // each (row, group) to finish, counted on arrivals[li * kArrivalStride] (zero on entry, left
-  // zero), and O / LSE are written here; null: the partials wait for combine_kernel.
+  // Non-null: the slices are merged in the same launch by the last workgroup of each (row, group)
+  // to finish, counted on arrivals[li * kArrivalStride] (zero on entry, left zero), and O / LSE
+  // are written here; null: the partials wait for combine_kernel.
   uint32_t* arrivals = nullptr;
   void* o = nullptr;
   int o_f32 = 0;
   int64_t osb = 0, osh = 0, osl = 0;
-  float* lse = nullptr;           // [B][Hq][Lq]
+  float* lse = nullptr;           // [B][Hq][Lq], or [B][Hq][Lq][2] (list, window) when win > 0
+  const float* gates = nullptr;   // win > 0: [B][Hq][Lq][2] branch gates, or null for 1 and 1
 };
 
 struct CombArgs {
@@ -54,7 +64,7 @@ struct CombArgs {
   int win = 0;                    // sliding window: its items follow the list's (decode only)
   int q_pos0 = 0, L = 0;
   const float* gates = nullptr;   // [B][Hq][Lq][2] branch gates, or null for 1 and 1
-  int per_item_from_count = 0;    // 1: each slice took max(1, ceil(cnt / items)) list entries
+  int per_item_from_count = 0;    // 1: each slice took split_per(cnt, items) list entries
 };
 
 void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s);

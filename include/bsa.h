@@ -360,7 +360,10 @@ bsa_status bsa_threshold_decode_fwd(const bsa_tensor* q, const bsa_tensor* k, co
  * for weights 1 and 1.  Writes o = g_sel O_sel + g_win O_win (q's dtype or
  * f32) and lse [B, Hq, Lq, 2] (natural log of each branch's softmax
  * denominator; -inf for an empty list).  K/V of the two branches stream in
- * the same launch.  workspace: bsa_window_decode_workspace_bytes() bytes.
+ * the same launch, which also merges them.  workspace:
+ * bsa_window_decode_workspace_bytes() bytes, laid out and kept as
+ * bsa_sparse_attention_fwd's (arrival counters in the first 65536 bytes,
+ * zero on the first call, left zero by every call).
  * Errors as bsa_sparse_attention_fwd; BSA_ERR_UNSUPPORTED for q_block > 1;
  * BSA_ERR_INVALID for w <= 0.
  * ------------------------------------------------------------------------ */
@@ -401,8 +404,10 @@ bsa_status bsa_token_select(const bsa_tensor* q, const bsa_tensor* k, const uint
  * [B, Hq, Lq] their number (<= cap): the layout bsa_token_select writes for
  * Lq = 1.  Writes o (q's dtype or f32) and lse [B, Hq, Lq] (natural log;
  * -inf and O = 0 for an empty list).  workspace:
- * bsa_token_attention_workspace_bytes() bytes.  Errors as
- * bsa_sparse_attention_fwd.
+ * bsa_token_attention_workspace_bytes() bytes, laid out and kept as
+ * bsa_sparse_attention_fwd's: arrival counters in the first 65536 bytes,
+ * zero on the first call with the workspace and left zero by every call.
+ * Errors as bsa_sparse_attention_fwd.
  * ------------------------------------------------------------------------ */
 size_t bsa_token_attention_workspace_bytes(const bsa_tensor* q, const bsa_tensor* k, int32_t cap);
 

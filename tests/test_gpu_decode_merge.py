@@ -113,3 +113,25 @@ def test_workspace_reused_across_shapes(bsa):
             assert torch.equal(o, o_f) and torch.equal(lse, l_f), f"{w.name} Lq={w.q.shape[2]} rep {rep}"
     # the counters are back to zero after every call
     assert not ws[:65536].any()
+
+
+@pytest.mark.parametrize("Lq,window", [(40, 300), (130, 700)])
+def test_window_merged_and_combined(bsa, Lq, window):
+    """Selected blocks plus a sliding window (two branches mixed by gates),
+    merged in the launch (8 x 40 triples) and by the combine (8 x 130), both
+    against the oracle's two branches."""
+    w = synth.decode_rows(Lq=Lq, L=4096, seed=14)
+    p = w.params
+    q, k, v = (to_dev(x, "bf16") for x in (w.q, w.k, w.v))
+    idx = torch.from_numpy(w.extra["idx"]).cuda()
+    cnt = torch.from_numpy(w.extra["cnt"]).cuda()
+    ap = bsa.attn_params(kv_block=p["kv_block"], q_block=1, cap=p["cap"], q_pos0=p["q_pos0"], scale=p["scale"])
+    gates = np.random.default_rng(Lq).uniform(0.1, 1.2, (1, q.shape[1], Lq, 2)).astype(np.float32)
+    o, lse = bsa.bsa_window_decode_fwd(q, k, v, idx, cnt, ap, window, gates=torch.from_numpy(gates).cuda(),
+                                       o=torch.zeros(q.shape, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    lists = [[[w.extra["idx"][0, g, r, :w.extra["cnt"][0, g, r]].astype(np.int64) for r in range(Lq)]
+              for g in range(w.k.shape[1])]]
+    O_ref, L_ref = orc.window_decode(dict(p, causal=0), w.f64("q"), w.f64("k"), w.f64("v"), lists, window,
+                                     gates.astype(np.float64))
+    check_outputs(from_dev(o), O_ref, lse.cpu().numpy(), L_ref, f"window {window} Lq {Lq}")
