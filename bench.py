@@ -910,7 +910,8 @@ def main():
                                   "bsa_sparse_attention_fwd_cold": round(d["t_att_cold"], 2)}
         # roofline of the attention over the selected blocks, caches evicted before each call
         ach = d["sel_bytes"] / (d["t_att_cold"] * 1e3)
-        line["roofline"] = {"kernel": "bsa_sparse_attention_fwd (decode split-KV + combine), cold caches",
+        line["roofline"] = {"kernel": "bsa_sparse_attention_fwd (one decode_kernel launch: split-KV slices merged "
+                                      "by the last workgroup), cold caches",
                             "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(ach / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic("gqa_decode_64k_hbm_counters.md"),
