@@ -697,20 +697,22 @@ __global__ __launch_bounds__(NT) void token_topk_kernel(TopkArgs a) {
   int call3 = 0;
 #pragma unroll 1
   for (int shift = 30; shift >= 0; shift -= 2) {
-    uint32_t c[3] = {0u, 0u, 0u};
+    // the wave's counts straight from ballots: one compare per (key, candidate), the
+    // population counts and sums on the scalar unit, no cross-lane reduction
+    const uint32_t x1 = tau | (1u << shift), x2 = tau | (2u << shift), x3 = tau | (3u << shift);
+    uint32_t ws[3] = {0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      c[0] += key[e] >= (tau | (1u << shift));
-      c[1] += key[e] >= (tau | (2u << shift));
-      c[2] += key[e] >= (tau | (3u << shift));
+      ws[0] += (uint32_t)__popcll(__ballot(key[e] >= x1));
+      ws[1] += (uint32_t)__popcll(__ballot(key[e] >= x2));
+      ws[2] += (uint32_t)__popcll(__ballot(key[e] >= x3));
+      // eight keys at a time: the compiler would otherwise hold every ballot in scalar registers
+      if (e % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
-    float ws[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) ws[j] = wave_sum_dpp((float)c[j]);
     uint32_t (*buf)[NW] = wsum3[call3++ & 1];
     if (lane == 0) {
 #pragma unroll
-      for (int j = 0; j < 3; ++j) buf[j][w] = (uint32_t)ws[j];
+      for (int j = 0; j < 3; ++j) buf[j][w] = ws[j];
     }
     __syncthreads();
     uint32_t tot[3] = {0u, 0u, 0u};
