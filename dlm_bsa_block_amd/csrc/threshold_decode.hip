@@ -613,6 +613,8 @@ void launch_threshold_decode(const bsa_tensor& q, const bsa_tensor& k, const bsa
 constexpr int kTokPart = 4096;          // tokens per first-pass part
 constexpr int kTokMaxBudget = 2048;     // tokens per head, at most
 constexpr int kTokMaxCand = 16384;      // first-pass candidates per head, at most
+constexpr int kTokBits = 2;             // bits of the N-th key found per counting step (divides 32)
+constexpr int kTokKeysPerGroup = 8;     // keys whose ballots are taken before they are summed
 
 struct TopkArgs {
   const float* scores;                  // pass 1: [rows][Lpad]
@@ -629,7 +631,7 @@ template <int NT, int PER, bool FIRST>
 __global__ __launch_bounds__(NT) void token_topk_kernel(TopkArgs a) {
   constexpr int NW = NT / 64;
   __shared__ uint32_t wsum[2][NW];                   // double-buffered: one barrier per block sum
-  __shared__ uint32_t wsum3[2][3][NW];               // the same for the three counts of a 2-bit step
+  __shared__ uint32_t wsum3[2][(1 << kTokBits) - 1][NW];   // the same for the counts of one step
   const int part = blockIdx.x, row = blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int e0 = tid * PER;                          // this thread's first element
@@ -695,33 +697,37 @@ __global__ __launch_bounds__(NT) void token_topk_kernel(TopkArgs a) {
   // together: their latencies overlap).
   uint32_t tau = 0u;
   int call3 = 0;
+  constexpr int NC = (1 << kTokBits) - 1;            // candidates per step
 #pragma unroll 1
-  for (int shift = 30; shift >= 0; shift -= 2) {
+  for (int shift = 32 - kTokBits; shift >= 0; shift -= kTokBits) {
     // the wave's counts straight from ballots: one compare per (key, candidate), the
     // population counts and sums on the scalar unit, no cross-lane reduction
-    const uint32_t x1 = tau | (1u << shift), x2 = tau | (2u << shift), x3 = tau | (3u << shift);
-    uint32_t ws[3] = {0u, 0u, 0u};
+    uint32_t ws[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) ws[j] = 0u;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      ws[0] += (uint32_t)__popcll(__ballot(key[e] >= x1));
-      ws[1] += (uint32_t)__popcll(__ballot(key[e] >= x2));
-      ws[2] += (uint32_t)__popcll(__ballot(key[e] >= x3));
-      // eight keys at a time: the compiler would otherwise hold every ballot in scalar registers
-      if (e % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+        ws[j] += (uint32_t)__popcll(__ballot(key[e] >= (tau | ((uint32_t)(j + 1) << shift))));
+      // a few keys at a time: the compiler would otherwise hold every ballot in scalar registers
+      if (e % kTokKeysPerGroup == kTokKeysPerGroup - 1) __builtin_amdgcn_sched_barrier(0);
     }
     uint32_t (*buf)[NW] = wsum3[call3++ & 1];
     if (lane == 0) {
 #pragma unroll
-      for (int j = 0; j < 3; ++j) buf[j][w] = ws[j];
+      for (int j = 0; j < NC; ++j) buf[j][w] = ws[j];
     }
     __syncthreads();
-    uint32_t tot[3] = {0u, 0u, 0u};
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww)
-#pragma unroll
-      for (int j = 0; j < 3; ++j) tot[j] += buf[j][ww];
     // counts fall with the candidate: take the largest one that still has N keys
-    const uint32_t dg = tot[2] >= (uint32_t)Ne ? 3u : tot[1] >= (uint32_t)Ne ? 2u : tot[0] >= (uint32_t)Ne ? 1u : 0u;
+    uint32_t dg = 0u;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      uint32_t t = 0u;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) t += buf[j][ww];
+      dg = t >= (uint32_t)Ne ? (uint32_t)(j + 1) : dg;
+    }
     tau |= dg << shift;
   }
   uint32_t n_gt = 0u, n_eq = 0u;
