@@ -135,3 +135,36 @@ def test_window_merged_and_combined(bsa, Lq, window):
     O_ref, L_ref = orc.window_decode(dict(p, causal=0), w.f64("q"), w.f64("k"), w.f64("v"), lists, window,
                                      gates.astype(np.float64))
     check_outputs(from_dev(o), O_ref, lse.cpu().numpy(), L_ref, f"window {window} Lq {Lq}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 128), (16, 8, 128), (32, 4, 128), (32, 8, 64)])
+def test_merged_group_sizes(bsa, Hq, Hkv, D):
+    """Group sizes 1, 2 and 8 (8: two (head, dim pair) positions per thread in
+    the merge) and head dim 64, merged in the launch."""
+    w = synth.decode_rows(Lq=20, L=3000, Hq=Hq, Hkv=Hkv, D=D, seed=15)
+    o, lse, _ = _run(bsa, w)
+    _check(w, o, lse, heads=tuple(sorted({0, Hq // 2 - 1, Hq - 1})))
+
+
+@pytest.mark.parametrize("Lq", [40, 70])
+def test_batch_two(bsa, Lq):
+    """Two batch entries (2 x 8 x 40 triples merged in the launch, 2 x 8 x 70
+    past the counter region), each against the oracle on its own lists."""
+    ws_ = [synth.decode_rows(Lq=Lq, L=3500, seed=s) for s in (16, 17)]
+    p = ws_[0].params
+    cat = lambda name: np.concatenate([getattr(x, name) for x in ws_])
+    q, k, v = (to_dev(cat(n), "bf16") for n in ("q", "k", "v"))
+    idx = torch.from_numpy(np.concatenate([x.extra["idx"] for x in ws_])).cuda()
+    cnt = torch.from_numpy(np.concatenate([x.extra["cnt"] for x in ws_])).cuda()
+    ap = bsa.attn_params(kv_block=p["kv_block"], q_block=1, cap=p["cap"], q_pos0=p["q_pos0"], scale=p["scale"])
+    o, lse = bsa.bsa_sparse_attention_fwd(q, k, v, idx, cnt, ap,
+                                          o=torch.zeros(q.shape, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    og, lg = from_dev(o), from_dev(lse)
+    for b, w in enumerate(ws_):
+        heads = [0, 9, 22, 31]
+        lists = [[[w.extra["idx"][0, g, r, :w.extra["cnt"][0, g, r]].astype(np.int64) for r in range(Lq)]
+                  for g in range(w.k.shape[1])]]
+        O_ref, L_ref = orc.sparse_attention(dict(p, causal=0), w.f64("q"), w.f64("k"), w.f64("v"), lists,
+                                            heads=heads)
+        check_outputs(og[b:b + 1, heads], O_ref[:, heads], lg[b:b + 1, heads], L_ref[:, heads], f"batch {b}")
