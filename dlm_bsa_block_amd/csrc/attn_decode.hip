@@ -8,11 +8,11 @@
 // section: GQA-aware access).  A thread's K and V loads are issued before any
 // arithmetic.  Each workgroup writes an unnormalised partial (m, l, acc) per
 // query head; the partials are merged in ascending slice order, so the result
-// does not depend on scheduling.  Without a sliding window the merge runs in the
-// same launch: partials go out with device-scope stores and the workgroup that
-// finishes a (row, group)'s last slice merges them (a kernel boundary costs
-// more than the counter and the device-scope loads).  With the window's second
-// branch, or for token lists, a combine kernel merges them.
+// does not depend on scheduling.  The merge runs in the same launch: partials go
+// out with device-scope stores and the workgroup that finishes a (row, group)'s
+// last slice merges them (a kernel boundary costs more than the counter and the
+// device-scope loads).  Past the counters' 1024 (batch, group, row) triples a
+// combine kernel merges them instead, with the same arithmetic.
 #include "common.h"
 #include "internal.h"
 #include "split.h"
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   const int64_t ntok = (int64_t)n_list * a.kv_block;
   // With a sliding window (NSA structure section), the items after the list's
   // own walk the row's window instead: the a.win keys ending at the row's
-  // position, key = key0 + t.  The combine merges the two runs of items apart.
+  // position, key = key0 + t.  The merge takes the two runs of items apart.
   int64_t t_lo = t_begin, t_end, key0 = -1;
   const int sel_items = (int)((ntok + a.tok_per_item - 1) / a.tok_per_item);
   if (a.win > 0 && item >= sel_items) {
