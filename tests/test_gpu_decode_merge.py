@@ -168,3 +168,30 @@ def test_batch_two(bsa, Lq):
         O_ref, L_ref = orc.sparse_attention(dict(p, causal=0), w.f64("q"), w.f64("k"), w.f64("v"), lists,
                                             heads=heads)
         check_outputs(og[b:b + 1, heads], O_ref[:, heads], lg[b:b + 1, heads], L_ref[:, heads], f"batch {b}")
+
+
+def test_repeated_calls_are_bitwise_equal(bsa):
+    """300 calls on one workspace, alternating a merged and a combined shape, at
+    the full 64K-like slice count per row (32 slices): every result equals the
+    first bit for bit.  A merge that read a partial before it was published
+    would differ from run to run."""
+    shapes = [synth.decode_rows(Lq=Lq, L=8192, seed=s) for Lq, s in ((4, 18), (130, 19))]
+    args = []
+    for w in shapes:
+        p = w.params
+        q, k, v = (to_dev(x, "bf16") for x in (w.q, w.k, w.v))
+        idx = torch.from_numpy(w.extra["idx"]).cuda()
+        cnt = torch.from_numpy(w.extra["cnt"]).cuda()
+        ap = bsa.attn_params(kv_block=p["kv_block"], q_block=1, cap=p["cap"], q_pos0=p["q_pos0"], scale=p["scale"])
+        args.append((q, k, v, idx, cnt, ap))
+    need = max(bsa.bsa_attention_workspace_bytes(a[0], a[1], a[5]) for a in args)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = [bsa.bsa_sparse_attention_fwd(*a, workspace=ws) for a in args]
+    first = [(o.clone(), l.clone()) for o, l in first]
+    for it in range(300):
+        o, lse = bsa.bsa_sparse_attention_fwd(*args[it % 2], workspace=ws)
+        if it % 50 == 49 or it < 2:
+            torch.cuda.synchronize()
+        assert torch.equal(o, first[it % 2][0]) and torch.equal(lse, first[it % 2][1]), f"call {it}"
+    torch.cuda.synchronize()
+    assert not ws[:65536].any()
