@@ -329,3 +329,33 @@ def test_product_path_does_not_import_oracle():
             src = open(os.path.join(pkg, f)).read()
             assert "oracle" not in src.replace("oracle/", ""), f
     assert "oracle" not in sys.modules.get("dlm_bsa_block_amd").__dict__
+
+
+def test_attention_workspace_layout(lib):
+    """The attention workspaces start with a fixed 64 KiB counter region whenever
+    they hold split partials, so calls of any shape find the counters where the
+    previous call left them; the direct prefill path needs no workspace."""
+    COUNTERS = 65536
+    pd = bsa.attn_params(kv_block=64, q_block=1, cap=16)
+    k = _t(H=8, Lq=65536)
+    # decode, 32 slices of 32 tokens per (row, group): partials of 8 rows x 32 slices x 4 heads
+    one = lib.bsa_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=1)), ctypes.byref(k), ctypes.byref(pd))
+    parts = 8 * 32 * 4
+    assert one == COUNTERS + ((parts * 128 * 4 + 255) // 256) * 256 + ((parts * 2 * 4 + 255) // 256) * 256
+    # more rows than counters (8 x 129 > 1024): the region is still there, the combine merges instead
+    many = lib.bsa_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=129)), ctypes.byref(k), ctypes.byref(pd))
+    assert many > COUNTERS and many - COUNTERS > 128 * (one - COUNTERS)
+    # MFMA split of a 32-row block: counters too (one workspace may serve both kinds of call)
+    ps = bsa.attn_params(kv_block=64, q_block=32, cap=512)
+    split = lib.bsa_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=32)), ctypes.byref(k), ctypes.byref(ps))
+    assert split > COUNTERS
+    # direct prefill (128-row blocks): no partials, no workspace
+    pp = bsa.attn_params(kv_block=128, q_block=128, cap=64)
+    assert lib.bsa_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=4096)), ctypes.byref(_t(H=8, Lq=4096)),
+                                             ctypes.byref(pp)) == 0
+    # the window decode and the token attention lay theirs out the same way
+    win = lib.bsa_window_decode_workspace_bytes(ctypes.byref(_t(H=32, Lq=1)), ctypes.byref(k), ctypes.byref(pd), 512)
+    assert win > one                                  # the window adds its slices after the list's
+    tok = lib.bsa_token_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=1)), ctypes.byref(k), 256)
+    parts_t = 32 * 8                                  # 32 query heads x 8 slices of 32 tokens
+    assert tok == COUNTERS + ((parts_t * 128 * 4 + 255) // 256) * 256 + ((parts_t * 2 * 4 + 255) // 256) * 256
