@@ -78,8 +78,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", default="all", choices=["all", "decode", "dlm", "prefill", "threshold", "tdecode", "tokens"],
+    ap.add_argument("--only", default="all", choices=["all", "decode", "dbatch", "dlm", "prefill", "threshold", "tdecode", "tokens"],
                     help="which workloads to run (the headline line needs decode)")
+    ap.add_argument("--decode-batch", type=int, default=32, help="sequences of the batched decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
     return ap.parse_args()
@@ -264,6 +265,84 @@ def bench_decode(torch, bsa, synth, steps, warmup, flush):
                 t_step_separate=t_step_separate,
                 sel_bytes=sel_bytes, t_sum=t_sum, t_sel=t_sel, t_selr=t_selr, t_att=t_att, t_att_cold=t_att_cold,
                 summary_bytes=Hkv * NB * D * 4, cnt=cnt.cpu().tolist(), workload=w, window=window)
+
+
+# ---------------------------------------------------------- batched decode ---
+def shifted_batch(torch, w, B):
+    """B distinct 64K sequences on the GPU: the base cache rolled along L by
+    synth.decode_batch_shifts (the same rule the tests apply on the host); one
+    query row per sequence, the base workload's."""
+    import synth
+    p = w.params
+    q1, k1, v1 = (to_dev(torch, x, "bf16") for x in (w.q, w.k, w.v))
+    _, Hkv, L, D = k1.shape
+    shifts = synth.decode_batch_shifts(B, L, p["kv_block"])
+    k = torch.empty((B, Hkv, L, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    for b, sh in enumerate(shifts):
+        k[b].copy_(torch.roll(k1[0], sh, dims=1))
+        v[b].copy_(torch.roll(v1[0], sh, dims=1))
+    q = q1.expand(B, -1, -1, -1).contiguous()
+    return q, k, v, shifts
+
+
+def bench_decode_batch(torch, bsa, synth, w, B, steps, flush):
+    """The 64K decode step and its attention pass for B sequences at once (each
+    with its own cache and its own selected blocks): the same kernels with B
+    times the work per launch, which shows the HBM rate they sustain once enough
+    selected K/V is in flight; batch 1 is latency-bound (a few memory round
+    trips per launch)."""
+    log(f"decode batch: building {B} shifted 64K sequences on the GPU")
+    p = w.params
+    q, k, v, _ = shifted_batch(torch, w, B)
+    _, Hkv, L, D = k.shape
+    NB = -(-L // p["kv_block"])
+    kmean, kenergy = bsa.bsa_build_block_summaries(k, p["kv_block"], p["layout"])
+    sp = bsa.select_params(kv_block=p["kv_block"], q_block=1, q_pos0=p["q_pos0"], topk=p["topk"],
+                           n_first=p["n_first"], n_last=p["n_last"], layout=p["layout"], scale=p["scale"])
+    sp.cap = bsa.list_capacity(NB, 1, sp)
+    idx = torch.empty((B, Hkv, 1, sp.cap), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Hkv, 1), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, q.shape[1], 1), dtype=torch.float32, device="cuda")
+    ws_step = torch.zeros(max(256, bsa.bsa_decode_step_workspace_bytes(q, k, sp)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        bsa.bsa_decode_step(q, k, v, kmean, sp, refresh_block=NB - 1, k_energy=kenergy, idx=idx, cnt=cnt, o=o,
+                            lse=lse, workspace=ws_step)
+
+    ap = bsa.attn_params(kv_block=p["kv_block"], q_block=1, cap=sp.cap, q_pos0=p["q_pos0"], scale=p["scale"])
+    ws_att = torch.zeros(max(256, bsa.bsa_attention_workspace_bytes(q, k, ap)), dtype=torch.uint8, device="cuda")
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+
+    def attend_first(nb):
+        def f():
+            bsa.bsa_sparse_attention_fwd(q[:nb], k[:nb], v[:nb], idx[:nb], cnt[:nb], ap, o=o2[:nb], lse=lse2[:nb],
+                                         workspace=ws_att)
+        return f
+
+    reps = max(20, steps // 4)
+    t_step = time_graph(torch, step, max(10, steps // 8), inner=4)
+    t_step_cold = time_cold(torch, step, 20, flush)
+    sel_bytes = int(cnt.sum().item()) * p["kv_block"] * D * 2 * 2
+    sum_bytes = B * Hkv * NB * D * 4
+    att = {}
+    for nb in sorted({1, 4, 8, 16, B}):
+        if nb > B:
+            continue
+        f = attend_first(nb)
+        tw = time_calls(torch, f, reps)
+        tc = time_cold(torch, f, 20, flush)
+        nbytes = int(cnt[:nb].sum().item()) * p["kv_block"] * D * 2 * 2
+        att[str(nb)] = dict(us_warm=round(tw, 2), us_cold=round(tc, 2), selected_kv_bytes=nbytes,
+                            gbs_cold=round(nbytes / (tc * 1e3), 1), hbm_frac_cold=round(nbytes / (tc * 1e3) / HBM_PEAK_GBS, 4))
+    del q, k, v, kmean, kenergy, ws_step, ws_att
+    return dict(batch=B, context=L, us_per_step=round(t_step, 2), us_per_step_cold=round(t_step_cold, 2),
+                selected_kv_bytes=sel_bytes, summary_bytes=sum_bytes,
+                step_gbs_cold=round((sel_bytes + sum_bytes) / (t_step_cold * 1e3), 1),
+                step_hbm_frac_cold=round((sel_bytes + sum_bytes) / (t_step_cold * 1e3) / HBM_PEAK_GBS, 4),
+                attention_by_batch=att,
+                construction="sequence b = the 64K GQA cache rolled by a distinct whole number of blocks")
 
 
 # -------------------------------------------------------------------- dlm ---
@@ -857,6 +936,10 @@ def main():
         result["decode"] = d
         secondary["select_window_decode_64k"] = d["window"]
         log(f"window decode: {d['window']}")
+    if args.only in ("all", "dbatch"):
+        wd = result["decode"]["workload"] if "decode" in result else synth.gqa_decode()
+        secondary["decode_batch_64k"] = bench_decode_batch(torch, bsa, synth, wd, args.decode_batch, args.steps, flush)
+        log(f"decode batch: {secondary['decode_batch_64k']}")
     if args.only in ("all", "tdecode"):
         secondary["threshold_decode_64k"] = bench_threshold_decode(
             torch, bsa, synth, reps, flush, result["decode"]["workload"] if "decode" in result else None)

@@ -291,6 +291,8 @@ static bsa_status validate_attention(const bsa_tensor* q, const bsa_tensor* k, c
   if (p->kv_block <= 0 || p->q_block <= 0 || p->cap <= 0) return fail(BSA_ERR_INVALID, "kv_block, q_block, cap > 0");
   if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return fail(BSA_ERR_INVALID, "scale must be finite and > 0");
   if (p->q_pos0 < 0) return fail(BSA_ERR_INVALID, "negative q_pos0");
+  if ((int64_t)p->cap * p->kv_block >= (int64_t(1) << 30))
+    return fail(BSA_ERR_UNSUPPORTED, "cap * kv_block too large");
   plan_attention(*q, *k, *p, pl);
   plan_attention_counters(pl);
   if (pl.kind == 0) {

@@ -17,16 +17,22 @@
 #include "internal.h"
 #include "split.h"
 #include "split_merge.h"
+#include "dec_chunk.h"
 
 namespace bsa {
 
-template <int DT, int D, int G, bool MERGE>
+// NSUB sub-chunks of kDecTok tokens form one chunk: the chunk's block indices
+// are requested together, then all of its K/V rows, then the sub-chunks are
+// computed in order (the same arithmetic as one sub-chunk at a time).
+template <int DT, int D, int G, bool MERGE, int NSUB>
 __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   constexpr int ES = DT == BSA_BF16 ? 2 : 4;
   constexpr int LPT = D / 8;            // lanes per token
   constexpr int TPP = 64 / LPT;         // tokens per wave pass
-  constexpr int TPW = kDecTok / 4;      // tokens per wave and chunk
-  constexpr int PASSES = TPW / TPP;
+  constexpr int TPW = kDecTok / 4;      // tokens per wave and sub-chunk
+  constexpr int PASSES = TPW / TPP;     // passes per sub-chunk
+  constexpr int NP = PASSES * NSUB;     // passes per chunk
+  constexpr int CT = kDecTok * NSUB;    // tokens per chunk
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sm_acc[4][G][D];
   __shared__ int last_sh;
@@ -45,13 +51,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   // loaded together: an index slot past the count holds a stale value that is
   // only used once the count has ruled it in.
   const int64_t cap_tok = (int64_t)a.cap * a.kv_block;
-  int blk[PASSES], off[PASSES];
+  int blk[NP], off[NP];
+  // token of pass q (sub-chunk q / PASSES) of the chunk at c0 held by this lane
+  auto tok = [&](int64_t c0, int q) __attribute__((always_inline)) {
+    return c0 + (q / PASSES) * kDecTok + w * TPW + (q % PASSES) * TPP + tg;
+  };
   auto load_blocks = [&](int64_t c0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int64_t t = c0 + w * TPW + p * TPP + tg;
-      const int e = (int)(t / a.kv_block);
-      off[p] = (int)(t - (int64_t)e * a.kv_block);
+    for (int p = 0; p < NP; ++p) {
+      const int64_t t = tok(c0, p);
+      // 32-bit: list tokens stay below 2^31 (checked on the host)
+      const int e = (int)((uint32_t)t / (uint32_t)a.kv_block);
+      off[p] = (int)t - e * a.kv_block;
       blk[p] = t < cap_tok ? a.idx[li * a.cap + e] : -1;
     }
   };
@@ -106,67 +117,37 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)gk * a.ksh + d0) * ES;
   const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)gk * a.vsh + d0) * ES;
 
-  for (int64_t c0 = t_lo; c0 < t_end; c0 += kDecTok) {
+  for (int64_t c0 = t_lo; c0 < t_end; c0 += CT) {
     if (c0 != t_begin && key0 < 0) load_blocks(c0);
-    int pos[PASSES];
-    bool ok[PASSES];
+    int pos[NP];
+    bool ok[NP];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int64_t t = c0 + w * TPW + p * TPP + tg;
+    for (int p = 0; p < NP; ++p) {
+      const int64_t t = tok(c0, p);
       const int64_t key = key0 >= 0 ? key0 + t : (int64_t)blk[p] * a.kv_block + off[p];
       ok[p] = t < t_end && (key0 >= 0 || blk[p] >= 0) && key < a.L && (!a.causal || key <= qpos);
       pos[p] = ok[p] ? (int)key : 0;
     }
-    // every pass loads (row 0 stands in for a masked token, then zeroed): a load under a
+    // every pass loads (row 0 stands in for a masked token, zeroed when widened): a load under a
     // branch would make the compiler wait for one pass's rows before requesting the next
-    float kx[PASSES][8], vx[PASSES][8];
+    Raw8<DT> kr[NP], vr[NP];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      load8<DT>(kb + (int64_t)pos[p] * a.ksl * ES, kx[p]);
-      load8<DT>(vb + (int64_t)pos[p] * a.vsl * ES, vx[p]);
+    for (int p = 0; p < NP; ++p) {
+      kr[p] = load_raw8<DT>(kb + (int64_t)pos[p] * a.ksl * ES);
+      vr[p] = load_raw8<DT>(vb + (int64_t)pos[p] * a.vsl * ES);
     }
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kx[p][e] = ok[p] ? kx[p][e] : 0.f;
-        vx[p][e] = ok[p] ? vx[p][e] : 0.f;
-      }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float s[PASSES];
+    for (int sc = 0; sc < NSUB; ++sc) {
+      // a sub-chunk past the slice's end has no visible token and leaves the state as it is
+      Raw8<DT> ks[PASSES], vs[PASSES];
+      bool oks[PASSES];
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
-        float dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot = fmaf(qx[h][e], kx[p][e], dot);
-        dot = group_sum<LPT>(dot);
-        s[p] = ok[p] ? dot : -INFINITY;
+        ks[p] = kr[sc * PASSES + p];
+        vs[p] = vr[sc * PASSES + p];
+        oks[p] = ok[sc * PASSES + p];
       }
-      float mx = s[0];
-#pragma unroll
-      for (int p = 1; p < PASSES; ++p) mx = fmaxf(mx, s[p]);
-      mx = groups_max<LPT>(mx);
-      const float m_new = fmaxf(wm[h], mx);
-      if (m_new == -INFINITY) continue;                  // nothing visible yet (wave-uniform)
-      const float alpha = fast_exp2(wm[h] - m_new);
-      float l = 0.f, acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-      for (int p = 0; p < PASSES; ++p) {
-        const float pr = ok[p] ? fast_exp2(s[p] - m_new) : 0.f;
-        l += pr;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(pr, vx[p][e], acc[e]);
-      }
-      l = groups_sum<LPT>(l);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = groups_sum<LPT>(acc[e]);
-      wm[h] = m_new;
-      wl[h] = fmaf(wl[h], alpha, l);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wacc[h][e] = fmaf(wacc[h][e], alpha, acc[e]);
+      dec_sub_chunk<DT, D, G, PASSES>(qx, ks, vs, oks, wm, wl, wacc);
     }
   }
 #pragma unroll
@@ -226,6 +207,242 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
     merge_published_window<G, D>(po, pml, sel_items, n_win, ml_sh, a.o, a.o_f32, o_off, a.osh, a.lse + 2 * r0,
                                  2 * (int64_t)a.Lq, a.gates ? a.gates + 2 * r0 : nullptr, 2 * (int64_t)a.Lq);
   }
+}
+
+// Decode attention for launches with many lists (bf16, D = 128, no window):
+// the same slices, partials and merge as decode_kernel, with the vector work
+// per token cut.  Per chunk of 128 list tokens each wave takes 32 keys:
+//  * scores on the matrix cores: S^T (16 keys x 16 query columns) = K Q^T with
+//    v_mfma_f32_16x16x32_bf16, K rows straight from HBM into the A operand,
+//    the G query heads as columns (zero past G); a lane then holds 4 keys of
+//    one head, and the head's max and sum over the wave's keys take two
+//    cross-row exchanges instead of a 16-lane reduction per (token, head);
+//  * p goes through LDS to the P V layout, where a lane holds 8 dims of every
+//    fourth token (16-byte V loads) and accumulates over its tokens with no
+//    exchange; the four token sets are summed once per slice.
+// The scores are bf16 products summed in fp32 on the matrix core, then scaled
+// by scale * log2 e (decode_kernel scales q first); both are within the
+// rounding of fp32 accumulation of the same products.
+template <int G, bool MERGE>
+__global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
+  constexpr int D = 128;
+  constexpr int CT = kDecTok * kDecWideSub;        // tokens per chunk: 32 per wave
+  constexpr int GP = G < 4 ? 4 : G;                // p row stride (16-byte reads)
+  __shared__ float sm_m[4][G], sm_l[4][G];
+  __shared__ float sm_acc[4][G][D];
+  __shared__ int last_sh;
+  __shared__ __attribute__((aligned(16))) uint64_t ml_sh[G * 32];   // the merge's (m, l): [head][slice of the batch]
+  __shared__ __attribute__((aligned(16))) float p_sh[4][32][GP];   // per wave: p of its 32 keys, per head
+  __shared__ float al_sh[4][G];                                     // per wave: the chunk's rescale per head
+
+  const int item = blockIdx.x, row = blockIdx.y, bg = blockIdx.z;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, kq = lane >> 4;       // scores: key / head column, key quad; P V: dim group, token set
+  const int64_t li = ((int64_t)b * a.Hkv + g) * a.NQB + row;
+  const int64_t t_begin = (int64_t)item * a.tok_per_item;
+  const int qpos = a.q_pos0 + row;
+  const int n_list = min(a.cnt[li], a.cap);             // (a count past the capacity reads no further)
+  // Q^T operand: column = head (columns past G load a valid row, then zeroed), k = dims 32 ks + 8 kq + 0..7
+  const int hq = g * G + min(col, G - 1);
+  u32x4 qw[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qw[ks] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.qsb + (int64_t)hq * a.qsh + (int64_t)row * a.qsl +
+                                                    32 * ks + 8 * kq) * 2);
+  if (a.row_mask && a.row_mask[(int64_t)b * a.Lq + row] == 0) return;   // a stable row is skipped
+  bf16x8 qb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, col < G ? qw[ks] : u32x4{0u, 0u, 0u, 0u});
+  const int64_t ntok = (int64_t)n_list * a.kv_block;
+  if (MERGE && ntok == 0 && item == 0) {                // nothing selected: O = 0, LSE = -inf
+    const int Hq = a.Hkv * G;
+    for (int i = tid; i < G * D; i += 256) {
+      const int h = i / D, d = i - h * D;
+      const int64_t oi = (int64_t)b * a.osb + (int64_t)(g * G + h) * a.osh + (int64_t)row * a.osl + d;
+      if (a.o_f32) static_cast<float*>(a.o)[oi] = 0.f;
+      else static_cast<uint16_t*>(a.o)[oi] = 0;
+      if (d == 0) a.lse[((int64_t)b * Hq + g * G + h) * a.Lq + row] = -INFINITY;
+    }
+  }
+  if (ntok == 0 || t_begin >= ntok) return;
+  const int64_t t_end = min(ntok, t_begin + a.tok_per_item);
+  const int sel_items = (int)((ntok + a.tok_per_item - 1) / a.tok_per_item);
+  const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh) * 2;
+  const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh) * 2;
+  const int32_t* lst = a.idx + li * a.cap;
+
+  float m_run = -INFINITY, l_run = 0.f;                 // scores layout: head col
+  float acc[G][8];                                      // P V layout: head h, dims 8 col + e, tokens = kq (mod 4)
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  // Per chunk a lane needs 10 list tokens: its K row in each 16-key half (key col) and its 8 V rows
+  // (tokens 4 rd + kq).  A token is clamped into the slice so that every index load is valid (no
+  // load under a branch); ok rules it out afterwards.  32-bit: list tokens < 2^30.
+  // A chunk's list entries are requested while the previous chunk is computed, so each chunk
+  // waits for one memory round trip (its K/V rows).
+  auto fetch_idx = [&](int64_t c0, int (&bl)[10]) __attribute__((always_inline)) {
+    const int64_t tw = c0 + 32 * w;
+#pragma unroll
+    for (int j = 0; j < 10; ++j) {
+      const int64_t t = j < 2 ? tw + 16 * j + col : tw + 4 * (j - 2) + kq;
+      const int tc = (int)min(t, t_end - 1);
+      bl[j] = lst[(uint32_t)tc / (uint32_t)a.kv_block];
+    }
+  };
+  struct Rows {
+    bf16x8 kf[2][4];
+    u32x4 vr[8];
+    bool kok[2], vok[8];
+  };
+  auto issue = [&](int64_t c0, const int (&bl)[10], Rows& R) __attribute__((always_inline)) {
+    const int64_t tw = c0 + 32 * w;
+    int pos[10];
+    bool ok[10];
+#pragma unroll
+    for (int j = 0; j < 10; ++j) {
+      const int64_t t = j < 2 ? tw + 16 * j + col : tw + 4 * (j - 2) + kq;
+      const int tc = (int)min(t, t_end - 1);
+      const int e = (int)((uint32_t)tc / (uint32_t)a.kv_block);
+      const int64_t key = (int64_t)bl[j] * a.kv_block + (tc - e * a.kv_block);
+      ok[j] = t < t_end && bl[j] >= 0 && key < a.L && (!a.causal || key <= qpos);
+      pos[j] = ok[j] ? (int)key : 0;
+    }
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      R.kok[kg] = ok[kg];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        R.kf[kg][ks] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(kb + ((int64_t)pos[kg] * a.ksl + 32 * ks + 8 * kq) * 2));
+    }
+#pragma unroll
+    for (int rd = 0; rd < 8; ++rd) {
+      R.vok[rd] = ok[2 + rd];
+      R.vr[rd] = *reinterpret_cast<const u32x4*>(vb + ((int64_t)pos[2 + rd] * a.vsl + 8 * col) * 2);
+    }
+  };
+  int bl[10];
+  Rows R;
+  fetch_idx(t_begin, bl);
+  for (int64_t c0 = t_begin; c0 < t_end; c0 += CT) {
+    issue(c0, bl, R);
+    if (c0 + CT < t_end) fetch_idx(c0 + CT, bl);        // uniform; arrives while this chunk is computed
+    // scores: lane holds keys 16 kg + 4 kq + r of head col; key validity from the A-row lanes' ballot
+    float sv[2][4];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      const uint32_t okm = (uint32_t)__builtin_amdgcn_ballot_w64(R.kok[kg]) & 0xFFFFu;
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(R.kf[kg][ks], qb[ks], c, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[kg][r] = (okm >> (4 * kq + r)) & 1u ? c[r] * a.c2 : -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    mt = groups_max<16>(mt);                            // over the four key quads: the head's max
+    const float m_new = fmaxf(m_run, mt);
+    const float msub = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - msub);        // 0 while nothing was visible
+    float lt = 0.f;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[kg][r] = fast_exp2(sv[kg][r] - msub);        // p; 0 for a masked key
+        lt += sv[kg][r];
+      }
+    lt = groups_sum<16>(lt);
+    l_run = fmaf(l_run, alpha, lt);
+    m_run = m_new;
+    if (col < G) {
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p_sh[w][16 * kg + 4 * kq + r][col] = sv[kg][r];
+      if (kq == 0) al_sh[w][col] = alpha;
+    }
+    wave_sync_lds();
+    // P V: rescale, then the lane's 8 tokens (4 rd + kq) in order
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float al = al_sh[w][h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+    }
+#pragma unroll
+    for (int rd = 0; rd < 8; ++rd) {
+      float pj[GP];
+#pragma unroll
+      for (int h4 = 0; h4 < GP; h4 += 4) {
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(&p_sh[w][4 * rd + kq][h4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pj[h4 + e] = t4[e];
+      }
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = R.vok[rd] ? bf16lo(R.vr[rd][i]) : 0.f;
+        v[2 * i + 1] = R.vok[rd] ? bf16hi(R.vr[rd][i]) : 0.f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pj[h], v[e], acc[h][e]);
+    }
+    wave_sync_lds();                                    // p_sh is rewritten by the next chunk
+  }
+  // the four token sets summed (the same bits on every row); row 0 of the wave holds the result
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = groups_sum<16>(acc[h][e]);
+  if (kq == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_acc[w][h][8 * col + e] = acc[h][e];
+    if (col < G) { sm_m[w][col] = m_run; sm_l[w][col] = l_run; }
+  }
+  __syncthreads();
+  // merge the 4 waves into this workgroup's partial
+  const int64_t pbase = (li * a.items + item) * G;
+  for (int i = tid; i < G * D; i += 256) {
+    const int h = i / D, d = i - h * D;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][h]);
+    float o = 0.f, lsum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        if (sm_m[ww][h] == -INFINITY) continue;
+        const float wgt = fast_exp2(sm_m[ww][h] - M);
+        o = fmaf(sm_acc[ww][h][d], wgt, o);
+        lsum = fmaf(sm_l[ww][h], wgt, lsum);
+      }
+    }
+    if (MERGE) {
+      st_dev(a.part_o + (pbase + h) * D + d, o);
+      if (d == 0) st_dev2(a.part_ml + (pbase + h) * 2, M, lsum);
+    } else {
+      a.part_o[(pbase + h) * D + d] = o;
+      if (d == 0) {
+        a.part_ml[(pbase + h) * 2] = M;
+        a.part_ml[(pbase + h) * 2 + 1] = lsum;
+      }
+    }
+  }
+  if (!MERGE) return;
+  if (!arrive_last(a.arrivals + li * kArrivalStride, sel_items, last_sh)) return;
+  const int Hq = a.Hkv * G;
+  const int64_t o_off = (int64_t)b * a.osb + (int64_t)(g * G) * a.osh + (int64_t)row * a.osl;
+  merge_published<G, D>(a.part_o + li * a.items * G * D, a.part_ml + li * a.items * G * 2, sel_items, ml_sh, a.o,
+                        a.o_f32, o_off, a.osh, a.lse + ((int64_t)b * Hq + g * G) * a.Lq + row, a.Lq);
 }
 
 // Merge the split partials of active (row, head) pairs of a query block in
@@ -378,10 +595,32 @@ void launch_combine(const CombArgs& a, int odt, int B, hipStream_t s) {
 
 void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s) {
   dim3 grid(a.items, a.NQB, B * a.Hkv);
-#define BSA_DEC(DT, DD, GG)                                                                           \
-  do {                                                                                                \
-    if (a.arrivals) hipLaunchKernelGGL((decode_kernel<DT, DD, GG, true>), grid, dim3(256), 0, s, a);  \
-    else hipLaunchKernelGGL((decode_kernel<DT, DD, GG, false>), grid, dim3(256), 0, s, a);            \
+  const bool wide = a.tok_per_item % (kDecTok * kDecWideSub) == 0;
+  if (wide && dt == BSA_BF16 && D == 128 && a.win == 0 && a.kv_div == 1) {
+    // many lists in one launch: the matrix-core form
+#define BSA_DECW(GG)                                                                                    \
+  do {                                                                                                  \
+    if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true>), grid, dim3(256), 0, s, a);       \
+    else hipLaunchKernelGGL((decode_wide_kernel<GG, false>), grid, dim3(256), 0, s, a);                 \
+  } while (0)
+    switch (G) {
+      case 1: BSA_DECW(1); break;
+      case 2: BSA_DECW(2); break;
+      case 4: BSA_DECW(4); break;
+      default: BSA_DECW(8); break;
+    }
+#undef BSA_DECW
+    return;
+  }
+#define BSA_DEC(DT, DD, GG)                                                                                     \
+  do {                                                                                                          \
+    if (wide) {                                                                                                 \
+      if (a.arrivals) hipLaunchKernelGGL((decode_kernel<DT, DD, GG, true, kDecWideSub>), grid, dim3(256), 0, s, a); \
+      else hipLaunchKernelGGL((decode_kernel<DT, DD, GG, false, kDecWideSub>), grid, dim3(256), 0, s, a);        \
+    } else {                                                                                                    \
+      if (a.arrivals) hipLaunchKernelGGL((decode_kernel<DT, DD, GG, true, 1>), grid, dim3(256), 0, s, a);       \
+      else hipLaunchKernelGGL((decode_kernel<DT, DD, GG, false, 1>), grid, dim3(256), 0, s, a);                 \
+    }                                                                                                           \
   } while (0)
 #define BSA_DEC_G(DT, DD)                              \
   do {                                                 \

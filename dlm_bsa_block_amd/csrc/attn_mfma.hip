@@ -690,9 +690,7 @@ bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_par
   if (p.q_block == 1) {
     pl.kind = 0;
     const int64_t toks = (int64_t)p.cap * p.kv_block;
-    // slices of at least kDecMinSlice tokens (whole chunks), at most kDecMaxItems of them
-    const int64_t per = std::max<int64_t>(kDecMinSlice / kDecTok, ceil_div(ceil_div(toks, kDecTok), kDecMaxItems));
-    pl.tok_per_item = (int)(per * kDecTok);
+    pl.tok_per_item = (int)dec_slice_tokens(toks, (int64_t)pl.B * pl.Hkv * pl.NQB);
     pl.items = (int)ceil_div(toks, pl.tok_per_item) + (win > 0 ? (int)ceil_div(win, pl.tok_per_item) : 0);
     pl.qv = pl.G;
   } else if (p.q_block * pl.G <= 128 && p.q_block <= 64) {
@@ -724,8 +722,7 @@ void plan_attention_counters(AttnPlan& pl) {
 void plan_token_attention(const bsa_tensor& q, const bsa_tensor& k, int cap, AttnPlan& pl) {
   pl.kind = 0;
   pl.B = q.B; pl.Hq = q.H; pl.Hkv = q.H; pl.G = 1; pl.D = q.D; pl.Lq = q.L; pl.L = k.L; pl.NQB = q.L;
-  const int64_t per = std::max<int64_t>(kDecMinSlice / kDecTok, ceil_div(ceil_div(cap, kDecTok), kDecMaxItems));
-  pl.tok_per_item = (int)(per * kDecTok);
+  pl.tok_per_item = (int)dec_slice_tokens(cap, (int64_t)pl.B * pl.Hkv * pl.NQB);
   pl.items = (int)ceil_div(cap, pl.tok_per_item);
   pl.qv = 1;
   const size_t n = (size_t)pl.B * pl.Hkv * pl.NQB * pl.items * pl.qv;

@@ -36,6 +36,7 @@
 #include "internal.h"
 #include "split.h"
 #include "split_merge.h"
+#include "dec_chunk.h"
 #include "wave_select.h"
 
 namespace bsa {
@@ -235,15 +236,17 @@ __global__ __launch_bounds__(256) void dstep_logits_kernel(DStepArgs a) {
 }
 
 // -------------------------------------------------------- select + attend ---
-template <int DT, int D, int G, int KPL>
+template <int DT, int D, int G, int KPL, int NSUB>
 __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
   constexpr int ES = DT == BSA_BF16 ? 2 : 4;
   constexpr int KPT = KPL / 4;          // keys per thread: blocks KPT t .. KPT t + KPT - 1
   constexpr int SPL = KPL / 8;          // softmax partials per lane and head (P <= 64 * SPL)
   constexpr int LPT = D / 8;            // lanes per token
   constexpr int TPP = 64 / LPT;         // tokens per wave pass
-  constexpr int TPW = kDecTok / 4;      // tokens per wave and chunk
-  constexpr int PASSES = TPW / TPP;
+  constexpr int TPW = kDecTok / 4;      // tokens per wave and sub-chunk
+  constexpr int PASSES = TPW / TPP;     // passes per sub-chunk
+  constexpr int NP = PASSES * NSUB;     // passes per chunk (NSUB sub-chunks' K/V rows requested at once)
+  constexpr int CT = kDecTok * NSUB;    // tokens per chunk
   __shared__ BlockTopkSmem topk_sh;
   __shared__ int32_t lst[64 * KPL];                 // the row's list, ascending
   __shared__ int last_sh;
@@ -353,69 +356,39 @@ __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
   }
   const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + d0) * ES;
   const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + d0) * ES;
-  for (int64_t c0 = t_begin; c0 < t_end; c0 += kDecTok) {
-    int pos[PASSES];
-    bool ok[PASSES];
+  for (int64_t c0 = t_begin; c0 < t_end; c0 += CT) {
+    int pos[NP];
+    bool ok[NP];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int64_t t = c0 + w * TPW + p * TPP + tg;
+    for (int p = 0; p < NP; ++p) {
+      const int64_t t = c0 + (p / PASSES) * kDecTok + w * TPW + (p % PASSES) * TPP + tg;
       const bool in = t < t_end;
-      const int e = in ? (int)(t / a.kv_block) : 0;
+      const int e = in ? (int)((uint32_t)t / (uint32_t)a.kv_block) : 0;   // list tokens < 2^31
       const int blk = in ? lst[e] : -1;
       const int64_t key = (int64_t)blk * a.kv_block + (t - (int64_t)e * a.kv_block);
       ok[p] = in && blk >= 0 && key < a.L && (!a.causal || key <= qpos);
       pos[p] = ok[p] ? (int)key : 0;
     }
-    // every pass loads (row 0 stands in for a masked token, then zeroed): a load under a
+    // every pass loads (row 0 stands in for a masked token, zeroed when widened): a load under a
     // branch would make the compiler wait for one pass's rows before requesting the next
-    float kx[PASSES][8], vx[PASSES][8];
+    Raw8<DT> kr[NP], vr[NP];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      load8<DT>(kb + (int64_t)pos[p] * a.ksl * ES, kx[p]);
-      load8<DT>(vb + (int64_t)pos[p] * a.vsl * ES, vx[p]);
+    for (int p = 0; p < NP; ++p) {
+      kr[p] = load_raw8<DT>(kb + (int64_t)pos[p] * a.ksl * ES);
+      vr[p] = load_raw8<DT>(vb + (int64_t)pos[p] * a.vsl * ES);
     }
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kx[p][e] = ok[p] ? kx[p][e] : 0.f;
-        vx[p][e] = ok[p] ? vx[p][e] : 0.f;
-      }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float s[PASSES];
+    for (int sc = 0; sc < NSUB; ++sc) {
+      // a sub-chunk past the slice's end has no visible token and leaves the state as it is
+      Raw8<DT> ks[PASSES], vs[PASSES];
+      bool oks[PASSES];
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
-        float dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot = fmaf(qx[h][e], kx[p][e], dot);
-        dot = group_sum<LPT>(dot);
-        s[p] = ok[p] ? dot : -INFINITY;
+        ks[p] = kr[sc * PASSES + p];
+        vs[p] = vr[sc * PASSES + p];
+        oks[p] = ok[sc * PASSES + p];
       }
-      float mx = s[0];
-#pragma unroll
-      for (int p = 1; p < PASSES; ++p) mx = fmaxf(mx, s[p]);
-      mx = groups_max<LPT>(mx);
-      const float m_new = fmaxf(wm[h], mx);
-      if (m_new == -INFINITY) continue;                  // nothing visible yet (wave-uniform)
-      const float alpha = fast_exp2(wm[h] - m_new);
-      float l = 0.f, acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-      for (int p = 0; p < PASSES; ++p) {
-        const float pr = ok[p] ? fast_exp2(s[p] - m_new) : 0.f;
-        l += pr;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(pr, vx[p][e], acc[e]);
-      }
-      l = groups_sum<LPT>(l);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = groups_sum<LPT>(acc[e]);
-      wm[h] = m_new;
-      wl[h] = fmaf(wl[h], alpha, l);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wacc[h][e] = fmaf(wacc[h][e], alpha, acc[e]);
+      dec_sub_chunk<DT, D, G, PASSES>(qx, ks, vs, oks, wm, wl, wacc);
     }
   }
 #pragma unroll
@@ -469,8 +442,7 @@ bool plan_decode_step(const bsa_tensor& q, const bsa_tensor& k, const bsa_select
   pl.KPL = pl.NB <= 1024 ? 16 : 64;
   pl.P = 4 * (int)ceil_div(pl.NB, 32);
   const int64_t toks = (int64_t)p.cap * p.kv_block;
-  const int64_t per = std::max<int64_t>(kDecMinSlice / kDecTok, ceil_div(ceil_div(toks, kDecTok), kDecMaxItems));
-  pl.tok_per_item = (int)(per * kDecTok);
+  pl.tok_per_item = (int)dec_slice_tokens(toks, (int64_t)pl.B * pl.Hkv * pl.Lq);
   pl.items = (int)ceil_div(toks, pl.tok_per_item);
   const size_t rows = (size_t)pl.B * pl.Hkv * pl.Lq;
   pl.z_bytes = align256(rows * pl.G * pl.NBp * 4);
@@ -511,11 +483,17 @@ void launch_decode_step(const bsa_tensor& q, const bsa_tensor& k, const bsa_tens
 
   const dim3 g1((unsigned)ceil_div(pl.NB, 32), (unsigned)pl.Lq, (unsigned)(pl.B * pl.Hkv));
   const dim3 g2((unsigned)pl.items, (unsigned)pl.Lq, (unsigned)(pl.B * pl.Hkv));
+  const bool wide = pl.tok_per_item % (kDecTok * kDecWideSub) == 0;
+#define BSA_DS_ATT(DT, DD, GG, KK)                                                                                  \
+  do {                                                                                                             \
+    if (wide) hipLaunchKernelGGL((dstep_attend_kernel<DT, DD, GG, KK, kDecWideSub>), g2, dim3(256), 0, s, a);    \
+    else hipLaunchKernelGGL((dstep_attend_kernel<DT, DD, GG, KK, 1>), g2, dim3(256), 0, s, a);                   \
+  } while (0)
 #define BSA_DS(DT, DD, GG)                                                                                  \
   do {                                                                                                     \
     hipLaunchKernelGGL((dstep_logits_kernel<DT, DD, GG>), g1, dim3(256), 0, s, a);                          \
-    if (pl.KPL == 16) hipLaunchKernelGGL((dstep_attend_kernel<DT, DD, GG, 16>), g2, dim3(256), 0, s, a);    \
-    else hipLaunchKernelGGL((dstep_attend_kernel<DT, DD, GG, 64>), g2, dim3(256), 0, s, a);                 \
+    if (pl.KPL == 16) BSA_DS_ATT(DT, DD, GG, 16);                                                           \
+    else BSA_DS_ATT(DT, DD, GG, 64);                                                                        \
   } while (0)
 #define BSA_DS_G(DT, DD)                       \
   do {                                         \
@@ -533,6 +511,7 @@ void launch_decode_step(const bsa_tensor& q, const bsa_tensor& k, const bsa_tens
   }
 #undef BSA_DS_G
 #undef BSA_DS
+#undef BSA_DS_ATT
 
 }
 

@@ -18,4 +18,6 @@ from .workloads import (  # noqa: F401
     threshold_prefill,
     threshold_decode,
     decode_rows,
+    decode_batch_shifts,
+    shift_sequence,
 )

@@ -410,6 +410,27 @@ def threshold_decode(seed: int = 5, L: int = 65536, Hq: int = 32, Hkv: int = 8, 
                     dict(needles=needles, seg_tiles=seg_tiles, alpha=alpha))
 
 
+def decode_batch_shifts(B: int, L: int, block: int, seed: int = 11) -> list:
+    """Token shifts that turn one GQA decode cache into a batch of B distinct
+    sequences: sequence b holds the base cache circularly shifted by
+    shifts[b] tokens along L (np.roll semantics, a multiple of the block size,
+    so blocks stay whole and the planted needles move to other blocks).
+    shifts[0] = 0 and the shifts are distinct, so every sequence selects its
+    own blocks; the query rows are the base workload's for every sequence."""
+    NB = -(-L // block)
+    if L % block:
+        raise ValueError("the batch shifts need L to be a multiple of the block size")
+    if B > NB:
+        raise ValueError("more sequences than blocks")
+    rest = _rng(seed, 70).permutation(np.arange(1, NB))[:B - 1]
+    return [0] + [int(j) * block for j in rest]
+
+
+def shift_sequence(x: np.ndarray, shift: int) -> np.ndarray:
+    """One sequence of a shifted batch: x [H, L, D] rolled by `shift` tokens."""
+    return np.roll(x, shift, axis=1)
+
+
 def decode_rows(seed: int = 7, Lq: int = 128, L: int = 4096, Hq: int = 32, Hkv: int = 8, D: int = 128,
                 block: int = 64, cap: int = 16) -> Workload:
     """Many single-row query blocks at once (rows decoded together over one

@@ -342,9 +342,16 @@ def test_attention_workspace_layout(lib):
     one = lib.bsa_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=1)), ctypes.byref(k), ctypes.byref(pd))
     parts = 8 * 32 * 4
     assert one == COUNTERS + ((parts * 128 * 4 + 255) // 256) * 256 + ((parts * 2 * 4 + 255) // 256) * 256
-    # more rows than counters (8 x 129 > 1024): the region is still there, the combine merges instead
+    # more rows than counters (8 x 129 > 1024): the region is still there, the combine merges instead;
+    # with 1032 lists in one launch each list is one slice of all its 1024 tokens (a launch with
+    # many lists keeps about 512 workgroups), so the partials hold one slice per (row, group)
     many = lib.bsa_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=129)), ctypes.byref(k), ctypes.byref(pd))
-    assert many > COUNTERS and many - COUNTERS > 128 * (one - COUNTERS)
+    parts = 8 * 129 * 1 * 4
+    assert many == COUNTERS + ((parts * 128 * 4 + 255) // 256) * 256 + ((parts * 2 * 4 + 255) // 256) * 256
+    # 32 rows (256 lists): slices of 512 tokens, 2 per list
+    mid = lib.bsa_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=32)), ctypes.byref(k), ctypes.byref(pd))
+    parts = 8 * 32 * 2 * 4
+    assert mid == COUNTERS + ((parts * 128 * 4 + 255) // 256) * 256 + ((parts * 2 * 4 + 255) // 256) * 256
     # MFMA split of a 32-row block: counters too (one workspace may serve both kinds of call)
     ps = bsa.attn_params(kv_block=64, q_block=32, cap=512)
     split = lib.bsa_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=32)), ctypes.byref(k), ctypes.byref(ps))

@@ -172,3 +172,61 @@ def test_decode_step_fractional_budget(bsa):
     idx, cnt, _ = _step_case(bsa, w)
     NB = -(-9000 // 64)
     assert (cnt == min(NB, 3 + -(-NB // 20))).all()
+
+
+def test_decode_step_shifted_batch_full_size(bsa):
+    """32 sequences of 64K in one call (the batched decode measurement's inputs
+    and launch): sequence b is the 64K cache rolled by synth.decode_batch_shifts.
+    Sampled sequences against the oracle (refreshed summary, lists with the tie
+    band, O and LSE); the attention entry point on the step's lists, at batch
+    32 (lengthened slices, scores on the matrix cores) and on the first 4
+    (32-token slices), against the oracle on the same lists."""
+    w = synth.gqa_decode()
+    p = w.params
+    B = 32
+    q1, k1, v1 = (to_dev(x, "bf16") for x in (w.q, w.k, w.v))
+    _, Hkv, L, D = k1.shape
+    shifts = synth.decode_batch_shifts(B, L, p["kv_block"])
+    k = torch.empty((B, Hkv, L, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    for b, sh in enumerate(shifts):
+        k[b].copy_(torch.roll(k1[0], sh, dims=1))
+        v[b].copy_(torch.roll(v1[0], sh, dims=1))
+    del k1, v1
+    q = q1.expand(B, -1, -1, -1).contiguous()
+    NB = L // p["kv_block"]
+    kmean, kenergy = bsa.bsa_build_block_summaries(k, p["kv_block"], p["layout"])
+    kmean[:, :, NB - 1] = 0.0                  # stale: the step pools it again
+    kenergy[:, :, NB - 1] = 0.0
+    sp = bsa.select_params(kv_block=p["kv_block"], q_block=1, q_pos0=p["q_pos0"], topk=p["topk"],
+                           n_first=p["n_first"], n_last=p["n_last"], layout=p["layout"], scale=p["scale"])
+    idx, cnt, o, lse = bsa.bsa_decode_step(q, k, v, kmean, sp, refresh_block=NB - 1, k_energy=kenergy)
+    ap = bsa.attn_params(kv_block=p["kv_block"], q_block=1, cap=sp.cap, q_pos0=p["q_pos0"], scale=p["scale"])
+    o2, lse2 = bsa.bsa_sparse_attention_fwd(q, k, v, idx, cnt, ap)
+    o4, lse4 = bsa.bsa_sparse_attention_fwd(q[:4], k[:4], v[:4], idx[:4], cnt[:4], ap)
+    torch.cuda.synchronize()
+    idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert (cnt_np == 16).all()
+    # distinct sequences select distinct lists
+    assert len({tuple(idx_np[b, 0, 0, :16].tolist()) for b in range(B)}) > B // 2
+    qf = w.f64("q")
+    for b in (0, 1, 17, B - 1):
+        print(f"shifted batch: oracle for sequence {b} (shift {shifts[b]})", flush=True)
+        kf = synth.storage_to_f64(synth.shift_sequence(w.k[0], shifts[b]), "bf16")[None]
+        vf = synth.storage_to_f64(synth.shift_sequence(w.v[0], shifts[b]), "bf16")[None]
+        km_ref, ke_ref = orc.block_summaries(kf, p["kv_block"], p["layout"])
+        assert np.allclose(from_dev(kmean[b, :, NB - 1]), km_ref[0, :, NB - 1], rtol=1e-5, atol=2e-6)
+        assert np.allclose(from_dev(kenergy[b, :, NB - 1]), ke_ref[0, :, NB - 1], rtol=1e-5, atol=1e-5)
+        sel = orc.select_blocks(p, km_ref, q=qf)
+        lists = [[[None] for _ in range(Hkv)]]
+        for g in range(Hkv):
+            band = ambiguous(sel["rows"][(0, g, 0)])
+            check_list(idx_np[b, g, 0], int(cnt_np[b, g, 0]), sel["lists"][0][g][0], band,
+                       f"shifted batch b{b} g{g}")
+            lists[0][g][0] = idx_np[b, g, 0, :cnt_np[b, g, 0]].astype(np.int64)
+        O_ref, L_ref = orc.sparse_attention(p, qf, kf, vf, lists)
+        check_outputs(from_dev(o[b:b + 1]), O_ref, lse[b:b + 1].cpu().numpy(), L_ref, f"shifted batch b{b}")
+        check_outputs(from_dev(o2[b:b + 1]), O_ref, lse2[b:b + 1].cpu().numpy(), L_ref, f"entry point, b{b}")
+        if b < 4:
+            check_outputs(from_dev(o4[b:b + 1]), O_ref, lse4[b:b + 1].cpu().numpy(), L_ref, f"batch of 4, b{b}")
+        del kf, vf
