@@ -331,70 +331,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
   for (int64_t c0 = t_begin; c0 < t_end; c0 += CT) {
     issue(c0, bl, R);
     if (c0 + CT < t_end) fetch_idx(c0 + CT, bl);        // uniform; arrives while this chunk is computed
-    // scores: lane holds keys 16 kg + 4 kq + r of head col; key validity from the A-row lanes' ballot
-    float sv[2][4];
-#pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-      const uint32_t okm = (uint32_t)__builtin_amdgcn_ballot_w64(R.kok[kg]) & 0xFFFFu;
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(R.kf[kg][ks], qb[ks], c, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[kg][r] = (okm >> (4 * kq + r)) & 1u ? c[r] * a.c2 : -INFINITY;
-    }
-    float mt = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
-    mt = groups_max<16>(mt);                            // over the four key quads: the head's max
-    const float m_new = fmaxf(m_run, mt);
-    const float msub = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - msub);        // 0 while nothing was visible
-    float lt = 0.f;
-#pragma unroll
-    for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[kg][r] = fast_exp2(sv[kg][r] - msub);        // p; 0 for a masked key
-        lt += sv[kg][r];
-      }
-    lt = groups_sum<16>(lt);
-    l_run = fmaf(l_run, alpha, lt);
-    m_run = m_new;
-    if (col < G) {
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p_sh[w][16 * kg + 4 * kq + r][col] = sv[kg][r];
-      if (kq == 0) al_sh[w][col] = alpha;
-    }
-    wave_sync_lds();
-    // P V: rescale, then the lane's 8 tokens (4 rd + kq) in order
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float al = al_sh[w][h];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-    }
-#pragma unroll
-    for (int rd = 0; rd < 8; ++rd) {
-      float pj[GP];
-#pragma unroll
-      for (int h4 = 0; h4 < GP; h4 += 4) {
-        const f32x4 t4 = *reinterpret_cast<const f32x4*>(&p_sh[w][4 * rd + kq][h4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pj[h4 + e] = t4[e];
-      }
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = R.vok[rd] ? bf16lo(R.vr[rd][i]) : 0.f;
-        v[2 * i + 1] = R.vok[rd] ? bf16hi(R.vr[rd][i]) : 0.f;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pj[h], v[e], acc[h][e]);
-    }
-    wave_sync_lds();                                    // p_sh is rewritten by the next chunk
+    dec_wide_chunk<G>(qb, R.kf, R.vr, R.kok, R.vok, a.c2, m_run, l_run, acc, p_sh[w], al_sh[w]);
   }
   // the four token sets summed (the same bits on every row); row 0 of the wave holds the result
 #pragma unroll

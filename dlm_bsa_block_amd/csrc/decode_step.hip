@@ -346,58 +346,127 @@ __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
   }
   if (t_begin >= ntok) return;                          // no slice of the list for this workgroup
   const int64_t t_end = min(ntok, t_begin + a.tok_per_item);
-  float wm[G], wl[G], wacc[G][8];
+  if constexpr (NSUB > 1 && DT == BSA_BF16 && D == 128) {
+    // lengthened slices (many lists in one launch): scores on the matrix cores, as the attention
+    // entry point's form for such launches (dec_wide_chunk), the list from LDS
+    constexpr int GP = G < 4 ? 4 : G;
+    __shared__ __attribute__((aligned(16))) float p_sh[4][32][GP];
+    __shared__ float al_sh[4][G];
+    const int col = lane & 15, kq = lane >> 4;
+    const int hq = g * G + min(col, G - 1);           // columns past G load a valid row, then zeroed
+    bf16x8 qb[4];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    wm[h] = -INFINITY;
-    wl[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) wacc[h][e] = 0.f;
-  }
-  const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + d0) * ES;
-  const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + d0) * ES;
-  for (int64_t c0 = t_begin; c0 < t_end; c0 += CT) {
-    int pos[NP];
-    bool ok[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int64_t t = c0 + (p / PASSES) * kDecTok + w * TPW + (p % PASSES) * TPP + tg;
-      const bool in = t < t_end;
-      const int e = in ? (int)((uint32_t)t / (uint32_t)a.kv_block) : 0;   // list tokens < 2^31
-      const int blk = in ? lst[e] : -1;
-      const int64_t key = (int64_t)blk * a.kv_block + (t - (int64_t)e * a.kv_block);
-      ok[p] = in && blk >= 0 && key < a.L && (!a.causal || key <= qpos);
-      pos[p] = ok[p] ? (int)key : 0;
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 qw = *reinterpret_cast<const u32x4*>(
+          a.q + ((int64_t)b * a.qsb + (int64_t)hq * a.qsh + (int64_t)row * a.qsl + 32 * ks + 8 * kq) * 2);
+      qb[ks] = __builtin_bit_cast(bf16x8, col < G ? qw : u32x4{0u, 0u, 0u, 0u});
     }
-    // every pass loads (row 0 stands in for a masked token, zeroed when widened): a load under a
-    // branch would make the compiler wait for one pass's rows before requesting the next
-    Raw8<DT> kr[NP], vr[NP];
+    float m_run = -INFINITY, l_run = 0.f, acc[G][8];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      kr[p] = load_raw8<DT>(kb + (int64_t)pos[p] * a.ksl * ES);
-      vr[p] = load_raw8<DT>(vb + (int64_t)pos[p] * a.vsl * ES);
-    }
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int sc = 0; sc < NSUB; ++sc) {
-      // a sub-chunk past the slice's end has no visible token and leaves the state as it is
-      Raw8<DT> ks[PASSES], vs[PASSES];
-      bool oks[PASSES];
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    const uint8_t* kbw = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh) * 2;
+    const uint8_t* vbw = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh) * 2;
+    for (int64_t c0 = t_begin; c0 < t_end; c0 += CT) {
+      const int64_t tw = c0 + 32 * w;                 // the wave's first token
+      // the lane's K rows (key col of each 16-key half) and V rows (tokens 4 rd + kq); list tokens < 2^31
+      int pos[10];
+      bool ok[10];
 #pragma unroll
-      for (int p = 0; p < PASSES; ++p) {
-        ks[p] = kr[sc * PASSES + p];
-        vs[p] = vr[sc * PASSES + p];
-        oks[p] = ok[sc * PASSES + p];
+      for (int j = 0; j < 10; ++j) {
+        const int64_t t = j < 2 ? tw + 16 * j + col : tw + 4 * (j - 2) + kq;
+        const bool in = t < t_end;
+        const int e = in ? (int)((uint32_t)t / (uint32_t)a.kv_block) : 0;
+        const int blk = in ? lst[e] : -1;
+        const int64_t key = (int64_t)blk * a.kv_block + (t - (int64_t)e * a.kv_block);
+        ok[j] = in && blk >= 0 && key < a.L && (!a.causal || key <= qpos);
+        pos[j] = ok[j] ? (int)key : 0;
       }
-      dec_sub_chunk<DT, D, G, PASSES>(qx, ks, vs, oks, wm, wl, wacc);
-    }
-  }
+      bf16x8 kf[2][4];
+      u32x4 vr[8];
+      bool kok[2], vok[8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (lane < LPT) {
+      for (int kg = 0; kg < 2; ++kg) {
+        kok[kg] = ok[kg];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[w][h][d0 + e] = wacc[h][e];
+        for (int ks = 0; ks < 4; ++ks)
+          kf[kg][ks] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(kbw + ((int64_t)pos[kg] * a.ksl + 32 * ks + 8 * kq) * 2));
+      }
+#pragma unroll
+      for (int rd = 0; rd < 8; ++rd) {
+        vok[rd] = ok[2 + rd];
+        vr[rd] = *reinterpret_cast<const u32x4*>(vbw + ((int64_t)pos[2 + rd] * a.vsl + 8 * col) * 2);
+      }
+      dec_wide_chunk<G>(qb, kf, vr, kok, vok, a.c2, m_run, l_run, acc, p_sh[w], al_sh[w]);
     }
-    if (lane == 0) { sm_m[w][h] = wm[h]; sm_l[w][h] = wl[h]; }
+    // the four token sets summed; row 0 of the wave holds dims 8 col .. 8 col + 7
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = groups_sum<16>(acc[h][e]);
+    if (kq == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm_acc[w][h][8 * col + e] = acc[h][e];
+      if (col < G) { sm_m[w][col] = m_run; sm_l[w][col] = l_run; }
+    }
+  } else {
+    float wm[G], wl[G], wacc[G][8];
+  #pragma unroll
+    for (int h = 0; h < G; ++h) {
+      wm[h] = -INFINITY;
+      wl[h] = 0.f;
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) wacc[h][e] = 0.f;
+    }
+    const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh + d0) * ES;
+    const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh + d0) * ES;
+    for (int64_t c0 = t_begin; c0 < t_end; c0 += CT) {
+      int pos[NP];
+      bool ok[NP];
+  #pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int64_t t = c0 + (p / PASSES) * kDecTok + w * TPW + (p % PASSES) * TPP + tg;
+        const bool in = t < t_end;
+        const int e = in ? (int)((uint32_t)t / (uint32_t)a.kv_block) : 0;   // list tokens < 2^31
+        const int blk = in ? lst[e] : -1;
+        const int64_t key = (int64_t)blk * a.kv_block + (t - (int64_t)e * a.kv_block);
+        ok[p] = in && blk >= 0 && key < a.L && (!a.causal || key <= qpos);
+        pos[p] = ok[p] ? (int)key : 0;
+      }
+      // every pass loads (row 0 stands in for a masked token, zeroed when widened): a load under a
+      // branch would make the compiler wait for one pass's rows before requesting the next
+      Raw8<DT> kr[NP], vr[NP];
+  #pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        kr[p] = load_raw8<DT>(kb + (int64_t)pos[p] * a.ksl * ES);
+        vr[p] = load_raw8<DT>(vb + (int64_t)pos[p] * a.vsl * ES);
+      }
+  #pragma unroll
+      for (int sc = 0; sc < NSUB; ++sc) {
+        // a sub-chunk past the slice's end has no visible token and leaves the state as it is
+        Raw8<DT> ks[PASSES], vs[PASSES];
+        bool oks[PASSES];
+  #pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          ks[p] = kr[sc * PASSES + p];
+          vs[p] = vr[sc * PASSES + p];
+          oks[p] = ok[sc * PASSES + p];
+        }
+        dec_sub_chunk<DT, D, G, PASSES>(qx, ks, vs, oks, wm, wl, wacc);
+      }
+    }
+  #pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (lane < LPT) {
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) sm_acc[w][h][d0 + e] = wacc[h][e];
+      }
+      if (lane == 0) { sm_m[w][h] = wm[h]; sm_l[w][h] = wl[h]; }
+    }
   }
   __syncthreads();
   // merge the 4 waves into this workgroup's partial, stored at device scope (no cache holds it back)

@@ -180,7 +180,8 @@ def test_decode_step_shifted_batch_full_size(bsa):
     Sampled sequences against the oracle (refreshed summary, lists with the tie
     band, O and LSE); the attention entry point on the step's lists, at batch
     32 (lengthened slices, scores on the matrix cores) and on the first 4
-    (32-token slices), against the oracle on the same lists."""
+    (32-token slices), against the oracle on the same lists.  At batch 32 the
+    step and the entry point share slices and arithmetic: the same bits."""
     w = synth.gqa_decode()
     p = w.params
     B = 32
@@ -205,6 +206,7 @@ def test_decode_step_shifted_batch_full_size(bsa):
     o2, lse2 = bsa.bsa_sparse_attention_fwd(q, k, v, idx, cnt, ap)
     o4, lse4 = bsa.bsa_sparse_attention_fwd(q[:4], k[:4], v[:4], idx[:4], cnt[:4], ap)
     torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
     idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
     assert (cnt_np == 16).all()
     # distinct sequences select distinct lists
