@@ -223,10 +223,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 // The scores are bf16 products summed in fp32 on the matrix core, then scaled
 // by scale * log2 e (decode_kernel scales q first); both are within the
 // rounding of fp32 accumulation of the same products.
-template <int G, bool MERGE>
+// NWAVE = 4: chunks of 128 tokens, 32 per wave (lengthened slices).  NWAVE = 1:
+// chunks of 32 tokens on wave 0 alone (the single row's 32-token slices: the
+// other waves only join the workgroup's merge).
+template <int G, bool MERGE, int NWAVE>
 __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
   constexpr int D = 128;
-  constexpr int CT = kDecTok * kDecWideSub;        // tokens per chunk: 32 per wave
+  constexpr int CT = 32 * NWAVE;                   // tokens per chunk: 32 per working wave
   constexpr int GP = G < 4 ? 4 : G;                // p row stride (16-byte reads)
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sm_acc[4][G][D];
@@ -325,13 +328,15 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
       R.vr[rd] = *reinterpret_cast<const u32x4*>(vb + ((int64_t)pos[2 + rd] * a.vsl + 8 * col) * 2);
     }
   };
-  int bl[10];
-  Rows R;
-  fetch_idx(t_begin, bl);
-  for (int64_t c0 = t_begin; c0 < t_end; c0 += CT) {
-    issue(c0, bl, R);
-    if (c0 + CT < t_end) fetch_idx(c0 + CT, bl);        // uniform; arrives while this chunk is computed
-    dec_wide_chunk<G>(qb, R.kf, R.vr, R.kok, R.vok, a.c2, m_run, l_run, acc, p_sh[w], al_sh[w]);
+  if (NWAVE == 4 || w == 0) {                           // (wave-uniform)
+    int bl[10];
+    Rows R;
+    fetch_idx(t_begin, bl);
+    for (int64_t c0 = t_begin; c0 < t_end; c0 += CT) {
+      issue(c0, bl, R);
+      if (c0 + CT < t_end) fetch_idx(c0 + CT, bl);      // uniform; arrives while this chunk is computed
+      dec_wide_chunk<G>(qb, R.kf, R.vr, R.kok, R.vok, a.c2, m_run, l_run, acc, p_sh[w], al_sh[w]);
+    }
   }
   // the four token sets summed (the same bits on every row); row 0 of the wave holds the result
 #pragma unroll
@@ -533,12 +538,17 @@ void launch_combine(const CombArgs& a, int odt, int B, hipStream_t s) {
 void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s) {
   dim3 grid(a.items, a.NQB, B * a.Hkv);
   const bool wide = a.tok_per_item % (kDecTok * kDecWideSub) == 0;
-  if (wide && dt == BSA_BF16 && D == 128 && a.win == 0 && a.kv_div == 1) {
-    // many lists in one launch: the matrix-core form
-#define BSA_DECW(GG)                                                                                    \
-  do {                                                                                                  \
-    if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true>), grid, dim3(256), 0, s, a);       \
-    else hipLaunchKernelGGL((decode_wide_kernel<GG, false>), grid, dim3(256), 0, s, a);                 \
+  if (dt == BSA_BF16 && D == 128 && a.win == 0 && a.kv_div == 1) {
+    // bf16 lists with D = 128: the matrix-core form, on all four waves for lengthened slices
+#define BSA_DECW(GG)                                                                                         \
+  do {                                                                                                       \
+    if (wide) {                                                                                              \
+      if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true, 4>), grid, dim3(256), 0, s, a);       \
+      else hipLaunchKernelGGL((decode_wide_kernel<GG, false, 4>), grid, dim3(256), 0, s, a);                 \
+    } else {                                                                                                 \
+      if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true, 1>), grid, dim3(256), 0, s, a);       \
+      else hipLaunchKernelGGL((decode_wide_kernel<GG, false, 1>), grid, dim3(256), 0, s, a);                 \
+    }                                                                                                        \
   } while (0)
     switch (G) {
       case 1: BSA_DECW(1); break;

@@ -348,7 +348,8 @@ __global__ __launch_bounds__(256) void dstep_attend_kernel(DStepArgs a) {
   const int64_t t_end = min(ntok, t_begin + a.tok_per_item);
   if constexpr (NSUB > 1 && DT == BSA_BF16 && D == 128) {
     // lengthened slices (many lists in one launch): scores on the matrix cores, as the attention
-    // entry point's form for such launches (dec_wide_chunk), the list from LDS
+    // entry point's form for such launches (dec_wide_chunk), the list from LDS.  (On 32-token
+    // slices the vector form below is faster here: measured 16.9 against 17.5 us per 64K step.)
     constexpr int GP = G < 4 ? 4 : G;
     __shared__ __attribute__((aligned(16))) float p_sh[4][32][GP];
     __shared__ float al_sh[4][G];
