@@ -993,7 +993,7 @@ def main():
                                   "bsa_sparse_attention_fwd_cold": round(d["t_att_cold"], 2)}
         # roofline of the attention over the selected blocks, caches evicted before each call
         ach = d["sel_bytes"] / (d["t_att_cold"] * 1e3)
-        line["roofline"] = {"kernel": "bsa_sparse_attention_fwd (one decode_kernel launch: split-KV slices merged "
+        line["roofline"] = {"kernel": "bsa_sparse_attention_fwd (one decode_wide_kernel launch: split-KV slices merged "
                                       "by the last workgroup), cold caches",
                             "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(ach / HBM_PEAK_GBS, 4),
