@@ -677,3 +677,23 @@ def test_generators_are_deterministic():
     a = synth.gqa_decode(L=1024, Hq=4, Hkv=1)
     b = synth.gqa_decode(L=1024, Hq=4, Hkv=1)
     assert np.array_equal(a.k, b.k) and np.array_equal(a.q, b.q) and np.array_equal(a.v, b.v)
+
+
+def test_decode_batch_shifts_give_distinct_whole_block_rolls():
+    """The batched decode inputs: sequence 0 unshifted, every shift a distinct
+    whole number of blocks, and shift_sequence is a circular roll along L (so
+    block j of the base cache is block (j + s / block) mod NB of sequence b)."""
+    L, block = 4096, 64
+    NB = L // block
+    sh = synth.decode_batch_shifts(32, L, block)
+    assert sh[0] == 0 and len(set(sh)) == 32
+    assert all(s % block == 0 and 0 <= s < L for s in sh)
+    assert sh == synth.decode_batch_shifts(32, L, block)          # seeded
+    x = np.arange(2 * L * 3, dtype=np.int64).reshape(2, L, 3)
+    for s in sh[:4]:
+        y = synth.shift_sequence(x, s)
+        for j in (0, 5, NB - 1):
+            jb = (j + s // block) % NB
+            assert np.array_equal(y[:, jb * block:(jb + 1) * block], x[:, j * block:(j + 1) * block])
+    with pytest.raises(ValueError):
+        synth.decode_batch_shifts(4, L + 1, block)
