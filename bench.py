@@ -1003,6 +1003,14 @@ def main():
         step_bytes = d["sel_bytes"] + d["summary_bytes"]
         line["decode_step_bytes"] = {"selected_kv": d["sel_bytes"], "summaries_scanned": d["summary_bytes"],
                                      "gbs": round(step_bytes / (us * 1e3), 1)}
+        db = secondary.get("decode_batch_64k")
+        if db is not None:
+            # the same attention pass with enough selected K/V in flight to be bandwidth-bound
+            a32 = db["attention_by_batch"][str(db["batch"])]
+            line["decode_attention_batched"] = {
+                "sequences": db["batch"], "selected_kv_bytes": a32["selected_kv_bytes"], "us_cold": a32["us_cold"],
+                "achieved_gbs": a32["gbs_cold"], "frac": a32["hbm_frac_cold"],
+                "frac_of_attainable": None if peaks is None else round(a32["gbs_cold"] / peaks["hbm_read_gbs"], 4)}
         if peaks is not None:
             line["attainable_peaks"] = peaks
             line["roofline"]["attainable_peak"] = peaks["hbm_read_gbs"]

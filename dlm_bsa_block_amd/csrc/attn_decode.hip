@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
   }
 }
 
-// Decode attention for launches with many lists (bf16, D = 128, no window):
+// Decode attention for bf16 lists with D = 128 (and their sliding windows):
 // the same slices, partials and merge as decode_kernel, with the vector work
 // per token cut.  Per chunk of 128 list tokens each wave takes 32 keys:
 //  * scores on the matrix cores: S^T (16 keys x 16 query columns) = K Q^T with
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 // NWAVE = 4: chunks of 128 tokens, 32 per wave (lengthened slices).  NWAVE = 1:
 // chunks of 32 tokens on wave 0 alone (the single row's 32-token slices: the
 // other waves only join the workgroup's merge).
-template <int G, bool MERGE, int NWAVE>
+template <int G, bool MERGE, int NWAVE, bool WIN>
 __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
   constexpr int D = 128;
   constexpr int CT = 32 * NWAVE;                   // tokens per chunk: 32 per working wave
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, col < G ? qw[ks] : u32x4{0u, 0u, 0u, 0u});
   const int64_t ntok = (int64_t)n_list * a.kv_block;
-  if (MERGE && ntok == 0 && item == 0) {                // nothing selected: O = 0, LSE = -inf
+  if (MERGE && !WIN && ntok == 0 && item == 0) {       // nothing selected: O = 0, LSE = -inf
     const int Hq = a.Hkv * G;
     for (int i = tid; i < G * D; i += 256) {
       const int h = i / D, d = i - h * D;
@@ -268,9 +268,20 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
       if (d == 0) a.lse[((int64_t)b * Hq + g * G + h) * a.Lq + row] = -INFINITY;
     }
   }
-  if (ntok == 0 || t_begin >= ntok) return;
-  const int64_t t_end = min(ntok, t_begin + a.tok_per_item);
+  // With a sliding window (NSA structure section) the items after the list's walk the row's
+  // window: the a.win keys ending at the row's position, key = key0 + t.
   const int sel_items = (int)((ntok + a.tok_per_item - 1) / a.tok_per_item);
+  int64_t t_lo = t_begin, t_end, key0 = -1;
+  if (WIN && item >= sel_items) {
+    const int64_t hi = min((int64_t)a.L, (int64_t)qpos + 1), lo = max((int64_t)0, hi - a.win);
+    t_lo = (int64_t)(item - sel_items) * a.tok_per_item;
+    if (t_lo >= hi - lo) return;                        // past the window
+    t_end = min(hi - lo, t_lo + a.tok_per_item);
+    key0 = lo;
+  } else {
+    if (ntok == 0 || t_begin >= ntok) return;
+    t_end = min(ntok, t_begin + a.tok_per_item);
+  }
   const uint8_t* kb = a.k + ((int64_t)b * a.ksb + (int64_t)g * a.ksh) * 2;
   const uint8_t* vb = a.v + ((int64_t)b * a.vsb + (int64_t)g * a.vsh) * 2;
   const int32_t* lst = a.idx + li * a.cap;
@@ -293,7 +304,8 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
     for (int j = 0; j < 10; ++j) {
       const int64_t t = j < 2 ? tw + 16 * j + col : tw + 4 * (j - 2) + kq;
       const int tc = (int)min(t, t_end - 1);
-      bl[j] = lst[(uint32_t)tc / (uint32_t)a.kv_block];
+      const int e = (int)((uint32_t)tc / (uint32_t)a.kv_block);
+      bl[j] = lst[WIN ? min(e, a.cap - 1) : e];        // (window items: unused, kept in the list)
     }
   };
   struct Rows {
@@ -310,8 +322,9 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
       const int64_t t = j < 2 ? tw + 16 * j + col : tw + 4 * (j - 2) + kq;
       const int tc = (int)min(t, t_end - 1);
       const int e = (int)((uint32_t)tc / (uint32_t)a.kv_block);
-      const int64_t key = (int64_t)bl[j] * a.kv_block + (tc - e * a.kv_block);
-      ok[j] = t < t_end && bl[j] >= 0 && key < a.L && (!a.causal || key <= qpos);
+      const bool wk = WIN && key0 >= 0;               // a window item: contiguous keys
+      const int64_t key = wk ? key0 + t : (int64_t)bl[j] * a.kv_block + (tc - e * a.kv_block);
+      ok[j] = t < t_end && (wk || bl[j] >= 0) && key < a.L && (!a.causal || key <= qpos);
       pos[j] = ok[j] ? (int)key : 0;
     }
 #pragma unroll
@@ -331,8 +344,8 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
   if (NWAVE == 4 || w == 0) {                           // (wave-uniform)
     int bl[10];
     Rows R;
-    fetch_idx(t_begin, bl);
-    for (int64_t c0 = t_begin; c0 < t_end; c0 += CT) {
+    fetch_idx(t_lo, bl);
+    for (int64_t c0 = t_lo; c0 < t_end; c0 += CT) {
       issue(c0, bl, R);
       if (c0 + CT < t_end) fetch_idx(c0 + CT, bl);      // uniform; arrives while this chunk is computed
       dec_wide_chunk<G>(qb, R.kf, R.vr, R.kok, R.vok, a.c2, m_run, l_run, acc, p_sh[w], al_sh[w]);
@@ -380,11 +393,23 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
     }
   }
   if (!MERGE) return;
-  if (!arrive_last(a.arrivals + li * kArrivalStride, sel_items, last_sh)) return;
+  int n_win = 0;
+  if constexpr (WIN) {
+    const int64_t hi = min((int64_t)a.L, (int64_t)qpos + 1), lo = max((int64_t)0, hi - a.win);
+    n_win = (int)((hi - lo + a.tok_per_item - 1) / a.tok_per_item);
+  }
+  if (!arrive_last(a.arrivals + li * kArrivalStride, sel_items + n_win, last_sh)) return;
   const int Hq = a.Hkv * G;
+  const float* po = a.part_o + li * a.items * G * D;
+  const float* pml = a.part_ml + li * a.items * G * 2;
   const int64_t o_off = (int64_t)b * a.osb + (int64_t)(g * G) * a.osh + (int64_t)row * a.osl;
-  merge_published<G, D>(a.part_o + li * a.items * G * D, a.part_ml + li * a.items * G * 2, sel_items, ml_sh, a.o,
-                        a.o_f32, o_off, a.osh, a.lse + ((int64_t)b * Hq + g * G) * a.Lq + row, a.Lq);
+  const int64_t r0 = ((int64_t)b * Hq + g * G) * a.Lq + row;     // head g G's (row) entry
+  if constexpr (!WIN) {
+    merge_published<G, D>(po, pml, sel_items, ml_sh, a.o, a.o_f32, o_off, a.osh, a.lse + r0, a.Lq);
+  } else {
+    merge_published_window<G, D>(po, pml, sel_items, n_win, ml_sh, a.o, a.o_f32, o_off, a.osh, a.lse + 2 * r0,
+                                 2 * (int64_t)a.Lq, a.gates ? a.gates + 2 * r0 : nullptr, 2 * (int64_t)a.Lq);
+  }
 }
 
 // Merge the split partials of active (row, head) pairs of a query block in
@@ -538,17 +563,22 @@ void launch_combine(const CombArgs& a, int odt, int B, hipStream_t s) {
 void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s) {
   dim3 grid(a.items, a.NQB, B * a.Hkv);
   const bool wide = a.tok_per_item % (kDecTok * kDecWideSub) == 0;
-  if (dt == BSA_BF16 && D == 128 && a.win == 0 && a.kv_div == 1) {
-    // bf16 lists with D = 128: the matrix-core form, on all four waves for lengthened slices
-#define BSA_DECW(GG)                                                                                         \
+  if (dt == BSA_BF16 && D == 128 && a.kv_div == 1) {
+    // bf16 lists with D = 128 (and their windows): the matrix-core form, on all four waves for
+    // lengthened slices
+#define BSA_DECW_W(GG, WW)                                                                                   \
   do {                                                                                                       \
     if (wide) {                                                                                              \
-      if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true, 4>), grid, dim3(256), 0, s, a);       \
-      else hipLaunchKernelGGL((decode_wide_kernel<GG, false, 4>), grid, dim3(256), 0, s, a);                 \
+      if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true, 4, WW>), grid, dim3(256), 0, s, a);   \
+      else hipLaunchKernelGGL((decode_wide_kernel<GG, false, 4, WW>), grid, dim3(256), 0, s, a);             \
     } else {                                                                                                 \
-      if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true, 1>), grid, dim3(256), 0, s, a);       \
-      else hipLaunchKernelGGL((decode_wide_kernel<GG, false, 1>), grid, dim3(256), 0, s, a);                 \
+      if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true, 1, WW>), grid, dim3(256), 0, s, a);   \
+      else hipLaunchKernelGGL((decode_wide_kernel<GG, false, 1, WW>), grid, dim3(256), 0, s, a);             \
     }                                                                                                        \
+  } while (0)
+#define BSA_DECW(GG)                                                                                         \
+  do {                                                                                                       \
+    if (a.win > 0) BSA_DECW_W(GG, true); else BSA_DECW_W(GG, false);                                        \
   } while (0)
     switch (G) {
       case 1: BSA_DECW(1); break;
@@ -557,6 +587,7 @@ void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s)
       default: BSA_DECW(8); break;
     }
 #undef BSA_DECW
+#undef BSA_DECW_W
     return;
   }
 #define BSA_DEC(DT, DD, GG)                                                                                     \
