@@ -223,9 +223,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 // The scores are bf16 products summed in fp32 on the matrix core, then scaled
 // by scale * log2 e (decode_kernel scales q first); both are within the
 // rounding of fp32 accumulation of the same products.
-// NWAVE = 4: chunks of 128 tokens, 32 per wave (lengthened slices).  NWAVE = 1:
-// chunks of 32 tokens on wave 0 alone (the single row's 32-token slices: the
-// other waves only join the workgroup's merge).
+// Chunks of 32 NWAVE tokens, 32 per working wave: NWAVE = 4 on lengthened
+// slices; NWAVE = 2 on a single row's 64-token slices, NWAVE = 1 on 32-token
+// slices (the other waves only join the workgroup's merge).
 template <int G, bool MERGE, int NWAVE, bool WIN>
 __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
   constexpr int D = 128;
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecArgs a) {
       R.vr[rd] = *reinterpret_cast<const u32x4*>(vb + ((int64_t)pos[2 + rd] * a.vsl + 8 * col) * 2);
     }
   };
-  if (NWAVE == 4 || w == 0) {                           // (wave-uniform)
+  if (w < NWAVE) {                                      // (wave-uniform)
     int bl[10];
     Rows R;
     fetch_idx(t_lo, bl);
@@ -571,6 +571,9 @@ void launch_decode(const DecArgs& a, int dt, int D, int G, int B, hipStream_t s)
     if (wide) {                                                                                              \
       if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true, 4, WW>), grid, dim3(256), 0, s, a);   \
       else hipLaunchKernelGGL((decode_wide_kernel<GG, false, 4, WW>), grid, dim3(256), 0, s, a);             \
+    } else if (a.tok_per_item % 64 == 0) {                                                                   \
+      if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true, 2, WW>), grid, dim3(256), 0, s, a);   \
+      else hipLaunchKernelGGL((decode_wide_kernel<GG, false, 2, WW>), grid, dim3(256), 0, s, a);             \
     } else {                                                                                                 \
       if (a.arrivals) hipLaunchKernelGGL((decode_wide_kernel<GG, true, 1, WW>), grid, dim3(256), 0, s, a);   \
       else hipLaunchKernelGGL((decode_wide_kernel<GG, false, 1, WW>), grid, dim3(256), 0, s, a);             \

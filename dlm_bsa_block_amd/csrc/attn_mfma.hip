@@ -690,7 +690,9 @@ bool plan_attention(const bsa_tensor& q, const bsa_tensor& k, const bsa_attn_par
   if (p.q_block == 1) {
     pl.kind = 0;
     const int64_t toks = (int64_t)p.cap * p.kv_block;
-    pl.tok_per_item = (int)dec_slice_tokens(toks, (int64_t)pl.B * pl.Hkv * pl.NQB);
+    const bool mfma_form = q.dtype == BSA_BF16 && q.D == 128;
+    pl.tok_per_item = (int)dec_slice_tokens(toks, (int64_t)pl.B * pl.Hkv * pl.NQB,
+                                            mfma_form ? kDecMinSliceMfma : kDecMinSlice);
     pl.items = (int)ceil_div(toks, pl.tok_per_item) + (win > 0 ? (int)ceil_div(win, pl.tok_per_item) : 0);
     pl.qv = pl.G;
   } else if (p.q_block * pl.G <= 128 && p.q_block <= 64) {

@@ -15,6 +15,7 @@ namespace bsa {
 constexpr int kDecTok = 32;         // list tokens per decode chunk (4 waves x 8 tokens)
 constexpr int kDecMaxItems = 512;   // decode slices per (row, group)
 constexpr int kDecMinSlice = 32;    // list tokens per decode slice, at least
+constexpr int kDecMinSliceMfma = 64;  // ... for the matrix-core form of the attention entry point
 constexpr int kDecLaunchWG = 512;   // decode workgroups per launch beyond which slices lengthen
 constexpr int kDecWideSub = 4;      // sub-chunks per chunk of a lengthened slice
 constexpr int kSplitBlocks = 16;    // list entries per MFMA split workgroup, at most
@@ -35,15 +36,16 @@ __host__ __device__ __forceinline__ int split_per(int n, int items) {
 // partial store, arrival count), so one launch with many lists (a batch of
 // decode rows) gives each workgroup more chunks, keeping the launch near
 // kDecLaunchWG workgroups; a single decode row keeps 32-token slices, which
-// spread its few lists over the most CUs.  A lengthened slice is a whole
+// spread its few lists over the most CUs (64 tokens for the matrix-core form of
+// the attention entry point, half the partials).  A lengthened slice is a whole
 // number of kDecWideSub-sub-chunk chunks, whose K/V rows a workgroup requests
 // at once.
-inline int64_t dec_slice_tokens(int64_t toks, int64_t lists) {
+inline int64_t dec_slice_tokens(int64_t toks, int64_t lists, int min_slice = kDecMinSlice) {
   const int64_t chunks = (toks + kDecTok - 1) / kDecTok;
-  int64_t per = std::max<int64_t>(kDecMinSlice / kDecTok, (chunks + kDecMaxItems - 1) / kDecMaxItems);
+  int64_t per = std::max<int64_t>(min_slice / kDecTok, (chunks + kDecMaxItems - 1) / kDecMaxItems);
   const int64_t share = std::max<int64_t>(1, kDecLaunchWG / std::max<int64_t>(1, lists));
   const int64_t want = (chunks + share - 1) / share;
-  if (want > per) per = (want + kDecWideSub - 1) / kDecWideSub * kDecWideSub;
+  if (want > 1) per = std::max<int64_t>(per, (want + kDecWideSub - 1) / kDecWideSub * kDecWideSub);
   return per * kDecTok;
 }
 

@@ -338,9 +338,10 @@ def test_attention_workspace_layout(lib):
     COUNTERS = 65536
     pd = bsa.attn_params(kv_block=64, q_block=1, cap=16)
     k = _t(H=8, Lq=65536)
-    # decode, 32 slices of 32 tokens per (row, group): partials of 8 rows x 32 slices x 4 heads
+    # decode of bf16 rows with D = 128 (the matrix-core form): 16 slices of 64 tokens per (row, group),
+    # partials of 8 rows x 16 slices x 4 heads
     one = lib.bsa_attention_workspace_bytes(ctypes.byref(_t(H=32, Lq=1)), ctypes.byref(k), ctypes.byref(pd))
-    parts = 8 * 32 * 4
+    parts = 8 * 16 * 4
     assert one == COUNTERS + ((parts * 128 * 4 + 255) // 256) * 256 + ((parts * 2 * 4 + 255) // 256) * 256
     # more rows than counters (8 x 129 > 1024): the region is still there, the combine merges instead;
     # with 1032 lists in one launch each list is one slice of all its 1024 tokens (a launch with
